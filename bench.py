@@ -1,0 +1,174 @@
+"""Benchmark: one GPTQ layer step on one MI355X.
+
+A step is the whole path on the 4096 x 4096 attention-projection workload:
+Hessian H = 2 X^T X from 131072 bf16 calibration tokens, then quantize_layer
+(damping, factorisation, blocked column sweep with trailing updates, packing)
+at 4 bits, group 128, block 128. Inputs are resident in HBM before the timed
+region; every step recomputes everything from X and W.
+
+Prints one JSON line (see the design doc for the fields).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GPTQ layer time & quantized weights/s (4096², 4-bit g128); Hessian TFLOP/s"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(wl, X_vals, p, sample_tokens=4096, sample_rows=64):
+    """The float64 oracle, untuned, on a bounded sample of the same workload,
+    scaled to the whole layer step."""
+    import numpy as np
+    from oracle import gptq_f64 as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = sum(i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas") or None
+    except Exception:
+        cores = None
+    T, n = X_vals.shape
+    t0 = time.perf_counter()
+    Hs = O.hessian(X_vals[:sample_tokens])
+    t_h = (time.perf_counter() - t0) * (T / sample_tokens)
+    t0 = time.perf_counter()
+    Hd, perm = O.prepare(Hs, p["damp"], p["act_order"], wl.n_quant)
+    U = O.upper_chol_of_inverse(Hd)
+    t_f = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.gptq_o2(wl.W[:sample_rows], Hs, p["bits"], p["group"], p["damp"], p["block"], p["act_order"],
+              wl.n_quant, U=U, perm=perm)
+    t_s = (time.perf_counter() - t0) * (wl.d_out / sample_rows)
+    total = t_h + t_f + t_s
+    return {
+        "value": wl.d_out * wl.n_quant / total, "unit": "weights/s", "cores": cores, "kind": "oracle",
+        "sample": (f"Hessian on {sample_tokens} of {T} tokens (time x{T // sample_tokens}); "
+                   f"factorisation at full n={n}; sweep on {sample_rows} of {wl.d_out} rows "
+                   f"(time x{wl.d_out // sample_rows}); float64 numpy"),
+        "seconds_est": {"hessian": t_h, "factor": t_f, "sweep": t_s, "step": total},
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
+              "(the multi-GPU layout is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import post_weight_quantization_28_amd as G
+    import synth
+
+    if not os.path.exists(G.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    G.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    log("bench: generating the 4096x4096 layer and 131072x4096 bf16 calibration tokens")
+    t0 = time.perf_counter()
+    wl = synth.make_workload("c2")
+    p = wl.params
+    log(f"bench: inputs ready in {time.perf_counter() - t0:.1f} s")
+    W = torch.from_numpy(wl.W_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    X = torch.from_numpy(wl.X_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    T, n = X.shape
+    d_out = W.shape[0]
+    nq = wl.n_quant
+
+    H = torch.empty((n, n), dtype=torch.float32, device=dev)
+    ws_h = torch.empty(G.hessian_workspace_bytes(T, n, torch.bfloat16), dtype=torch.uint8, device=dev)
+    params = G.make_params(p["bits"], p["group"], p["damp"], p["block"], p["act_order"], nq, n)
+    ws_q = torch.empty(G.workspace_bytes(d_out, n, params), dtype=torch.uint8, device=dev)
+    outs = {
+        "qweight": torch.empty((d_out, (nq * p["bits"] + 31) // 32), dtype=torch.int32, device=dev),
+        "scales": torch.empty((d_out, nq // p["group"]), dtype=torch.float32, device=dev),
+        "zeros": torch.empty((d_out, nq // p["group"]), dtype=torch.uint8, device=dev),
+        "g_idx": torch.empty((nq,), dtype=torch.int32, device=dev),
+        "w_hat": torch.empty((d_out, n), dtype=torch.float32, device=dev),
+        "row_loss": torch.empty((d_out,), dtype=torch.float32, device=dev),
+    }
+
+    def step():
+        G.accumulate_hessian(X, H=H, zero_first=True, workspace=ws_h)
+        G.quantize_layer(W, H, bits=p["bits"], group=p["group"], damp=p["damp"], block=p["block"],
+                         act_order=p["act_order"], n_quant=nq, workspace=ws_q, outputs=outs)
+
+    for i in range(args.warmup):
+        step()
+        log(f"bench: warmup {i + 1}/{args.warmup}")
+    torch.cuda.synchronize()
+
+    G.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    prof = G.profile_collect()
+    G.profile_enable(False)
+    log(f"bench: {args.steps} steps in {elapsed:.3f} s")
+
+    ms_step = 1e3 * elapsed / args.steps
+    per_class = {k: (v[0] / args.steps) for k, v in prof.items()}
+    syrk_ms, syrk_n = prof["hessian_syrk"]
+    syrk_avg_s = syrk_ms / max(syrk_n, 1) / 1e3
+    hess_flops = float(T) * n * (n + 1)        # symmetric count per launch
+    achieved = hess_flops / syrk_avg_s / 1e12
+    hess_ms = per_class["hessian_syrk"] + per_class["hessian_reduce"]
+    quant_ms = sum(v for k, v in per_class.items() if not k.startswith("hessian"))
+    line = {
+        "metric": METRIC,
+        "value": d_out * nq / (ms_step / 1e3),
+        "unit": "weights/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "attention-projection GPTQ layer: W 4096x4096 bf16, X 131072x4096 bf16 "
+                               "Student-t(4) with 41 outlier channels x30; 4-bit asymmetric, group 128, "
+                               "block 128, damp 0.01, act-order off",
+                   "d_out": d_out, "d_in": n, "tokens": T, "bits": p["bits"], "group": p["group"],
+                   "block": p["block"], "damp": p["damp"], "act_order": p["act_order"],
+                   "parallelism": "single GPU"},
+        "hessian_tflops": hess_flops / (hess_ms / 1e3) / 1e12,
+        "hessian_ms": hess_ms,
+        "quantize_ms_kernels": quant_ms,
+        "kernel_ms_per_step": per_class,
+        "roofline": {"bound": "mfma", "kernel": "k_hessian_bf16", "achieved": achieved,
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        log("bench: timing the float64 oracle on a bounded sample (cpu_baseline)")
+        line["cpu_baseline"] = cpu_baseline(wl, wl.X, p)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,177 @@
+/*
+ * gptq.h - C ABI of the MI355X (gfx950) GPTQ layer quantizer.
+ *
+ * The method (pages cited by title and section):
+ *  - "GPTQ" (wikiprompt.org), "Enfoque Técnico": second-order (Hessian)
+ *    information of the layer loss; weight columns are quantized one at a
+ *    time and the columns not yet quantized receive a closed-form correction
+ *    derived from Optimal Brain Quantization; grouped quantization with a
+ *    scale per group; 4, 3 and 2 bits.
+ *  - "El balance de errores de la inferencia de pocos bits" (auturnal.com),
+ *    section 1: uniform affine format with a scale and a zero point; a
+ *    format must state its signed range, grouping direction, group size,
+ *    scale precision, rounding rule, clipping method and packing layout.
+ *  - "Resumen Técnico: GPTQ-intrinsic LoRA" (gist.science 2606.01412),
+ *    "Declaración del Problema": the objective ||X W - X W_hat||_F^2 over a
+ *    calibration matrix X; "Metodología" 2: standard GPTQ factorises the
+ *    regularised Hessian by Cholesky with a parameter lambda, and the
+ *    augmented variant appends full-precision columns that are never rounded.
+ *
+ * Format fixed by this library (the pages leave these open):
+ *  - H = 2 X^T X, fp32, full symmetric n x n, row-major.
+ *  - lambda = damp * mean(diag H); a zero diagonal entry is replaced by 1
+ *    before ordering and damping.
+ *  - groups: g consecutive columns of one output row, in processing order;
+ *    range = [min(0, min v), max(0, max v)] of the group's current values
+ *    when the sweep reaches its first column, (-1, 1) if degenerate; no
+ *    clipping search. s = (xmax - xmin) / (2^b - 1) (fp32),
+ *    z = rint(-xmin / s) stored as uint8 in [0, 2^b - 1],
+ *    q = clamp(rint(w / s) + z, 0, 2^b - 1), rint = round half to even,
+ *    reconstruction s * (q - z). Codes are unsigned.
+ *  - act_order: columns 0..n_quant-1 processed by descending diag(H)
+ *    (stable); columns n_quant..n-1 stay last.
+ *  - packing: per row, code k (original column order) occupies bits
+ *    [k*b, k*b + b) of an LSB-first stream of little-endian uint32 words;
+ *    ceil(n_quant*b/32) words per row; codes may straddle two words.
+ *
+ * Conventions for every call:
+ *  - Matrices are row-major. W is d_out x n (PyTorch Linear layout), X is
+ *    T x n. All data pointers are DEVICE pointers owned by the caller; the
+ *    library never allocates or frees device memory. Scratch memory is the
+ *    caller's ``workspace`` (size from the matching *_workspace_bytes call,
+ *    256-byte aligned base).
+ *  - ``stream`` is a hipStream_t (NULL = the legacy default stream). Work is
+ *    enqueued on it in order.
+ *  - Argument errors return GPTQ_EINVAL before anything is enqueued.
+ *  - HIP launch or runtime errors return GPTQ_EHIP; gptq_last_error() gives
+ *    the text (thread-local).
+ */
+#ifndef GPTQ_MI355X_H
+#define GPTQ_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GPTQ_OK = 0,
+  GPTQ_EINVAL = -1,      /* bad argument; nothing enqueued */
+  GPTQ_ENOTPD = -2,      /* damped Hessian not positive definite */
+  GPTQ_ENONFINITE = -3,  /* NaN/Inf in W or H */
+  GPTQ_EHIP = -4,        /* HIP runtime or launch failure */
+  GPTQ_EWORKSPACE = -5   /* workspace NULL, misaligned or too small */
+} gptq_status;
+
+typedef enum { GPTQ_BF16 = 0, GPTQ_F32 = 1 } gptq_dtype;
+
+typedef struct {
+  uint32_t struct_size; /* sizeof(gptq_params) */
+  int32_t bits;         /* 2, 3 or 4 */
+  int32_t group;        /* g >= 1; n_quant % g == 0; g % block == 0 or block % g == 0 */
+  float damp;           /* lambda = damp * mean(diag H); >= 0, finite */
+  int32_t block;        /* lazy-batch width B: 32, 64 or 128 */
+  int32_t act_order;    /* 0 or 1 */
+  int64_t n_quant;      /* 1..n; columns n_quant..n-1 receive feedback only */
+} gptq_params;
+
+typedef struct {
+  /* all device pointers, caller-allocated; NULL = not wanted (except where noted) */
+  uint32_t *qweight; /* d_out x ceil(n_quant*bits/32) packed codes, original column order */
+  uint8_t *codes;    /* d_out x n_quant unpacked codes, original column order */
+  float *scales;     /* REQUIRED: d_out x (n_quant/group), group order (processing order) */
+  uint8_t *zeros;    /* REQUIRED: d_out x (n_quant/group), integer zero points */
+  int32_t *g_idx;    /* n_quant: group index of each original column */
+  float *w_hat;      /* d_out x n: s*(q-z) for quantized columns, the fp32
+                        feedback-updated values for columns >= n_quant;
+                        original column order */
+  float *row_loss;   /* d_out: sum over the row's columns of e_j^2,
+                        e_j = (w_j - w_hat_j) / U_jj */
+} gptq_outputs;
+
+/* ---- Hessian accumulation ------------------------------------------------
+ * H (n x n fp32, row-major, ld = n) += 2 X^T X, or H = 2 X^T X when
+ * zero_first != 0. X: T x n, row stride ldx >= n elements, dtype xdt
+ * (bf16 products are exact in fp32; accumulation is fp32, split over token
+ * chunks and summed in a fixed order: results are bitwise reproducible).
+ * H stays exactly symmetric. T == 0 only applies zero_first.
+ * Asynchronous on ``stream``. Workspace: gptq_hessian_workspace_bytes.
+ * ("GPTQ", "Enfoque Técnico": second-order information; factor 2 and fp32
+ * storage are this library's convention.) */
+gptq_status gptq_hessian_workspace_bytes(int64_t T, int64_t n, gptq_dtype xdt,
+                                         size_t *bytes);
+gptq_status gptq_accumulate_hessian(void *stream, const void *X, gptq_dtype xdt,
+                                    int64_t T, int64_t n, int64_t ldx, float *H,
+                                    int zero_first, void *workspace,
+                                    size_t workspace_bytes);
+
+/* ---- Layer quantization ----------------------------------------------------
+ * GPTQ of W (d_out x n, dtype wdt, row stride ldw >= n) against H (n x n fp32,
+ * symmetric, not modified). Steps: dead-column fix and damping, optional
+ * act-order, upper Cholesky factor U of (H + lambda I)^-1 (U^T U = H_d^-1),
+ * column sweep in blocks of B with in-block error feedback and a lazy-batch
+ * trailing update, then un-permutation and packing.
+ * Synchronises ``stream`` before returning to read the device status:
+ * GPTQ_ENOTPD / GPTQ_ENONFINITE set *fail_col (if fail_col != NULL) to the
+ * first offending ORIGINAL column (-1 if unknown); outputs are then
+ * unspecified. d_out == 0 is a no-op. */
+gptq_status gptq_workspace_bytes(int64_t d_out, int64_t n, const gptq_params *p,
+                                 size_t *bytes);
+gptq_status gptq_quantize_layer(void *stream, const void *W, gptq_dtype wdt,
+                                int64_t d_out, int64_t n, int64_t ldw,
+                                const float *H, const gptq_params *p,
+                                void *workspace, size_t workspace_bytes,
+                                const gptq_outputs *out, int64_t *fail_col);
+
+/* ---- The factorisation alone (steps 2-3 of quantize_layer) ----------------
+ * U_out (n x n fp32 row-major): upper Cholesky factor of the damped,
+ * dead-fixed, (optionally) act-order-permuted H's inverse, in processing
+ * order (strict lower part zero). perm_out (n int32, may be NULL): original
+ * column at each processing position. Same workspace as quantize_layer with
+ * d_out = 0 is NOT enough: use gptq_workspace_bytes(0, n, p, ...) + 0 (it
+ * accounts for the factor buffers). Synchronises like quantize_layer.
+ * ("Resumen Técnico: GPTQ-intrinsic LoRA", "Detalles de Implementación":
+ * Cholesky of the regularised Hessian.) */
+gptq_status gptq_factor_hinv(void *stream, const float *H, int64_t n,
+                             const gptq_params *p, void *workspace,
+                             size_t workspace_bytes, float *U_out,
+                             int32_t *perm_out, int64_t *fail_col);
+
+/* ---- Packing (the layout above) -------------------------------------------
+ * codes: d_out x n_quant uint8 (values must be < 2^bits; higher bits are
+ * masked off), qweight: d_out x ceil(n_quant*bits/32) uint32. Asynchronous. */
+gptq_status gptq_pack_codes(void *stream, const uint8_t *codes, int64_t d_out,
+                            int64_t n_quant, int32_t bits, uint32_t *qweight);
+gptq_status gptq_unpack_codes(void *stream, const uint32_t *qweight,
+                              int64_t d_out, int64_t n_quant, int32_t bits,
+                              uint8_t *codes);
+
+/* ---- Diagnostics ------------------------------------------------------------ */
+const char *gptq_status_string(int status);
+const char *gptq_last_error(void); /* thread-local detail of the last failure */
+
+/* Kernel timing with hipEvents recorded on the caller's stream around each
+ * launch, by kernel class. enable != 0 starts recording (and clears what was
+ * recorded); gptq_profile_collect synchronises the recorded events and
+ * returns, for class c in [0, GPTQ_PROF_NCLASSES), the summed milliseconds
+ * and launch count, then clears. */
+enum {
+  GPTQ_PROF_HESSIAN_SYRK = 0,
+  GPTQ_PROF_HESSIAN_REDUCE = 1,
+  GPTQ_PROF_PREP = 2,
+  GPTQ_PROF_FACTOR_LEAF = 3,
+  GPTQ_PROF_FACTOR_GEMM = 4,
+  GPTQ_PROF_SWEEP = 5,
+  GPTQ_PROF_TRAILING = 6,
+  GPTQ_PROF_PACK = 7,
+  GPTQ_PROF_NCLASSES = 8
+};
+gptq_status gptq_profile_enable(int enable);
+gptq_status gptq_profile_collect(double *ms, int64_t *count);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPTQ_MI355X_H */

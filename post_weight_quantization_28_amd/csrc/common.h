@@ -1,0 +1,99 @@
+// Internal declarations shared by the HIP translation units of libgptq.
+// Each .hip file owns its kernels and exposes host-side launchers; the C ABI
+// in gptq_abi.cpp only calls launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace gq {
+
+// Device-side status written by kernels: flags (bit 0: not positive
+// definite, bit 1: non-finite input) and the smallest
+// ORIGINAL column that raised it.
+struct DevStatus {
+  int flags;
+  int pad;
+  unsigned long long col;
+};
+constexpr int kNotPD = 1;
+constexpr int kNonFinite = 2;
+
+__device__ inline void raise_status(DevStatus* st, int flag, long long col) {
+  atomicOr(&st->flags, flag);
+  atomicMin(&st->col, (unsigned long long)col);
+}
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---- hessian.hip
+// Token-chunk splits used for n x n fp32 partials (fixed per (T, dtype)).
+int hessian_splits(int64_t T, int xdt_bf16);
+hipError_t launch_hessian_partials_bf16(hipStream_t s, const uint16_t* X, int64_t T,
+                                        int64_t n, int64_t ldx, float* part, int splits);
+hipError_t launch_hessian_partials_f32(hipStream_t s, const float* X, int64_t T,
+                                       int64_t n, int64_t ldx, float* part, int splits);
+hipError_t launch_hessian_reduce(hipStream_t s, const float* part, int splits, int64_t n,
+                                 float* H, int zero_first);
+
+// ---- prep.hip
+hipError_t launch_fill_f32(hipStream_t s, float* p, size_t count, float v);
+hipError_t launch_prep_diag(hipStream_t s, const float* H, int64_t n, float* diag,
+                            double* lam_out, float damp, DevStatus* st);
+hipError_t launch_order(hipStream_t s, const float* diag, int64_t n, int64_t n_quant,
+                        int act_order, int32_t* perm, int32_t* invperm);
+hipError_t launch_build_flipped(hipStream_t s, const float* H, int64_t n, const int32_t* perm,
+                                const float* diag, const double* lam, float* A,
+                                DevStatus* st);
+hipError_t launch_w_prep(hipStream_t s, const void* W, int wdt_bf16, int64_t d_out,
+                         int64_t n, int64_t ldw, const int32_t* perm, float* Wf,
+                         DevStatus* st);
+hipError_t launch_status_init(hipStream_t s, DevStatus* st);
+
+// ---- factor.hip
+constexpr int kLeaf = 64;
+hipError_t launch_leaf(hipStream_t s, float* A, float* X, int64_t n, int64_t off, int64_t m,
+                       const int32_t* perm, DevStatus* st);
+// C[M x N] = alpha * op(A) * op(B) + beta * C, fp32 MFMA.
+//  ta: A stored K x M (element (m,k) at A[k*lda + m]) instead of M x K
+//  tb: B stored N x K (element (k,n) at B[n*ldb + k]) instead of K x N
+//  kmode: 0 full K; 1 k < (column-tile end); 2 k >= (column-tile start);
+//         3 k < (row-tile end)   (triangular operands with zero fill)
+//  lower_only: skip tiles strictly above the diagonal (square tiles)
+struct GemmArgs {
+  int64_t M, N, K;
+  const float* A; int64_t lda; int ta;
+  const float* B; int64_t ldb; int tb;
+  float* C; int64_t ldc;
+  float alpha, beta;
+  int kmode, lower_only;
+  const DevStatus* st;   // if non-null and flagged, the kernel returns at once
+};
+hipError_t launch_gemm_f32(hipStream_t s, const GemmArgs& g);
+hipError_t launch_rotate(hipStream_t s, const float* X, float* U, int64_t n);
+
+// ---- sweep.hip
+struct SweepArgs {
+  float* Wf; int64_t ldw;       // d_out x n working weights (processing order)
+  const float* U; int64_t ldu;  // n x n upper factor
+  int64_t d_out, i0, ncols;     // block [i0, i0 + ncols)
+  int block;                    // B
+  int group, bits;
+  float* scales; uint8_t* zeros; int64_t ngroups;
+  uint8_t* codes; int64_t n_quant;   // processing order, d_out x n_quant
+  float* E;                     // d_out x B
+  float* row_loss;
+  const DevStatus* st;
+};
+hipError_t launch_sweep(hipStream_t s, const SweepArgs& a);
+
+// ---- pack.hip
+hipError_t launch_pack(hipStream_t s, const uint8_t* codes, int64_t ldc, const int32_t* invperm,
+                       int64_t d_out, int64_t n_quant, int bits, uint32_t* qweight);
+hipError_t launch_unpack(hipStream_t s, const uint32_t* qweight, int64_t d_out, int64_t n_quant,
+                         int bits, uint8_t* codes);
+hipError_t launch_finish(hipStream_t s, const float* Wf, const uint8_t* codes_p,
+                         const int32_t* invperm, int64_t d_out, int64_t n, int64_t n_quant,
+                         int group, float* w_hat, uint8_t* codes_out, int32_t* g_idx);
+
+}  // namespace gq

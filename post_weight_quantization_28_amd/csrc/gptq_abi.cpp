@@ -1,0 +1,420 @@
+// C ABI of libgptq: argument validation, workspace carving, launch order,
+// kernel timing. Every step of the computation runs in the HIP kernels of
+// the sibling .hip files; this file only sequences them on the caller's
+// stream. Declarations and the contract are in include/gptq.h.
+#include "../../include/gptq.h"
+#include "common.h"
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+using namespace gq;
+
+namespace {
+
+thread_local std::string g_err;
+
+gptq_status fail(gptq_status st, const char* msg) {
+  g_err = msg;
+  return st;
+}
+
+gptq_status hip_fail(hipError_t e, const char* where) {
+  g_err = std::string(where) + ": " + hipGetErrorString(e);
+  return GPTQ_EHIP;
+}
+
+#define HIP_TRY(expr, where)                   \
+  do {                                         \
+    hipError_t _e = (expr);                    \
+    if (_e != hipSuccess) return hip_fail(_e, where); \
+  } while (0)
+
+// ---------------------------------------------------------------- timing
+struct ProfRec {
+  int cls;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof_recs;
+std::vector<hipEvent_t> g_prof_pool;
+
+hipEvent_t prof_event() {
+  if (!g_prof_pool.empty()) {
+    hipEvent_t e = g_prof_pool.back();
+    g_prof_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Records a start event on construction and a stop event on destruction
+// when timing is enabled.
+class Timed {
+ public:
+  Timed(int cls, hipStream_t s) : cls_(cls), s_(s) {
+    if (!g_prof_on) return;
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    a_ = prof_event();
+    b_ = prof_event();
+    if (a_ && b_) hipEventRecord(a_, s_);
+  }
+  ~Timed() {
+    if (!a_ || !b_) return;
+    hipEventRecord(b_, s_);
+    std::lock_guard<std::mutex> lk(g_prof_mu);
+    g_prof_recs.push_back({cls_, a_, b_});
+  }
+
+ private:
+  int cls_;
+  hipStream_t s_;
+  hipEvent_t a_ = nullptr, b_ = nullptr;
+};
+
+// ---------------------------------------------------------------- workspace
+struct Carver {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) / 256 * 256;
+    return o;
+  }
+};
+
+struct QLayout {
+  size_t status, lam, diag, perm, invperm, A, X, Wf, E, codes, loss, total;
+};
+
+QLayout q_layout(int64_t d_out, int64_t n, const gptq_params* p) {
+  QLayout L{};
+  Carver c;
+  L.status = c.take(sizeof(DevStatus));
+  L.lam = c.take(sizeof(double));
+  L.diag = c.take(sizeof(float) * n);
+  L.perm = c.take(sizeof(int32_t) * n);
+  L.invperm = c.take(sizeof(int32_t) * n);
+  L.A = c.take(sizeof(float) * n * n);
+  L.X = c.take(sizeof(float) * n * n);
+  L.Wf = c.take(sizeof(float) * d_out * n);
+  L.E = c.take(sizeof(float) * d_out * p->block);
+  L.codes = c.take((size_t)d_out * p->n_quant);
+  L.loss = c.take(sizeof(float) * d_out);
+  L.total = c.off;
+  return L;
+}
+
+gptq_status check_params(int64_t d_out, int64_t n, const gptq_params* p) {
+  if (!p) return fail(GPTQ_EINVAL, "params is NULL");
+  if (p->struct_size < sizeof(gptq_params)) return fail(GPTQ_EINVAL, "params.struct_size too small");
+  if (d_out < 0 || n < 1) return fail(GPTQ_EINVAL, "need d_out >= 0 and n >= 1");
+  if (n > (int64_t)1 << 30 || d_out > (int64_t)1 << 30) return fail(GPTQ_EINVAL, "dimension too large");
+  if (p->bits < 2 || p->bits > 4) return fail(GPTQ_EINVAL, "bits must be 2, 3 or 4");
+  if (p->block != 32 && p->block != 64 && p->block != 128)
+    return fail(GPTQ_EINVAL, "block must be 32, 64 or 128");
+  if (p->n_quant < 1 || p->n_quant > n) return fail(GPTQ_EINVAL, "n_quant must be in [1, n]");
+  if (p->group < 1) return fail(GPTQ_EINVAL, "group must be >= 1");
+  if (p->n_quant % p->group != 0) return fail(GPTQ_EINVAL, "group must divide n_quant");
+  if (!(p->group % p->block == 0 || p->block % p->group == 0))
+    return fail(GPTQ_EINVAL, "group and block must nest (one divides the other)");
+  if (!(p->damp >= 0.f) || !std::isfinite(p->damp)) return fail(GPTQ_EINVAL, "damp must be finite and >= 0");
+  if (p->act_order != 0 && p->act_order != 1) return fail(GPTQ_EINVAL, "act_order must be 0 or 1");
+  return GPTQ_OK;
+}
+
+gptq_status check_ws(void* ws, size_t have, size_t need) {
+  if (need == 0) return GPTQ_OK;
+  if (!ws) return fail(GPTQ_EWORKSPACE, "workspace is NULL");
+  if ((uintptr_t)ws % 256 != 0) return fail(GPTQ_EWORKSPACE, "workspace must be 256-byte aligned");
+  if (have < need) return fail(GPTQ_EWORKSPACE, "workspace too small");
+  return GPTQ_OK;
+}
+
+// ---------------------------------------------------------------- factorisation
+hipError_t factor_rec(hipStream_t s, float* A, float* X, int64_t n, int64_t off, int64_t m,
+                      const int32_t* perm, DevStatus* st) {
+  if (m <= kLeaf) {
+    Timed t(GPTQ_PROF_FACTOR_LEAF, s);
+    return launch_leaf(s, A, X, n, off, m, perm, st);
+  }
+  int64_t k = ceil_div(m / 2, kLeaf) * kLeaf;
+  if (k >= m) k = m - kLeaf;
+  hipError_t e = factor_rec(s, A, X, n, off, k, perm, st);
+  if (e != hipSuccess) return e;
+  const int64_t r = m - k;
+  float* A21 = A + (off + k) * n + off;
+  float* A22 = A + (off + k) * n + off + k;
+  float* X11 = X + off * n + off;
+  float* X21 = X + (off + k) * n + off;
+  float* X22 = X + (off + k) * n + off + k;
+  {
+    Timed t(GPTQ_PROF_FACTOR_GEMM, s);
+    // T1 = A21 X11^T  (into X21's place)
+    GemmArgs g{r, k, k, A21, n, 0, X11, n, 1, X21, n, 1.f, 0.f, 1, 0, st};
+    if ((e = launch_gemm_f32(s, g)) != hipSuccess) return e;
+    // A22 -= T1 T1^T  (lower tiles)
+    GemmArgs h{r, r, k, X21, n, 0, X21, n, 1, A22, n, -1.f, 1.f, 0, 1, st};
+    if ((e = launch_gemm_f32(s, h)) != hipSuccess) return e;
+    // T2 = T1 X11  (into A21's place)
+    GemmArgs q{r, k, k, X21, n, 0, X11, n, 0, A21, n, 1.f, 0.f, 2, 0, st};
+    if ((e = launch_gemm_f32(s, q)) != hipSuccess) return e;
+  }
+  if ((e = factor_rec(s, A, X, n, off + k, r, perm, st)) != hipSuccess) return e;
+  {
+    Timed t(GPTQ_PROF_FACTOR_GEMM, s);
+    // X21 = -X22 T2
+    GemmArgs g{r, k, r, X22, n, 0, A21, n, 0, X21, n, -1.f, 0.f, 3, 0, st};
+    if ((e = launch_gemm_f32(s, g)) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Steps 2-3 shared by quantize_layer and factor_hinv. On return (enqueued)
+// the upper factor U is in the A buffer (processing order).
+gptq_status enqueue_factor(hipStream_t s, const float* H, int64_t n, const gptq_params* p,
+                           char* ws, const QLayout& L) {
+  DevStatus* st = reinterpret_cast<DevStatus*>(ws + L.status);
+  double* lam = reinterpret_cast<double*>(ws + L.lam);
+  float* diag = reinterpret_cast<float*>(ws + L.diag);
+  int32_t* perm = reinterpret_cast<int32_t*>(ws + L.perm);
+  int32_t* invperm = reinterpret_cast<int32_t*>(ws + L.invperm);
+  float* A = reinterpret_cast<float*>(ws + L.A);
+  float* X = reinterpret_cast<float*>(ws + L.X);
+  {
+    Timed t(GPTQ_PROF_PREP, s);
+    HIP_TRY(launch_status_init(s, st), "status init");
+    HIP_TRY(launch_fill_f32(s, X, (size_t)n * n, 0.f), "fill");
+    HIP_TRY(launch_prep_diag(s, H, n, diag, lam, p->damp, st), "prep diag");
+    HIP_TRY(launch_order(s, diag, n, p->n_quant, p->act_order, perm, invperm), "order");
+    HIP_TRY(launch_build_flipped(s, H, n, perm, diag, lam, A, st), "build");
+  }
+  HIP_TRY(factor_rec(s, A, X, n, 0, n, perm, st), "factor");
+  {
+    Timed t(GPTQ_PROF_PREP, s);
+    HIP_TRY(launch_rotate(s, X, A, n), "rotate");
+  }
+  return GPTQ_OK;
+}
+
+gptq_status read_status(hipStream_t s, const DevStatus* st, const int32_t* perm, int64_t* fail_col) {
+  DevStatus h{};
+  HIP_TRY(hipMemcpyAsync(&h, st, sizeof(h), hipMemcpyDeviceToHost, s), "status copy");
+  HIP_TRY(hipStreamSynchronize(s), "synchronize");
+  (void)perm;
+  if (h.flags == 0) return GPTQ_OK;
+  if (fail_col) *fail_col = (h.col == ~0ull) ? -1 : (int64_t)h.col;
+  if (h.flags & kNonFinite) return fail(GPTQ_ENONFINITE, "non-finite value in W or H");
+  return fail(GPTQ_ENOTPD, "damped Hessian is not positive definite");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gptq_status_string(int status) {
+  switch (status) {
+    case GPTQ_OK: return "ok";
+    case GPTQ_EINVAL: return "invalid argument";
+    case GPTQ_ENOTPD: return "damped Hessian not positive definite";
+    case GPTQ_ENONFINITE: return "non-finite input";
+    case GPTQ_EHIP: return "HIP error";
+    case GPTQ_EWORKSPACE: return "workspace missing, misaligned or too small";
+    default: return "unknown status";
+  }
+}
+
+const char* gptq_last_error(void) { return g_err.c_str(); }
+
+gptq_status gptq_profile_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (auto& r : g_prof_recs) {
+    g_prof_pool.push_back(r.a);
+    g_prof_pool.push_back(r.b);
+  }
+  g_prof_recs.clear();
+  g_prof_on = enable != 0;
+  return GPTQ_OK;
+}
+
+gptq_status gptq_profile_collect(double* ms, int64_t* count) {
+  if (!ms || !count) return fail(GPTQ_EINVAL, "NULL output");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  for (int c = 0; c < GPTQ_PROF_NCLASSES; ++c) {
+    ms[c] = 0.0;
+    count[c] = 0;
+  }
+  for (auto& r : g_prof_recs) {
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e != hipSuccess) return hip_fail(e, "event sync");
+    float t = 0.f;
+    e = hipEventElapsedTime(&t, r.a, r.b);
+    if (e != hipSuccess) return hip_fail(e, "event elapsed");
+    ms[r.cls] += t;
+    count[r.cls] += 1;
+    g_prof_pool.push_back(r.a);
+    g_prof_pool.push_back(r.b);
+  }
+  g_prof_recs.clear();
+  return GPTQ_OK;
+}
+
+gptq_status gptq_hessian_workspace_bytes(int64_t T, int64_t n, gptq_dtype xdt, size_t* bytes) {
+  if (!bytes) return fail(GPTQ_EINVAL, "bytes is NULL");
+  if (T < 0 || n < 1 || n > ((int64_t)1 << 30)) return fail(GPTQ_EINVAL, "need T >= 0, n >= 1");
+  if (xdt != GPTQ_BF16 && xdt != GPTQ_F32) return fail(GPTQ_EINVAL, "bad dtype");
+  if (T == 0) {
+    *bytes = 0;
+    return GPTQ_OK;
+  }
+  const int sp = hessian_splits(T, xdt == GPTQ_BF16);
+  *bytes = (size_t)sp * n * n * sizeof(float);
+  return GPTQ_OK;
+}
+
+gptq_status gptq_accumulate_hessian(void* stream, const void* X, gptq_dtype xdt, int64_t T, int64_t n,
+                                    int64_t ldx, float* H, int zero_first, void* workspace,
+                                    size_t workspace_bytes) {
+  hipStream_t s = (hipStream_t)stream;
+  size_t need = 0;
+  gptq_status st = gptq_hessian_workspace_bytes(T, n, xdt, &need);
+  if (st != GPTQ_OK) return st;
+  if (!H) return fail(GPTQ_EINVAL, "H is NULL");
+  if (T > 0 && !X) return fail(GPTQ_EINVAL, "X is NULL");
+  if (ldx < n) return fail(GPTQ_EINVAL, "ldx < n");
+  if ((st = check_ws(workspace, workspace_bytes, need)) != GPTQ_OK) return st;
+  if (T == 0) {
+    if (zero_first) HIP_TRY(launch_fill_f32(s, H, (size_t)n * n, 0.f), "fill");
+    return GPTQ_OK;
+  }
+  const int sp = hessian_splits(T, xdt == GPTQ_BF16);
+  float* part = reinterpret_cast<float*>(workspace);
+  {
+    Timed t(GPTQ_PROF_HESSIAN_SYRK, s);
+    if (xdt == GPTQ_BF16)
+      HIP_TRY(launch_hessian_partials_bf16(s, reinterpret_cast<const uint16_t*>(X), T, n, ldx, part, sp),
+              "hessian partials");
+    else
+      HIP_TRY(launch_hessian_partials_f32(s, reinterpret_cast<const float*>(X), T, n, ldx, part, sp),
+              "hessian partials");
+  }
+  {
+    Timed t(GPTQ_PROF_HESSIAN_REDUCE, s);
+    HIP_TRY(launch_hessian_reduce(s, part, sp, n, H, zero_first), "hessian reduce");
+  }
+  return GPTQ_OK;
+}
+
+gptq_status gptq_workspace_bytes(int64_t d_out, int64_t n, const gptq_params* p, size_t* bytes) {
+  if (!bytes) return fail(GPTQ_EINVAL, "bytes is NULL");
+  gptq_status st = check_params(d_out, n, p);
+  if (st != GPTQ_OK) return st;
+  *bytes = q_layout(d_out, n, p).total;
+  return GPTQ_OK;
+}
+
+gptq_status gptq_factor_hinv(void* stream, const float* H, int64_t n, const gptq_params* p,
+                             void* workspace, size_t workspace_bytes, float* U_out, int32_t* perm_out,
+                             int64_t* fail_col) {
+  hipStream_t s = (hipStream_t)stream;
+  gptq_status st = check_params(0, n, p);
+  if (st != GPTQ_OK) return st;
+  if (!H || !U_out) return fail(GPTQ_EINVAL, "H or U_out is NULL");
+  const QLayout L = q_layout(0, n, p);
+  if ((st = check_ws(workspace, workspace_bytes, L.total)) != GPTQ_OK) return st;
+  char* ws = reinterpret_cast<char*>(workspace);
+  if ((st = enqueue_factor(s, H, n, p, ws, L)) != GPTQ_OK) return st;
+  HIP_TRY(hipMemcpyAsync(U_out, ws + L.A, sizeof(float) * n * n, hipMemcpyDeviceToDevice, s), "copy U");
+  if (perm_out)
+    HIP_TRY(hipMemcpyAsync(perm_out, ws + L.perm, sizeof(int32_t) * n, hipMemcpyDeviceToDevice, s),
+            "copy perm");
+  return read_status(s, reinterpret_cast<DevStatus*>(ws + L.status), nullptr, fail_col);
+}
+
+gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int64_t d_out, int64_t n,
+                                int64_t ldw, const float* H, const gptq_params* p, void* workspace,
+                                size_t workspace_bytes, const gptq_outputs* out, int64_t* fail_col) {
+  hipStream_t s = (hipStream_t)stream;
+  gptq_status st = check_params(d_out, n, p);
+  if (st != GPTQ_OK) return st;
+  if (wdt != GPTQ_BF16 && wdt != GPTQ_F32) return fail(GPTQ_EINVAL, "bad dtype");
+  if (!out) return fail(GPTQ_EINVAL, "outputs is NULL");
+  if (!H) return fail(GPTQ_EINVAL, "H is NULL");
+  if (d_out == 0) return GPTQ_OK;
+  if (!W) return fail(GPTQ_EINVAL, "W is NULL");
+  if (ldw < n) return fail(GPTQ_EINVAL, "ldw < n");
+  if (!out->scales || !out->zeros) return fail(GPTQ_EINVAL, "scales and zeros are required");
+  const QLayout L = q_layout(d_out, n, p);
+  if ((st = check_ws(workspace, workspace_bytes, L.total)) != GPTQ_OK) return st;
+  if (fail_col) *fail_col = -1;
+
+  char* ws = reinterpret_cast<char*>(workspace);
+  DevStatus* dst = reinterpret_cast<DevStatus*>(ws + L.status);
+  int32_t* perm = reinterpret_cast<int32_t*>(ws + L.perm);
+  int32_t* invperm = reinterpret_cast<int32_t*>(ws + L.invperm);
+  float* U = reinterpret_cast<float*>(ws + L.A);
+  float* Wf = reinterpret_cast<float*>(ws + L.Wf);
+  float* E = reinterpret_cast<float*>(ws + L.E);
+  uint8_t* codes = reinterpret_cast<uint8_t*>(ws + L.codes);
+  float* loss = out->row_loss ? out->row_loss : reinterpret_cast<float*>(ws + L.loss);
+
+  if ((st = enqueue_factor(s, H, n, p, ws, L)) != GPTQ_OK) return st;
+  {
+    Timed t(GPTQ_PROF_PREP, s);
+    HIP_TRY(launch_w_prep(s, W, wdt == GPTQ_BF16, d_out, n, ldw, perm, Wf, dst), "w prep");
+    HIP_TRY(launch_fill_f32(s, loss, (size_t)d_out, 0.f), "fill");
+  }
+  const int64_t nq = p->n_quant;
+  const int B = p->block;
+  for (int64_t i0 = 0; i0 < nq; i0 += B) {
+    const int64_t nc = std::min<int64_t>(B, nq - i0);
+    SweepArgs a{};
+    a.Wf = Wf; a.ldw = n; a.U = U; a.ldu = n; a.d_out = d_out; a.i0 = i0; a.ncols = nc;
+    a.block = B; a.group = p->group; a.bits = p->bits;
+    a.scales = out->scales; a.zeros = out->zeros; a.ngroups = nq / p->group;
+    a.codes = codes; a.n_quant = nq; a.E = E; a.row_loss = loss; a.st = dst;
+    {
+      Timed t(GPTQ_PROF_SWEEP, s);
+      HIP_TRY(launch_sweep(s, a), "sweep");
+    }
+    const int64_t i1 = i0 + nc;
+    if (i1 < n) {
+      Timed t(GPTQ_PROF_TRAILING, s);
+      GemmArgs g{d_out, n - i1, nc, E, B, 0, U + i0 * n + i1, n, 0, Wf + i1, n, -1.f, 1.f, 0, 0, dst};
+      HIP_TRY(launch_gemm_f32(s, g), "trailing update");
+    }
+  }
+  {
+    Timed t(GPTQ_PROF_PACK, s);
+    HIP_TRY(launch_finish(s, Wf, codes, invperm, d_out, n, nq, p->group, out->w_hat, out->codes, out->g_idx),
+            "finish");
+    if (out->qweight) HIP_TRY(launch_pack(s, codes, nq, invperm, d_out, nq, p->bits, out->qweight), "pack");
+  }
+  return read_status(s, dst, perm, fail_col);
+}
+
+gptq_status gptq_pack_codes(void* stream, const uint8_t* codes, int64_t d_out, int64_t n_quant,
+                            int32_t bits, uint32_t* qweight) {
+  if (bits < 2 || bits > 4) return fail(GPTQ_EINVAL, "bits must be 2, 3 or 4");
+  if (d_out < 0 || n_quant < 0) return fail(GPTQ_EINVAL, "negative size");
+  if (d_out * n_quant > 0 && (!codes || !qweight)) return fail(GPTQ_EINVAL, "NULL pointer");
+  HIP_TRY(launch_pack((hipStream_t)stream, codes, n_quant, nullptr, d_out, n_quant, bits, qweight), "pack");
+  return GPTQ_OK;
+}
+
+gptq_status gptq_unpack_codes(void* stream, const uint32_t* qweight, int64_t d_out, int64_t n_quant,
+                              int32_t bits, uint8_t* codes) {
+  if (bits < 2 || bits > 4) return fail(GPTQ_EINVAL, "bits must be 2, 3 or 4");
+  if (d_out < 0 || n_quant < 0) return fail(GPTQ_EINVAL, "negative size");
+  if (d_out * n_quant > 0 && (!codes || !qweight)) return fail(GPTQ_EINVAL, "NULL pointer");
+  HIP_TRY(launch_unpack((hipStream_t)stream, qweight, d_out, n_quant, bits, codes), "unpack");
+  return GPTQ_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,174 @@
+// Preparation of the damped, ordered Hessian and the fp32 working weights.
+//
+// "Resumen Técnico: GPTQ-intrinsic LoRA", "Detalles de Implementación":
+// standard GPTQ regularises the Hessian with lambda before its Cholesky
+// factorisation (here lambda = damp * mean(diag H)).
+// "GPTQ" (wikiprompt.org), "Enfoque Técnico": the weights to quantize are
+// picked greedily (here: act-order, descending diag H, stable).
+//
+// The factorisation works on the index-reversed matrix A = J H_d J (J the
+// reversal permutation): the lower Cholesky factor L of A gives the upper
+// factor of H_d^{-1} as U = J L^{-1} J, so building A flipped here lets every
+// later kernel work with lower-triangular storage.
+#include "common.h"
+
+namespace gq {
+
+__global__ void k_status_init(DevStatus* st) {
+  st->flags = 0;
+  st->pad = 0;
+  st->col = ~0ull;
+}
+
+hipError_t launch_status_init(hipStream_t s, DevStatus* st) {
+  hipLaunchKernelGGL(k_status_init, dim3(1), dim3(1), 0, s, st);
+  return hipGetLastError();
+}
+
+__global__ void k_fill_f32(float* __restrict__ p, size_t count, float v) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride) p[i] = v;
+}
+
+hipError_t launch_fill_f32(hipStream_t s, float* p, size_t count, float v) {
+  if (count == 0) return hipSuccess;
+  size_t blocks = (count + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(k_fill_f32, dim3((unsigned)blocks), dim3(256), 0, s, p, count, v);
+  return hipGetLastError();
+}
+
+// diag[i] = H_ii (zero -> 1), lam = damp * mean(diag); one workgroup, fixed
+// reduction order (per-thread strided partial sums in double, then a tree).
+__global__ void __launch_bounds__(1024)
+k_prep_diag(const float* __restrict__ H, int64_t n, float* __restrict__ diag,
+            double* __restrict__ lam_out, float damp, DevStatus* st) {
+  __shared__ double red[1024];
+  double acc = 0.0;
+  for (int64_t i = threadIdx.x; i < n; i += 1024) {
+    float v = H[i * n + i];
+    if (!isfinite(v)) raise_status(st, kNonFinite, i);
+    if (v == 0.f) v = 1.f;
+    diag[i] = v;
+    acc += (double)v;
+  }
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 512; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) lam_out[0] = (double)damp * (red[0] / (double)n);
+}
+
+hipError_t launch_prep_diag(hipStream_t s, const float* H, int64_t n, float* diag,
+                            double* lam_out, float damp, DevStatus* st) {
+  hipLaunchKernelGGL(k_prep_diag, dim3(1), dim3(1024), 0, s, H, n, diag, lam_out, damp, st);
+  return hipGetLastError();
+}
+
+// Stable descending rank over the first nq diagonal entries: NaN sorts
+// last, equal keys keep index order, so the ranks are always a permutation.
+__device__ inline float order_key(float d) { return isnan(d) ? -INFINITY : d; }
+
+__global__ void __launch_bounds__(256)
+k_order(const float* __restrict__ diag, int64_t n, int64_t nq, int act_order,
+        int32_t* __restrict__ perm, int32_t* __restrict__ invperm) {
+  __shared__ float keys[1024];
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool mine = i < nq;
+  const float ki = mine ? order_key(diag[i]) : 0.f;
+  int64_t rank = 0;
+  if (act_order) {
+    for (int64_t base = 0; base < nq; base += 1024) {
+      __syncthreads();
+      for (int t = threadIdx.x; t < 1024; t += 256)
+        keys[t] = (base + t < nq) ? order_key(diag[base + t]) : 0.f;
+      __syncthreads();
+      if (mine) {
+        const int64_t lim = min((int64_t)1024, nq - base);
+        for (int64_t t = 0; t < lim; ++t) {
+          const float kj = keys[t];
+          const int64_t j = base + t;
+          rank += (kj > ki) || (kj == ki && j < i);
+        }
+      }
+    }
+  } else {
+    rank = i;
+  }
+  if (i < n) {
+    const int64_t r = mine ? rank : i;
+    perm[r] = (int32_t)i;
+    invperm[i] = (int32_t)r;
+  }
+}
+
+hipError_t launch_order(hipStream_t s, const float* diag, int64_t n, int64_t n_quant,
+                        int act_order, int32_t* perm, int32_t* invperm) {
+  hipLaunchKernelGGL(k_order, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s, diag, n,
+                     n_quant, act_order, perm, invperm);
+  return hipGetLastError();
+}
+
+// A[a][b] = H_d[p][q], p = perm[n-1-a], q = perm[n-1-b]; lower part only
+// (b <= a). The diagonal uses the dead-fixed value plus lambda.
+__global__ void __launch_bounds__(256)
+k_build_flipped(const float* __restrict__ H, int64_t n, const int32_t* __restrict__ perm,
+                const float* __restrict__ diag, const double* __restrict__ lam,
+                float* __restrict__ A, DevStatus* st) {
+  const int64_t a = blockIdx.x;
+  const int64_t p = perm[n - 1 - a];
+  const float lamf = (float)lam[0];
+  for (int64_t b = threadIdx.x; b <= a; b += 256) {
+    const int64_t q = perm[n - 1 - b];
+    float v;
+    if (b == a) {
+      v = diag[p] + lamf;
+    } else {
+      v = H[p * n + q];
+      if (!isfinite(v)) raise_status(st, kNonFinite, min(p, q));
+    }
+    A[a * n + b] = v;
+  }
+}
+
+hipError_t launch_build_flipped(hipStream_t s, const float* H, int64_t n, const int32_t* perm,
+                                const float* diag, const double* lam, float* A, DevStatus* st) {
+  hipLaunchKernelGGL(k_build_flipped, dim3((unsigned)n), dim3(256), 0, s, H, n, perm, diag, lam,
+                     A, st);
+  return hipGetLastError();
+}
+
+// Wf[r][p] = float(W[r][perm[p]])
+template <bool kBF16>
+__global__ void __launch_bounds__(256)
+k_w_prep(const void* __restrict__ Wv, int64_t n, int64_t ldw, const int32_t* __restrict__ perm,
+         float* __restrict__ Wf, DevStatus* st) {
+  const int64_t r = blockIdx.x;
+  for (int64_t p = threadIdx.x; p < n; p += 256) {
+    const int64_t c = perm[p];
+    float v;
+    if (kBF16) {
+      const uint16_t u = reinterpret_cast<const uint16_t*>(Wv)[r * ldw + c];
+      v = __uint_as_float((uint32_t)u << 16);
+    } else {
+      v = reinterpret_cast<const float*>(Wv)[r * ldw + c];
+    }
+    if (!isfinite(v)) raise_status(st, kNonFinite, c);
+    Wf[r * n + p] = v;
+  }
+}
+
+hipError_t launch_w_prep(hipStream_t s, const void* W, int wdt_bf16, int64_t d_out, int64_t n,
+                         int64_t ldw, const int32_t* perm, float* Wf, DevStatus* st) {
+  if (d_out == 0) return hipSuccess;
+  dim3 grid((unsigned)d_out);
+  if (wdt_bf16)
+    hipLaunchKernelGGL(k_w_prep<true>, grid, dim3(256), 0, s, W, n, ldw, perm, Wf, st);
+  else
+    hipLaunchKernelGGL(k_w_prep<false>, grid, dim3(256), 0, s, W, n, ldw, perm, Wf, st);
+  return hipGetLastError();
+}
+
+}  // namespace gq

@@ -8,16 +8,22 @@ shape with the same statistics, for tests that must finish in seconds.
 
 Random numbers come from ``numpy.random.Generator(PCG64(1000*index + id))``
 with tensor ids 0 = W, 1 = X, 2 = outlier-channel choice, 3 = second factor
-(gate y or spike Z), 4 = spike basis V. Samples are drawn in float64,
+(gate y or spike Z), 4 = spike basis V; the token-chunked tensors (X, y, Z)
+use one generator per chunk of CHUNK tokens, seeded with
+``SeedSequence([1000*index + id, chunk])``, whose float64 uniforms are
+turned into normals (Box-Muller) and Student-t(4) values (closed-form
+inverse CDF) in float64. Samples are drawn in float64,
 rounded once to float32 (round to nearest even) and, for bf16 tensors, once
 more to bf16 (round to nearest even on the float32 bits). The same bf16 or
 float32 values are handed to the GPU path and, upcast exactly, to the oracle.
 
 Nothing here implements the quantization method.
 """
+import os
 from dataclasses import dataclass, field
 
 import numpy as np
+import torch
 
 RECIPES = {
     # tiny layer: fp32 everything, 4 outlier channels x20
@@ -54,24 +60,24 @@ def rng(index, tensor_id):
 
 
 def f32_to_bf16_bits(a):
-    """float array -> uint16 bf16 bit patterns (RNE on the float32 bits;
-    inputs here are finite)."""
-    u = np.ascontiguousarray(np.asarray(a, np.float32)).view(np.uint32)
-    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
-    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+    """float array -> uint16 bf16 bit patterns: round to float32 (nearest
+    even), then to bf16 (nearest even on the float32 bits). torch's CPU
+    casts implement exactly these roundings and run multi-threaded."""
+    t = torch.from_numpy(np.ascontiguousarray(a)).to(torch.float32).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
 
 
 def bf16_bits_to_f32(b):
-    return (np.asarray(b, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    u = np.asarray(b, np.uint16)
+    return torch.from_numpy(u.view(np.int16)).view(torch.bfloat16).to(torch.float32).numpy()
 
 
 def _round(a, dtype):
     """float64 samples -> (float32 values, uint16 bits or None)."""
-    f32 = np.asarray(a, np.float64).astype(np.float32)
     if dtype == "bf16":
-        bits = f32_to_bf16_bits(f32)
+        bits = f32_to_bf16_bits(a)
         return bf16_bits_to_f32(bits), bits
-    return f32, None
+    return torch.from_numpy(np.ascontiguousarray(a)).to(torch.float32).numpy(), None
 
 
 def gen_W(recipe, d_out, n):
@@ -99,48 +105,102 @@ def _spike_basis(recipe, n):
     return q
 
 
-def iter_X(recipe, T, n, chunk=16384):
-    """Yield (t0, values float32-or-float64, bf16 bits or None) token chunks
-    of the calibration matrix in order. Chunking does not change the values:
-    each generator is consumed row by row."""
+CHUNK = 16384   # tokens per calibration chunk; each chunk has its own stream
+
+
+def chunk_rng(index, tensor_id, c):
+    """Generator for chunk c of tensor ``tensor_id``: independent per chunk
+    so chunks can be drawn in parallel and in any order."""
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([1000 * index + tensor_id, c])))
+
+
+def _uniform_open(r, shape):
+    """Uniforms in the open interval (0, 1) from the generator's doubles."""
+    return torch.from_numpy(r.random(shape)).add_(2.0 ** -54)
+
+
+def _normal(r, shape):
+    """N(0, 1) by Box-Muller from two uniform fields (float64)."""
+    u1 = _uniform_open(r, shape)
+    u2 = torch.from_numpy(r.random(shape))
+    return torch.sqrt(-2.0 * torch.log(u1)) * torch.cos((2.0 * np.pi) * u2)
+
+
+def _student_t4(r, shape):
+    """Student-t with 4 degrees of freedom by its closed-form inverse CDF:
+    t = sign(u - 1/2) * 2 * sqrt(cos(arccos(sqrt(a)) / 3) / sqrt(a) - 1),
+    a = 4 u (1 - u)."""
+    u = _uniform_open(r, shape)
+    a = 4.0 * u * (1.0 - u)
+    sa = torch.sqrt(a)
+    t = 2.0 * torch.sqrt(torch.clamp(torch.cos(torch.arccos(sa) / 3.0) / sa - 1.0, min=0.0))
+    return torch.where(u < 0.5, -t, t)
+
+
+def _x_chunk(recipe, c, T, n, cols, V):
     kind = recipe["x_kind"]
-    rx = rng(recipe["index"], 1)
-    ry = rng(recipe["index"], 3)
+    t0 = c * CHUNK
+    m = min(CHUNK, T - t0)
+    rx = chunk_rng(recipe["index"], 1, c)
+    if kind == "gauss_outliers":
+        x = _normal(rx, (m, n))
+    elif kind in ("t4_outliers", "t4"):
+        x = _student_t4(rx, (m, n))
+    elif kind == "silu_gated":
+        a = _normal(rx, (m, n))
+        y = _normal(chunk_rng(recipe["index"], 3, c), (m, n))
+        x = a * torch.sigmoid(a) * y
+    elif kind == "gauss_spike":
+        z = _normal(chunk_rng(recipe["index"], 3, c), (m, recipe["spike_rank"]))
+        x = _normal(rx, (m, n)) + recipe["spike_scale"] * (z @ torch.from_numpy(V).T)
+    else:
+        raise ValueError(kind)
+    if cols.size:
+        x[:, torch.from_numpy(cols)] *= recipe.get("outlier_scale", 1.0)
+    x = x.numpy()
+    if recipe["x_dtype"] == "f64":
+        return t0, x, None
+    vals, bits = _round(x, recipe["x_dtype"])
+    return t0, vals, bits
+
+
+def iter_X(recipe, T, n, workers=None):
+    """Yield (t0, values float32-or-float64, bf16 bits or None) for the
+    calibration matrix in chunks of CHUNK tokens, in order. Chunks are drawn
+    in a thread pool (each has its own generator, so the values do not depend
+    on the number of workers)."""
+    from concurrent.futures import ThreadPoolExecutor
     cols = _outlier_channels(recipe, n)
-    V = _spike_basis(recipe, n) if kind == "gauss_spike" else None
-    for t0 in range(0, T, chunk):
-        m = min(chunk, T - t0)
-        if kind == "gauss_outliers":
-            x = rx.standard_normal((m, n))
-        elif kind in ("t4_outliers", "t4"):
-            x = rx.standard_t(4.0, (m, n))
-        elif kind == "silu_gated":
-            a = rx.standard_normal((m, n))
-            y = ry.standard_normal((m, n))
-            x = a / (1.0 + np.exp(-a)) * y
-        elif kind == "gauss_spike":
-            z = ry.standard_normal((m, recipe["spike_rank"]))
-            x = rx.standard_normal((m, n)) + recipe["spike_scale"] * (z @ V.T)
-        else:
-            raise ValueError(kind)
-        if cols.size:
-            x[:, cols] *= recipe.get("outlier_scale", 1.0)
-        if recipe["x_dtype"] == "f64":
-            yield t0, x, None
-        else:
-            vals, bits = _round(x, recipe["x_dtype"])
-            yield t0, vals, bits
+    V = _spike_basis(recipe, n) if recipe["x_kind"] == "gauss_spike" else None
+    nch = (T + CHUNK - 1) // CHUNK
+    workers = workers or min(2, max(nch, 1))
+    if workers <= 1 or nch <= 1:
+        for c in range(nch):
+            yield _x_chunk(recipe, c, T, n, cols, V)
+        return
+    with ThreadPoolExecutor(workers) as ex:
+        futs = [ex.submit(_x_chunk, recipe, c, T, n, cols, V) for c in range(min(nch, workers))]
+        nxt = len(futs)
+        for c in range(nch):
+            res = futs[c].result()
+            futs[c] = None
+            if nxt < nch:
+                futs.append(ex.submit(_x_chunk, recipe, nxt, T, n, cols, V))
+                nxt += 1
+            yield res
 
 
-def x_full(recipe, T, n, chunk=16384):
-    """Whole calibration matrix: (values, bits or None)."""
-    vals, bits = [], []
-    for _, v, b in iter_X(recipe, T, n, chunk):
-        vals.append(v)
-        bits.append(b)
-    v = np.concatenate(vals)
-    b = None if bits[0] is None else np.concatenate(bits)
-    return v, b
+def x_full(recipe, T, n, workers=None):
+    """Whole calibration matrix: (values, bits or None), filled chunk by chunk."""
+    vals = bits = None
+    for t0, v, b in iter_X(recipe, T, n, workers):
+        if vals is None:
+            vals = np.empty((T, n), v.dtype)
+            bits = None if b is None else np.empty((T, n), np.uint16)
+        vals[t0:t0 + v.shape[0]] = v
+        if b is not None:
+            bits[t0:t0 + v.shape[0]] = b
+    return vals, bits
 
 
 def augment_basis(x_vals, r):
