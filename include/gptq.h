@@ -70,7 +70,7 @@ typedef enum { GPTQ_BF16 = 0, GPTQ_F32 = 1 } gptq_dtype;
 typedef struct {
   uint32_t struct_size; /* sizeof(gptq_params) */
   int32_t bits;         /* 2, 3 or 4 */
-  int32_t group;        /* g >= 1; n_quant % g == 0; g % block == 0 or block % g == 0 */
+  int32_t group;        /* g >= 8; n_quant % g == 0; g % block == 0 or block % g == 0 */
   float damp;           /* lambda = damp * mean(diag H); >= 0, finite */
   int32_t block;        /* lazy-batch width B: 32, 64 or 128 */
   int32_t act_order;    /* 0 or 1 */
@@ -126,12 +126,12 @@ gptq_status gptq_quantize_layer(void *stream, const void *W, gptq_dtype wdt,
                                 const gptq_outputs *out, int64_t *fail_col);
 
 /* ---- The factorisation alone (steps 2-3 of quantize_layer) ----------------
- * U_out (n x n fp32 row-major): upper Cholesky factor of the damped,
- * dead-fixed, (optionally) act-order-permuted H's inverse, in processing
- * order (strict lower part zero). perm_out (n int32, may be NULL): original
- * column at each processing position. Same workspace as quantize_layer with
- * d_out = 0 is NOT enough: use gptq_workspace_bytes(0, n, p, ...) + 0 (it
- * accounts for the factor buffers). Synchronises like quantize_layer.
+ * U_out (n x n fp32 row-major): upper Cholesky factor U of the inverse of
+ * the damped, dead-fixed, (optionally) act-order-permuted H, in processing
+ * order (U^T U = H_d^-1; strict lower part zero). perm_out (n int32, may be
+ * NULL): original column at each processing position. Uses p->damp,
+ * p->act_order and p->n_quant only; workspace: gptq_workspace_bytes(0, n, p).
+ * Synchronises like quantize_layer.
  * ("Resumen Técnico: GPTQ-intrinsic LoRA", "Detalles de Implementación":
  * Cholesky of the regularised Hessian.) */
 gptq_status gptq_factor_hinv(void *stream, const float *H, int64_t n,
@@ -152,21 +152,19 @@ gptq_status gptq_unpack_codes(void *stream, const uint32_t *qweight,
 const char *gptq_status_string(int status);
 const char *gptq_last_error(void); /* thread-local detail of the last failure */
 
-/* Kernel timing with hipEvents recorded on the caller's stream around each
- * launch, by kernel class. enable != 0 starts recording (and clears what was
- * recorded); gptq_profile_collect synchronises the recorded events and
- * returns, for class c in [0, GPTQ_PROF_NCLASSES), the summed milliseconds
- * and launch count, then clears. */
+/* Timing with hipEvents recorded on the caller's stream: around the
+ * Hessian Gram kernel, around the Hessian reduction, and around a whole
+ * quantize_layer call (events are deliberately coarse: an event record
+ * between every pair of small kernels costs microseconds of GPU time).
+ * enable != 0 starts recording (and clears what was recorded);
+ * gptq_profile_collect synchronises the recorded events and returns, for
+ * class c in [0, GPTQ_PROF_NCLASSES), the summed milliseconds and the
+ * number of timed intervals, then clears. */
 enum {
   GPTQ_PROF_HESSIAN_SYRK = 0,
   GPTQ_PROF_HESSIAN_REDUCE = 1,
-  GPTQ_PROF_PREP = 2,
-  GPTQ_PROF_FACTOR_LEAF = 3,
-  GPTQ_PROF_FACTOR_GEMM = 4,
-  GPTQ_PROF_SWEEP = 5,
-  GPTQ_PROF_TRAILING = 6,
-  GPTQ_PROF_PACK = 7,
-  GPTQ_PROF_NCLASSES = 8
+  GPTQ_PROF_QUANTIZE = 2,
+  GPTQ_PROF_NCLASSES = 3
 };
 gptq_status gptq_profile_enable(int enable);
 gptq_status gptq_profile_collect(double *ms, int64_t *count);

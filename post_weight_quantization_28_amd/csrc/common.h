@@ -31,6 +31,8 @@ __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + 
 int hessian_splits(int64_t T, int xdt_bf16);
 hipError_t launch_hessian_partials_bf16(hipStream_t s, const uint16_t* X, int64_t T,
                                         int64_t n, int64_t ldx, float* part, int splits);
+hipError_t launch_hessian_partials_bf16_w8(hipStream_t s, const uint16_t* X, int64_t T,
+                                           int64_t n, int64_t ldx, float* part, int splits);
 hipError_t launch_hessian_partials_f32(hipStream_t s, const float* X, int64_t T,
                                        int64_t n, int64_t ldx, float* part, int splits);
 hipError_t launch_hessian_reduce(hipStream_t s, const float* part, int splits, int64_t n,
@@ -70,7 +72,26 @@ struct GemmArgs {
   const DevStatus* st;   // if non-null and flagged, the kernel returns at once
 };
 hipError_t launch_gemm_f32(hipStream_t s, const GemmArgs& g);
+hipError_t launch_gemm_pair(hipStream_t s, const GemmArgs& a, const GemmArgs* b);
 hipError_t launch_rotate(hipStream_t s, const float* X, float* U, int64_t n);
+
+// ---- slab.hip
+// C[M x N] = alpha A[M x K] B + beta C for K <= 128 (B: K x N, or N x K when
+// tb). Columns are split over at most max_split workgroups per 128-row slab;
+// pass max_split = 1 when C aliases A.
+struct SlabArgs {
+  int64_t M, N, K;
+  const float* A; int64_t lda;
+  const float* B; int64_t ldb; int tb;
+  float* C; int64_t ldc;
+  float alpha, beta;
+  int lower_only;
+  int nsplit;            // set by the launcher
+  const DevStatus* st;
+  int bvec;              // set by the launcher: B rows 16-byte aligned
+};
+hipError_t launch_slab(hipStream_t s, SlabArgs g, int max_split);
+hipError_t launch_slab_pair(hipStream_t s, SlabArgs a, int split_a, const SlabArgs* b, int split_b);
 
 // ---- sweep.hip
 struct SweepArgs {
@@ -79,6 +100,8 @@ struct SweepArgs {
   int64_t d_out, i0, ncols;     // block [i0, i0 + ncols)
   int block;                    // B
   int group, bits;
+  int64_t gbase;                // group index of column i0
+  int gshift;                   // log2(group) when groups split a block, else 31
   float* scales; uint8_t* zeros; int64_t ngroups;
   uint8_t* codes; int64_t n_quant;   // processing order, d_out x n_quant
   float* E;                     // d_out x B

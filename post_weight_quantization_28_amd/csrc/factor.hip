@@ -5,104 +5,158 @@
 //
 // With A = J H_d J = L L^T (J = index reversal, L lower), the factor GPTQ's
 // sweep needs is U = J L^{-1} J (upper, U^T U = H_d^{-1}). L and X = L^{-1}
-// are built together by recursive halving of A:
-//   [A11  .  ]      L11, X11 = rec(A11)
-//   [A21 A22 ]      T1 = A21 X11^T          (= L21)
-//                   A22 -= T1 T1^T          (Schur complement, lower tiles)
-//                   T2 = T1 X11             (= L21 L11^{-1})
-//                   L22, X22 = rec(A22)
-//                   X21 = -X22 T2
-// so L itself is never stored: only X = L^{-1} (lower; its upper part is
-// kept zero) and the two temporaries, which live in blocks that are dead at
-// that point (T1 in X21's place, T2 in A21's place). Every product is a
-// fp32 v_mfma_f32_32x32x2f32 GEMM; leaves of up to 64 columns are factored
-// and inverted inside one workgroup in LDS.
+// are built together, right-looking, one 64-column panel p = [k0, k1) at a
+// time (R below = the rows of X not yet final; X starts as the identity):
+//   leaf:    L11 = chol(A11), D = L11^{-1}      (one workgroup, registers)
+//            X[p, p] = D
+//   panel:   X[p, 0:k0] = D X[p, 0:k0]         (block row p of X is final)
+//            A[k1:, p]  = A[k1:, p] D^T        (= L21, in place)
+//   update:  A[k1:, k1:] -= L21 L21^T           (Schur complement, lower tiles)
+//            X[k1:, 0:k1] -= L21 X[p, 0:k1]     (forward substitution of L X = I)
+// The two GEMMs of a step share one launch. L itself is never stored beyond
+// its panel. All products are fp32 v_mfma_f32_32x32x2f32.
 #include "common.h"
+
+#include <algorithm>
+#include <utility>
 
 namespace gq {
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------- leaf
-// m <= 64 columns at offset off of the flipped matrix (ld = n). Writes the
-// lower triangle of X[off:off+m, off:off+m] = L11^{-1}. A non-positive or
-// non-finite pivot raises kNotPD with the original column perm[n-1-(off+k)].
-__global__ void __launch_bounds__(256)
-k_leaf(const float* __restrict__ A, float* __restrict__ X, int64_t n, int64_t off, int m,
+// Cholesky and inverse of the m <= 64 diagonal block A[k0:k0+m, k0:k0+m]
+// (lower part read), in ONE wavefront: lane i holds row i in 64 registers,
+// so the 64 pivot steps need no workgroup barrier. Step k: the pivot comes
+// from lane k (v_readlane), every lane scales its entry of column k, the
+// column goes through LDS and is read back by all lanes as broadcasts
+// (same address in every lane) for the rank-1 update of their own row.
+// The inverse X = L^{-1} is then formed column-per-lane: lane c holds
+// column c of X and, for row i, subtracts L[i][k] x_k (row i of L read from
+// LDS as broadcasts) before scaling by 1/L[i][i]. All loops are unrolled so
+// every register index is a constant. Writes the lower triangle of
+// X[k0:k0+m, k0:k0+m]; a non-positive or non-finite pivot raises kNotPD
+// with the original column perm[n-1-(k0+k)].
+template <int K>
+__device__ __forceinline__ void leaf_chol_step(float (&a)[64], float (*sCol)[64], float* sInv, int lane,
+                                               int& bad) {
+  const float d2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a[K]), K));
+  const bool ok = d2 > 0.f && isfinite(d2);
+  bad = (!ok && bad == 64) ? K : bad;
+  const float inv = ok ? __builtin_amdgcn_rsqf(d2) : 1.f;   // 1 / sqrt(d2)
+  const float d = ok ? d2 * inv : 1.f;
+  float l = (lane > K) ? a[K] * inv : 0.f;
+  l = (lane == K) ? d : l;
+  a[K] = l;
+  sCol[K][lane] = l;
+  if (lane == K) sInv[K] = inv;
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int q = (K + 1) / 4; q < 16; ++q) {
+    const float4 c = *reinterpret_cast<const float4*>(&sCol[K][4 * q]);
+    if (4 * q + 0 > K) a[4 * q + 0] = fmaf(-l, c.x, a[4 * q + 0]);
+    if (4 * q + 1 > K) a[4 * q + 1] = fmaf(-l, c.y, a[4 * q + 1]);
+    if (4 * q + 2 > K) a[4 * q + 2] = fmaf(-l, c.z, a[4 * q + 2]);
+    if (4 * q + 3 > K) a[4 * q + 3] = fmaf(-l, c.w, a[4 * q + 3]);
+  }
+  // materialise this step's updates here (otherwise the compiler sinks them
+  // to their next use and keeps every broadcast value alive)
+#pragma unroll
+  for (int j = K + 1; j < 64; ++j) asm volatile("" : "+v"(a[j]));
+}
+
+template <int... Ks>
+__device__ __forceinline__ void leaf_chol(float (&a)[64], float (*sCol)[64], float* sInv, int lane,
+                                          int& bad, std::integer_sequence<int, Ks...>) {
+  (leaf_chol_step<Ks>(a, sCol, sInv, lane, bad), ...);
+}
+
+template <int I>
+__device__ __forceinline__ void leaf_inv_step(float (&x)[64], const float (*sRow)[68], const float* sInv,
+                                              int lane) {
+  // four independent partial sums keep the dependent FMA chain short
+  float acc[4] = {(lane == I) ? 1.f : 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; 4 * q < I; ++q) {
+    const float4 r = *reinterpret_cast<const float4*>(&sRow[I][4 * q]);
+    if (4 * q + 0 < I) acc[0] = fmaf(-r.x, x[4 * q + 0], acc[0]);
+    if (4 * q + 1 < I) acc[1] = fmaf(-r.y, x[4 * q + 1], acc[1]);
+    if (4 * q + 2 < I) acc[2] = fmaf(-r.z, x[4 * q + 2], acc[2]);
+    if (4 * q + 3 < I) acc[3] = fmaf(-r.w, x[4 * q + 3], acc[3]);
+  }
+  x[I] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * sInv[I];
+  asm volatile("" : "+v"(x[I]));
+}
+
+template <int... Is>
+__device__ __forceinline__ void leaf_inv(float (&x)[64], const float (*sRow)[68], const float* sInv,
+                                         int lane, std::integer_sequence<int, Is...>) {
+  (leaf_inv_step<Is>(x, sRow, sInv, lane), ...);
+}
+
+__global__ void __launch_bounds__(64)
+k_leaf(const float* __restrict__ A, float* __restrict__ X, int64_t n, int64_t k0, int m,
        const int32_t* __restrict__ perm, DevStatus* st) {
-  __shared__ float sA[64][65];
-  __shared__ float sX[64][65];
-  __shared__ float sD[64];
-  const int tid = threadIdx.x;
-  const int tx = tid & 15, ty = tid >> 4;
-  for (int e = tid; e < 64 * 64; e += 256) {
-    const int i = e >> 6, j = e & 63;
-    float v;
-    if (i < m && j < m) v = (j <= i) ? A[(off + i) * n + off + j] : 0.f;
-    else v = (i == j) ? 1.f : 0.f;
-    sA[i][j] = v;
-    sX[i][j] = (i == j) ? 1.f : 0.f;
+  __shared__ __align__(16) float sCol[64][64];   // sCol[k][i] = L[i][k]
+  __shared__ __align__(16) float sRow[64][68];   // sRow[i][k] = L[i][k]
+  __shared__ float sInv[64];                      // 1 / L[k][k]
+  const int lane = threadIdx.x;
+  const int li = min(lane, m - 1);
+  const float* arow = A + (k0 + li) * n + k0;
+  float a[64];
+#pragma unroll
+  for (int j = 0; j < 64; ++j) {
+    const float v = arow[min(j, m - 1)];                  // always in bounds
+    a[j] = (lane < m && j < m) ? ((j <= lane) ? v : 0.f) : ((lane == j) ? 1.f : 0.f);
   }
-  __syncthreads();
-  // right-looking Cholesky: column k scaled, trailing lower part updated
-  for (int k = 0; k < 64; ++k) {
-    const float d2 = sA[k][k];
-    const bool ok = d2 > 0.f && isfinite(d2);
-    if (tid == 0 && k < m && !ok) raise_status(st, kNotPD, perm[n - 1 - (off + k)]);
-    const float d = ok ? sqrtf(d2) : 1.f;
-    if (tid == 0) sD[k] = d;
-    const float inv = 1.f / d;
-    if (tid > k && tid < 64) sA[tid][k] *= inv;
-    __syncthreads();
-    for (int a = 0; a < 4; ++a) {
-      const int i = k + 1 + ty + 16 * a;
-      if (i >= 64) break;
-      const float lik = sA[i][k];
-      for (int b = 0; b < 4; ++b) {
-        const int j = k + 1 + tx + 16 * b;
-        if (j <= i) sA[i][j] -= lik * sA[j][k];
-      }
-    }
-    __syncthreads();
-  }
-  // X = L^{-1}: forward substitution on the identity, row by row
-  for (int i = 0; i < 64; ++i) {
-    const float inv = 1.f / sD[i];
-    if (tid <= i) sX[i][tid] *= inv;
-    __syncthreads();
-    for (int a = 0; a < 4; ++a) {
-      const int r = i + 1 + ty + 16 * a;
-      if (r >= 64) break;
-      const float lri = sA[r][i];
-      for (int b = 0; b < 4; ++b) {
-        const int c = tx + 16 * b;
-        if (c <= i) sX[r][c] -= lri * sX[i][c];
-      }
-    }
-    __syncthreads();
-  }
-  for (int e = tid; e < 64 * 64; e += 256) {
-    const int i = e >> 6, j = e & 63;
-    if (i < m && j <= i) X[(off + i) * n + off + j] = sX[i][j];
-  }
+  int bad = 64;   // first pivot that failed (uniform across the wave)
+  leaf_chol(a, sCol, sInv, lane, bad, std::make_integer_sequence<int, 64>{});
+  if (lane == 0 && bad < m) raise_status(st, kNotPD, perm[n - 1 - (k0 + bad)]);
+  // publish the rows of L for the inverse
+#pragma unroll
+  for (int j = 0; j < 64; j += 4)
+    *reinterpret_cast<float4*>(&sRow[lane][j]) =
+        make_float4(lane >= j ? a[j] : 0.f, lane >= j + 1 ? a[j + 1] : 0.f,
+                    lane >= j + 2 ? a[j + 2] : 0.f, lane >= j + 3 ? a[j + 3] : 0.f);
+  __builtin_amdgcn_wave_barrier();
+  // x[i] = column `lane` of L^{-1}, row i
+  float x[64];
+  leaf_inv(x, sRow, sInv, lane, std::make_integer_sequence<int, 64>{});
+  float* xrow = X + k0 * n + k0 + lane;
+#pragma unroll
+  for (int i = 0; i < 64; ++i)
+    if (i < m && lane <= i) xrow[i * n] = x[i];
 }
 
 hipError_t launch_leaf(hipStream_t s, float* A, float* X, int64_t n, int64_t off, int64_t m,
                        const int32_t* perm, DevStatus* st) {
-  hipLaunchKernelGGL(k_leaf, dim3(1), dim3(256), 0, s, A, X, n, off, (int)m, perm, st);
+  hipLaunchKernelGGL(k_leaf, dim3(1), dim3(64), 0, s, A, X, n, off, (int)m, perm, st);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- GEMM
-// C = alpha op(A) op(B) + beta C with 4 waves (2x2), each wave owning a
-// (BM/2) x (BN/2) block of 32x32 MFMA tiles; K staged through LDS in chunks
-// of 16 as [k][m] and [k][n] (consecutive lanes read consecutive m or n).
-constexpr int kGBK = 16;
+// C = alpha op(A) op(B) + beta C. 256 threads as 2 x 2 waves, each wave a
+// (BM/2) x (BN/2) block of 32x32 v_mfma_f32_32x32x2f32 tiles. K is staged
+// through LDS in chunks of 32. Each operand keeps its memory layout in LDS,
+// so every global->LDS move is a plain 16-byte copy:
+//  * k-contiguous operands ([m][k] / [n][k], pitch 36 floats) are read with
+//    one ds_read_b128 per four MFMAs;
+//  * m- or n-contiguous ones ([k][m] / [k][n], pitch BM+4) with four
+//    conflict-free ds_read_b32.
+// For MFMA s (0..3) of a group of four, lanes 0-31 take k = 8q + s and
+// lanes 32-63 take k = 8q + 4 + s, identically for A and B. The next chunk
+// is prefetched into registers while the current one is multiplied; alpha
+// is applied while staging A, and beta * C is loaded straight into the
+// accumulators, so the epilogue only stores.
+constexpr int kGBK = 32;
+constexpr int kGP = kGBK + 4;
 
 template <int BM, int BN>
 struct GemmSmem {
-  float a[2][kGBK][BM + 4];
-  float b[2][kGBK][BN + 4];
+  static constexpr int SA = (BM * kGP > kGBK * (BM + 4)) ? BM * kGP : kGBK * (BM + 4);
+  static constexpr int SB = (BN * kGP > kGBK * (BN + 4)) ? BN * kGP : kGBK * (BN + 4);
+  float a[2][SA];
+  float b[2][SB];
 };
 
 // Load 4 consecutive elements along the contiguous dimension; zero outside.
@@ -123,19 +177,54 @@ __device__ inline float4 load4(const float* __restrict__ p, int64_t ld, int64_t 
   return v;
 }
 
-template <int BM, int BN>
-__global__ void __launch_bounds__(256)
-k_gemm_f32(GemmArgs g) {
+struct GemmPair {
+  GemmArgs p[2];
+  int ntn[2];     // tiles along N per problem
+  int nt0;        // tiles of problem 0 (problem 1 follows)
+};
+
+// Staging of one operand tile (R rows of the output dimension x kGBK).
+// KC: the operand is k-contiguous in memory (M x K for A, N x K for B).
+template <int R, bool KC>
+struct Operand {
+  static constexpr int L = R * kGBK / 4 / 256;   // float4 per thread
+  __device__ static float4 load(const float* p, int64_t ld, int64_t r0, int64_t k0, int64_t RN,
+                                int64_t K, int idx) {
+    if constexpr (KC) {
+      const int r = idx / (kGBK / 4), k4 = idx % (kGBK / 4);
+      return load4(p, ld, r0 + r, k0 + 4 * k4, RN, K);
+    } else {
+      const int k = idx / (R / 4), r4 = idx % (R / 4);
+      return load4(p, ld, k0 + k, r0 + 4 * r4, K, RN);
+    }
+  }
+  __device__ static void store(float* s, int idx, float4 v) {
+    if constexpr (KC) {
+      const int r = idx / (kGBK / 4), k4 = idx % (kGBK / 4);
+      *reinterpret_cast<float4*>(s + r * kGP + 4 * k4) = v;
+    } else {
+      const int k = idx / (R / 4), r4 = idx % (R / 4);
+      *reinterpret_cast<float4*>(s + k * (R + 4) + 4 * r4) = v;
+    }
+  }
+  // the four values of row r for k = kb + 0..3
+  __device__ static float4 frag(const float* s, int r, int kb) {
+    if constexpr (KC) {
+      return *reinterpret_cast<const float4*>(s + r * kGP + kb);
+    } else {
+      return make_float4(s[kb * (R + 4) + r], s[(kb + 1) * (R + 4) + r], s[(kb + 2) * (R + 4) + r],
+                         s[(kb + 3) * (R + 4) + r]);
+    }
+  }
+};
+
+template <int BM, int BN, bool TA, bool TB>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, int tm, int tn, GemmSmem<BM, BN>& sm) {
   constexpr int WM = BM / 2, WN = BN / 2;          // per-wave block
   constexpr int FM = WM / 32, FN = WN / 32;        // MFMA tiles per wave
-  constexpr int LA = BM * kGBK / 4 / 256;          // float4 loads per thread
-  constexpr int LB = BN * kGBK / 4 / 256;
-  static_assert(LA >= 1 && LB >= 1, "tile too small");
-  __shared__ GemmSmem<BM, BN> sm;
-
-  if (g.st != nullptr && g.st->flags != 0) return;
-  const int tm = blockIdx.y, tn = blockIdx.x;
-  if (g.lower_only && tn * BN > tm * BM + BM - 1) return;
+  using OA = Operand<BM, !TA>;
+  using OB = Operand<BN, TB>;
+  static_assert(OA::L >= 1 && OB::L >= 1, "tile too small");
   const int64_t m0 = (int64_t)tm * BM, n0 = (int64_t)tn * BN;
   int64_t klo = 0, khi = g.K;
   if (g.kmode == 1) khi = min(g.K, n0 + BN);
@@ -144,6 +233,7 @@ k_gemm_f32(GemmArgs g) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 31, lk = 4 * (lane >> 5);
 
   f32x16_t acc[FM][FN];
 #pragma unroll
@@ -151,62 +241,30 @@ k_gemm_f32(GemmArgs g) {
 #pragma unroll
     for (int b = 0; b < FN; ++b)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+      for (int r = 0; r < 16; ++r) {
+        float v = 0.f;
+        if (g.beta != 0.f) {
+          const int64_t i = m0 + WM * wm + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          const int64_t j = n0 + WN * wn + 32 * b + lr;
+          if (i < g.M && j < g.N) v = g.beta * g.C[i * g.ldc + j];
+        }
+        acc[a][b][r] = v;
+      }
 
-  float4 ra[LA], rb[LB];
+  float4 ra[OA::L], rb[OB::L];
   auto gload = [&](int64_t k0) {
 #pragma unroll
-    for (int v = 0; v < LA; ++v) {
-      const int idx = tid + 256 * v;
-      if (!g.ta) {   // A is M x K, k contiguous: 4 k values of row m
-        const int m = idx / (kGBK / 4), k4 = idx % (kGBK / 4);
-        ra[v] = load4(g.A, g.lda, m0 + m, k0 + 4 * k4, g.M, g.K);
-      } else {       // A stored K x M, m contiguous: 4 m values of row k
-        const int k = idx / (BM / 4), m4 = idx % (BM / 4);
-        ra[v] = load4(g.A, g.lda, k0 + k, m0 + 4 * m4, g.K, g.M);
-      }
-    }
+    for (int v = 0; v < OA::L; ++v) ra[v] = OA::load(g.A, g.lda, m0, k0, g.M, g.K, tid + 256 * v);
 #pragma unroll
-    for (int v = 0; v < LB; ++v) {
-      const int idx = tid + 256 * v;
-      if (!g.tb) {   // B is K x N, n contiguous
-        const int k = idx / (BN / 4), n4 = idx % (BN / 4);
-        rb[v] = load4(g.B, g.ldb, k0 + k, n0 + 4 * n4, g.K, g.N);
-      } else {       // B stored N x K, k contiguous
-        const int nn = idx / (kGBK / 4), k4 = idx % (kGBK / 4);
-        rb[v] = load4(g.B, g.ldb, n0 + nn, k0 + 4 * k4, g.N, g.K);
-      }
-    }
+    for (int v = 0; v < OB::L; ++v) rb[v] = OB::load(g.B, g.ldb, n0, k0, g.N, g.K, tid + 256 * v);
   };
   auto sstore = [&](int buf) {
+    const float al = g.alpha;
 #pragma unroll
-    for (int v = 0; v < LA; ++v) {
-      const int idx = tid + 256 * v;
-      if (!g.ta) {
-        const int m = idx / (kGBK / 4), k4 = idx % (kGBK / 4);
-        sm.a[buf][4 * k4 + 0][m] = ra[v].x;
-        sm.a[buf][4 * k4 + 1][m] = ra[v].y;
-        sm.a[buf][4 * k4 + 2][m] = ra[v].z;
-        sm.a[buf][4 * k4 + 3][m] = ra[v].w;
-      } else {
-        const int k = idx / (BM / 4), m4 = idx % (BM / 4);
-        *reinterpret_cast<float4*>(&sm.a[buf][k][4 * m4]) = ra[v];
-      }
-    }
+    for (int v = 0; v < OA::L; ++v)
+      OA::store(sm.a[buf], tid + 256 * v, make_float4(al * ra[v].x, al * ra[v].y, al * ra[v].z, al * ra[v].w));
 #pragma unroll
-    for (int v = 0; v < LB; ++v) {
-      const int idx = tid + 256 * v;
-      if (!g.tb) {
-        const int k = idx / (BN / 4), n4 = idx % (BN / 4);
-        *reinterpret_cast<float4*>(&sm.b[buf][k][4 * n4]) = rb[v];
-      } else {
-        const int nn = idx / (kGBK / 4), k4 = idx % (kGBK / 4);
-        sm.b[buf][4 * k4 + 0][nn] = rb[v].x;
-        sm.b[buf][4 * k4 + 1][nn] = rb[v].y;
-        sm.b[buf][4 * k4 + 2][nn] = rb[v].z;
-        sm.b[buf][4 * k4 + 3][nn] = rb[v].w;
-      }
-    }
+    for (int v = 0; v < OB::L; ++v) OB::store(sm.b[buf], tid + 256 * v, rb[v]);
   };
 
   const int64_t nk = khi > klo ? ceil_div(khi - klo, kGBK) : 0;
@@ -220,18 +278,21 @@ k_gemm_f32(GemmArgs g) {
     const bool more = it + 1 < nk;
     if (more) gload(klo + (it + 1) * kGBK);
 #pragma unroll
-    for (int ks = 0; ks < kGBK / 2; ++ks) {
-      const int kk = 2 * ks + (lane >> 5);
-      float af[FM], bf[FN];
+    for (int kq = 0; kq < kGBK / 8; ++kq) {
+      float4 fa[FM], fb[FN];
 #pragma unroll
-      for (int a = 0; a < FM; ++a) af[a] = sm.a[cur][kk][WM * wm + 32 * a + (lane & 31)];
+      for (int a = 0; a < FM; ++a) fa[a] = OA::frag(sm.a[cur], WM * wm + 32 * a + lr, 8 * kq + lk);
 #pragma unroll
-      for (int b = 0; b < FN; ++b) bf[b] = sm.b[cur][kk][WN * wn + 32 * b + (lane & 31)];
+      for (int b = 0; b < FN; ++b) fb[b] = OB::frag(sm.b[cur], WN * wn + 32 * b + lr, 8 * kq + lk);
 #pragma unroll
       for (int a = 0; a < FM; ++a)
 #pragma unroll
-        for (int b = 0; b < FN; ++b)
-          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(af[a], bf[b], acc[a][b], 0, 0, 0);
+        for (int b = 0; b < FN; ++b) {
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[a].x, fb[b].x, acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[a].y, fb[b].y, acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[a].z, fb[b].z, acc[a][b], 0, 0, 0);
+          acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[a].w, fb[b].w, acc[a][b], 0, 0, 0);
+        }
     }
     if (more) sstore(cur ^ 1);
     __syncthreads();
@@ -244,26 +305,61 @@ k_gemm_f32(GemmArgs g) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t i = m0 + WM * wm + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int64_t j = n0 + WN * wn + 32 * b + (lane & 31);
-        if (i < g.M && j < g.N) {
-          float v = g.alpha * acc[a][b][r];
-          if (g.beta != 0.f) v += g.beta * g.C[i * g.ldc + j];
-          g.C[i * g.ldc + j] = v;
-        }
+        const int64_t j = n0 + WN * wn + 32 * b + lr;
+        if (i < g.M && j < g.N) g.C[i * g.ldc + j] = acc[a][b][r];
       }
 }
 
-hipError_t launch_gemm_f32(hipStream_t s, const GemmArgs& g) {
-  if (g.M <= 0 || g.N <= 0) return hipSuccess;
-  if (g.M * g.N >= (int64_t)512 * 512) {
-    dim3 grid((unsigned)ceil_div(g.N, 128), (unsigned)ceil_div(g.M, 128));
-    hipLaunchKernelGGL((k_gemm_f32<128, 128>), grid, dim3(256), 0, s, g);
+template <int BM, int BN>
+__global__ void __launch_bounds__(256)
+k_gemm_f32(GemmPair gp) {
+  __shared__ __align__(16) GemmSmem<BM, BN> sm;
+  const int which = (int)blockIdx.x >= gp.nt0;
+  const int t = (int)blockIdx.x - (which ? gp.nt0 : 0);
+  const GemmArgs& g = gp.p[which];
+  if (g.st != nullptr && g.st->flags != 0) return;
+  const int tm = t / gp.ntn[which], tn = t % gp.ntn[which];
+  if (g.lower_only && tn * BN > tm * BM + BM - 1) return;
+  if (g.ta) {
+    if (g.tb) gemm_tile<BM, BN, true, true>(g, tm, tn, sm);
+    else gemm_tile<BM, BN, true, false>(g, tm, tn, sm);
   } else {
-    dim3 grid((unsigned)ceil_div(g.N, 64), (unsigned)ceil_div(g.M, 64));
-    hipLaunchKernelGGL((k_gemm_f32<64, 64>), grid, dim3(256), 0, s, g);
+    if (g.tb) gemm_tile<BM, BN, false, true>(g, tm, tn, sm);
+    else gemm_tile<BM, BN, false, false>(g, tm, tn, sm);
   }
+}
+
+template <int BM, int BN>
+static hipError_t launch_pair(hipStream_t s, const GemmArgs& a, const GemmArgs* b) {
+  GemmPair gp{};
+  gp.p[0] = a;
+  gp.ntn[0] = (int)ceil_div(a.N, BN);
+  gp.nt0 = (a.M > 0 && a.N > 0) ? (int)(ceil_div(a.M, BM) * gp.ntn[0]) : 0;
+  int nt1 = 0;
+  if (b && b->M > 0 && b->N > 0) {
+    gp.p[1] = *b;
+    gp.ntn[1] = (int)ceil_div(b->N, BN);
+    nt1 = (int)(ceil_div(b->M, BM) * gp.ntn[1]);
+  } else {
+    gp.p[1] = a;
+    gp.ntn[1] = 1;
+  }
+  const int total = gp.nt0 + nt1;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL((k_gemm_f32<BM, BN>), dim3(total), dim3(256), 0, s, gp);
   return hipGetLastError();
 }
+
+// One launch for one or two independent products; the tile shape follows
+// the larger one.
+hipError_t launch_gemm_pair(hipStream_t s, const GemmArgs& a, const GemmArgs* b) {
+  int64_t big = a.M * a.N;
+  if (b) big = std::max(big, b->M * b->N);
+  if (big >= (int64_t)512 * 512) return launch_pair<128, 128>(s, a, b);
+  return launch_pair<64, 64>(s, a, b);
+}
+
+hipError_t launch_gemm_f32(hipStream_t s, const GemmArgs& g) { return launch_gemm_pair(s, g, nullptr); }
 
 // ---------------------------------------------------------------- rotate
 // U[i][j] = X[n-1-i][n-1-j]: the flat array reversed.

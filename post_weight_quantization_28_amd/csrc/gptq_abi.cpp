@@ -8,6 +8,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -120,10 +121,21 @@ gptq_status check_params(int64_t d_out, int64_t n, const gptq_params* p) {
   if (p->block != 32 && p->block != 64 && p->block != 128)
     return fail(GPTQ_EINVAL, "block must be 32, 64 or 128");
   if (p->n_quant < 1 || p->n_quant > n) return fail(GPTQ_EINVAL, "n_quant must be in [1, n]");
-  if (p->group < 1) return fail(GPTQ_EINVAL, "group must be >= 1");
+  if (p->group < 8) return fail(GPTQ_EINVAL, "group must be >= 8");
   if (p->n_quant % p->group != 0) return fail(GPTQ_EINVAL, "group must divide n_quant");
   if (!(p->group % p->block == 0 || p->block % p->group == 0))
     return fail(GPTQ_EINVAL, "group and block must nest (one divides the other)");
+  if (!(p->damp >= 0.f) || !std::isfinite(p->damp)) return fail(GPTQ_EINVAL, "damp must be finite and >= 0");
+  if (p->act_order != 0 && p->act_order != 1) return fail(GPTQ_EINVAL, "act_order must be 0 or 1");
+  return GPTQ_OK;
+}
+
+// gptq_factor_hinv only uses n, damp, act_order and n_quant.
+gptq_status check_factor_params(int64_t n, const gptq_params* p) {
+  if (!p) return fail(GPTQ_EINVAL, "params is NULL");
+  if (p->struct_size < sizeof(gptq_params)) return fail(GPTQ_EINVAL, "params.struct_size too small");
+  if (n < 1 || n > (int64_t)1 << 30) return fail(GPTQ_EINVAL, "need 1 <= n <= 2^30");
+  if (p->n_quant < 1 || p->n_quant > n) return fail(GPTQ_EINVAL, "n_quant must be in [1, n]");
   if (!(p->damp >= 0.f) || !std::isfinite(p->damp)) return fail(GPTQ_EINVAL, "damp must be finite and >= 0");
   if (p->act_order != 0 && p->act_order != 1) return fail(GPTQ_EINVAL, "act_order must be 0 or 1");
   return GPTQ_OK;
@@ -138,40 +150,29 @@ gptq_status check_ws(void* ws, size_t have, size_t need) {
 }
 
 // ---------------------------------------------------------------- factorisation
-hipError_t factor_rec(hipStream_t s, float* A, float* X, int64_t n, int64_t off, int64_t m,
-                      const int32_t* perm, DevStatus* st) {
-  if (m <= kLeaf) {
-    Timed t(GPTQ_PROF_FACTOR_LEAF, s);
-    return launch_leaf(s, A, X, n, off, m, perm, st);
-  }
-  int64_t k = ceil_div(m / 2, kLeaf) * kLeaf;
-  if (k >= m) k = m - kLeaf;
-  hipError_t e = factor_rec(s, A, X, n, off, k, perm, st);
-  if (e != hipSuccess) return e;
-  const int64_t r = m - k;
-  float* A21 = A + (off + k) * n + off;
-  float* A22 = A + (off + k) * n + off + k;
-  float* X11 = X + off * n + off;
-  float* X21 = X + (off + k) * n + off;
-  float* X22 = X + (off + k) * n + off + k;
-  {
-    Timed t(GPTQ_PROF_FACTOR_GEMM, s);
-    // T1 = A21 X11^T  (into X21's place)
-    GemmArgs g{r, k, k, A21, n, 0, X11, n, 1, X21, n, 1.f, 0.f, 1, 0, st};
-    if ((e = launch_gemm_f32(s, g)) != hipSuccess) return e;
-    // A22 -= T1 T1^T  (lower tiles)
-    GemmArgs h{r, r, k, X21, n, 0, X21, n, 1, A22, n, -1.f, 1.f, 0, 1, st};
-    if ((e = launch_gemm_f32(s, h)) != hipSuccess) return e;
-    // T2 = T1 X11  (into A21's place)
-    GemmArgs q{r, k, k, X21, n, 0, X11, n, 0, A21, n, 1.f, 0.f, 2, 0, st};
-    if ((e = launch_gemm_f32(s, q)) != hipSuccess) return e;
-  }
-  if ((e = factor_rec(s, A, X, n, off + k, r, perm, st)) != hipSuccess) return e;
-  {
-    Timed t(GPTQ_PROF_FACTOR_GEMM, s);
-    // X21 = -X22 T2
-    GemmArgs g{r, k, r, X22, n, 0, A21, n, 0, X21, n, -1.f, 0.f, 3, 0, st};
-    if ((e = launch_gemm_f32(s, g)) != hipSuccess) return e;
+// Right-looking Cholesky of the flipped matrix A with the inverse X = L^{-1}
+// carried along (see factor.hip): three launches per 64-column panel.
+hipError_t factor_panels(hipStream_t s, float* A, float* X, int64_t n, const int32_t* perm,
+                         DevStatus* st) {
+  hipError_t e;
+  constexpr int kAny = 1 << 30;
+  for (int64_t k0 = 0; k0 < n; k0 += kLeaf) {
+    const int64_t m = std::min<int64_t>(kLeaf, n - k0);
+    const int64_t k1 = k0 + m, r = n - k1;
+    if ((e = launch_leaf(s, A, X, n, k0, m, perm, st)) != hipSuccess) return e;
+    float* D = X + k0 * n + k0;          // L11^{-1}, lower
+    float* Xp = X + k0 * n;              // block row p of X
+    float* L21 = A + k1 * n + k0;
+    // X[p, 0:k0] = D X[p, 0:k0]  and  L21 = A21 D^T  (both in place; the
+    // second overwrites its own A operand, so one workgroup per slab)
+    SlabArgs g1{m, k0, m, D, n, Xp, n, 0, Xp, n, 1.f, 0.f, 0, 0, st};
+    SlabArgs g2{r, m, m, L21, n, D, n, 1, L21, n, 1.f, 0.f, 0, 0, st};
+    if ((e = launch_slab_pair(s, g1, kAny, &g2, 1)) != hipSuccess) return e;
+    if (r == 0) continue;
+    // A22 -= L21 L21^T (lower)  and  X[k1:, 0:k1] -= L21 X[p, 0:k1]
+    SlabArgs g3{r, r, m, L21, n, L21, n, 1, A + k1 * n + k1, n, -1.f, 1.f, 1, 0, st};
+    SlabArgs g4{r, k1, m, L21, n, Xp, n, 0, X + k1 * n, n, -1.f, 1.f, 0, 0, st};
+    if ((e = launch_slab_pair(s, g3, kAny, &g4, kAny)) != hipSuccess) return e;
   }
   return hipSuccess;
 }
@@ -188,18 +189,14 @@ gptq_status enqueue_factor(hipStream_t s, const float* H, int64_t n, const gptq_
   float* A = reinterpret_cast<float*>(ws + L.A);
   float* X = reinterpret_cast<float*>(ws + L.X);
   {
-    Timed t(GPTQ_PROF_PREP, s);
     HIP_TRY(launch_status_init(s, st), "status init");
     HIP_TRY(launch_fill_f32(s, X, (size_t)n * n, 0.f), "fill");
     HIP_TRY(launch_prep_diag(s, H, n, diag, lam, p->damp, st), "prep diag");
     HIP_TRY(launch_order(s, diag, n, p->n_quant, p->act_order, perm, invperm), "order");
     HIP_TRY(launch_build_flipped(s, H, n, perm, diag, lam, A, st), "build");
   }
-  HIP_TRY(factor_rec(s, A, X, n, 0, n, perm, st), "factor");
-  {
-    Timed t(GPTQ_PROF_PREP, s);
-    HIP_TRY(launch_rotate(s, X, A, n), "rotate");
-  }
+  HIP_TRY(factor_panels(s, A, X, n, perm, st), "factor");
+  HIP_TRY(launch_rotate(s, X, A, n), "rotate");
   return GPTQ_OK;
 }
 
@@ -313,7 +310,7 @@ gptq_status gptq_accumulate_hessian(void* stream, const void* X, gptq_dtype xdt,
 
 gptq_status gptq_workspace_bytes(int64_t d_out, int64_t n, const gptq_params* p, size_t* bytes) {
   if (!bytes) return fail(GPTQ_EINVAL, "bytes is NULL");
-  gptq_status st = check_params(d_out, n, p);
+  gptq_status st = d_out == 0 ? check_factor_params(n, p) : check_params(d_out, n, p);
   if (st != GPTQ_OK) return st;
   *bytes = q_layout(d_out, n, p).total;
   return GPTQ_OK;
@@ -323,11 +320,12 @@ gptq_status gptq_factor_hinv(void* stream, const float* H, int64_t n, const gptq
                              void* workspace, size_t workspace_bytes, float* U_out, int32_t* perm_out,
                              int64_t* fail_col) {
   hipStream_t s = (hipStream_t)stream;
-  gptq_status st = check_params(0, n, p);
+  gptq_status st = check_factor_params(n, p);
   if (st != GPTQ_OK) return st;
   if (!H || !U_out) return fail(GPTQ_EINVAL, "H or U_out is NULL");
   const QLayout L = q_layout(0, n, p);
   if ((st = check_ws(workspace, workspace_bytes, L.total)) != GPTQ_OK) return st;
+  if (fail_col) *fail_col = -1;
   char* ws = reinterpret_cast<char*>(workspace);
   if ((st = enqueue_factor(s, H, n, p, ws, L)) != GPTQ_OK) return st;
   HIP_TRY(hipMemcpyAsync(U_out, ws + L.A, sizeof(float) * n * n, hipMemcpyDeviceToDevice, s), "copy U");
@@ -357,6 +355,8 @@ gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int
   char* ws = reinterpret_cast<char*>(workspace);
   DevStatus* dst = reinterpret_cast<DevStatus*>(ws + L.status);
   int32_t* perm = reinterpret_cast<int32_t*>(ws + L.perm);
+  {
+  Timed whole(GPTQ_PROF_QUANTIZE, s);
   int32_t* invperm = reinterpret_cast<int32_t*>(ws + L.invperm);
   float* U = reinterpret_cast<float*>(ws + L.A);
   float* Wf = reinterpret_cast<float*>(ws + L.Wf);
@@ -365,11 +365,8 @@ gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int
   float* loss = out->row_loss ? out->row_loss : reinterpret_cast<float*>(ws + L.loss);
 
   if ((st = enqueue_factor(s, H, n, p, ws, L)) != GPTQ_OK) return st;
-  {
-    Timed t(GPTQ_PROF_PREP, s);
-    HIP_TRY(launch_w_prep(s, W, wdt == GPTQ_BF16, d_out, n, ldw, perm, Wf, dst), "w prep");
-    HIP_TRY(launch_fill_f32(s, loss, (size_t)d_out, 0.f), "fill");
-  }
+  HIP_TRY(launch_w_prep(s, W, wdt == GPTQ_BF16, d_out, n, ldw, perm, Wf, dst), "w prep");
+  HIP_TRY(launch_fill_f32(s, loss, (size_t)d_out, 0.f), "fill");
   const int64_t nq = p->n_quant;
   const int B = p->block;
   for (int64_t i0 = 0; i0 < nq; i0 += B) {
@@ -377,24 +374,23 @@ gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int
     SweepArgs a{};
     a.Wf = Wf; a.ldw = n; a.U = U; a.ldu = n; a.d_out = d_out; a.i0 = i0; a.ncols = nc;
     a.block = B; a.group = p->group; a.bits = p->bits;
+    a.gbase = i0 / p->group;
+    a.gshift = 31;
+    if (p->group < B)
+      for (int sh = 0; sh < 31; ++sh)
+        if ((1 << sh) == p->group) a.gshift = sh;
     a.scales = out->scales; a.zeros = out->zeros; a.ngroups = nq / p->group;
     a.codes = codes; a.n_quant = nq; a.E = E; a.row_loss = loss; a.st = dst;
-    {
-      Timed t(GPTQ_PROF_SWEEP, s);
-      HIP_TRY(launch_sweep(s, a), "sweep");
-    }
+    HIP_TRY(launch_sweep(s, a), "sweep");
     const int64_t i1 = i0 + nc;
     if (i1 < n) {
-      Timed t(GPTQ_PROF_TRAILING, s);
-      GemmArgs g{d_out, n - i1, nc, E, B, 0, U + i0 * n + i1, n, 0, Wf + i1, n, -1.f, 1.f, 0, 0, dst};
-      HIP_TRY(launch_gemm_f32(s, g), "trailing update");
+      SlabArgs g{d_out, n - i1, nc, E, B, U + i0 * n + i1, n, 0, Wf + i1, n, -1.f, 1.f, 0, 0, dst};
+      HIP_TRY(launch_slab(s, g, 1 << 30), "trailing update");
     }
   }
-  {
-    Timed t(GPTQ_PROF_PACK, s);
-    HIP_TRY(launch_finish(s, Wf, codes, invperm, d_out, n, nq, p->group, out->w_hat, out->codes, out->g_idx),
-            "finish");
-    if (out->qweight) HIP_TRY(launch_pack(s, codes, nq, invperm, d_out, nq, p->bits, out->qweight), "pack");
+  HIP_TRY(launch_finish(s, Wf, codes, invperm, d_out, n, nq, p->group, out->w_hat, out->codes, out->g_idx),
+          "finish");
+  if (out->qweight) HIP_TRY(launch_pack(s, codes, nq, invperm, d_out, nq, p->bits, out->qweight), "pack");
   }
   return read_status(s, dst, perm, fail_col);
 }

@@ -193,6 +193,104 @@ k_hessian_bf16(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx
       }
 }
 
+// Same tile with 8 waves (2 per SIMD): wave (wm, wn) in a 2 x 4 grid owns
+// 128 x 64 of the tile (4 x 2 accumulators); threads 0-255 stage the A
+// block of a stage and threads 256-511 the B block, so each thread keeps one
+// 8 x 8 block in flight. Two waves per SIMD let one wave's transposes and
+// LDS traffic overlap the other's MFMAs.
+template <bool kAligned>
+__global__ void __launch_bounds__(512)
+k_hessian_bf16_w8(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx,
+                  float* __restrict__ part, int64_t chunk) {
+  __shared__ uint32_t smem[2 * 2 * kHStage];
+  const int nt = (int)ceil_div(n, kHT);
+  int bi, bj;
+  upper_tile(blockIdx.x, nt, bi, bj);
+  const int split = blockIdx.y;
+  const int64_t kbeg = (int64_t)split * chunk;
+  const int64_t kend = min(T, kbeg + chunk);
+  const int64_t iA = (int64_t)bi * kHT, iB = (int64_t)bj * kHT;
+  float* __restrict__ P = part + (int64_t)split * n * n;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int half = tid >> 8;                     // 0: stages A, 1: stages B
+  const int lt = tid & 255;
+  const int lb_c = lt >> 3, lb_t = lt & 7;
+  const int64_t ibase = half ? iB : iA;
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+  const int64_t nstage = kend > kbeg ? ceil_div(kend - kbeg, kHBK) : 0;
+  uint4 rr[8];
+  if (nstage > 0) {
+    load_block<kAligned>(X, ldx, kbeg + 8 * lb_t, kend, ibase + 8 * lb_c, n, rr);
+    store_block_t(smem + half * kHStage, 8 * lb_c, 4 * lb_t, rr);
+  }
+  __syncthreads();
+
+  for (int64_t st = 0; st < nstage; ++st) {
+    const int cur = (int)(st & 1);
+    const bool more = st + 1 < nstage;
+    if (more) load_block<kAligned>(X, ldx, kbeg + (st + 1) * kHBK + 8 * lb_t, kend, ibase + 8 * lb_c, n, rr);
+    const uint32_t* sA = smem + cur * 2 * kHStage;
+    const uint32_t* sB = sA + kHStage;
+#pragma unroll
+    for (int ks = 0; ks < kHBK / 16; ++ks) {
+      bf16x8_t af[4], bfr[2];
+      const int koff = 8 * ks + 4 * (lane >> 5);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const int row = 128 * wm + 32 * mb + (lane & 31);
+        af[mb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(sA + row * kHPitch + koff));
+      }
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const int row = 64 * wn + 32 * nb + (lane & 31);
+        bfr[nb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(sB + row * kHPitch + koff));
+      }
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
+    }
+    if (more) store_block_t(smem + (cur ^ 1) * 2 * kHStage + half * kHStage, 8 * lb_c, 4 * lb_t, rr);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t i = iA + 128 * wm + 32 * mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int64_t j = iB + 64 * wn + 32 * nb + (lane & 31);
+        if (i < n && j < n) P[i * n + j] = acc[mb][nb][r];
+      }
+}
+
+hipError_t launch_hessian_partials_bf16_w8(hipStream_t s, const uint16_t* X, int64_t T, int64_t n,
+                                           int64_t ldx, float* part, int splits) {
+  const int nt = (int)ceil_div(n, kHT);
+  const int64_t chunk = ceil_div(ceil_div(T, splits), kHBK) * kHBK;
+  dim3 grid(nt * (nt + 1) / 2, splits);
+  const bool aligned = (n % 8 == 0) && (ldx % 8 == 0) && ((uintptr_t)X % 16 == 0);
+  if (aligned)
+    hipLaunchKernelGGL(k_hessian_bf16_w8<true>, grid, dim3(512), 0, s, X, T, n, ldx, part, chunk);
+  else
+    hipLaunchKernelGGL(k_hessian_bf16_w8<false>, grid, dim3(512), 0, s, X, T, n, ldx, part, chunk);
+  return hipGetLastError();
+}
+
 hipError_t launch_hessian_partials_bf16(hipStream_t s, const uint16_t* X, int64_t T, int64_t n,
                                         int64_t ldx, float* part, int splits) {
   const int nt = (int)ceil_div(n, kHT);

@@ -44,27 +44,42 @@ __device__ inline float row_max16(float v) {
 }
 
 template <int CPL>
+struct Regs {
+  float v[CPL];
+};
+
+template <int CPL>
 struct SweepState {
   float w[CPL];
   float ev[CPL];
   uint32_t qv[CPL];
+  float un[2][CPL];  // U rows, loaded one step ahead (even / odd steps)
+  float invn[2];     // 1 / U_jj for the same steps
   float s, inv_s, z, loss;
+  int nc, gmask;   // columns in this block; group-1 when groups split the block, else -1
+};
+
+struct Grid {
+  float s, z, inv_s;
 };
 
 // (s, z) from the current values of columns [lo, hi) of this block's row
-// (registers) plus, when the group runs past the block, columns
-// [i0 + B, i0 + hi) read from Wf.
+// (the lane's CPL registers, passed by value) plus, when the group runs past
+// the block, columns [i0 + B, i0 + hi) read from Wf. Groups are at least 8
+// columns wide, so inside a block this code is instantiated only at every
+// 8th unrolled step (inlining it into every step would overflow the
+// instruction cache).
 template <int CPL>
-__device__ inline void group_start(SweepState<CPL>& S, const SweepArgs& a, int L, int64_t row,
-                                   bool row_ok, int lo, int hi, float maxq) {
+__device__ __forceinline__ Grid group_start(const Regs<CPL>& w, const SweepArgs& a, int L,
+                                            int64_t row, bool row_ok, int lo, int hi, float maxq) {
   constexpr int B = 16 * CPL;
   float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     const int col = L * CPL + c;
     if (col >= lo && col < hi) {
-      mn = fminf(mn, S.w[c]);
-      mx = fmaxf(mx, S.w[c]);
+      mn = fminf(mn, w.v[c]);
+      mx = fmaxf(mx, w.v[c]);
     }
   }
   if (hi > B && row_ok) {
@@ -82,39 +97,68 @@ __device__ inline void group_start(SweepState<CPL>& S, const SweepArgs& a, int L
     xmin = -1.f;
     xmax = 1.f;
   }
-  S.s = (xmax - xmin) / maxq;
-  S.z = rintf(-xmin / S.s);
-  S.inv_s = 1.f / S.s;
+  Grid g;
+  g.s = (xmax - xmin) / maxq;
+  g.z = rintf(-xmin / g.s);
+  g.inv_s = 1.f / g.s;
   if (row_ok && L == 0) {
-    const int64_t gi = (a.i0 + lo) / a.group;
-    a.scales[row * a.ngroups + gi] = S.s;
-    a.zeros[row * a.ngroups + gi] = (uint8_t)S.z;
+    const int64_t gi = a.gbase + (lo >> a.gshift);
+    a.scales[row * a.ngroups + gi] = g.s;
+    a.zeros[row * a.ngroups + gi] = (uint8_t)g.z;
   }
+  return g;
+}
+
+template <int CPL>
+__device__ __forceinline__ void start_group(SweepState<CPL>& S, const SweepArgs& a, int L, int64_t row,
+                                   bool row_ok, int lo, float maxq) {
+  Regs<CPL> r;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) r.v[c] = S.w[c];
+  const Grid g = group_start<CPL>(r, a, L, row, row_ok, lo, lo + a.group, maxq);
+  S.s = g.s;
+  S.z = g.z;
+  S.inv_s = g.inv_s;
+}
+
+template <int CPL, int P>
+__device__ __forceinline__ void load_urow(SweepState<CPL>& S, const float (*sU)[16 * CPL],
+                                          const float* sInv, int L, int j) {
+  const float* ur = &sU[j][L * CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; c += 2) {
+    const float2 u = *reinterpret_cast<const float2*>(ur + c);
+    S.un[P][c] = u.x;
+    S.un[P][c + 1] = u.y;
+  }
+  S.invn[P] = sInv[j];
 }
 
 template <int CPL, int J>
 __device__ inline void sweep_step(SweepState<CPL>& S, const SweepArgs& a, const float (*sU)[16 * CPL],
                                   const float* sInv, int L, int64_t row, bool row_ok, float maxq) {
+  constexpr int B = 16 * CPL;
   constexpr int O = J / CPL, C = J % CPL;
-  if (J >= a.ncols) return;
-  if (J > 0 && ((a.i0 + J) % a.group) == 0) group_start<CPL>(S, a, L, row, row_ok, J, J + a.group, maxq);
+  if (J >= S.nc) return;
+  if constexpr (J > 0 && (J % 8) == 0) {
+    if ((J & S.gmask) == 0) start_group<CPL>(S, a, L, row, row_ok, J, maxq);
+  }
+  // this step's U row was loaded by the previous step; start the next load
+  constexpr int P = J & 1;
+  const float* u = S.un[P];
+  const float invd = S.invn[P];
+  if constexpr (J + 1 < B) load_urow<CPL, P ^ 1>(S, sU, sInv, L, J + 1);
   const float wj = bcast16<O>(S.w[C]);
   const float q = fminf(fmaxf(rintf(wj * S.inv_s) + S.z, 0.f), maxq);
   const float what = S.s * (q - S.z);
-  const float e = (wj - what) * sInv[J];
+  const float e = (wj - what) * invd;
   S.loss = fmaf(e, e, S.loss);
-  const float* ur = &sU[J][L * CPL];
 #pragma unroll
-  for (int c = 0; c < CPL; c += 2) {
-    const float2 u = *reinterpret_cast<const float2*>(ur + c);
-    S.w[c + 0] = fmaf(-e, u.x, S.w[c + 0]);
-    S.w[c + 1] = fmaf(-e, u.y, S.w[c + 1]);
-  }
-  if (L == O) {
-    S.w[C] = what;
-    S.qv[C] = (uint32_t)q;
-    S.ev[C] = e;
-  }
+  for (int c = 0; c < CPL; ++c) S.w[c] = fmaf(-e, u[c], S.w[c]);
+  const bool own = L == O;
+  S.w[C] = own ? what : S.w[C];
+  S.qv[C] = own ? (uint32_t)q : S.qv[C];
+  S.ev[C] = own ? e : S.ev[C];
 }
 
 template <int CPL, int... Js>
@@ -140,17 +184,36 @@ k_sweep(SweepArgs a) {
   const int nc = (int)a.ncols;
   const float maxq = (float)((1 << a.bits) - 1);
 
-  // strictly-upper U tile of the block and 1 / U_jj
-  for (int e = tid; e < B * B; e += 256) {
-    const int r = e / B, c = e % B;
-    float v = 0.f;
-    if (c > r && c < nc) v = a.U[(a.i0 + r) * a.ldu + a.i0 + c];
-    sU[r][c] = v;
+  // strictly-upper U tile of the block and 1 / U_jj (float4 loads; the
+  // tile's rows start 16-byte aligned when ldu and i0 are multiples of 4)
+  const float* Ublk = a.U + a.i0 * a.ldu + a.i0;
+  const bool vec = ((a.ldu & 3) == 0) && ((a.i0 & 3) == 0) && (((uintptr_t)a.U & 15) == 0);
+  constexpr int NV = B * B / 4 / 256;   // float4 per thread
+  // issue every prologue load (U tile, its diagonal, this row's weights)
+  // before the first store so the latencies overlap
+  float ut[NV][4];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int e4 = tid + 256 * v;
+    const int r = e4 / (B / 4), c0 = 4 * (e4 % (B / 4));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ut[v][q] = 0.f;
+    if (r < nc) {
+      const float* src = Ublk + (int64_t)r * a.ldu + c0;
+      if (vec && c0 + 3 < nc) {
+        const float4 t = *reinterpret_cast<const float4*>(src);
+        ut[v][0] = t.x; ut[v][1] = t.y; ut[v][2] = t.z; ut[v][3] = t.w;
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) ut[v][q] = (c0 + q < nc) ? src[q] : 0.f;
+      }
+    }
   }
-  for (int r = tid; r < B; r += 256) sInv[r] = r < nc ? 1.f / a.U[(a.i0 + r) * a.ldu + a.i0 + r] : 0.f;
-
+  const float diag = (tid < B && tid < nc) ? Ublk[(int64_t)tid * a.ldu + tid] : 1.f;
   SweepState<CPL> S;
   S.loss = 0.f;
+  S.nc = nc;
+  S.gmask = (a.group < B) ? a.group - 1 : -1;   // groups nest: a power of two below B
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
     const int col = L * CPL + c;
@@ -158,17 +221,26 @@ k_sweep(SweepArgs a) {
     S.ev[c] = 0.f;
     S.qv[c] = 0;
   }
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int e4 = tid + 256 * v;
+    const int r = e4 / (B / 4), c0 = 4 * (e4 % (B / 4));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sU[r][c0 + q] = (c0 + q > r) ? ut[v][q] : 0.f;
+  }
+  if (tid < B) sInv[tid] = tid < nc ? 1.f / diag : 0.f;
   __syncthreads();
 
   if ((a.i0 % a.group) == 0) {
-    group_start<CPL>(S, a, L, row, row_ok, 0, a.group, maxq);
+    start_group<CPL>(S, a, L, row, row_ok, 0, maxq);
   } else {
-    const int64_t gi = a.i0 / a.group;
+    const int64_t gi = a.gbase;
     S.s = row_ok ? a.scales[row * a.ngroups + gi] : 1.f;
     S.z = row_ok ? (float)a.zeros[row * a.ngroups + gi] : 0.f;
     S.inv_s = 1.f / S.s;
   }
 
+  load_urow<CPL, 0>(S, sU, sInv, L, 0);
   sweep_all<CPL>(S, a, sU, sInv, L, row, row_ok, maxq, std::make_integer_sequence<int, B>{});
 
   if (row_ok) {

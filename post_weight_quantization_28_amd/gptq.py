@@ -16,8 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libgptq.so")
 
 OK, EINVAL, ENOTPD, ENONFINITE, EHIP, EWORKSPACE = 0, -1, -2, -3, -4, -5
 BF16, F32 = 0, 1
-PROF_CLASSES = ["hessian_syrk", "hessian_reduce", "prep", "factor_leaf",
-                "factor_gemm", "sweep", "trailing", "pack"]
+PROF_CLASSES = ["hessian_syrk", "hessian_reduce", "quantize"]
 
 
 class GPTQError(RuntimeError):
@@ -216,7 +215,7 @@ def factor_hinv(H, damp=0.01, act_order=False, n_quant=None, workspace=None):
     processing order, and the processing-order permutation."""
     lib = load()
     n = H.shape[0]
-    p = make_params(4, 1, damp, 128, act_order, n_quant, n)
+    p = make_params(4, 128, damp, 128, act_order, n_quant, n)
     need = workspace_bytes(0, n, p)
     ws, wsp = _workspace(need, H.device, workspace)
     U = torch.empty((n, n), dtype=torch.float32, device=H.device)

@@ -82,7 +82,7 @@ CASES = [
     # name, workload kwargs, param overrides
     ("c1", dict(), dict()),
     ("c2", dict(d_out=200, n=640, T=8192), dict()),
-    ("c3", dict(d_out=136, n=768, T=8192), dict()),
+    ("c3", dict(d_out=512, n=1024, T=8192), dict()),
     ("c5", dict(d_out=128, n=512, T=8192, aug_rank=32), dict()),
     ("c2", dict(d_out=64, n=512, T=4096), dict(block=64, group=32)),
     ("c2", dict(d_out=48, n=512, T=4096), dict(block=32, group=256)),
