@@ -27,12 +27,10 @@ __device__ inline void raise_status(DevStatus* st, int flag, long long col) {
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // ---- hessian.hip
-// Token-chunk splits used for n x n fp32 partials (fixed per (T, dtype)).
-int hessian_splits(int64_t T, int xdt_bf16);
+// Token-chunk splits used for n x n fp32 partials (fixed per (T, n)).
+int hessian_splits(int64_t T, int64_t n);
 hipError_t launch_hessian_partials_bf16(hipStream_t s, const uint16_t* X, int64_t T,
                                         int64_t n, int64_t ldx, float* part, int splits);
-hipError_t launch_hessian_partials_bf16_w8(hipStream_t s, const uint16_t* X, int64_t T,
-                                           int64_t n, int64_t ldx, float* part, int splits);
 hipError_t launch_hessian_partials_f32(hipStream_t s, const float* X, int64_t T,
                                        int64_t n, int64_t ldx, float* part, int splits);
 hipError_t launch_hessian_reduce(hipStream_t s, const float* part, int splits, int64_t n,

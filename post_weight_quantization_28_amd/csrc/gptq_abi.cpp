@@ -270,7 +270,7 @@ gptq_status gptq_hessian_workspace_bytes(int64_t T, int64_t n, gptq_dtype xdt, s
     *bytes = 0;
     return GPTQ_OK;
   }
-  const int sp = hessian_splits(T, xdt == GPTQ_BF16);
+  const int sp = hessian_splits(T, n);
   *bytes = (size_t)sp * n * n * sizeof(float);
   return GPTQ_OK;
 }
@@ -290,7 +290,7 @@ gptq_status gptq_accumulate_hessian(void* stream, const void* X, gptq_dtype xdt,
     if (zero_first) HIP_TRY(launch_fill_f32(s, H, (size_t)n * n, 0.f), "fill");
     return GPTQ_OK;
   }
-  const int sp = hessian_splits(T, xdt == GPTQ_BF16);
+  const int sp = hessian_splits(T, n);
   float* part = reinterpret_cast<float*>(workspace);
   {
     Timed t(GPTQ_PROF_HESSIAN_SYRK, s);

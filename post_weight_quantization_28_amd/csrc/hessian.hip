@@ -8,17 +8,20 @@
 // Design (MI355X):
 //  * Only output tiles on or above the diagonal are computed (symmetry).
 //  * 256x256 output tile per workgroup of 4 waves (2x2), each wave a 128x128
-//    block = 4x4 v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 per lane).
+//    block = 4x4 v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 per lane,
+//    held in AGPRs).
 //  * X is row-major (tokens x channels) while MFMA wants 8 consecutive
-//    tokens per lane: each thread loads an 8-token x 8-channel block with
-//    eight 16-byte loads, transposes it in registers with v_perm_b32 and
-//    stores eight 16-byte rows into LDS laid out [channel][token]. Row pitch
-//    36 dwords keeps both the transposed stores and the fragment reads free
-//    of bank conflicts. Two LDS stages (144 KiB) double-buffer the loads.
+//    tokens of one channel per lane. For 16-byte aligned X the tile streams
+//    through a 4-deep LDS ring filled by LDS-DMA in X's own layout and read
+//    with gfx950's transposing LDS reads (k_hessian_dma below). Other X
+//    (odd row stride) takes k_hessian_bf16: 16-byte register loads of
+//    8x8 blocks transposed with v_perm_b32 into a [channel][token] LDS layout.
 //  * The token range is split into chunks; each chunk writes an fp32 partial
 //    Gram matrix and a second kernel sums the partials in a fixed order,
 //    scales by 2, adds to H and mirrors it: deterministic, exactly
-//    symmetric, and the chunked sum bounds fp32 accumulation error.
+//    symmetric, and the chunked sum bounds fp32 accumulation error. The
+//    number of chunks is chosen so that tiles x chunks fills whole waves of
+//    the 256 CUs (one 128-160 KiB workgroup per CU).
 #include "common.h"
 
 namespace gq {
@@ -31,14 +34,24 @@ constexpr int kHBK = 64;      // tokens per LDS stage
 constexpr int kHPitch = 36;   // dwords per LDS row (32 data + 4 pad)
 constexpr int kHStage = kHT * kHPitch;  // dwords per operand per stage
 
-int hessian_splits(int64_t T, int xdt_bf16) {
-  // ~16384 tokens per partial (fp32 MFMA accumulation stays ~1e-6 relative),
-  // at most 8 partials.
-  int64_t s = ceil_div(T, 16384);
-  if (s < 1) s = 1;
-  if (s > 8) s = 8;
-  (void)xdt_bf16;
-  return (int)s;
+int hessian_splits(int64_t T, int64_t n) {
+  // Chunks of at least 4096 tokens (fp32 accumulation of a chunk stays
+  // ~1e-6 relative) and at most 16; among the candidates the count whose
+  // workgroups fill the 256 CUs best, the smallest on ties.
+  const int64_t nt = ceil_div(n, 256);
+  const int64_t tiles = nt * (nt + 1) / 2;
+  int64_t lo = ceil_div(T, 65536), hi = ceil_div(T, 4096);
+  if (lo < 1) lo = 1;
+  if (hi > 16) hi = 16;
+  if (lo > hi) lo = hi;
+  int best = (int)lo;
+  double best_fill = -1.0;
+  for (int64_t sp = lo; sp <= hi; ++sp) {
+    const int64_t items = tiles * sp;
+    const double fill = (double)items / (double)(256 * ceil_div(items, 256));
+    if (fill > best_fill + 1e-9) { best_fill = fill; best = (int)sp; }
+  }
+  return best;
 }
 
 __device__ inline void upper_tile(int t, int nt, int& bi, int& bj) {
@@ -47,6 +60,12 @@ __device__ inline void upper_tile(int t, int nt, int& bi, int& bj) {
   while (t >= nt - row) { t -= nt - row; ++row; }
   bi = row;
   bj = row + t;
+}
+
+// Work item of block b: (split, tile), tile-fastest.
+__device__ inline void hessian_item(int b, int ntile, int& tile, int& split) {
+  split = b / ntile;
+  tile = b - split * ntile;
 }
 
 // Load an 8(token) x 8(channel) bf16 block: rows X[t0+r][c0..c0+7].
@@ -108,9 +127,9 @@ k_hessian_bf16(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx
                float* __restrict__ part, int64_t chunk) {
   __shared__ uint32_t smem[2 * 2 * kHStage];
   const int nt = (int)ceil_div(n, kHT);
-  int bi, bj;
-  upper_tile(blockIdx.x, nt, bi, bj);
-  const int split = blockIdx.y;
+  int tile, split, bi, bj;
+  hessian_item(blockIdx.x, nt * (nt + 1) / 2, tile, split);
+  upper_tile(tile, nt, bi, bj);
   const int64_t kbeg = (int64_t)split * chunk;
   const int64_t kend = min(T, kbeg + chunk);
   const int64_t iA = (int64_t)bi * kHT, iB = (int64_t)bj * kHT;
@@ -193,114 +212,203 @@ k_hessian_bf16(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx
       }
 }
 
-// Same tile with 8 waves (2 per SIMD): wave (wm, wn) in a 2 x 4 grid owns
-// 128 x 64 of the tile (4 x 2 accumulators); threads 0-255 stage the A
-// block of a stage and threads 256-511 the B block, so each thread keeps one
-// 8 x 8 block in flight. Two waves per SIMD let one wave's transposes and
-// LDS traffic overlap the other's MFMAs.
-template <bool kAligned>
-__global__ void __launch_bounds__(512)
-k_hessian_bf16_w8(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx,
-                  float* __restrict__ part, int64_t chunk) {
-  __shared__ uint32_t smem[2 * 2 * kHStage];
+// ---------------------------------------------------------------------------
+// Streaming variant for 16-byte aligned X: LDS-DMA staging + transpose reads.
+//
+//  * global_load_lds_dwordx4 moves 16-byte chunks (8 channels of one token)
+//    straight from HBM into LDS without passing through VGPRs, so four
+//    32-token stages (128 KiB of LDS) can be in flight at once: the load of
+//    stage s+3 is issued while stage s is multiplied.
+//  * LDS keeps X's own layout, [token][channel] with 512-byte rows per
+//    operand; the 16-byte chunk index of row t is XOR-swizzled with
+//    kSwz[t % 4] (each DMA lane fetches the global chunk that belongs to its
+//    fixed LDS slot).
+//  * ds_read_b64_tr_b16 turns it into MFMA operands: within each group of 16
+//    lanes, lane a + 4j reads 4 channels of token j and lane 4a + b receives
+//    channel b of lane a's piece for the 4 tokens, i.e. 4 consecutive tokens
+//    of one channel; two such reads give the 8-token K-slice that
+//    v_mfma_f32_32x32x16_bf16 takes per lane. A group's 16 reads hit 4 rows
+//    x 32 bytes; the swizzle spreads them over all banks.
+//  * Chunks past the last channel or the end of the token chunk are fetched
+//    from a zero source, so ragged edges need no predication in the loop.
+//  * The compiler is not told about the DMA (inline asm): it would otherwise
+//    wait for every outstanding DMA before each LDS read. Completion is
+//    tracked by hand with vmcnt, and one s_barrier per stage makes a stage
+//    visible to all waves and frees the slot that the next DMA overwrites.
+// ---------------------------------------------------------------------------
+constexpr int kDK = 32;                  // tokens per stage
+constexpr int kDOpBytes = kDK * 512;     // one operand of one stage
+constexpr int kDSlotBytes = 2 * kDOpBytes;
+
+__device__ __align__(16) const uint32_t kZeroChunk[4] = {0u, 0u, 0u, 0u};
+
+__device__ __forceinline__ int dma_swz(int t) {
+  // XOR applied to the 16-byte chunk index of token row t (values < 16, so
+  // a row's 32 chunks are permuted among themselves).
+  return (0xAC60 >> (4 * (t & 3))) & 15;   // t%4 -> 0, 6, 12, 10
+}
+
+// Wait until at most `stages` stages of this wave's DMA are outstanding, then
+// barrier; one asm block, so no LDS read can be scheduled between the two.
+__device__ __forceinline__ void wait_dma_barrier(int stages) {
+  if (stages <= 0) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  else if (stages == 1) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
+  else if (stages == 2) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
+}
+
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds_base) : "memory");
+}
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ v4i16_t lds_tr16(uint32_t byte_off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) v4i16_t*>(byte_off));
+}
+
+template <int kSlots>
+__global__ void __launch_bounds__(256)
+k_hessian_dma(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx,
+              float* __restrict__ part, int64_t chunk) {
+  __shared__ __align__(16) uint8_t dsm[kSlots * kDSlotBytes];
   const int nt = (int)ceil_div(n, kHT);
-  int bi, bj;
-  upper_tile(blockIdx.x, nt, bi, bj);
-  const int split = blockIdx.y;
+  int tile, split, bi, bj;
+  hessian_item(blockIdx.x, nt * (nt + 1) / 2, tile, split);
+  upper_tile(tile, nt, bi, bj);
   const int64_t kbeg = (int64_t)split * chunk;
   const int64_t kend = min(T, kbeg + chunk);
   const int64_t iA = (int64_t)bi * kHT, iB = (int64_t)bj * kHT;
   float* __restrict__ P = part + (int64_t)split * n * n;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
-  const int half = tid >> 8;                     // 0: stages A, 1: stages B
-  const int lt = tid & 255;
-  const int lb_c = lt >> 3, lb_t = lt & 7;
-  const int64_t ibase = half ? iB : iA;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dsm));
 
-  f32x16_t acc[4][2];
+  // DMA plan: a stage is 2 operands x 16 row pairs = 32 wave-instructions;
+  // wave w issues q = 0..7 -> instruction 8w+q: operand (8w+q)/16, rows
+  // 2p, 2p+1 with p = (8w+q)%16; lane l fills row 2p + l/32, slot chunk l%32.
+  const uint16_t* src[8];
+  bool cvalid[8];
+  int trow[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int idx = 8 * wave + q;
+    const int op = idx >> 4, p = idx & 15;
+    const int t = 2 * p + (lane >> 5);
+    const int c = (lane & 31) ^ dma_swz(t);
+    const int64_t ch = (op ? iB : iA) + 8 * c;
+    cvalid[q] = ch < n;
+    trow[q] = t;
+    src[q] = X + (kbeg + t) * ldx + (cvalid[q] ? ch : 0);
+  }
+  auto issue = [&](int st, uint32_t slot) {
+    const int64_t tok = kbeg + st * kDK;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int idx = 8 * wave + q;
+      const int op = idx >> 4, p = idx & 15;
+      const bool ok = cvalid[q] && (tok + trow[q] < kend);
+      const void* g = ok ? (const void*)(src[q] + st * kDK * ldx) : (const void*)kZeroChunk;
+      dma16(g, __builtin_amdgcn_readfirstlane(slot + op * kDOpBytes + p * 1024));
+    }
+  };
+
+  // Transpose-read addressing (per lane, fixed): group G = lane/16, s = lane%16.
+  const int G = lane >> 4, sl = lane & 15;
+  const int trow_off = 8 * (G >> 1) + (sl >> 2);          // + 16 ks + 4 h
+  const int cbase = 2 * (G & 1) + ((sl >> 1) & 1);       // + 16 wm + 4 mb (chunks)
+  const int half8 = (sl & 1) * 8;
+
+  f32x16_t acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 2; ++b)
+    for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  const int64_t nstage = kend > kbeg ? ceil_div(kend - kbeg, kHBK) : 0;
-  uint4 rr[8];
-  if (nstage > 0) {
-    load_block<kAligned>(X, ldx, kbeg + 8 * lb_t, kend, ibase + 8 * lb_c, n, rr);
-    store_block_t(smem + half * kHStage, 8 * lb_c, 4 * lb_t, rr);
-  }
-  __syncthreads();
-
-  for (int64_t st = 0; st < nstage; ++st) {
-    const int cur = (int)(st & 1);
-    const bool more = st + 1 < nstage;
-    if (more) load_block<kAligned>(X, ldx, kbeg + (st + 1) * kHBK + 8 * lb_t, kend, ibase + 8 * lb_c, n, rr);
-    const uint32_t* sA = smem + cur * 2 * kHStage;
-    const uint32_t* sB = sA + kHStage;
+  // Fragments of one 16-token K-step: two transpose reads per 32-row block.
+  struct Frag { v4i16_t a[2][4], b[2][4]; };
+  auto load = [&](uint32_t slot, int ks, Frag& f) {
 #pragma unroll
-    for (int ks = 0; ks < kHBK / 16; ++ks) {
-      bf16x8_t af[4], bfr[2];
-      const int koff = 8 * ks + 4 * (lane >> 5);
+    for (int h = 0; h < 2; ++h) {
+      const int t = 16 * ks + 4 * h + trow_off;
+      const int swz = dma_swz(t);
+      const uint32_t rowA = slot + t * 512 + half8;
+      const uint32_t rowB = rowA + kDOpBytes;
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const int row = 128 * wm + 32 * mb + (lane & 31);
-        af[mb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(sA + row * kHPitch + koff));
-      }
+      for (int mb = 0; mb < 4; ++mb) f.a[h][mb] = lds_tr16(rowA + ((16 * wm + 4 * mb + cbase) ^ swz) * 16);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int row = 64 * wn + 32 * nb + (lane & 31);
-        bfr[nb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(sB + row * kHPitch + koff));
-      }
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
+      for (int nb = 0; nb < 4; ++nb) f.b[h][nb] = lds_tr16(rowB + ((16 * wn + 4 * nb + cbase) ^ swz) * 16);
     }
-    if (more) store_block_t(smem + (cur ^ 1) * 2 * kHStage + half * kHStage, 8 * lb_c, 4 * lb_t, rr);
-    __syncthreads();
+  };
+  auto mma = [&](const Frag& f) {
+    bf16x8_t af[4], bfr[4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+      af[mb] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(f.a[0][mb], f.a[1][mb], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb)
+      bfr[nb] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(f.b[0][nb], f.b[1][nb], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 4; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
+  };
+  auto slot_of = [&](int st) { return lds0 + (uint32_t)(st % kSlots) * kDSlotBytes; };
+
+  // Pipeline: the DMA of stage s + kSlots - 1 is issued while stage s is
+  // multiplied; the barrier that publishes stage s + 1 sits between the two
+  // K-steps of stage s, so the first fragments of s + 1 are read while the
+  // second K-step of s runs.
+  const int nstage = kend > kbeg ? (int)ceil_div(kend - kbeg, kDK) : 0;
+#pragma unroll
+  for (int ps = 0; ps < kSlots - 1; ++ps)
+    if (ps < nstage) issue(ps, slot_of(ps));
+  Frag f0, f1;
+  if (nstage > 0) {
+    wait_dma_barrier(min(kSlots - 2, nstage - 1));
+    load(slot_of(0), 0, f0);
+  }
+  for (int st = 0; st < nstage; ++st) {
+    load(slot_of(st), 1, f1);
+    mma(f0);
+    if (st + 1 < nstage) {
+      wait_dma_barrier(min(kSlots - 3, nstage - 2 - st));
+      if (st + kSlots - 1 < nstage) issue(st + kSlots - 1, slot_of(st + kSlots - 1));
+      load(slot_of(st + 1), 0, f0);
+    }
+    mma(f1);
   }
 
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < 4; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t i = iA + 128 * wm + 32 * mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int64_t j = iB + 64 * wn + 32 * nb + (lane & 31);
+        const int64_t j = iB + 128 * wn + 32 * nb + (lane & 31);
         if (i < n && j < n) P[i * n + j] = acc[mb][nb][r];
       }
-}
-
-hipError_t launch_hessian_partials_bf16_w8(hipStream_t s, const uint16_t* X, int64_t T, int64_t n,
-                                           int64_t ldx, float* part, int splits) {
-  const int nt = (int)ceil_div(n, kHT);
-  const int64_t chunk = ceil_div(ceil_div(T, splits), kHBK) * kHBK;
-  dim3 grid(nt * (nt + 1) / 2, splits);
-  const bool aligned = (n % 8 == 0) && (ldx % 8 == 0) && ((uintptr_t)X % 16 == 0);
-  if (aligned)
-    hipLaunchKernelGGL(k_hessian_bf16_w8<true>, grid, dim3(512), 0, s, X, T, n, ldx, part, chunk);
-  else
-    hipLaunchKernelGGL(k_hessian_bf16_w8<false>, grid, dim3(512), 0, s, X, T, n, ldx, part, chunk);
-  return hipGetLastError();
 }
 
 hipError_t launch_hessian_partials_bf16(hipStream_t s, const uint16_t* X, int64_t T, int64_t n,
                                         int64_t ldx, float* part, int splits) {
   const int nt = (int)ceil_div(n, kHT);
+  const int items = nt * (nt + 1) / 2 * splits;
   const int64_t chunk = ceil_div(ceil_div(T, splits), kHBK) * kHBK;
-  dim3 grid(nt * (nt + 1) / 2, splits);
   const bool aligned = (n % 8 == 0) && (ldx % 8 == 0) && ((uintptr_t)X % 16 == 0);
   if (aligned)
-    hipLaunchKernelGGL(k_hessian_bf16<true>, grid, dim3(256), 0, s, X, T, n, ldx, part, chunk);
+    hipLaunchKernelGGL(k_hessian_dma<4>, dim3(items), dim3(256), 0, s, X, T, n, ldx, part, chunk);
   else
-    hipLaunchKernelGGL(k_hessian_bf16<false>, grid, dim3(256), 0, s, X, T, n, ldx, part, chunk);
+    hipLaunchKernelGGL(k_hessian_bf16<false>, dim3(items), dim3(256), 0, s, X, T, n, ldx, part, chunk);
   return hipGetLastError();
 }
 
