@@ -15,33 +15,39 @@
 // range) instead of once per tile.
 #include "common.h"
 
+#include <algorithm>
+
 namespace gq {
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kSM = 128;         // slab rows
 constexpr int kSN = 64;          // column tile
-constexpr int kSK = 128;         // max K
-constexpr int kPA = kSK + 4;     // A pitch ([m][k])
-constexpr int kPBt = kSK + 4;    // B pitch when stored [n][k]
 constexpr int kPBn = kSN + 4;    // B pitch when stored [k][n]
 
+// LDS for K <= KT: the A slab [m][k] and two B tiles. KT = 64 needs 69 KiB,
+// so two workgroups share a CU; KT = 128 needs 135 KiB.
+template <int KT>
 struct SlabSmem {
-  float a[kSM * kPA];
-  float b[2][(kSN * kPBt > kSK * kPBn) ? kSN * kPBt : kSK * kPBn];
+  static constexpr int PA = KT + 4;    // A pitch ([m][k])
+  static constexpr int PBt = KT + 4;   // B pitch when stored [n][k]
+  static constexpr int BSZ = (kSN * PBt > KT * kPBn) ? kSN * PBt : KT * kPBn;
+  float a[kSM * PA];
+  float b[2][BSZ];
 };
 
-// B tile (K x 64) -> registers: 8 float4 per thread. Full, 16-byte aligned
-// tiles take a branch-free path.
-template <bool TB>
-__device__ __forceinline__ void slab_load_b(const SlabArgs& g, int64_t n0, int tid, float4 (&rb)[8]) {
-  const bool full = g.bvec && (TB ? (n0 + kSN <= g.N && g.K == kSK) : (n0 + kSN <= g.N && g.K == kSK));
+// B tile (K x 64) -> registers: KT/16 float4 per thread. Full, 16-byte
+// aligned tiles take a branch-free path.
+template <bool TB, int KT>
+__device__ __forceinline__ void slab_load_b(const SlabArgs& g, int64_t n0, int tid, float4 (&rb)[KT / 16]) {
+  constexpr int V = KT / 16, Q = KT / 4;   // float4 per thread; float4 per B row (TB)
+  const bool full = g.bvec && n0 + kSN <= g.N && g.K == KT;
   if (full) {
 #pragma unroll
-    for (int v = 0; v < 8; ++v) {
+    for (int v = 0; v < V; ++v) {
       const int idx = tid + 256 * v;
       if constexpr (TB) {
-        const int nn = idx >> 5, k4 = idx & 31;
+        const int nn = idx / Q, k4 = idx % Q;
         rb[v] = *reinterpret_cast<const float4*>(g.B + (n0 + nn) * g.ldb + 4 * k4);
       } else {
         const int k = idx >> 4, n4 = idx & 15;
@@ -51,11 +57,11 @@ __device__ __forceinline__ void slab_load_b(const SlabArgs& g, int64_t n0, int t
     return;
   }
 #pragma unroll
-  for (int v = 0; v < 8; ++v) {
+  for (int v = 0; v < V; ++v) {
     const int idx = tid + 256 * v;
     float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-    if constexpr (TB) {   // B stored N x K: rows n, 32 float4 per row
-      const int nn = idx >> 5, k4 = idx & 31;
+    if constexpr (TB) {   // B stored N x K
+      const int nn = idx / Q, k4 = idx % Q;
       const int64_t n = n0 + nn, k = 4 * k4;
       if (n < g.N && k < g.K) {
         const float* p = g.B + n * g.ldb + k;
@@ -85,14 +91,15 @@ __device__ __forceinline__ void slab_load_b(const SlabArgs& g, int64_t n0, int t
   }
 }
 
-template <bool TB>
-__device__ __forceinline__ void slab_store_b(float* s, int tid, const float4 (&rb)[8]) {
+template <bool TB, int KT>
+__device__ __forceinline__ void slab_store_b(float* s, int tid, const float4 (&rb)[KT / 16]) {
+  constexpr int V = KT / 16, Q = KT / 4;
 #pragma unroll
-  for (int v = 0; v < 8; ++v) {
+  for (int v = 0; v < V; ++v) {
     const int idx = tid + 256 * v;
     if constexpr (TB) {
-      const int nn = idx >> 5, k4 = idx & 31;
-      *reinterpret_cast<float4*>(s + nn * kPBt + 4 * k4) = rb[v];
+      const int nn = idx / Q, k4 = idx % Q;
+      *reinterpret_cast<float4*>(s + nn * SlabSmem<KT>::PBt + 4 * k4) = rb[v];
     } else {
       const int k = idx >> 4, n4 = idx & 15;
       *reinterpret_cast<float4*>(s + k * kPBn + 4 * n4) = rb[v];
@@ -113,7 +120,9 @@ __device__ __forceinline__ void slab_load_c(const SlabArgs& g, int64_t m0, int64
 }
 
 template <bool TB, int KT>
-__device__ __forceinline__ void slab_body(const SlabArgs& g, int wg, SlabSmem& sm) {
+__device__ __forceinline__ void slab_body(const SlabArgs& g, int wg, SlabSmem<KT>& sm) {
+  constexpr int PA = SlabSmem<KT>::PA, PBt = SlabSmem<KT>::PBt;
+  constexpr int VA = KT / 8, QA = KT / 4;   // A: float4 per thread; float4 per row
   const int slab = wg / g.nsplit, part = wg % g.nsplit;
   const int64_t m0 = (int64_t)slab * kSM;
   int64_t ntile = ceil_div(g.N, kSN);
@@ -128,11 +137,11 @@ __device__ __forceinline__ void slab_body(const SlabArgs& g, int wg, SlabSmem& s
 
   // prologue: the A slab, the first B tile and the first C tile are all
   // requested before anything waits, so their latencies overlap
-  float4 xa[16];
+  float4 xa[VA];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
+  for (int v = 0; v < VA; ++v) {
     const int idx = tid + 256 * v;
-    const int m = idx >> 5, k = 4 * (idx & 31);
+    const int m = idx / QA, k = 4 * (idx % QA);
     float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
     const int64_t row = m0 + m;
     if (row < g.M && k < g.K) {
@@ -147,28 +156,28 @@ __device__ __forceinline__ void slab_body(const SlabArgs& g, int wg, SlabSmem& s
     }
     xa[v] = x;
   }
-  float4 rb[8];
-  slab_load_b<TB>(g, t0 * kSN, tid, rb);
+  float4 rb[KT / 16];
+  slab_load_b<TB, KT>(g, t0 * kSN, tid, rb);
   float cold[2][16];
   slab_load_c(g, m0, t0 * kSN, wm, wn, lane, cold);
   {
     const float al = g.alpha;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
+    for (int v = 0; v < VA; ++v) {
       const int idx = tid + 256 * v;
-      const int m = idx >> 5, k = 4 * (idx & 31);
-      *reinterpret_cast<float4*>(&sm.a[m * kPA + k]) =
+      const int m = idx / QA, k = 4 * (idx % QA);
+      *reinterpret_cast<float4*>(&sm.a[m * PA + k]) =
           make_float4(al * xa[v].x, al * xa[v].y, al * xa[v].z, al * xa[v].w);
     }
   }
-  slab_store_b<TB>(sm.b[0], tid, rb);
+  slab_store_b<TB, KT>(sm.b[0], tid, rb);
   __syncthreads();
 
   for (int64_t t = t0; t < t1; ++t) {
     const int cur = (int)((t - t0) & 1);
     const int64_t n0 = t * kSN;
     const bool more = t + 1 < t1;
-    if (more) slab_load_b<TB>(g, n0 + kSN, tid, rb);
+    if (more) slab_load_b<TB, KT>(g, n0 + kSN, tid, rb);
     if (t > t0) slab_load_c(g, m0, n0, wm, wn, lane, cold);
     f32x16_t acc[2];
 #pragma unroll
@@ -181,14 +190,14 @@ __device__ __forceinline__ void slab_body(const SlabArgs& g, int wg, SlabSmem& s
       const int kb = 8 * kq + lk;
       float4 fb;
       if constexpr (TB) {
-        fb = *reinterpret_cast<const float4*>(sb + (32 * wn + lr) * kPBt + kb);
+        fb = *reinterpret_cast<const float4*>(sb + (32 * wn + lr) * PBt + kb);
       } else {
         const float* q = sb + kb * kPBn + 32 * wn + lr;
         fb = make_float4(q[0], q[kPBn], q[2 * kPBn], q[3 * kPBn]);
       }
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
-        const float4 fa = *reinterpret_cast<const float4*>(&sm.a[(64 * wm + 32 * a + lr) * kPA + kb]);
+        const float4 fa = *reinterpret_cast<const float4*>(&sm.a[(64 * wm + 32 * a + lr) * PA + kb]);
         acc[a] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa.x, fb.x, acc[a], 0, 0, 0);
         acc[a] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa.y, fb.y, acc[a], 0, 0, 0);
         acc[a] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa.z, fb.z, acc[a], 0, 0, 0);
@@ -203,7 +212,7 @@ __device__ __forceinline__ void slab_body(const SlabArgs& g, int wg, SlabSmem& s
         const int64_t j = n0 + 32 * wn + lr;
         if (i < g.M && j < g.N) g.C[i * g.ldc + j] = acc[a][r] + g.beta * cold[a][r];
       }
-    if (more) slab_store_b<TB>(sm.b[cur ^ 1], tid, rb);
+    if (more) slab_store_b<TB, KT>(sm.b[cur ^ 1], tid, rb);
     __syncthreads();
   }
 }
@@ -213,20 +222,16 @@ struct SlabPair {
   int nwg0;
 };
 
-__global__ void __launch_bounds__(256)
+template <int KT>
+__global__ void __launch_bounds__(256, KT == 64 ? 2 : 1)
 k_slab(SlabPair sp) {
-  __shared__ __align__(16) SlabSmem sm;
+  __shared__ __align__(16) SlabSmem<KT> sm;
   const int which = (int)blockIdx.x >= sp.nwg0;
   const SlabArgs& g = sp.p[which];
   if (g.st != nullptr && g.st->flags != 0) return;
   const int wg = (int)blockIdx.x - (which ? sp.nwg0 : 0);
-  if (g.K > 64) {
-    if (g.tb) slab_body<true, 128>(g, wg, sm);
-    else slab_body<false, 128>(g, wg, sm);
-  } else {
-    if (g.tb) slab_body<true, 64>(g, wg, sm);
-    else slab_body<false, 64>(g, wg, sm);
-  }
+  if (g.tb) slab_body<true, KT>(g, wg, sm);
+  else slab_body<false, KT>(g, wg, sm);
 }
 
 static int slab_setup(SlabArgs& g, int max_split) {
@@ -255,7 +260,11 @@ hipError_t launch_slab_pair(hipStream_t s, SlabArgs a, int split_a, const SlabAr
   }
   const int total = sp.nwg0 + n1;
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_slab, dim3(total), dim3(256), 0, s, sp);
+  const int64_t kmax = std::max<int64_t>(a.K, b ? b->K : 0);
+  if (kmax <= 64)
+    hipLaunchKernelGGL(k_slab<64>, dim3(total), dim3(256), 0, s, sp);
+  else
+    hipLaunchKernelGGL(k_slab<128>, dim3(total), dim3(256), 0, s, sp);
   return hipGetLastError();
 }
 
