@@ -54,6 +54,28 @@ hipError_t launch_status_init(hipStream_t s, DevStatus* st);
 constexpr int kLeaf = 64;
 hipError_t launch_leaf(hipStream_t s, float* A, float* X, int64_t n, int64_t off, int64_t m,
                        const int32_t* perm, DevStatus* st);
+// LDS of one leaf: sCol[k][i] = L[i][k], sRow[i][k] = L[i][k], sInv[k] = 1/L[k][k].
+struct LeafSmem {
+  float sCol[64][64];
+  float sRow[64][68];
+  float sInv[64];
+};
+// The next diagonal block's update and leaf, run beside a trailing update.
+struct LeafTask {
+  const float* L21;      // rows k1.., columns of panel k (row pitch n)
+  float* A;              // flipped matrix (lower part used)
+  float* X;              // L^{-1} being built
+  int64_t n, k1;
+  int m2, mk;            // next block size, panel-k width
+  const int32_t* perm;
+  DevStatus* st;
+};
+struct LeafTaskSmem {
+  float lrows[64][65];
+  float blk[64][65];
+  LeafSmem leaf;
+};
+
 // C[M x N] = alpha * op(A) * op(B) + beta * C, fp32 MFMA.
 //  ta: A stored K x M (element (m,k) at A[k*lda + m]) instead of M x K
 //  tb: B stored N x K (element (k,n) at B[n*ldb + k]) instead of K x N
@@ -87,9 +109,13 @@ struct SlabArgs {
   int nsplit;            // set by the launcher
   const DevStatus* st;
   int bvec;              // set by the launcher: B rows 16-byte aligned
+  int64_t lower_off;     // with lower_only: keep columns j <= i + lower_off
 };
 hipError_t launch_slab(hipStream_t s, SlabArgs g, int max_split);
 hipError_t launch_slab_pair(hipStream_t s, SlabArgs a, int split_a, const SlabArgs* b, int split_b);
+// launch_slab_pair plus one more workgroup (dispatched first) running `lt`.
+hipError_t launch_slab_pair_leaf(hipStream_t s, SlabArgs a, int split_a, const SlabArgs* b,
+                                 int split_b, const LeafTask& lt);
 
 // ---- sweep.hip
 struct SweepArgs {

@@ -156,11 +156,12 @@ hipError_t factor_panels(hipStream_t s, float* A, float* X, int64_t n, const int
                          DevStatus* st) {
   hipError_t e;
   constexpr int kAny = 1 << 30;
+  if ((e = launch_leaf(s, A, X, n, 0, std::min<int64_t>(kLeaf, n), perm, st)) != hipSuccess) return e;
   for (int64_t k0 = 0; k0 < n; k0 += kLeaf) {
     const int64_t m = std::min<int64_t>(kLeaf, n - k0);
     const int64_t k1 = k0 + m, r = n - k1;
-    if ((e = launch_leaf(s, A, X, n, k0, m, perm, st)) != hipSuccess) return e;
-    float* D = X + k0 * n + k0;          // L11^{-1}, lower
+    // the leaf of panel p = [k0, k1) has run: D = L11^{-1} is in X[p, p]
+    float* D = X + k0 * n + k0;
     float* Xp = X + k0 * n;              // block row p of X
     float* L21 = A + k1 * n + k0;
     // X[p, 0:k0] = D X[p, 0:k0]  and  L21 = A21 D^T  (both in place; the
@@ -169,10 +170,16 @@ hipError_t factor_panels(hipStream_t s, float* A, float* X, int64_t n, const int
     SlabArgs g2{r, m, m, L21, n, D, n, 1, L21, n, 1.f, 0.f, 0, 0, st};
     if ((e = launch_slab_pair(s, g1, kAny, &g2, 1)) != hipSuccess) return e;
     if (r == 0) continue;
-    // A22 -= L21 L21^T (lower)  and  X[k1:, 0:k1] -= L21 X[p, 0:k1]
-    SlabArgs g3{r, r, m, L21, n, L21, n, 1, A + k1 * n + k1, n, -1.f, 1.f, 1, 0, st};
+    // One launch: the next diagonal block (m2 rows) is updated and factored
+    // by its own workgroup, while the rest runs
+    //   A[k1+m2:, k1:] -= L21[m2:] L21^T   (lower, i.e. j <= i + m2)
+    //   X[k1:, 0:k1]   -= L21 X[p, 0:k1]   (forward substitution of L X = I)
+    const int64_t m2 = std::min<int64_t>(kLeaf, r);
+    SlabArgs g3{r - m2, r, m, L21 + m2 * n, n, L21, n, 1, A + (k1 + m2) * n + k1, n, -1.f, 1.f, 1, 0, st};
+    g3.lower_off = m2;
     SlabArgs g4{r, k1, m, L21, n, Xp, n, 0, X + k1 * n, n, -1.f, 1.f, 0, 0, st};
-    if ((e = launch_slab_pair(s, g3, kAny, &g4, kAny)) != hipSuccess) return e;
+    LeafTask lt{L21, A, X, n, k1, (int)m2, (int)m, perm, st};
+    if ((e = launch_slab_pair_leaf(s, g3, kAny, &g4, kAny, lt)) != hipSuccess) return e;
   }
   return hipSuccess;
 }

@@ -14,6 +14,7 @@
 // With the slab resident, A is read from memory once per (slab, column
 // range) instead of once per tile.
 #include "common.h"
+#include "leaf.h"
 
 #include <algorithm>
 
@@ -126,7 +127,7 @@ __device__ __forceinline__ void slab_body(const SlabArgs& g, int wg, SlabSmem<KT
   const int slab = wg / g.nsplit, part = wg % g.nsplit;
   const int64_t m0 = (int64_t)slab * kSM;
   int64_t ntile = ceil_div(g.N, kSN);
-  if (g.lower_only) ntile = min(ntile, ceil_div(m0 + kSM, kSN));
+  if (g.lower_only) ntile = min(ntile, ceil_div(m0 + kSM + g.lower_off, kSN));
   const int64_t per = ceil_div(ntile, g.nsplit);
   const int64_t t0 = part * per, t1 = min(ntile, t0 + per);
   if (t0 >= t1) return;
@@ -234,6 +235,27 @@ k_slab(SlabPair sp) {
   else slab_body<false, KT>(g, wg, sm);
 }
 
+// A slab pair plus the next diagonal block's update and leaf in workgroup 0
+// (dispatched first, so the leaf runs while the trailing update streams).
+__global__ void __launch_bounds__(256, 2)
+k_slab_leaf(SlabPair sp, LeafTask lt) {
+  __shared__ __align__(16) union {
+    SlabSmem<64> slab;
+    LeafTaskSmem leaf;
+  } sm;
+  if (lt.st != nullptr && lt.st->flags != 0) return;
+  if (blockIdx.x == 0) {
+    leaf_task_run(lt, sm.leaf);
+    return;
+  }
+  const int b = (int)blockIdx.x - 1;
+  const int which = b >= sp.nwg0;
+  const SlabArgs& g = sp.p[which];
+  const int wg = b - (which ? sp.nwg0 : 0);
+  if (g.tb) slab_body<true, 64>(g, wg, sm.slab);
+  else slab_body<false, 64>(g, wg, sm.slab);
+}
+
 static int slab_setup(SlabArgs& g, int max_split) {
   if (g.M <= 0 || g.N <= 0) return 0;
   g.bvec = ((uintptr_t)g.B % 16 == 0) && (g.ldb % 4 == 0);
@@ -265,6 +287,23 @@ hipError_t launch_slab_pair(hipStream_t s, SlabArgs a, int split_a, const SlabAr
     hipLaunchKernelGGL(k_slab<64>, dim3(total), dim3(256), 0, s, sp);
   else
     hipLaunchKernelGGL(k_slab<128>, dim3(total), dim3(256), 0, s, sp);
+  return hipGetLastError();
+}
+
+hipError_t launch_slab_pair_leaf(hipStream_t s, SlabArgs a, int split_a, const SlabArgs* b,
+                                 int split_b, const LeafTask& lt) {
+  if (a.K > 64 || (b && b->K > 64) || lt.mk > 64 || lt.m2 > 64 || lt.m2 < 1) return hipErrorInvalidValue;
+  SlabPair sp{};
+  sp.p[0] = a;
+  sp.nwg0 = slab_setup(sp.p[0], split_a);
+  int n1 = 0;
+  if (b) {
+    sp.p[1] = *b;
+    n1 = slab_setup(sp.p[1], split_b);
+  } else {
+    sp.p[1] = sp.p[0];
+  }
+  hipLaunchKernelGGL(k_slab_leaf, dim3(1 + sp.nwg0 + n1), dim3(256), 0, s, sp, lt);
   return hipGetLastError();
 }
 
