@@ -6,9 +6,11 @@ Hessian H = 2 X^T X from 131072 bf16 calibration tokens, then quantize_layer
 at 4 bits, group 128, block 128. Inputs are resident in HBM before the timed
 region; every step recomputes everything from X and W.
 
-Prints one JSON line (see the design doc for the fields).
+Prints one JSON line: the step throughput, the Hessian kernel against the bf16
+MFMA roofline, and the float64 oracle timed on the host cores.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -21,6 +23,27 @@ if ROOT not in sys.path:
 METRIC = "GPTQ layer time & quantized weights/s (4096², 4-bit g128); Hessian TFLOP/s"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+
+# HBM bytes moved by one k_hessian_dma launch on this workload, from two
+# rocprofv3 counter runs of `bench.py --steps 1 --warmup 0 --no-cpu-baseline
+# --copy-calibration` (FETCH_SIZE, then WRITE_SIZE, each scaled by what the
+# same counter reads for the 1 GiB copy/fill that --copy-calibration runs).
+# Valid only for the kernel source with the recorded SHA-256; reported as
+# null once hessian.hip changes.
+HESSIAN_TRAFFIC = {
+    "bytes": 4546975103,
+    "source_sha256": "9039300add581f8d609e5d3e578ce3157871e88326374f64da6e19793852f449",
+    "profile": "profiles/k_hessian_dma_c2_hbm_traffic.md",
+}
+HESSIAN_SRC = os.path.join(ROOT, "post_weight_quantization_28_amd", "csrc", "hessian.hip")
+
+
+def hessian_traffic():
+    with open(HESSIAN_SRC, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if HESSIAN_TRAFFIC["bytes"] is None or sha != HESSIAN_TRAFFIC["source_sha256"]:
+        return None
+    return HESSIAN_TRAFFIC["bytes"]
 
 
 def log(*a):
@@ -65,10 +88,14 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="before warm-up, run one plain 1 GiB device copy and one 1 GiB fill "
+                         "(known bytes) for calibrating HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU; --gpus {args.gpus} is not supported "
-              "(the multi-GPU layout is described in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py: --gpus {args.gpus} is not supported; the library and this benchmark "
+              "run on one GPU (a token-sharded Hessian and row-sharded sweep are not implemented)",
+              file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
@@ -107,6 +134,15 @@ def main():
         "w_hat": torch.empty((d_out, n), dtype=torch.float32, device=dev),
         "row_loss": torch.empty((d_out,), dtype=torch.float32, device=dev),
     }
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1)          # writes 1 GiB
+        b.copy_(a)          # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del a, b
+        log("bench: ran the 1 GiB fill and copy for counter calibration")
 
     def step():
         G.accumulate_hessian(X, H=H, zero_first=True, workspace=ws_h)
@@ -160,9 +196,10 @@ def main():
         "hessian_ms": hess_ms,
         "quantize_ms": quant_ms,
         "layer_weights_per_s_quantize_only": d_out * nq / (quant_ms / 1e3),
-        "roofline": {"bound": "mfma", "kernel": "k_hessian_bf16", "achieved": achieved,
+        "roofline": {"bound": "mfma", "kernel": "k_hessian_dma", "achieved": achieved,
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": None},
+                     "traffic": hessian_traffic(),
+                     "work": "T*n*(n+1) flop per launch (upper triangle of 2 X^T X)"},
     }
     if not args.no_cpu_baseline:
         log("bench: timing the float64 oracle on a bounded sample (cpu_baseline)")

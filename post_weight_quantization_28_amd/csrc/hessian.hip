@@ -62,10 +62,20 @@ __device__ inline void upper_tile(int t, int nt, int& bi, int& bj) {
   bj = row + t;
 }
 
-// Work item of block b: (split, tile), tile-fastest.
-__device__ inline void hessian_item(int b, int ntile, int& tile, int& split) {
-  split = b / ntile;
-  tile = b - split * ntile;
+// Work item of block b: (split, tile), tile-fastest, in XCD-contiguous runs.
+// The dispatcher deals consecutive block ids to the 8 XCDs in turn (b, b+8,
+// ... share one XCD and its L2), so block b takes item (b % 8) * per + b / 8:
+// each XCD then walks one contiguous run of items, i.e. mostly one token
+// chunk at a time, and its resident tiles stream the same X rows through
+// its L2. Returns false for the padding blocks of the last run.
+__device__ inline bool hessian_item(int b, int ntile, int splits, int& tile, int& split) {
+  const int total = ntile * splits;
+  const int per = (total + 7) >> 3;
+  const int w = (b & 7) * per + (b >> 3);
+  if (w >= total) return false;
+  split = w / ntile;
+  tile = w - split * ntile;
+  return true;
 }
 
 // Load an 8(token) x 8(channel) bf16 block: rows X[t0+r][c0..c0+7].
@@ -127,9 +137,9 @@ k_hessian_bf16(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx
                float* __restrict__ part, int64_t chunk) {
   __shared__ uint32_t smem[2 * 2 * kHStage];
   const int nt = (int)ceil_div(n, kHT);
-  int tile, split, bi, bj;
-  hessian_item(blockIdx.x, nt * (nt + 1) / 2, tile, split);
-  upper_tile(tile, nt, bi, bj);
+  int bi, bj;
+  const int split = (int)blockIdx.x / (nt * (nt + 1) / 2);
+  upper_tile((int)blockIdx.x - split * (nt * (nt + 1) / 2), nt, bi, bj);
   const int64_t kbeg = (int64_t)split * chunk;
   const int64_t kend = min(T, kbeg + chunk);
   const int64_t iA = (int64_t)bi * kHT, iB = (int64_t)bj * kHT;
@@ -272,11 +282,11 @@ __device__ __forceinline__ v4i16_t lds_tr16(uint32_t byte_off) {
 template <int kSlots>
 __global__ void __launch_bounds__(256)
 k_hessian_dma(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx,
-              float* __restrict__ part, int64_t chunk) {
+              float* __restrict__ part, int64_t chunk, int splits) {
   __shared__ __align__(16) uint8_t dsm[kSlots * kDSlotBytes];
   const int nt = (int)ceil_div(n, kHT);
   int tile, split, bi, bj;
-  hessian_item(blockIdx.x, nt * (nt + 1) / 2, tile, split);
+  if (!hessian_item(blockIdx.x, nt * (nt + 1) / 2, splits, tile, split)) return;
   upper_tile(tile, nt, bi, bj);
   const int64_t kbeg = (int64_t)split * chunk;
   const int64_t kend = min(T, kbeg + chunk);
@@ -406,7 +416,8 @@ hipError_t launch_hessian_partials_bf16(hipStream_t s, const uint16_t* X, int64_
   const int64_t chunk = ceil_div(ceil_div(T, splits), kHBK) * kHBK;
   const bool aligned = (n % 8 == 0) && (ldx % 8 == 0) && ((uintptr_t)X % 16 == 0);
   if (aligned)
-    hipLaunchKernelGGL(k_hessian_dma<4>, dim3(items), dim3(256), 0, s, X, T, n, ldx, part, chunk);
+    hipLaunchKernelGGL(k_hessian_dma<4>, dim3(8 * ((items + 7) / 8)), dim3(256), 0, s, X, T, n, ldx, part,
+                       chunk, splits);
   else
     hipLaunchKernelGGL(k_hessian_bf16<false>, dim3(items), dim3(256), 0, s, X, T, n, ldx, part, chunk);
   return hipGetLastError();
@@ -430,6 +441,9 @@ hipError_t launch_hessian_partials_f32(hipStream_t s, const float* X, int64_t T,
 }
 
 // H[i][j] (i <= j) = base + 2 * sum_s part[s][i][j]; H[j][i] = H[i][j].
+// One 64x64 tile on or above the diagonal per workgroup; thread (ty, tx)
+// sums rows ty + 16 q of columns 4 tx .. 4 tx + 3 with 16-byte loads when
+// the row stride allows, so each thread keeps 4 x splits loads in flight.
 __global__ void __launch_bounds__(256)
 k_hessian_reduce(const float* __restrict__ part, int splits, int64_t n, float* __restrict__ H,
                  int zero_first) {
@@ -437,24 +451,53 @@ k_hessian_reduce(const float* __restrict__ part, int splits, int64_t n, float* _
   const int nt = (int)ceil_div(n, 64);
   int a, b;
   upper_tile(blockIdx.x, nt, a, b);
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;
   const int64_t nn = n * n;
-  for (int r = ty; r < 64; r += 4) {
-    const int64_t i = (int64_t)a * 64 + r, j = (int64_t)b * 64 + tx;
-    float v = 0.f;
-    if (i < n && j < n && i <= j) {
-      float sum = 0.f;
-      for (int sp = 0; sp < splits; ++sp) sum += part[sp * nn + i * n + j];
-      v = (zero_first ? 0.f : H[i * n + j]) + 2.f * sum;
-      H[i * n + j] = v;
+  const int64_t j0 = (int64_t)b * 64 + 4 * tx;
+  const bool vec = (n % 4 == 0) && (j0 + 3 < n);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = ty + 16 * q;
+    const int64_t i = (int64_t)a * 64 + r;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (i < n) {
+      if (vec) {
+        float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int sp = 0; sp < splits; ++sp) {
+          const float4 x = *reinterpret_cast<const float4*>(part + sp * nn + i * n + j0);
+          sum.x += x.x; sum.y += x.y; sum.z += x.z; sum.w += x.w;
+        }
+        const float s4[4] = {sum.x, sum.y, sum.z, sum.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int64_t jj = j0 + c;
+          if (i <= jj) {
+            v[c] = (zero_first ? 0.f : H[i * n + jj]) + 2.f * s4[c];
+            H[i * n + jj] = v[c];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int64_t jj = j0 + c;
+          if (jj < n && i <= jj) {
+            float sum = 0.f;
+            for (int sp = 0; sp < splits; ++sp) sum += part[sp * nn + i * n + jj];
+            v[c] = (zero_first ? 0.f : H[i * n + jj]) + 2.f * sum;
+            H[i * n + jj] = v[c];
+          }
+        }
+      }
     }
-    tile[r][tx] = v;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) tile[r][4 * tx + c] = v[c];
   }
   __syncthreads();
-  // mirror: H[64b + r][64a + tx] = tile[tx][r] where (64a+tx) < (64b+r)
-  for (int r = ty; r < 64; r += 4) {
-    const int64_t i = (int64_t)b * 64 + r, j = (int64_t)a * 64 + tx;
-    if (i < n && j < n && j < i) H[i * n + j] = tile[tx][r];
+  // mirror: H[64b + r][64a + c] = tile[c][r] where (64a + c) < (64b + r)
+  const int cx = threadIdx.x & 63, ry = threadIdx.x >> 6;
+  for (int r = ry; r < 64; r += 4) {
+    const int64_t i = (int64_t)b * 64 + r, jj = (int64_t)a * 64 + cx;
+    if (i < n && jj < n && jj < i) H[i * n + jj] = tile[cx][r];
   }
 }
 
