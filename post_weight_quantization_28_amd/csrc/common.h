@@ -80,8 +80,11 @@ struct LeafTaskSmem {
 //  ta: A stored K x M (element (m,k) at A[k*lda + m]) instead of M x K
 //  tb: B stored N x K (element (k,n) at B[n*ldb + k]) instead of K x N
 //  kmode: 0 full K; 1 k < (column-tile end); 2 k >= (column-tile start);
-//         3 k < (row-tile end)   (triangular operands with zero fill)
+//         3 k < (row-tile end); 4 k >= (row-tile start)
+//         (triangular operands whose other part is zero)
 //  lower_only: skip tiles strictly above the diagonal (square tiles)
+//  batch: number of independent instances; instance b uses A + b*sA,
+//         B + b*sB, C + b*sC (batch 0 is treated as 1)
 struct GemmArgs {
   int64_t M, N, K;
   const float* A; int64_t lda; int ta;
@@ -90,6 +93,8 @@ struct GemmArgs {
   float alpha, beta;
   int kmode, lower_only;
   const DevStatus* st;   // if non-null and flagged, the kernel returns at once
+  int batch;
+  int64_t sA, sB, sC;
 };
 hipError_t launch_gemm_f32(hipStream_t s, const GemmArgs& g);
 hipError_t launch_gemm_pair(hipStream_t s, const GemmArgs& a, const GemmArgs* b);

@@ -4,17 +4,21 @@
 // standard GPTQ is Cholesky-based on the lambda-regularised Hessian.
 //
 // With A = J H_d J = L L^T (J = index reversal, L lower), the factor GPTQ's
-// sweep needs is U = J L^{-1} J (upper, U^T U = H_d^{-1}). L and X = L^{-1}
-// are built together, right-looking, one 64-column panel p = [k0, k1) at a
-// time (R below = the rows of X not yet final; X starts as the identity):
-//   leaf:    L11 = chol(A11), D = L11^{-1}      (one workgroup, registers)
-//            X[p, p] = D
-//   panel:   X[p, 0:k0] = D X[p, 0:k0]         (block row p of X is final)
-//            A[k1:, p]  = A[k1:, p] D^T        (= L21, in place)
-//   update:  A[k1:, k1:] -= L21 L21^T           (Schur complement, lower tiles)
-//            X[k1:, 0:k1] -= L21 X[p, 0:k1]     (forward substitution of L X = I)
-// The two GEMMs of a step share one launch. L itself is never stored beyond
-// its panel. All products are fp32 v_mfma_f32_32x32x2f32.
+// sweep needs is U = J L^{-1} J (upper, U^T U = H_d^{-1}).
+//
+// Phase 1, right-looking Cholesky in 64-column panels p = [k0, k1):
+//   leaf:    L11 = chol(A11), D = L11^{-1} -> X[p, p]   (one wavefront)
+//   panel:   A[k1:, p] = A[k1:, p] D^T                 (= L21, in place)
+//   update:  A[k1:, k1:] -= L21 L21^T                   (lower part)
+// The next panel's leaf runs inside the update launch (see slab.hip).
+// Phase 2, X = L^{-1} by recursive doubling over the diagonal blocks: with
+// the inverses X_ii, X_jj of two adjacent blocks of h rows,
+//   X_ji = -X_jj (L_ji X_ii),
+// for h = 64, 128, ... ; every level is two batched GEMM launches (all
+// block pairs of the level at once) that skip the zero triangles of X_ii
+// and X_jj. The product L_ji X_ii is kept, transposed, in the free upper
+// triangle of A.
+// All products are fp32 v_mfma_f32_32x32x2f32.
 #include "common.h"
 #include "leaf.h"
 
@@ -84,7 +88,8 @@ __device__ inline float4 load4(const float* __restrict__ p, int64_t ld, int64_t 
 struct GemmPair {
   GemmArgs p[2];
   int ntn[2];     // tiles along N per problem
-  int nt0;        // tiles of problem 0 (problem 1 follows)
+  int per[2];     // tiles per batch instance
+  int nt0;        // tiles of problem 0, all instances (problem 1 follows)
 };
 
 // Staging of one operand tile (R rows of the output dimension x kGBK).
@@ -134,6 +139,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int tm, int tn, Gem
   if (g.kmode == 1) khi = min(g.K, n0 + BN);
   else if (g.kmode == 2) klo = (n0 / kGBK) * kGBK;
   else if (g.kmode == 3) khi = min(g.K, m0 + BM);
+  else if (g.kmode == 4) klo = (m0 / kGBK) * kGBK;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -219,9 +225,15 @@ __global__ void __launch_bounds__(256)
 k_gemm_f32(GemmPair gp) {
   __shared__ __align__(16) GemmSmem<BM, BN> sm;
   const int which = (int)blockIdx.x >= gp.nt0;
-  const int t = (int)blockIdx.x - (which ? gp.nt0 : 0);
-  const GemmArgs& g = gp.p[which];
+  int t = (int)blockIdx.x - (which ? gp.nt0 : 0);
+  GemmArgs g = gp.p[which];
   if (g.st != nullptr && g.st->flags != 0) return;
+  const int per = gp.per[which];          // tiles of one batch instance
+  const int b = t / per;
+  t -= b * per;
+  g.A += b * g.sA;
+  g.B += b * g.sB;
+  g.C += b * g.sC;
   const int tm = t / gp.ntn[which], tn = t % gp.ntn[which];
   if (g.lower_only && tn * BN > tm * BM + BM - 1) return;
   if (g.ta) {
@@ -238,15 +250,18 @@ static hipError_t launch_pair(hipStream_t s, const GemmArgs& a, const GemmArgs* 
   GemmPair gp{};
   gp.p[0] = a;
   gp.ntn[0] = (int)ceil_div(a.N, BN);
-  gp.nt0 = (a.M > 0 && a.N > 0) ? (int)(ceil_div(a.M, BM) * gp.ntn[0]) : 0;
+  gp.per[0] = (int)(ceil_div(a.M, BM) * gp.ntn[0]);
+  gp.nt0 = (a.M > 0 && a.N > 0 && a.K >= 0) ? gp.per[0] * std::max(a.batch, 1) : 0;
   int nt1 = 0;
   if (b && b->M > 0 && b->N > 0) {
     gp.p[1] = *b;
     gp.ntn[1] = (int)ceil_div(b->N, BN);
-    nt1 = (int)(ceil_div(b->M, BM) * gp.ntn[1]);
+    gp.per[1] = (int)(ceil_div(b->M, BM) * gp.ntn[1]);
+    nt1 = gp.per[1] * std::max(b->batch, 1);
   } else {
     gp.p[1] = a;
     gp.ntn[1] = 1;
+    gp.per[1] = 1;
   }
   const int total = gp.nt0 + nt1;
   if (total == 0) return hipSuccess;
@@ -257,9 +272,13 @@ static hipError_t launch_pair(hipStream_t s, const GemmArgs& a, const GemmArgs* 
 // One launch for one or two independent products; the tile shape follows
 // the larger one.
 hipError_t launch_gemm_pair(hipStream_t s, const GemmArgs& a, const GemmArgs* b) {
-  int64_t big = a.M * a.N;
-  if (b) big = std::max(big, b->M * b->N);
-  if (big >= (int64_t)512 * 512) return launch_pair<128, 128>(s, a, b);
+  // 128 x 128 tiles when they alone fill the 256 CUs, else 64 x 64
+  auto tiles128 = [](const GemmArgs& g) {
+    return ceil_div(g.M, 128) * ceil_div(g.N, 128) * std::max(g.batch, 1);
+  };
+  int64_t t = tiles128(a);
+  if (b) t = std::max(t, tiles128(*b));
+  if (t >= 256) return launch_pair<128, 128>(s, a, b);
   return launch_pair<64, 64>(s, a, b);
 }
 

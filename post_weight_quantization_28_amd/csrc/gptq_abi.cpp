@@ -156,30 +156,60 @@ hipError_t factor_panels(hipStream_t s, float* A, float* X, int64_t n, const int
                          DevStatus* st) {
   hipError_t e;
   constexpr int kAny = 1 << 30;
+  // ---- phase 1: Cholesky, leaves write D = L11^{-1} into X's diagonal
   if ((e = launch_leaf(s, A, X, n, 0, std::min<int64_t>(kLeaf, n), perm, st)) != hipSuccess) return e;
   for (int64_t k0 = 0; k0 < n; k0 += kLeaf) {
     const int64_t m = std::min<int64_t>(kLeaf, n - k0);
     const int64_t k1 = k0 + m, r = n - k1;
-    // the leaf of panel p = [k0, k1) has run: D = L11^{-1} is in X[p, p]
-    float* D = X + k0 * n + k0;
-    float* Xp = X + k0 * n;              // block row p of X
+    if (r == 0) break;
+    const float* D = X + k0 * n + k0;    // L11^{-1}, lower
     float* L21 = A + k1 * n + k0;
-    // X[p, 0:k0] = D X[p, 0:k0]  and  L21 = A21 D^T  (both in place; the
-    // second overwrites its own A operand, so one workgroup per slab)
-    SlabArgs g1{m, k0, m, D, n, Xp, n, 0, Xp, n, 1.f, 0.f, 0, 0, st};
+    // L21 = A21 D^T in place (overwrites its own A operand: one workgroup per slab)
     SlabArgs g2{r, m, m, L21, n, D, n, 1, L21, n, 1.f, 0.f, 0, 0, st};
-    if ((e = launch_slab_pair(s, g1, kAny, &g2, 1)) != hipSuccess) return e;
-    if (r == 0) continue;
+    if ((e = launch_slab(s, g2, 1)) != hipSuccess) return e;
     // One launch: the next diagonal block (m2 rows) is updated and factored
-    // by its own workgroup, while the rest runs
+    // by its own workgroup while the rest runs
     //   A[k1+m2:, k1:] -= L21[m2:] L21^T   (lower, i.e. j <= i + m2)
-    //   X[k1:, 0:k1]   -= L21 X[p, 0:k1]   (forward substitution of L X = I)
     const int64_t m2 = std::min<int64_t>(kLeaf, r);
     SlabArgs g3{r - m2, r, m, L21 + m2 * n, n, L21, n, 1, A + (k1 + m2) * n + k1, n, -1.f, 1.f, 1, 0, st};
     g3.lower_off = m2;
-    SlabArgs g4{r, k1, m, L21, n, Xp, n, 0, X + k1 * n, n, -1.f, 1.f, 0, 0, st};
     LeafTask lt{L21, A, X, n, k1, (int)m2, (int)m, perm, st};
-    if ((e = launch_slab_pair_leaf(s, g3, kAny, &g4, kAny, lt)) != hipSuccess) return e;
+    if ((e = launch_slab_pair_leaf(s, g3, kAny, nullptr, 0, lt)) != hipSuccess) return e;
+  }
+  // ---- phase 2: off-diagonal blocks of X = L^{-1}
+  for (int64_t h = kLeaf; h < n; h *= 2) {
+    const int64_t full = n / (2 * h);                        // pairs whose j block is complete
+    const int64_t bp_last = full * 2 * h + h;                // j-block start of a partial pair
+    const int64_t hj_last = bp_last < n ? n - bp_last : 0;   // its rows (0: none)
+    const int64_t step = 2 * h * (n + 1);
+    auto gemms = [&](int64_t ap, int64_t hj, int batch, GemmArgs& g1, GemmArgs& g2) {
+      const int64_t bp = ap + h;
+      // g1: T^T (h x hj) = X_ii^T L_ji^T, into A[ap:ap+h, bp:bp+hj] (upper, free)
+      g1 = GemmArgs{};
+      g1.M = h; g1.N = hj; g1.K = h;
+      g1.A = X + ap * n + ap; g1.lda = n; g1.ta = 1;
+      g1.B = A + bp * n + ap; g1.ldb = n; g1.tb = 1;
+      g1.C = A + ap * n + bp; g1.ldc = n;
+      g1.alpha = 1.f; g1.beta = 0.f; g1.kmode = 4; g1.st = st;
+      g1.batch = batch; g1.sA = step; g1.sB = step; g1.sC = step;
+      // g2: X_ji (hj x h) = -X_jj T
+      g2 = GemmArgs{};
+      g2.M = hj; g2.N = h; g2.K = hj;
+      g2.A = X + bp * n + bp; g2.lda = n; g2.ta = 0;
+      g2.B = A + ap * n + bp; g2.ldb = n; g2.tb = 1;
+      g2.C = X + bp * n + ap; g2.ldc = n;
+      g2.alpha = -1.f; g2.beta = 0.f; g2.kmode = 3; g2.st = st;
+      g2.batch = batch; g2.sA = step; g2.sB = step; g2.sC = step;
+    };
+    GemmArgs f1{}, f2{}, p1{}, p2{};
+    if (full > 0) gemms(0, h, (int)full, f1, f2);
+    if (hj_last > 0) gemms(full * 2 * h, hj_last, 1, p1, p2);
+    const GemmArgs* first1 = full > 0 ? &f1 : &p1;
+    const GemmArgs* second1 = (full > 0 && hj_last > 0) ? &p1 : nullptr;
+    const GemmArgs* first2 = full > 0 ? &f2 : &p2;
+    const GemmArgs* second2 = (full > 0 && hj_last > 0) ? &p2 : nullptr;
+    if ((e = launch_gemm_pair(s, *first1, second1)) != hipSuccess) return e;
+    if ((e = launch_gemm_pair(s, *first2, second2)) != hipSuccess) return e;
   }
   return hipSuccess;
 }
