@@ -54,12 +54,6 @@ hipError_t launch_status_init(hipStream_t s, DevStatus* st);
 constexpr int kLeaf = 64;
 hipError_t launch_leaf(hipStream_t s, float* A, float* X, int64_t n, int64_t off, int64_t m,
                        const int32_t* perm, DevStatus* st);
-// LDS of one leaf: sCol[k][i] = L[i][k], sRow[i][k] = L[i][k], sInv[k] = 1/L[k][k].
-struct LeafSmem {
-  float sCol[64][64];
-  float sRow[64][68];
-  float sInv[64];
-};
 // The next diagonal block's update and leaf, run beside a trailing update.
 struct LeafTask {
   const float* L21;      // rows k1.., columns of panel k (row pitch n)
@@ -69,11 +63,6 @@ struct LeafTask {
   int m2, mk;            // next block size, panel-k width
   const int32_t* perm;
   DevStatus* st;
-};
-struct LeafTaskSmem {
-  float lrows[64][65];
-  float blk[64][65];
-  LeafSmem leaf;
 };
 
 // C[M x N] = alpha * op(A) * op(B) + beta * C, fp32 MFMA.

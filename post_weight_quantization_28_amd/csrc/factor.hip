@@ -7,7 +7,7 @@
 // sweep needs is U = J L^{-1} J (upper, U^T U = H_d^{-1}).
 //
 // Phase 1, right-looking Cholesky in 64-column panels p = [k0, k1):
-//   leaf:    L11 = chol(A11), D = L11^{-1} -> X[p, p]   (one wavefront)
+//   leaf:    L11 = chol(A11), D = L11^{-1} -> X[p, p]   (one workgroup)
 //   panel:   A[k1:, p] = A[k1:, p] D^T                 (= L21, in place)
 //   update:  A[k1:, k1:] -= L21 L21^T                   (lower part)
 // The next panel's leaf runs inside the update launch (see slab.hip).
@@ -29,7 +29,7 @@ namespace gq {
 
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
-__global__ void __launch_bounds__(64)
+__global__ void __launch_bounds__(256)
 k_leaf(const float* __restrict__ A, float* __restrict__ X, int64_t n, int64_t k0, int m,
        const int32_t* __restrict__ perm, DevStatus* st) {
   __shared__ __align__(16) LeafSmem sm;
@@ -38,7 +38,7 @@ k_leaf(const float* __restrict__ A, float* __restrict__ X, int64_t n, int64_t k0
 
 hipError_t launch_leaf(hipStream_t s, float* A, float* X, int64_t n, int64_t off, int64_t m,
                        const int32_t* perm, DevStatus* st) {
-  hipLaunchKernelGGL(k_leaf, dim3(1), dim3(64), 0, s, A, X, n, off, (int)m, perm, st);
+  hipLaunchKernelGGL(k_leaf, dim3(1), dim3(256), 0, s, A, X, n, off, (int)m, perm, st);
   return hipGetLastError();
 }
 
