@@ -111,6 +111,22 @@ hipError_t launch_slab_pair(hipStream_t s, SlabArgs a, int split_a, const SlabAr
 hipError_t launch_slab_pair_leaf(hipStream_t s, SlabArgs a, int split_a, const SlabArgs* b,
                                  int split_b, const LeafTask& lt);
 
+// ---- trail.hip
+// C[M x N] -= (Ahi + Alo)(Bhi + Blo) without the lo*lo term: split-bf16
+// products, fp32 accumulation. A is M x K (row-major, lda), B is K x N
+// (row-major, ldb), all bf16 bits. Requires lda, ldb, N and K multiples of 8
+// and 16-byte aligned A/B bases (hipErrorInvalidValue otherwise).
+struct TrailArgs {
+  int64_t M, N, K;
+  const uint16_t *Ahi, *Alo; int64_t lda;
+  const uint16_t *Bhi, *Blo; int64_t ldb;
+  float* C; int64_t ldc;
+  const DevStatus* st;
+};
+hipError_t launch_trail_x3(hipStream_t s, const TrailArgs& g);
+// hi = bf16(x), lo = bf16(x - hi), elementwise over count floats.
+hipError_t launch_split_bf16(hipStream_t s, const float* x, int64_t count, uint16_t* hi, uint16_t* lo);
+
 // ---- sweep.hip
 struct SweepArgs {
   float* Wf; int64_t ldw;       // d_out x n working weights (processing order)
@@ -122,7 +138,7 @@ struct SweepArgs {
   int gshift;                   // log2(group) when groups split a block, else 31
   float* scales; uint8_t* zeros; int64_t ngroups;
   uint8_t* codes; int64_t n_quant;   // processing order, d_out x n_quant
-  float* E;                     // d_out x B
+  float* E; int64_t lde;        // d_out x B block errors (row pitch lde)
   float* row_loss;
   const DevStatus* st;
 };

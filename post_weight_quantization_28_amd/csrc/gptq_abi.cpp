@@ -90,13 +90,30 @@ struct Carver {
   }
 };
 
+// Columns per super-block of the two-level lazy batch: a multiple of the
+// block width B, and of the group size when groups span several blocks, so
+// that no group straddles two super-blocks (its statistics are taken from
+// values that have received every earlier column's update).
+int64_t super_width(const gptq_params* p) {
+  const int64_t B = p->block, g = p->group;
+  if (g <= B) return 512;                  // 512 is a multiple of B = 32, 64, 128
+  return g <= 512 ? g * (512 / g) : g;     // g % B == 0
+}
+
+// The split-bf16 far-field update needs 8-element aligned rows and column
+// origins; otherwise every block applies its own fp32 update to all later
+// columns.
+bool use_two_level(int64_t n, const gptq_params* p) { return n % 8 == 0 && super_width(p) % 8 == 0; }
+
 struct QLayout {
-  size_t status, lam, diag, perm, invperm, A, X, Wf, E, codes, loss, total;
+  size_t status, lam, diag, perm, invperm, A, X, Wf, E, Ehi, Elo, Uhi, Ulo, codes, loss, total;
 };
 
 QLayout q_layout(int64_t d_out, int64_t n, const gptq_params* p) {
   QLayout L{};
   Carver c;
+  const bool two = d_out > 0 && use_two_level(n, p);
+  const int64_t ew = two ? super_width(p) : p->block;
   L.status = c.take(sizeof(DevStatus));
   L.lam = c.take(sizeof(double));
   L.diag = c.take(sizeof(float) * n);
@@ -105,7 +122,11 @@ QLayout q_layout(int64_t d_out, int64_t n, const gptq_params* p) {
   L.A = c.take(sizeof(float) * n * n);
   L.X = c.take(sizeof(float) * n * n);
   L.Wf = c.take(sizeof(float) * d_out * n);
-  L.E = c.take(sizeof(float) * d_out * p->block);
+  L.E = c.take(sizeof(float) * d_out * ew);
+  L.Ehi = c.take(two ? sizeof(uint16_t) * d_out * ew : 0);
+  L.Elo = c.take(two ? sizeof(uint16_t) * d_out * ew : 0);
+  L.Uhi = c.take(two ? sizeof(uint16_t) * n * n : 0);
+  L.Ulo = c.take(two ? sizeof(uint16_t) * n * n : 0);
   L.codes = c.take((size_t)d_out * p->n_quant);
   L.loss = c.take(sizeof(float) * d_out);
   L.total = c.off;
@@ -406,23 +427,49 @@ gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int
   HIP_TRY(launch_fill_f32(s, loss, (size_t)d_out, 0.f), "fill");
   const int64_t nq = p->n_quant;
   const int B = p->block;
-  for (int64_t i0 = 0; i0 < nq; i0 += B) {
-    const int64_t nc = std::min<int64_t>(B, nq - i0);
-    SweepArgs a{};
-    a.Wf = Wf; a.ldw = n; a.U = U; a.ldu = n; a.d_out = d_out; a.i0 = i0; a.ncols = nc;
-    a.block = B; a.group = p->group; a.bits = p->bits;
-    a.gbase = i0 / p->group;
-    a.gshift = 31;
-    if (p->group < B)
-      for (int sh = 0; sh < 31; ++sh)
-        if ((1 << sh) == p->group) a.gshift = sh;
-    a.scales = out->scales; a.zeros = out->zeros; a.ngroups = nq / p->group;
-    a.codes = codes; a.n_quant = nq; a.E = E; a.row_loss = loss; a.st = dst;
-    HIP_TRY(launch_sweep(s, a), "sweep");
-    const int64_t i1 = i0 + nc;
-    if (i1 < n) {
-      SlabArgs g{d_out, n - i1, nc, E, B, U + i0 * n + i1, n, 0, Wf + i1, n, -1.f, 1.f, 0, 0, dst};
-      HIP_TRY(launch_slab(s, g, 1 << 30), "trailing update");
+  const bool two = use_two_level(n, p);
+  const int64_t sw = two ? super_width(p) : B;   // columns per super-block; E's row pitch
+  uint16_t* Ehi = reinterpret_cast<uint16_t*>(ws + L.Ehi);
+  uint16_t* Elo = reinterpret_cast<uint16_t*>(ws + L.Elo);
+  uint16_t* Uhi = reinterpret_cast<uint16_t*>(ws + L.Uhi);
+  uint16_t* Ulo = reinterpret_cast<uint16_t*>(ws + L.Ulo);
+  if (two) HIP_TRY(launch_split_bf16(s, U, n * n, Uhi, Ulo), "split U");
+  // Two-level lazy batch. Inside a super-block [s0, s1) each block updates
+  // the super-block's later columns at once (fp32, K = B); when the
+  // super-block is done, all of its errors update the columns right of it
+  // in one split-bf16 product (K = s1 - s0). Without the split path the
+  // super-block is the block itself and the far field is fp32.
+  for (int64_t s0 = 0; s0 < nq; s0 += sw) {
+    const int64_t s1 = std::min<int64_t>(s0 + sw, nq);
+    for (int64_t i0 = s0; i0 < s1; i0 += B) {
+      const int64_t nc = std::min<int64_t>(B, s1 - i0);
+      float* Eb = E + (i0 - s0);
+      SweepArgs a{};
+      a.Wf = Wf; a.ldw = n; a.U = U; a.ldu = n; a.d_out = d_out; a.i0 = i0; a.ncols = nc;
+      a.block = B; a.group = p->group; a.bits = p->bits;
+      a.gbase = i0 / p->group;
+      a.gshift = 31;
+      if (p->group < B)
+        for (int sh = 0; sh < 31; ++sh)
+          if ((1 << sh) == p->group) a.gshift = sh;
+      a.scales = out->scales; a.zeros = out->zeros; a.ngroups = nq / p->group;
+      a.codes = codes; a.n_quant = nq; a.E = Eb; a.lde = sw; a.row_loss = loss; a.st = dst;
+      HIP_TRY(launch_sweep(s, a), "sweep");
+      const int64_t i1 = i0 + nc;
+      const int64_t near_end = two ? s1 : n;
+      if (i1 < near_end) {
+        SlabArgs g{d_out, near_end - i1, nc, Eb, sw, U + i0 * n + i1, n, 0, Wf + i1, n, -1.f, 1.f, 0, 0, dst};
+        HIP_TRY(launch_slab(s, g, 1 << 30), "near-field update");
+      }
+    }
+    if (two && s1 < n) {
+      HIP_TRY(launch_split_bf16(s, E, d_out * sw, Ehi, Elo), "split E");
+      TrailArgs t{};
+      t.M = d_out; t.N = n - s1; t.K = s1 - s0;
+      t.Ahi = Ehi; t.Alo = Elo; t.lda = sw;
+      t.Bhi = Uhi + s0 * n + s1; t.Blo = Ulo + s0 * n + s1; t.ldb = n;
+      t.C = Wf + s1; t.ldc = n; t.st = dst;
+      HIP_TRY(launch_trail_x3(s, t), "far-field update");
     }
   }
   HIP_TRY(launch_finish(s, Wf, codes, invperm, d_out, n, nq, p->group, out->w_hat, out->codes, out->g_idx),

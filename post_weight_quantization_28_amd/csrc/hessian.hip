@@ -23,6 +23,7 @@
 //    number of chunks is chosen so that tiles x chunks fills whole waves of
 //    the 256 CUs (one 128-160 KiB workgroup per CU).
 #include "common.h"
+#include "dma.h"
 
 namespace gq {
 
@@ -249,35 +250,6 @@ k_hessian_bf16(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx
 constexpr int kDK = 32;                  // tokens per stage
 constexpr int kDOpBytes = kDK * 512;     // one operand of one stage
 constexpr int kDSlotBytes = 2 * kDOpBytes;
-
-__device__ __align__(16) const uint32_t kZeroChunk[4] = {0u, 0u, 0u, 0u};
-
-__device__ __forceinline__ int dma_swz(int t) {
-  // XOR applied to the 16-byte chunk index of token row t (values < 16, so
-  // a row's 32 chunks are permuted among themselves).
-  return (0xAC60 >> (4 * (t & 3))) & 15;   // t%4 -> 0, 6, 12, 10
-}
-
-// Wait until at most `stages` stages of this wave's DMA are outstanding, then
-// barrier; one asm block, so no LDS read can be scheduled between the two.
-__device__ __forceinline__ void wait_dma_barrier(int stages) {
-  if (stages <= 0) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  else if (stages == 1) asm volatile("s_waitcnt vmcnt(8)\n\ts_barrier" ::: "memory");
-  else if (stages == 2) asm volatile("s_waitcnt vmcnt(16)\n\ts_barrier" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(24)\n\ts_barrier" ::: "memory");
-}
-
-__device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(lds_base) : "memory");
-}
-
-typedef short v4i16_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ v4i16_t lds_tr16(uint32_t byte_off) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      reinterpret_cast<__attribute__((address_space(3))) v4i16_t*>(byte_off));
-}
 
 template <int kSlots>
 __global__ void __launch_bounds__(256)

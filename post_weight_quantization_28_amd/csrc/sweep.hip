@@ -251,7 +251,7 @@ k_sweep(SweepArgs a) {
         a.Wf[row * a.ldw + a.i0 + col] = S.w[c];
         a.codes[row * a.n_quant + a.i0 + col] = (uint8_t)S.qv[c];
       }
-      a.E[row * B + col] = S.ev[c];
+      a.E[row * a.lde + col] = S.ev[c];
     }
     if (L == 0) a.row_loss[row] += S.loss;
   }

@@ -87,6 +87,10 @@ CASES = [
     ("c2", dict(d_out=64, n=512, T=4096), dict(block=64, group=32)),
     ("c2", dict(d_out=48, n=512, T=4096), dict(block=32, group=256)),
     ("c3", dict(d_out=40, n=384, T=4096), dict(bits=2, group=64, block=128)),
+    # n % 8 != 0 (per-block fp32 far field) with trailing columns kept in fp32
+    ("c2", dict(d_out=72, n=300, T=4096), dict(n_quant=256, group=64)),
+    # several super-blocks of 512 columns, the last one partial
+    ("c2", dict(d_out=96, n=1408, T=4096), dict()),
 ]
 
 
@@ -95,23 +99,24 @@ def test_quantize_parity(name, kw, over):
     wl = synth.make_workload(name, **kw)
     p = dict(wl.params)
     p.update(over)
-    say("quantize", name, kw, p)
+    nq = p.pop("n_quant", wl.n_quant)
+    say("quantize", name, kw, p, "n_quant", nq)
     H64 = O.hessian(wl.X)
     H32 = torch.from_numpy(H64.astype(np.float32)).cuda()
     res = G.quantize_layer(w_dev(wl), H32, bits=p["bits"], group=p["group"], damp=p["damp"],
-                           block=p["block"], act_order=p["act_order"], n_quant=wl.n_quant,
+                           block=p["block"], act_order=p["act_order"], n_quant=nq,
                            want_codes=True)
     torch.cuda.synchronize()
     orc = O.gptq_o2(wl.W, H64.astype(np.float32), p["bits"], p["group"], p["damp"], p["block"],
-                    p["act_order"], wl.n_quant)
+                    p["act_order"], nq)
     rep = {}
-    check_quant(res, wl, H64, orc, p, wl.n_quant, rep)
+    check_quant(res, wl, H64, orc, p, nq, rep)
     say("  ", rep)
     # packed words are the layout applied to the GPU's own codes
     assert np.array_equal(res.qweight.cpu().numpy().view(np.uint32),
                           P.pack(res.codes.cpu().numpy(), p["bits"]))
     # row_loss identity on the GPU's own result: sum e^2 = delta^T Hd delta
-    Hd, perm = O.prepare(H64.astype(np.float32), p["damp"], p["act_order"], wl.n_quant)
+    Hd, perm = O.prepare(H64.astype(np.float32), p["damp"], p["act_order"], nq)
     D = (wl.W.astype(np.float64) - res.w_hat.cpu().numpy())[:, perm]
     q = np.einsum("ri,ij,rj->r", D, Hd, D)
     assert np.allclose(res.row_loss.cpu().numpy(), q, rtol=2e-3)
