@@ -234,7 +234,10 @@ k_gemm_f32(GemmPair gp) {
   g.A += b * g.sA;
   g.B += b * g.sB;
   g.C += b * g.sC;
-  const int tm = t / gp.ntn[which], tn = t % gp.ntn[which];
+  int tm = t / gp.ntn[which];
+  const int tn = t % gp.ntn[which];
+  // triangular K ranges: dispatch the longest row tiles first
+  if (g.kmode == 3) tm = per / gp.ntn[which] - 1 - tm;
   if (g.lower_only && tn * BN > tm * BM + BM - 1) return;
   if (g.ta) {
     if (g.tb) gemm_tile<BM, BN, true, true>(g, tm, tn, sm);
@@ -272,13 +275,15 @@ static hipError_t launch_pair(hipStream_t s, const GemmArgs& a, const GemmArgs* 
 // One launch for one or two independent products; the tile shape follows
 // the larger one.
 hipError_t launch_gemm_pair(hipStream_t s, const GemmArgs& a, const GemmArgs* b) {
-  // 128 x 128 tiles when they alone fill the 256 CUs, else 64 x 64
+  // 128 x 128 tiles only when there are enough of them for four rounds of
+  // the 256 CUs; otherwise 64 x 64 (four workgroups per CU), which also
+  // balances the uneven K ranges of triangular operands
   auto tiles128 = [](const GemmArgs& g) {
     return ceil_div(g.M, 128) * ceil_div(g.N, 128) * std::max(g.batch, 1);
   };
   int64_t t = tiles128(a);
   if (b) t = std::max(t, tiles128(*b));
-  if (t >= 256) return launch_pair<128, 128>(s, a, b);
+  if (t >= 1024) return launch_pair<128, 128>(s, a, b);
   return launch_pair<64, 64>(s, a, b);
 }
 
