@@ -25,6 +25,8 @@
 #include "common.h"
 #include "dma.h"
 
+#include <type_traits>
+
 namespace gq {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -224,38 +226,46 @@ k_hessian_bf16(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx
 }
 
 // ---------------------------------------------------------------------------
-// Streaming variant for 16-byte aligned X: LDS-DMA staging + transpose reads.
+// Streaming variant for 16-byte aligned X: buffer LDS-DMA staging and
+// transposing LDS reads.
 //
-//  * global_load_lds_dwordx4 moves 16-byte chunks (8 channels of one token)
-//    straight from HBM into LDS without passing through VGPRs, so four
-//    32-token stages (128 KiB of LDS) can be in flight at once: the load of
-//    stage s+3 is issued while stage s is multiplied.
+//  * buffer_load_dwordx4 ... lds moves 16-byte chunks (8 channels of one
+//    token) straight from HBM into LDS without passing through VGPRs, so
+//    four 32-token stages (128 KiB of LDS) are in flight at once: the load
+//    of stage s+3 is issued while stage s is multiplied. The buffer
+//    descriptor spans this workgroup's token chunk, so each lane's offset is
+//    fixed and one scalar offset advances a whole stage; chunks past the
+//    chunk's last token or the last channel are outside the descriptor's
+//    range and read as zeros (the hardware bounds check), so the loop has
+//    no per-chunk predication.
 //  * LDS keeps X's own layout, [token][channel] with 512-byte rows per
 //    operand; the 16-byte chunk index of row t is XOR-swizzled with
-//    kSwz[t % 4] (each DMA lane fetches the global chunk that belongs to its
+//    dma_swz(t) (each DMA lane fetches the global chunk that belongs to its
 //    fixed LDS slot).
-//  * ds_read_b64_tr_b16 turns it into MFMA operands: within each group of 16
-//    lanes, lane a + 4j reads 4 channels of token j and lane 4a + b receives
-//    channel b of lane a's piece for the 4 tokens, i.e. 4 consecutive tokens
-//    of one channel; two such reads give the 8-token K-slice that
-//    v_mfma_f32_32x32x16_bf16 takes per lane. A group's 16 reads hit 4 rows
-//    x 32 bytes; the swizzle spreads them over all banks.
-//  * Chunks past the last channel or the end of the token chunk are fetched
-//    from a zero source, so ragged edges need no predication in the loop.
-//  * The compiler is not told about the DMA (inline asm): it would otherwise
-//    wait for every outstanding DMA before each LDS read. Completion is
-//    tracked by hand with vmcnt, and one s_barrier per stage makes a stage
-//    visible to all waves and frees the slot that the next DMA overwrites.
+//  * ds_read_b64_tr_b16 turns it into MFMA operands (4 consecutive tokens of
+//    one channel per read, two reads per 8-token K slice). A group's 16
+//    reads hit 4 rows x 32 bytes; the swizzle spreads them over all banks.
+//    Every read address is one of 8 per-lane bases (slot base added once
+//    per stage) plus a constant in the instruction's offset field.
+//  * The DMA is issued from inline asm and completion tracked with vmcnt, in
+//    the same asm block as the barrier that publishes a stage (see dma.h).
 // ---------------------------------------------------------------------------
 constexpr int kDK = 32;                  // tokens per stage
 constexpr int kDOpBytes = kDK * 512;     // one operand of one stage
 constexpr int kDSlotBytes = 2 * kDOpBytes;
+constexpr int kDSlots = 4;
 
-template <int kSlots>
+typedef int v4i32_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void dma16_buf(uint32_t voff, v4i32_t rsrc, uint32_t soff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(lds_base), "s"(soff) : "memory");
+}
+
 __global__ void __launch_bounds__(256)
 k_hessian_dma(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx,
               float* __restrict__ part, int64_t chunk, int splits) {
-  __shared__ __align__(16) uint8_t dsm[kSlots * kDSlotBytes];
+  __shared__ __align__(16) uint8_t dsm[kDSlots * kDSlotBytes];
   const int nt = (int)ceil_div(n, kHT);
   int tile, split, bi, bj;
   if (!hessian_item(blockIdx.x, nt * (nt + 1) / 2, splits, tile, split)) return;
@@ -271,12 +281,24 @@ k_hessian_dma(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx,
   const int wm = wave >> 1, wn = wave & 1;
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dsm));
 
+  // buffer over this chunk's tokens: [kbeg, kend) x ldx bf16
+  v4i32_t rsrc;
+  {
+    const uint64_t base = (uint64_t)(uintptr_t)(X + kbeg * ldx);
+    const int64_t bytes = kend > kbeg ? (kend - kbeg) * ldx * 2 : 0;
+    rsrc.x = (int)(uint32_t)base;
+    rsrc.y = (int)(uint32_t)(base >> 32);      // stride 0
+    rsrc.z = (int)(uint32_t)bytes;             // the launcher keeps this below 2^31
+    rsrc.w = 0x00020000;                       // raw buffer, 32-bit data format
+    rsrc.x = __builtin_amdgcn_readfirstlane(rsrc.x);
+    rsrc.y = __builtin_amdgcn_readfirstlane(rsrc.y);
+    rsrc.z = __builtin_amdgcn_readfirstlane(rsrc.z);
+  }
   // DMA plan: a stage is 2 operands x 16 row pairs = 32 wave-instructions;
   // wave w issues q = 0..7 -> instruction 8w+q: operand (8w+q)/16, rows
   // 2p, 2p+1 with p = (8w+q)%16; lane l fills row 2p + l/32, slot chunk l%32.
-  const uint16_t* src[8];
-  bool cvalid[8];
-  int trow[8];
+  // A chunk past the last channel gets an offset beyond the buffer.
+  uint32_t voff[8];
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const int idx = 8 * wave + q;
@@ -284,27 +306,37 @@ k_hessian_dma(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx,
     const int t = 2 * p + (lane >> 5);
     const int c = (lane & 31) ^ dma_swz(t);
     const int64_t ch = (op ? iB : iA) + 8 * c;
-    cvalid[q] = ch < n;
-    trow[q] = t;
-    src[q] = X + (kbeg + t) * ldx + (cvalid[q] ? ch : 0);
+    voff[q] = ch < n ? (uint32_t)((t * ldx + ch) * 2) : 0x80000000u;
   }
-  auto issue = [&](int st, uint32_t slot) {
-    const int64_t tok = kbeg + st * kDK;
+  const uint32_t stage_bytes = (uint32_t)(kDK * ldx * 2);
+  auto issue = [&](int st, int slot) {
+    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)st * stage_bytes);
 #pragma unroll
     for (int q = 0; q < 8; ++q) {
       const int idx = 8 * wave + q;
       const int op = idx >> 4, p = idx & 15;
-      const bool ok = cvalid[q] && (tok + trow[q] < kend);
-      const void* g = ok ? (const void*)(src[q] + st * kDK * ldx) : (const void*)kZeroChunk;
-      dma16(g, __builtin_amdgcn_readfirstlane(slot + op * kDOpBytes + p * 1024));
+      dma16_buf(voff[q], rsrc, soff,
+                __builtin_amdgcn_readfirstlane(lds0 + slot * kDSlotBytes + op * kDOpBytes + p * 1024));
     }
   };
 
-  // Transpose-read addressing (per lane, fixed): group G = lane/16, s = lane%16.
+  // Transpose-read addresses (per lane, relative to a slot): group G =
+  // lane/16, s = lane%16, token row t = 16 ks + 4 h + 8 (G/2) + s/4 and
+  // chunk (16 w + 4 b + 2 (G%2) + (s/2)%2) ^ dma_swz(t), b = mb or nb.
   const int G = lane >> 4, sl = lane & 15;
-  const int trow_off = 8 * (G >> 1) + (sl >> 2);          // + 16 ks + 4 h
-  const int cbase = 2 * (G & 1) + ((sl >> 1) & 1);       // + 16 wm + 4 mb (chunks)
+  const int trow_off = 8 * (G >> 1) + (sl >> 2);
+  const int cbase = 2 * (G & 1) + ((sl >> 1) & 1);
+  const int swz = dma_swz(trow_off);           // t % 4 == trow_off % 4
   const int half8 = (sl & 1) * 8;
+  // per-lane read offsets of the 4 A and 4 B fragments at ks = 0, h = 0;
+  // a stage adds its slot base once per fragment, and (ks, h) move by
+  // constants that fit the instructions' 16-bit offset field
+  uint32_t off[8];
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    off[b] = trow_off * 512 + (((16 * wm + 4 * b + cbase) ^ swz) * 16) + half8;
+    off[4 + b] = kDOpBytes + trow_off * 512 + (((16 * wn + 4 * b + cbase) ^ swz) * 16) + half8;
+  }
 
   f32x16_t acc[4][4];
 #pragma unroll
@@ -314,59 +346,41 @@ k_hessian_dma(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx,
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
-  // Fragments of one 16-token K-step: two transpose reads per 32-row block.
-  struct Frag { v4i16_t a[2][4], b[2][4]; };
-  auto load = [&](uint32_t slot, int ks, Frag& f) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int t = 16 * ks + 4 * h + trow_off;
-      const int swz = dma_swz(t);
-      const uint32_t rowA = slot + t * 512 + half8;
-      const uint32_t rowB = rowA + kDOpBytes;
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb) f.a[h][mb] = lds_tr16(rowA + ((16 * wm + 4 * mb + cbase) ^ swz) * 16);
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb) f.b[h][nb] = lds_tr16(rowB + ((16 * wn + 4 * nb + cbase) ^ swz) * 16);
-    }
-  };
-  auto mma = [&](const Frag& f) {
-    bf16x8_t af[4], bfr[4];
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-      af[mb] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(f.a[0][mb], f.a[1][mb], 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
-      bfr[nb] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(f.b[0][nb], f.b[1][nb], 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 4; ++nb)
-        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
-  };
-  auto slot_of = [&](int st) { return lds0 + (uint32_t)(st % kSlots) * kDSlotBytes; };
-
-  // Pipeline: the DMA of stage s + kSlots - 1 is issued while stage s is
-  // multiplied; the barrier that publishes stage s + 1 sits between the two
-  // K-steps of stage s, so the first fragments of s + 1 are read while the
-  // second K-step of s runs.
   const int nstage = kend > kbeg ? (int)ceil_div(kend - kbeg, kDK) : 0;
 #pragma unroll
-  for (int ps = 0; ps < kSlots - 1; ++ps)
-    if (ps < nstage) issue(ps, slot_of(ps));
-  Frag f0, f1;
-  if (nstage > 0) {
-    wait_dma_barrier(min(kSlots - 2, nstage - 1));
-    load(slot_of(0), 0, f0);
-  }
+  for (int ps = 0; ps < kDSlots - 1; ++ps)
+    if (ps < nstage) issue(ps, ps);
   for (int st = 0; st < nstage; ++st) {
-    load(slot_of(st), 1, f1);
-    mma(f0);
-    if (st + 1 < nstage) {
-      wait_dma_barrier(min(kSlots - 3, nstage - 2 - st));
-      if (st + kSlots - 1 < nstage) issue(st + kSlots - 1, slot_of(st + kSlots - 1));
-      load(slot_of(st + 1), 0, f0);
+    wait_dma_barrier(min(kDSlots - 2, nstage - 1 - st));
+    if (st + kDSlots - 1 < nstage) issue(st + kDSlots - 1, (st + kDSlots - 1) % kDSlots);
+    const uint32_t sbase = lds0 + (uint32_t)(st % kDSlots) * kDSlotBytes;
+    uint32_t bs[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) bs[b] = off[b] + sbase;
+#pragma unroll
+    for (int ks = 0; ks < kDK / 16; ++ks) {
+      v4i16_t ra[2][4], rb[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t row = (16 * ks + 4 * h) * 512;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          ra[h][b] = lds_tr16(bs[b] + row);
+          rb[h][b] = lds_tr16(bs[4 + b] + row);
+        }
+      }
+      bf16x8_t af[4], bfr[4];
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        af[b] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(ra[0][b], ra[1][b], 0, 1, 2, 3, 4, 5, 6, 7));
+        bfr[b] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(rb[0][b], rb[1][b], 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
     }
-    mma(f1);
   }
 
 #pragma unroll
@@ -387,8 +401,9 @@ hipError_t launch_hessian_partials_bf16(hipStream_t s, const uint16_t* X, int64_
   const int items = nt * (nt + 1) / 2 * splits;
   const int64_t chunk = ceil_div(ceil_div(T, splits), kHBK) * kHBK;
   const bool aligned = (n % 8 == 0) && (ldx % 8 == 0) && ((uintptr_t)X % 16 == 0);
-  if (aligned)
-    hipLaunchKernelGGL(k_hessian_dma<4>, dim3(8 * ((items + 7) / 8)), dim3(256), 0, s, X, T, n, ldx, part,
+  // 32-bit buffer offsets: a token chunk must span less than 2^31 bytes
+  if (aligned && chunk * ldx * 2 < ((int64_t)1 << 31))
+    hipLaunchKernelGGL(k_hessian_dma, dim3(8 * ((items + 7) / 8)), dim3(256), 0, s, X, T, n, ldx, part,
                        chunk, splits);
   else
     hipLaunchKernelGGL(k_hessian_bf16<false>, dim3(items), dim3(256), 0, s, X, T, n, ldx, part, chunk);
