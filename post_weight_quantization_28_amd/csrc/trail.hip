@@ -12,13 +12,15 @@
 // and the rounding of the lo parts leave a relative error of about 2^-16
 // per product, against 2^-8 for plain bf16 operands.
 //
-// Layout (MI355X): 128 x 128 output tile per workgroup of 4 waves (2 x 2,
-// each 64 x 64 = 2 x 2 accumulators). K streams through a 4-slot LDS ring
-// of 32-deep stages filled by LDS-DMA: A_hi, A_lo as [row][k] (64-byte rows,
-// chunk index XOR-swizzled with (row / 2) % 4) read with ds_read_b128, and
-// B_hi, B_lo as [k][column] (256-byte rows, swizzled like the Hessian tile)
-// read with transposing ds_read_b64_tr_b16. Each wave issues the 8 DMA
-// instructions of one of the four operand parts per stage.
+// Layout (MI355X): 256 x 128 output tile per workgroup of 4 waves (2 x 2,
+// each 128 x 64 = 4 x 2 accumulators). K streams through a 3-slot LDS ring
+// of 32-deep stages (48 KiB each) filled by buffer LDS-DMA: A_hi, A_lo as
+// [row][k] (64-byte rows, chunk index XOR-swizzled with (row / 2) % 4) read
+// with ds_read_b128, and B_hi, B_lo as [k][column] (256-byte rows, swizzled
+// like the Hessian tile) read with transposing ds_read_b64_tr_b16. The
+// buffer descriptors end at the last row of A and at row K of B, so rows
+// past M and k past K read as zeros; B chunks past N get an offset outside
+// the buffer. Each wave issues 12 of the 48 DMA instructions of a stage.
 #include "common.h"
 #include "dma.h"
 
@@ -26,121 +28,153 @@ namespace gq {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef int v4i32_t __attribute__((ext_vector_type(4)));
 
+constexpr int kTM = 256, kTN = 128;        // workgroup tile
 constexpr int kTK = 32;                    // k per stage
-constexpr int kTSlots = 4;
-constexpr int kTPart = 128 * kTK * 2;      // bytes of one operand part per stage (8 KiB)
-constexpr int kTSlot = 4 * kTPart;         // Ahi, Alo, Bhi, Blo
+constexpr int kTSlots = 3;
+constexpr int kTA = kTM * kTK * 2;         // bytes of A_hi (or A_lo) per stage: 16 KiB
+constexpr int kTB = kTK * kTN * 2;         // bytes of B_hi (or B_lo) per stage: 8 KiB
+constexpr int kTSlot = 2 * kTA + 2 * kTB;  // 48 KiB
 
 __device__ __forceinline__ int swz_a(int row) { return (row >> 1) & 3; }
+
+__device__ __forceinline__ void dma16_rsrc(uint32_t voff, v4i32_t rsrc, uint32_t soff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(lds_base), "s"(soff) : "memory");
+}
+
+__device__ __forceinline__ v4i32_t make_rsrc(const void* base, int64_t bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  v4i32_t r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));   // stride 0
+  r.z = __builtin_amdgcn_readfirstlane((int)(uint32_t)(bytes > 0 ? bytes : 0));
+  r.w = 0x00020000;                                                    // raw, 32-bit format
+  return r;
+}
+
+// Wait until at most `stages` stages of 12 DMA instructions of this wave are
+// outstanding, then barrier (one asm block, as in dma.h).
+__device__ __forceinline__ void wait_dma12_barrier(int stages) {
+  if (stages <= 0) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
+}
 
 __global__ void __launch_bounds__(256)
 k_trail_x3(TrailArgs g) {
   __shared__ __align__(16) uint8_t sm[kTSlots * kTSlot];
   if (g.st != nullptr && g.st->flags != 0) return;
-  const int ntn = (int)ceil_div(g.N, 128);
+  const int ntn = (int)ceil_div(g.N, kTN);
   const int tm = (int)blockIdx.x / ntn, tn = (int)blockIdx.x % ntn;
-  const int64_t m0 = (int64_t)tm * 128, n0 = (int64_t)tn * 128;
+  const int64_t m0 = (int64_t)tm * kTM, n0 = (int64_t)tn * kTN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(sm));
 
-  // DMA plan: wave w fills part w (0 A_hi, 1 A_lo, 2 B_hi, 3 B_lo) with 8
-  // instructions of 64 x 16 bytes.
-  //  A: instruction p covers rows 16p .. 16p+15 (4 chunks of 8 k each).
-  //  B: instruction p covers k rows 4p .. 4p+3 (16 chunks of 8 columns).
-  const bool isA = wave < 2;
-  const uint16_t* base = wave == 0 ? g.Ahi : wave == 1 ? g.Alo : wave == 2 ? g.Bhi : g.Blo;
-  int rr[8], cc[8];
-  bool rowok[8];
+  // buffers: A rows [m0, M), B rows [0, K) from column n0 on
+  const v4i32_t rAh = make_rsrc(g.Ahi + m0 * g.lda, (g.M - m0) * g.lda * 2);
+  const v4i32_t rAl = make_rsrc(g.Alo + m0 * g.lda, (g.M - m0) * g.lda * 2);
+  const int64_t bbytes = ((g.K - 1) * g.ldb + (g.N - n0)) * 2;
+  const v4i32_t rBh = make_rsrc(g.Bhi + n0, bbytes);
+  const v4i32_t rBl = make_rsrc(g.Blo + n0, bbytes);
+
+  // DMA plan: instruction idx = 12 w + q, q = 0..11:
+  //   0..15 A_hi, 16..31 A_lo: rows 16p .. 16p+15, 4 chunks of 8 k each
+  //   32..39 B_hi, 40..47 B_lo: k rows 4p .. 4p+3, 16 chunks of 8 columns
+  uint32_t voff[12];
 #pragma unroll
-  for (int p = 0; p < 8; ++p) {
-    if (isA) {
+  for (int q = 0; q < 12; ++q) {
+    const int idx = 12 * wave + q;
+    if (idx < 32) {
+      const int p = idx & 15;
       const int r = 16 * p + (lane >> 2);
-      rr[p] = r;
-      cc[p] = (lane & 3) ^ swz_a(r);
-      rowok[p] = m0 + r < g.M;
+      const int c = (lane & 3) ^ swz_a(r);
+      voff[q] = (uint32_t)((r * g.lda + 8 * c) * 2);
     } else {
+      const int p = idx & 7;
       const int kr = 4 * p + (lane >> 4);
-      rr[p] = kr;
-      cc[p] = (lane & 15) ^ dma_swz(kr);
-      rowok[p] = n0 + 8 * cc[p] < g.N;      // column chunk inside N
+      const int c = (lane & 15) ^ dma_swz(kr);
+      voff[q] = (n0 + 8 * c < g.N) ? (uint32_t)((kr * g.ldb + 8 * c) * 2) : 0x80000000u;
     }
   }
-  auto issue = [&](int st, uint32_t slot) {
-    const int64_t k0 = (int64_t)st * kTK;
+  auto issue = [&](int st, int slot) {
+    const uint32_t sa = __builtin_amdgcn_readfirstlane((uint32_t)(st * kTK * 2));
+    const uint32_t sb = __builtin_amdgcn_readfirstlane((uint32_t)(st * kTK * g.ldb * 2));
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const void* src;
-      if (isA) {
-        const int64_t k = k0 + 8 * cc[p];
-        src = (rowok[p] && k < g.K) ? (const void*)(base + (m0 + rr[p]) * g.lda + k) : (const void*)kZeroChunk;
-      } else {
-        const int64_t k = k0 + rr[p];
-        src = (rowok[p] && k < g.K) ? (const void*)(base + k * g.ldb + n0 + 8 * cc[p]) : (const void*)kZeroChunk;
-      }
-      dma16(src, __builtin_amdgcn_readfirstlane(slot + wave * kTPart + p * 1024));
+    for (int q = 0; q < 12; ++q) {
+      const int idx = 12 * wave + q;
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(
+          lds0 + slot * kTSlot +
+          (idx < 16 ? (idx & 15) * 1024
+                    : idx < 32 ? kTA + (idx & 15) * 1024
+                               : idx < 40 ? 2 * kTA + (idx & 7) * 1024 : 2 * kTA + kTB + (idx & 7) * 1024));
+      const v4i32_t r = idx < 16 ? rAh : idx < 32 ? rAl : idx < 40 ? rBh : rBl;
+      dma16_rsrc(voff[q], r, idx < 32 ? sa : sb, dst);
     }
   };
 
-  // fragment addressing
-  const int G = lane >> 4, sl = lane & 15;
-  const int trow = 8 * (G >> 1) + (sl >> 2);          // + 16 ks + 4 h
-  const int tchunk = 2 * (G & 1) + ((sl >> 1) & 1);   // + (64 wn + 32 nb) / 8
-  const int half8 = (sl & 1) * 8;
-  const int arow = lane & 31, akc = lane >> 5;          // + 64 wm + 32 mb ; + 2 ks
-
-  f32x16_t acc[2][2];
+  // fragment bases (per lane, relative to a slot)
+  //  A: row 128 wm + 32 mb + lane % 32, k chunk (2 ks + lane / 32) ^ swz_a(row)
+  //  B: k row 16 ks + 4 h + 8 (G/2) + s/4, column chunk (8 wn + 4 nb + 2 (G%2) + (s/2)%2) ^ dma_swz
+  const int arow = 128 * wm + (lane & 31);
+  const int sa_l = swz_a(arow);                  // same for every mb (32 mb adds 16 rows x 2)
+  uint32_t offA[2];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+  for (int ks = 0; ks < 2; ++ks) offA[ks] = arow * 64 + (((2 * ks + (lane >> 5)) ^ sa_l) * 16);
+  const int G = lane >> 4, sl = lane & 15;
+  const int trow = 8 * (G >> 1) + (sl >> 2);
+  const int swzb = dma_swz(trow);
+  uint32_t offB[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+    offB[nb] = 2 * kTA + trow * 256 + (((8 * wn + 4 * nb + 2 * (G & 1) + ((sl >> 1) & 1)) ^ swzb) * 16) +
+               (sl & 1) * 8;
+
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 2; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
   const int nstage = (int)ceil_div(g.K, kTK);
-  auto slot_of = [&](int st) { return lds0 + (uint32_t)(st % kTSlots) * kTSlot; };
 #pragma unroll
   for (int ps = 0; ps < kTSlots - 1; ++ps)
-    if (ps < nstage) issue(ps, slot_of(ps));
-
+    if (ps < nstage) issue(ps, ps);
   for (int st = 0; st < nstage; ++st) {
-    wait_dma_barrier(min(kTSlots - 2, nstage - 1 - st));
-    if (st + kTSlots - 1 < nstage) issue(st + kTSlots - 1, slot_of(st + kTSlots - 1));
-    const uint32_t slot = slot_of(st);
+    wait_dma12_barrier(min(kTSlots - 2, nstage - 1 - st));
+    if (st + kTSlots - 1 < nstage) issue(st + kTSlots - 1, (st + kTSlots - 1) % kTSlots);
+    const uint32_t sbase = lds0 + (uint32_t)(st % kTSlots) * kTSlot;
+    uint32_t bA[2], bB[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      bA[q] = offA[q] + sbase;
+      bB[q] = offB[q] + sbase;
+    }
 #pragma unroll
     for (int ks = 0; ks < kTK / 16; ++ks) {
-      bf16x8_t ah[2], al[2], bh[2], bl[2];
+      bf16x8_t ah[4], al[4], bh[2], bl[2];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const int r = 64 * wm + 32 * mb + arow;
-        const uint32_t off = r * 64 + (((2 * ks + akc) ^ swz_a(r)) * 16);
+      for (int mb = 0; mb < 4; ++mb) {
+        const uint32_t o = bA[ks] + mb * 32 * 64;
         ah[mb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const __attribute__((address_space(3))) uint4*>(
-                                                  (uintptr_t)(slot + off)));
+                                                  (uintptr_t)o));
         al[mb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const __attribute__((address_space(3))) uint4*>(
-                                                  (uintptr_t)(slot + kTPart + off)));
+                                                  (uintptr_t)(o + kTA)));
       }
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        v4i16_t h0, h1, l0, l1;
-        {
-          const int t = 16 * ks + trow;
-          const uint32_t off = t * 256 + (((8 * wn + 4 * nb + tchunk) ^ dma_swz(t)) * 16) + half8;
-          h0 = lds_tr16(slot + 2 * kTPart + off);
-          l0 = lds_tr16(slot + 3 * kTPart + off);
-        }
-        {
-          const int t = 16 * ks + 4 + trow;
-          const uint32_t off = t * 256 + (((8 * wn + 4 * nb + tchunk) ^ dma_swz(t)) * 16) + half8;
-          h1 = lds_tr16(slot + 2 * kTPart + off);
-          l1 = lds_tr16(slot + 3 * kTPart + off);
-        }
+        const uint32_t o = bB[nb] + 16 * ks * 256;
+        const v4i16_t h0 = lds_tr16(o), h1 = lds_tr16(o + 4 * 256);
+        const v4i16_t l0 = lds_tr16(o + kTB), l1 = lds_tr16(o + kTB + 4 * 256);
         bh[nb] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
         bl[nb] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7));
       }
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mb], bh[nb], acc[mb][nb], 0, 0, 0);
@@ -150,19 +184,30 @@ k_trail_x3(TrailArgs g) {
     }
   }
 
-  // C -= acc: lane holds D[i][j], j = lane % 32, i = 8 (r / 4) + 4 (lane / 32) + r % 4
+  // C -= acc: lane holds D[i][j], j = lane % 32, i = 8 (r / 4) + 4 (lane / 32) + r % 4.
+  // Every C value is loaded before the first store: a store followed by a
+  // load the compiler cannot prove disjoint would serialise the 128
+  // read-modify-writes on memory latency.
+  float cv[4][2][16];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
+  for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t i = m0 + 64 * wm + 32 * mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int64_t i = m0 + 128 * wm + 32 * mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         const int64_t j = n0 + 64 * wn + 32 * nb + (lane & 31);
-        if (i < g.M && j < g.N) {
-          float* c = g.C + i * g.ldc + j;
-          *c = *c - acc[mb][nb][r];
-        }
+        cv[mb][nb][r] = (i < g.M && j < g.N) ? g.C[i * g.ldc + j] : 0.f;
+      }
+#pragma unroll
+  for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t i = m0 + 128 * wm + 32 * mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int64_t j = n0 + 64 * wn + 32 * nb + (lane & 31);
+        if (i < g.M && j < g.N) g.C[i * g.ldc + j] = cv[mb][nb][r] - acc[mb][nb][r];
       }
 }
 
@@ -173,7 +218,9 @@ hipError_t launch_trail_x3(hipStream_t s, const TrailArgs& g) {
   if ((g.lda % 8) || (g.ldb % 8) || (g.N % 8) || (g.K % 8) || ((uintptr_t)g.Ahi % 16) ||
       ((uintptr_t)g.Alo % 16) || ((uintptr_t)g.Bhi % 16) || ((uintptr_t)g.Blo % 16))
     return hipErrorInvalidValue;
-  const int64_t tiles = ceil_div(g.M, 128) * ceil_div(g.N, 128);
+  // 32-bit buffer offsets
+  if (g.M * g.lda * 2 >= ((int64_t)1 << 31) || g.K * g.ldb * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  const int64_t tiles = ceil_div(g.M, kTM) * ceil_div(g.N, kTN);
   hipLaunchKernelGGL(k_trail_x3, dim3((unsigned)tiles), dim3(256), 0, s, g);
   return hipGetLastError();
 }
