@@ -15,7 +15,7 @@
 // Layout (MI355X): 256 x 128 output tile per workgroup of 4 waves (2 x 2,
 // each 128 x 64 = 4 x 2 accumulators). K streams through a 3-slot LDS ring
 // of 32-deep stages (48 KiB each) filled by buffer LDS-DMA: A_hi, A_lo as
-// [row][k] (64-byte rows, chunk index XOR-swizzled with (row / 2) % 4) read
+// [row][k] (64-byte rows, chunk index XOR-swizzled with (row / 4) % 4) read
 // with ds_read_b128, and B_hi, B_lo as [k][column] (256-byte rows, swizzled
 // like the Hessian tile) read with transposing ds_read_b64_tr_b16. The
 // buffer descriptors end at the last row of A and at row K of B, so rows
@@ -37,7 +37,10 @@ constexpr int kTA = kTM * kTK * 2;         // bytes of A_hi (or A_lo) per stage:
 constexpr int kTB = kTK * kTN * 2;         // bytes of B_hi (or B_lo) per stage: 8 KiB
 constexpr int kTSlot = 2 * kTA + 2 * kTB;  // 48 KiB
 
-__device__ __forceinline__ int swz_a(int row) { return (row >> 1) & 3; }
+// A rows are 64 bytes: rows r and r + 4 share banks, so the 16-byte chunk
+// index is XORed with (r / 4) % 4 (16 consecutive rows of one chunk column
+// then cover all 64 banks)
+__device__ __forceinline__ int swz_a(int row) { return (row >> 2) & 3; }
 
 __device__ __forceinline__ void dma16_rsrc(uint32_t voff, v4i32_t rsrc, uint32_t soff, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
@@ -65,8 +68,15 @@ __global__ void __launch_bounds__(256)
 k_trail_x3(TrailArgs g) {
   __shared__ __align__(16) uint8_t sm[kTSlots * kTSlot];
   if (g.st != nullptr && g.st->flags != 0) return;
+  // XCD-contiguous tile order: block b runs on XCD b % 8; give each XCD a
+  // contiguous run of row-major tiles, so the rows of A it needs stay in its
+  // L2 and each column tile of B is fetched once per XCD
   const int ntn = (int)ceil_div(g.N, kTN);
-  const int tm = (int)blockIdx.x / ntn, tn = (int)blockIdx.x % ntn;
+  const int ntiles = (int)ceil_div(g.M, kTM) * ntn;
+  const int per = (ntiles + 7) >> 3;
+  const int w = ((int)blockIdx.x & 7) * per + ((int)blockIdx.x >> 3);
+  if (((int)blockIdx.x >> 3) >= per || w >= ntiles) return;
+  const int tm = w / ntn, tn = w % ntn;
   const int64_t m0 = (int64_t)tm * kTM, n0 = (int64_t)tn * kTN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -119,7 +129,7 @@ k_trail_x3(TrailArgs g) {
   //  A: row 128 wm + 32 mb + lane % 32, k chunk (2 ks + lane / 32) ^ swz_a(row)
   //  B: k row 16 ks + 4 h + 8 (G/2) + s/4, column chunk (8 wn + 4 nb + 2 (G%2) + (s/2)%2) ^ dma_swz
   const int arow = 128 * wm + (lane & 31);
-  const int sa_l = swz_a(arow);                  // same for every mb (32 mb adds 16 rows x 2)
+  const int sa_l = swz_a(arow);                  // same for every mb (32 mb adds 8 to row / 4)
   uint32_t offA[2];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) offA[ks] = arow * 64 + (((2 * ks + (lane >> 5)) ^ sa_l) * 16);
@@ -221,7 +231,7 @@ hipError_t launch_trail_x3(hipStream_t s, const TrailArgs& g) {
   // 32-bit buffer offsets
   if (g.M * g.lda * 2 >= ((int64_t)1 << 31) || g.K * g.ldb * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const int64_t tiles = ceil_div(g.M, kTM) * ceil_div(g.N, kTN);
-  hipLaunchKernelGGL(k_trail_x3, dim3((unsigned)tiles), dim3(256), 0, s, g);
+  hipLaunchKernelGGL(k_trail_x3, dim3((unsigned)(8 * ceil_div(tiles, 8))), dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
