@@ -6,20 +6,24 @@
 // "Resumen Técnico: GPTQ-intrinsic LoRA", "Detalles de Implementación":
 // the standard method factorises the regularised Hessian by Cholesky.
 //
-// Work split (wave w = 0..3, lane = threadIdx.x % 64):
+// Work split (wave w = 0..3, lane = threadIdx.x % 64), in 16 blocks of 4
+// consecutive pivots; block b is owned by wave b % 4:
 //  * Cholesky, right-looking: lane i holds row i; wave w holds the columns
-//    j = 4q + w (q = 0..15) in registers a[q]. Step K: the owner wave of
-//    column K (K % 4) takes the pivot from lane K (v_readlane), scales the
-//    column and publishes it in LDS; after one barrier every wave applies
-//    the rank-1 update to its own columns j > K (at most 16 FMAs per lane).
-//  * Inverse X = L^{-1}, column-oriented forward substitution, one step
-//    behind: lane c holds column c of X; wave w holds the rows i = 4q + w.
-//    In step K the owner of row K-1 divides it by L[K-1][K-1] and publishes
-//    it; after the same barrier every wave subtracts L[i][K-1] X[K-1][c]
-//    from its rows i > K-1.
-//  Both chains share one barrier per step. L's columns are stored
-//  wave-interleaved (colw[k][16 w + q] = L[4q + w][k]) so that each wave
-//  reads the 16 values it needs as four 16-byte broadcasts.
+//    of its blocks, j = 16q + 4w + c (q, c = 0..3), in registers a[q][c].
+//    The owner of block b takes its 4 pivots in registers: pivot from lane
+//    K (v_readlane), scale the column, update the block's later columns
+//    with the column's entries read by v_readlane.
+//  * Inverse X = L^{-1}, column-oriented forward substitution: lane c holds
+//    column c of X; wave w holds the rows of its blocks, x[q][c'] =
+//    X[16q + 4w + c'][lane]. The owner of block b finalises rows 4b..4b+3
+//    right after the block's pivots (divide by L_kk, eliminate within the
+//    block).
+//  * One barrier per block publishes the 4 columns of L and the 4 rows of
+//    X; every wave then applies the rank-4 update to its later Cholesky
+//    columns and its later X rows. L's columns are stored in the order
+//    pos(i) = 16 w_i + 4 q_i + c_i of i = 16 q_i + 4 w_i + c_i, so a wave
+//    reads the 16 values of its own index set as four 16-byte broadcasts
+//    (and the same values serve both updates).
 // A non-positive or non-finite pivot raises kNotPD with the original column
 // perm[n-1-(k0+k)] (the matrix is the index-reversed Hessian).
 #pragma once
@@ -30,81 +34,89 @@
 namespace gq {
 
 struct LeafSmem {
-  float colw[64][64];   // colw[k][16 w + q] = L[4q + w][k]
+  float colw[64][64];   // colw[k][pos(i)] = L[i][k]
   float xrow[64][64];   // xrow[k][c] = X[k][c], final rows of L^{-1}
-  float inv[64];        // 1 / L[k][k]
   int bad;              // first failed pivot (64: none)
 };
 
 struct LeafState {
-  float a[16];          // A[lane][4q + w] -> Schur complement, lower part used
-  float x[16];          // X[4q + w][lane]
-  float lj[16];         // colw[K-1][16 w .. 16 w + 15] from the previous step
+  float a[4][4];        // A[lane][16q + 4w + c] -> Schur complement / L columns
+  float x[4][4];        // X[16q + 4w + c][lane]
 };
 
-__device__ __forceinline__ void leaf_read16(const float* p, float (&v)[16]) {
-#pragma unroll
-  for (int q = 0; q < 16; q += 4) {
-    const float4 t = *reinterpret_cast<const float4*>(p + q);
-    v[q] = t.x; v[q + 1] = t.y; v[q + 2] = t.z; v[q + 3] = t.w;
-  }
+__device__ __forceinline__ int leaf_pos(int i) { return 16 * ((i >> 2) & 3) + 4 * (i >> 4) + (i & 3); }
+
+__device__ __forceinline__ float lane_val(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-template <int K>
-__device__ __forceinline__ void leaf_step(LeafState& S, LeafSmem& sm, int w, int lane) {
-  constexpr int qK = K / 4, oK = K % 4;
-  // ---- before the barrier: pivot column K, and row K-1 of X
-  if (w == oK) {
-    const float d2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(S.a[qK]), K));
-    const bool ok = d2 > 0.f && isfinite(d2);
-    if (!ok && lane == 0) atomicMin(&sm.bad, K);
-    const float inv = ok ? __builtin_amdgcn_rsqf(d2) : 1.f;   // 1 / sqrt(d2)
-    const float d = ok ? d2 * inv : 1.f;
-    float l = (lane > K) ? S.a[qK] * inv : 0.f;
-    l = (lane == K) ? d : l;
-    sm.colw[K][16 * (lane & 3) + (lane >> 2)] = l;
-    if (lane == K) sm.inv[K] = inv;
-  }
-  if constexpr (K >= 1) {
-    constexpr int qP = (K - 1) / 4, oP = (K - 1) % 4;
-    if (w == oP) {
-      S.x[qP] *= sm.inv[K - 1];
-      sm.xrow[K - 1][lane] = S.x[qP];
+template <int BLK>
+__device__ __forceinline__ void leaf_block(LeafState& S, LeafSmem& sm, int w, int lane) {
+  constexpr int qb = BLK / 4, ob = BLK % 4, K0 = 4 * BLK;
+  if (w == ob) {
+    // ---- the block's 4 pivots
+    float invs[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int K = K0 + c;
+      const float d2 = lane_val(S.a[qb][c], K);
+      const bool ok = d2 > 0.f && isfinite(d2);
+      if (!ok && lane == 0) atomicMin(&sm.bad, K);
+      const float inv = ok ? __builtin_amdgcn_rsqf(d2) : 1.f;   // 1 / sqrt(d2)
+      const float d = ok ? d2 * inv : 1.f;
+      float l = (lane > K) ? S.a[qb][c] * inv : 0.f;
+      l = (lane == K) ? d : l;
+      S.a[qb][c] = l;
+      invs[c] = inv;
+#pragma unroll
+      for (int c2 = c + 1; c2 < 4; ++c2) S.a[qb][c2] = fmaf(-l, lane_val(l, K0 + c2), S.a[qb][c2]);
+    }
+    // ---- rows K0..K0+3 of X: forward substitution inside the block
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      S.x[qb][c] *= invs[c];
+#pragma unroll
+      for (int c2 = c + 1; c2 < 4; ++c2) S.x[qb][c2] = fmaf(-lane_val(S.a[qb][c], K0 + c2), S.x[qb][c], S.x[qb][c2]);
+    }
+    const int pl = leaf_pos(lane);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      sm.colw[K0 + c][pl] = S.a[qb][c];
+      sm.xrow[K0 + c][lane] = S.x[qb][c];
     }
   }
   __syncthreads();
-  // ---- after the barrier: rank-1 update with column K, substitution with row K-1
-  const float li = sm.colw[K][16 * (lane & 3) + (lane >> 2)];
-  float lk[16];
-  leaf_read16(&sm.colw[K][16 * w], lk);
+  // ---- rank-4 updates of the later blocks of every wave. Blocks with
+  // q > qb are later for every wave; block 4 qb + w only for w > ob, which
+  // is applied branch-free by zeroing the multipliers of the other waves.
+  if constexpr (BLK < 15) {
+    const int pl = leaf_pos(lane);
+    const bool later = w > ob;
 #pragma unroll
-  for (int q = qK; q < 16; ++q) {
-    if (q == qK) {
-      if (w > oK) S.a[q] = fmaf(-li, lk[q], S.a[q]);
-    } else {
-      S.a[q] = fmaf(-li, lk[q], S.a[q]);
-    }
-  }
-  if constexpr (K >= 1) {
-    constexpr int qP = (K - 1) / 4, oP = (K - 1) % 4;
-    const float xk = sm.xrow[K - 1][lane];
+    for (int c = 0; c < 4; ++c) {
+      const int k = K0 + c;
+      const float li = sm.colw[k][pl];
+      const float xk = sm.xrow[k][lane];
+      const float lq = later ? li : 0.f, xq = later ? xk : 0.f;
 #pragma unroll
-    for (int q = qP; q < 16; ++q) {
-      if (q == qP) {
-        if (w > oP) S.x[q] = fmaf(-S.lj[q], xk, S.x[q]);
-      } else {
-        S.x[q] = fmaf(-S.lj[q], xk, S.x[q]);
+      for (int q = qb; q < 4; ++q) {
+        const float4 t = *reinterpret_cast<const float4*>(&sm.colw[k][16 * w + 4 * q]);
+        const float lj[4] = {t.x, t.y, t.z, t.w};
+        const float lm = (q == qb) ? lq : li, xm = (q == qb) ? xq : xk;
+#pragma unroll
+        for (int c2 = 0; c2 < 4; ++c2) {
+          S.a[q][c2] = fmaf(-lm, lj[c2], S.a[q][c2]);
+          S.x[q][c2] = fmaf(-lj[c2], xm, S.x[q][c2]);
+        }
       }
     }
   }
-#pragma unroll
-  for (int q = 0; q < 16; ++q) S.lj[q] = lk[q];
 }
 
-template <int... Ks>
-__device__ __forceinline__ void leaf_steps(LeafState& S, LeafSmem& sm, int w, int lane,
-                                           std::integer_sequence<int, Ks...>) {
-  (leaf_step<Ks>(S, sm, w, lane), ...);
+template <int... Bs>
+__device__ __forceinline__ void leaf_blocks(LeafState& S, LeafSmem& sm, int w, int lane,
+                                            std::integer_sequence<int, Bs...>) {
+  (leaf_block<Bs>(S, sm, w, lane), ...);
 }
 
 // All 256 threads of the workgroup: factors the m x m block whose lower part
@@ -118,24 +130,25 @@ __device__ __forceinline__ void leaf_run(const float* src, int64_t lds, float* _
   LeafState S;
   if (threadIdx.x == 0) sm.bad = 64;
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int j = 4 * q + w;
-    const float v = src[min(lane, m - 1) * lds + min(j, m - 1)];   // always in bounds
-    S.a[q] = (lane < m && j < m) ? ((j <= lane) ? v : 0.f) : ((lane == j) ? 1.f : 0.f);
-    S.x[q] = (j == lane) ? 1.f : 0.f;
-    S.lj[q] = 0.f;
-  }
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int j = 16 * q + 4 * w + c;
+      const float v = src[min(lane, m - 1) * lds + min(j, m - 1)];   // always in bounds
+      S.a[q][c] = (lane < m && j < m) ? ((j <= lane) ? v : 0.f) : ((lane == j) ? 1.f : 0.f);
+      S.x[q][c] = (j == lane) ? 1.f : 0.f;
+    }
   __syncthreads();   // sm.bad initialised before any pivot can fail
-  leaf_steps(S, sm, w, lane, std::make_integer_sequence<int, 64>{});
-  // last row of X: divide by L[63][63]
-  if (w == 3) S.x[15] *= sm.inv[63];
+  leaf_blocks(S, sm, w, lane, std::make_integer_sequence<int, 16>{});
   if (threadIdx.x == 0 && sm.bad < m) raise_status(st, kNotPD, perm[n - 1 - (k0 + sm.bad)]);
   float* xcol = X + k0 * n + k0 + lane;
 #pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const int i = 4 * q + w;
-    if (i < m && lane < m && lane <= i) xcol[(int64_t)i * n] = S.x[q];
-  }
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int i = 16 * q + 4 * w + c;
+      if (i < m && lane < m && lane <= i) xcol[(int64_t)i * n] = S.x[q][c];
+    }
 }
 
 // Step k's Schur update of the next diagonal block followed by its leaf, for
