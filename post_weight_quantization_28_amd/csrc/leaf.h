@@ -155,57 +155,69 @@ __device__ __forceinline__ void leaf_run(const float* src, int64_t lds, float* _
 // the workgroup that runs beside step k's trailing update:
 //   Ad = A[k1:k1+m2, k1:k1+m2] - L21[0:m2] L21[0:m2]^T   (lower part)
 //   D' = chol(Ad)^{-1} -> X[k1:k1+m2, k1:k1+m2]
-// L21's first m2 rows are staged transposed (lt[k][i] = L21[i][k]); thread
-// (r4, c4) accumulates the 4 x 4 block rows 4 r4.., columns 4 c4.. with two
-// 16-byte reads per k.
+// Every global load (L21's first m2 rows, the block) is issued up front with
+// clamped, always-valid addresses. L21 is staged row-major (k contiguous);
+// waves 0-2 each take one lower 32 x 32 tile of the product on
+// v_mfma_f32_32x32x2f32. Within each group of 8 k, lane half h feeds k =
+// 4h + t to the t-th MFMA, so a lane reads its 4 k values as one 16-byte
+// LDS read; the result is combined with the block read straight into the
+// accumulator layout.
+typedef float leaf_f32x16 __attribute__((ext_vector_type(16)));
+
 struct LeafTaskSmem {
   union {
-    struct {
-      float lt[64][68];
-      float blk[64][65];
-    } s;
+    float lrow[64][68];   // L21[i][k], zero outside m2 x mk
     LeafSmem leaf;
   } u;
-  float blk2[64][65];   // the updated block, input of the leaf
+  float blk2[64][65];     // the updated block, input of the leaf
 };
 
 __device__ inline void leaf_task_run(const LeafTask& t, LeafTaskSmem& sm) {
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t n = t.n;
-  for (int e = tid; e < 64 * 64; e += 256) {
-    const int i = e >> 6, j = e & 63;
-    sm.u.s.lt[j][i] = (i < t.m2 && j < t.mk) ? t.L21[i * n + j] : 0.f;
-    sm.u.s.blk[i][j] = (i < t.m2 && j <= i) ? t.A[(t.k1 + i) * n + t.k1 + j] : 0.f;
+  const int m2 = t.m2, mk = t.mk;
+  float lv[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int i = (tid >> 6) + 4 * v;
+    lv[v] = t.L21[(int64_t)min(i, m2 - 1) * n + min(lane, mk - 1)];
+  }
+  // tile (ta, tb) of this wave: (0,0), (1,0), (1,1); wave 3 has none
+  const int ta = wave >= 1 ? 1 : 0, tb = wave == 2 ? 1 : 0;
+  const int lr = lane & 31, lh = lane >> 5;
+  float av[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = 32 * ta + 8 * (r >> 2) + 4 * lh + (r & 3), col = 32 * tb + lr;
+    av[r] = t.A[(t.k1 + min(row, m2 - 1)) * n + t.k1 + min(col, m2 - 1)];
+  }
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int i = (tid >> 6) + 4 * v;
+    sm.u.lrow[i][lane] = (i < m2 && lane < mk) ? lv[v] : 0.f;
   }
   __syncthreads();
-  {
-    const int r4 = tid >> 4, c4 = tid & 15;
-    if (4 * c4 <= 4 * r4 + 3) {   // block touches the lower triangle
-      float acc[4][4];
+  if (wave < 3) {
+    leaf_f32x16 acc;
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
+    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) acc[a][b] = 0.f;
-      for (int k = 0; k < t.mk; ++k) {
-        const float4 li = *reinterpret_cast<const float4*>(&sm.u.s.lt[k][4 * r4]);
-        const float4 lj = *reinterpret_cast<const float4*>(&sm.u.s.lt[k][4 * c4]);
-        const float lv[4] = {li.x, li.y, li.z, li.w}, jv[4] = {lj.x, lj.y, lj.z, lj.w};
+    for (int p = 0; p < 8; ++p) {
+      const float4 fa = *reinterpret_cast<const float4*>(&sm.u.lrow[32 * ta + lr][8 * p + 4 * lh]);
+      const float4 fb = *reinterpret_cast<const float4*>(&sm.u.lrow[32 * tb + lr][8 * p + 4 * lh]);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa.x, fb.x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa.y, fb.y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa.z, fb.z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa.w, fb.w, acc, 0, 0, 0);
+    }
 #pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-          for (int b = 0; b < 4; ++b) acc[a][b] = fmaf(lv[a], jv[b], acc[a][b]);
-      }
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const int i = 4 * r4 + a, j = 4 * c4 + b;
-          sm.blk2[i][j] = (j <= i) ? sm.u.s.blk[i][j] - acc[a][b] : 0.f;
-        }
+    for (int r = 0; r < 16; ++r) {
+      const int row = 32 * ta + 8 * (r >> 2) + 4 * lh + (r & 3), col = 32 * tb + lr;
+      sm.blk2[row][col] = (col <= row) ? av[r] - acc[r] : 0.f;
     }
   }
   __syncthreads();
-  leaf_run(&sm.blk2[0][0], 65, t.X, n, t.k1, t.m2, t.perm, t.st, sm.u.leaf);
+  leaf_run(&sm.blk2[0][0], 65, t.X, n, t.k1, m2, t.perm, t.st, sm.u.leaf);
 }
 
 }  // namespace gq

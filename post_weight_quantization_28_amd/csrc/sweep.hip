@@ -15,47 +15,86 @@
 // E (d_out x B) collects e_j for the trailing update of the later blocks.
 //
 // Layout (MI355X): a wavefront holds 4 rows; the 16 lanes of a DPP row own
-// one weight row, CPL = B/16 consecutive columns each, in registers. The
-// value being decided is broadcast to its 16 lanes with DPP row_newbcast
-// (no LDS round trip), every lane rounds it redundantly and applies the
-// rank-1 feedback to its own columns with U's row j read from LDS (the
-// block's strictly-upper U tile, 64 KiB at B = 128, shared by the 16 rows of
-// the workgroup). The loop over j is fully unrolled so the owner lane and
-// the register slot are compile-time constants.
+// one weight row, column 16c + L in register slot c of lane L (c < CPL =
+// B/16, cyclic). Column j is decided by lane j % 16 from slot j / 16: the
+// value is broadcast to its 16 lanes with DPP row_newbcast (no LDS round
+// trip), every lane rounds it redundantly and applies the rank-1 feedback to
+// its own slots with U's row j read from LDS. Because the layout is cyclic,
+// every slot below (j + 1) / 16 holds only finished columns and is skipped
+// at compile time: the feedback costs half of a dense row update. The loop
+// over j is fully unrolled (owner lane and slots are compile-time
+// constants) and branch-free, so the U row for step j + 2 is in flight
+// while step j computes. Codes and errors are kept by a select with a
+// constant lane mask; w_hat and the row loss are formed once at the end.
 #include "common.h"
 #include <utility>
 
 namespace gq {
 
 template <int O>
-__device__ inline float bcast16(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x150 + O, 0xF, 0xF, false));
+__device__ __forceinline__ float bcast16(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x150 + O, 0xF, 0xF, false));
 }
 
-__device__ inline float row_min16(float v) {
-#pragma unroll
-  for (int m = 8; m > 0; m >>= 1) v = fminf(v, __shfl_xor(v, m, 16));
-  return v;
+// Reductions over the 16 lanes of a DPP row by rotations of 8, 4, 2, 1 (all
+// lanes end with the full result; no LDS round trip)
+template <int N>
+__device__ __forceinline__ float ror16(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x120 + N, 0xF, 0xF, false));
 }
-__device__ inline float row_max16(float v) {
-#pragma unroll
-  for (int m = 8; m > 0; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 16));
-  return v;
+__device__ __forceinline__ float row_min16(float v) {
+  v = fminf(v, ror16<8>(v));
+  v = fminf(v, ror16<4>(v));
+  v = fminf(v, ror16<2>(v));
+  return fminf(v, ror16<1>(v));
+}
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, ror16<8>(v));
+  v = fmaxf(v, ror16<4>(v));
+  v = fmaxf(v, ror16<2>(v));
+  return fmaxf(v, ror16<1>(v));
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += ror16<8>(v);
+  v += ror16<4>(v);
+  v += ror16<2>(v);
+  return v + ror16<1>(v);
 }
 
+// r = (lane is lane O of its 16-lane row) ? a : b, with the lane mask a
+// compile-time constant in an SGPR pair (no per-step compare)
+template <int O>
+__device__ __forceinline__ float sel_owner(float a, float b) {
+  constexpr uint64_t mask = 0x0001000100010001ull << O;
+  float r;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(b), "v"(a), "s"(mask));
+  return r;
+}
+
+// LDS position of slot c of lane L in U row r: slots in groups of V =
+// min(4, CPL), group-major, so a V-wide vector read by the 16 lanes of a row
+// covers consecutive banks. The lane index is XOR-swizzled by the row and
+// group parity: the prologue's scalar stores (4 columns of one row per
+// thread) then hit 64 distinct banks per instruction, and each row read is
+// still a permutation of whole chunks.
 template <int CPL>
-struct Regs {
-  float v[CPL];
-};
+__device__ __forceinline__ constexpr int upos(int r, int c, int L) {
+  constexpr int V = CPL < 4 ? CPL : 4;
+  const int g = c / V;
+  const int sw = (r & 1) | ((g & 1) << 1);
+  return r * 16 * CPL + g * 16 * V + V * (L ^ sw) + (c % V);
+}
 
 template <int CPL>
 struct SweepState {
   float w[CPL];
-  float ev[CPL];
-  uint32_t qv[CPL];
-  float un[2][CPL];  // U rows, loaded one step ahead (even / odd steps)
-  float invn[2];     // 1 / U_jj for the same steps
-  float s, inv_s, z, loss;
+  float ev[CPL];       // e of the lane's columns (0 until decided)
+  float qv[CPL];       // codes as floats
+  float gs[CPL], gz[CPL];   // (s, z) of each slot's group, for w_hat at the end
+  float un[3][CPL];    // U rows of steps j, j+1, j+2 (ring of three)
+  float invn[3];       // 1 / U_jj for the same steps
+  float s, inv_s, z;
+  float nz, mz;        // -z and maxq - z: the clamp range of rint(w / s)
   int nc, gmask;   // columns in this block; group-1 when groups split the block, else -1
 };
 
@@ -64,22 +103,20 @@ struct Grid {
 };
 
 // (s, z) from the current values of columns [lo, hi) of this block's row
-// (the lane's CPL registers, passed by value) plus, when the group runs past
-// the block, columns [i0 + B, i0 + hi) read from Wf. Groups are at least 8
-// columns wide, so inside a block this code is instantiated only at every
-// 8th unrolled step (inlining it into every step would overflow the
-// instruction cache).
-template <int CPL>
-__device__ __forceinline__ Grid group_start(const Regs<CPL>& w, const SweepArgs& a, int L,
-                                            int64_t row, bool row_ok, int lo, int hi, float maxq) {
+// (the lane's slots) plus, when the group runs past the block, columns
+// [i0 + B, i0 + hi) read from Wf. Groups are at least 8 columns wide, so
+// inside a block this code is instantiated only at every 8th unrolled step.
+template <int CPL, int LO>
+__device__ __forceinline__ Grid group_start(const float (&w)[CPL], const SweepArgs& a, int L,
+                                            int64_t row, bool row_ok, int hi, float maxq) {
   constexpr int B = 16 * CPL;
   float mn = INFINITY, mx = -INFINITY;
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) {
-    const int col = L * CPL + c;
-    if (col >= lo && col < hi) {
-      mn = fminf(mn, w.v[c]);
-      mx = fmaxf(mx, w.v[c]);
+  for (int c = LO / 16; c < CPL; ++c) {
+    const int col = 16 * c + L;
+    if (col >= LO && col < hi) {
+      mn = fminf(mn, w[c]);
+      mx = fmaxf(mx, w[c]);
     }
   }
   if (hi > B && row_ok) {
@@ -102,79 +139,97 @@ __device__ __forceinline__ Grid group_start(const Regs<CPL>& w, const SweepArgs&
   g.z = rintf(-xmin / g.s);
   g.inv_s = 1.f / g.s;
   if (row_ok && L == 0) {
-    const int64_t gi = a.gbase + (lo >> a.gshift);
+    const int64_t gi = a.gbase + (LO >> a.gshift);
     a.scales[row * a.ngroups + gi] = g.s;
     a.zeros[row * a.ngroups + gi] = (uint8_t)g.z;
   }
   return g;
 }
 
-template <int CPL>
+template <int CPL, int LO>
 __device__ __forceinline__ void start_group(SweepState<CPL>& S, const SweepArgs& a, int L, int64_t row,
-                                   bool row_ok, int lo, float maxq) {
-  Regs<CPL> r;
-#pragma unroll
-  for (int c = 0; c < CPL; ++c) r.v[c] = S.w[c];
-  const Grid g = group_start<CPL>(r, a, L, row, row_ok, lo, lo + a.group, maxq);
+                                            bool row_ok, float maxq) {
+  const int hi = LO + a.group;
+  const Grid g = group_start<CPL, LO>(S.w, a, L, row, row_ok, hi, maxq);
   S.s = g.s;
   S.z = g.z;
   S.inv_s = g.inv_s;
+  S.nz = -g.z;
+  S.mz = maxq - g.z;
+#pragma unroll
+  for (int c = LO / 16; c < CPL; ++c) {
+    const int col = 16 * c + L;
+    const bool in = col >= LO && col < hi;
+    S.gs[c] = in ? g.s : S.gs[c];
+    S.gz[c] = in ? g.z : S.gz[c];
+  }
 }
 
-template <int CPL, int P>
-__device__ __forceinline__ void load_urow(SweepState<CPL>& S, const float (*sU)[16 * CPL],
-                                          const float* sInv, int L, int j) {
-  const float* ur = &sU[j][L * CPL];
+// U row j (slots c >= C0 only; earlier slots are finished for every lane)
+template <int CPL, int P, int C0>
+__device__ __forceinline__ void load_urow(SweepState<CPL>& S, const float* sU, const float* sInv, int L,
+                                          int j) {
+  constexpr int V = CPL < 4 ? CPL : 4;
 #pragma unroll
-  for (int c = 0; c < CPL; c += 2) {
-    const float2 u = *reinterpret_cast<const float2*>(ur + c);
-    S.un[P][c] = u.x;
-    S.un[P][c + 1] = u.y;
+  for (int g = C0 / V; g < CPL / V; ++g) {
+    const float* p = sU + upos<CPL>(j, g * V, L);
+    if constexpr (V == 4) {
+      const float4 u = *reinterpret_cast<const float4*>(p);
+      S.un[P][4 * g] = u.x; S.un[P][4 * g + 1] = u.y; S.un[P][4 * g + 2] = u.z; S.un[P][4 * g + 3] = u.w;
+    } else {
+      const float2 u = *reinterpret_cast<const float2*>(p);
+      S.un[P][2 * g] = u.x; S.un[P][2 * g + 1] = u.y;
+    }
   }
   S.invn[P] = sInv[j];
 }
 
 template <int CPL, int J>
-__device__ inline void sweep_step(SweepState<CPL>& S, const SweepArgs& a, const float (*sU)[16 * CPL],
-                                  const float* sInv, int L, int64_t row, bool row_ok, float maxq) {
+__device__ __forceinline__ void sweep_step(SweepState<CPL>& S, const SweepArgs& a, const float* sU,
+                                           const float* sInv, int L, int64_t row, bool row_ok, float maxq) {
   constexpr int B = 16 * CPL;
-  constexpr int O = J / CPL, C = J % CPL;
-  if (J >= S.nc) return;
+  constexpr int O = J % 16, C = J / 16;   // owner lane and slot of column J
+  constexpr int C0 = (J + 1) / 16;        // first slot with a column after J
   if constexpr (J > 0 && (J % 8) == 0) {
-    if ((J & S.gmask) == 0) start_group<CPL>(S, a, L, row, row_ok, J, maxq);
+    if (J < S.nc && (J & S.gmask) == 0) start_group<CPL, J>(S, a, L, row, row_ok, maxq);
   }
-  // this step's U row was loaded by the previous step; start the next load
-  constexpr int P = J & 1;
+  constexpr int P = J % 3;
+  if constexpr (J + 2 < B) load_urow<CPL, (J + 2) % 3, (J + 3) / 16>(S, sU, sInv, L, J + 2);
+  // keep those reads here (two steps ahead of their use): only ALU work may
+  // be scheduled across this point
+  __builtin_amdgcn_sched_barrier(0x407);
   const float* u = S.un[P];
   const float invd = S.invn[P];
-  if constexpr (J + 1 < B) load_urow<CPL, P ^ 1>(S, sU, sInv, L, J + 1);
+  // q - z = clamp(rint(w / s), -z, maxq - z) exactly (z is an integer), so
+  // the dependent chain is mul, round, med3, fma, mul
   const float wj = bcast16<O>(S.w[C]);
-  const float q = fminf(fmaxf(rintf(wj * S.inv_s) + S.z, 0.f), maxq);
-  const float what = S.s * (q - S.z);
-  const float e = (wj - what) * invd;
-  S.loss = fmaf(e, e, S.loss);
+  const float qz = __builtin_amdgcn_fmed3f(rintf(wj * S.inv_s), S.nz, S.mz);
+  const float e = fmaf(-S.s, qz, wj) * invd;   // (w - s (q - z)) / U_jj
+  const float q = qz + S.z;
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) S.w[c] = fmaf(-e, u[c], S.w[c]);
-  const bool own = L == O;
-  S.w[C] = own ? what : S.w[C];
-  S.qv[C] = own ? (uint32_t)q : S.qv[C];
-  S.ev[C] = own ? e : S.ev[C];
+  for (int c = C0; c < CPL; ++c) S.w[c] = fmaf(-e, u[c], S.w[c]);
+  S.qv[C] = sel_owner<O>(q, S.qv[C]);
+  S.ev[C] = sel_owner<O>(e, S.ev[C]);
 }
 
 template <int CPL, int... Js>
-__device__ inline void sweep_all(SweepState<CPL>& S, const SweepArgs& a, const float (*sU)[16 * CPL],
-                                 const float* sInv, int L, int64_t row, bool row_ok, float maxq,
-                                 std::integer_sequence<int, Js...>) {
+__device__ __forceinline__ void sweep_all(SweepState<CPL>& S, const SweepArgs& a, const float* sU,
+                                          const float* sInv, int L, int64_t row, bool row_ok, float maxq,
+                                          std::integer_sequence<int, Js...>) {
   (sweep_step<CPL, Js>(S, a, sU, sInv, L, row, row_ok, maxq), ...);
 }
 
+// One wave per SIMD is all a d_out = 4096 layer provides (16 lanes per row),
+// so the scheduler is told to favour latency over occupancy.
 template <int CPL>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 k_sweep(SweepArgs a) {
   constexpr int B = 16 * CPL;
-  __shared__ float sU[B][B];
-  __shared__ float sInv[B];
-  if (a.st->flags != 0) return;
+  // one array, 1 / U_jj first: the per-step diagonal read then takes a
+  // constant offset from a single base register
+  __shared__ float smem[B + B * B];
+  float* sInv = smem;
+  float* sU = smem + B;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -192,68 +247,87 @@ k_sweep(SweepArgs a) {
   // issue every prologue load (U tile, its diagonal, this row's weights)
   // before the first store so the latencies overlap
   float ut[NV][4];
+  if (vec && nc == B) {   // whole tile, aligned: no per-lane predicates
 #pragma unroll
-  for (int v = 0; v < NV; ++v) {
-    const int e4 = tid + 256 * v;
-    const int r = e4 / (B / 4), c0 = 4 * (e4 % (B / 4));
+    for (int v = 0; v < NV; ++v) {
+      const int e4 = tid + 256 * v;
+      const int r = e4 / (B / 4), c0 = 4 * (e4 % (B / 4));
+      const float4 t = *reinterpret_cast<const float4*>(Ublk + (int64_t)r * a.ldu + c0);
+      ut[v][0] = t.x; ut[v][1] = t.y; ut[v][2] = t.z; ut[v][3] = t.w;
+    }
+  } else {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) ut[v][q] = 0.f;
-    if (r < nc) {
-      const float* src = Ublk + (int64_t)r * a.ldu + c0;
-      if (vec && c0 + 3 < nc) {
-        const float4 t = *reinterpret_cast<const float4*>(src);
-        ut[v][0] = t.x; ut[v][1] = t.y; ut[v][2] = t.z; ut[v][3] = t.w;
-      } else {
+    for (int v = 0; v < NV; ++v) {
+      const int e4 = tid + 256 * v;
+      const int r = e4 / (B / 4), c0 = 4 * (e4 % (B / 4));
+      const float* src = Ublk + (int64_t)min(r, nc - 1) * a.ldu;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) ut[v][q] = (c0 + q < nc) ? src[q] : 0.f;
-      }
+      for (int q = 0; q < 4; ++q) ut[v][q] = (r < nc && c0 + q < nc) ? src[min(c0 + q, nc - 1)] : 0.f;
     }
   }
   const float diag = (tid < B && tid < nc) ? Ublk[(int64_t)tid * a.ldu + tid] : 1.f;
+  const float loss0 = (row_ok && L == 0) ? a.row_loss[row] : 0.f;
+  // checked after the loads above are issued (they only read valid buffers):
+  // nothing is stored when an earlier step failed
+  if (a.st->flags != 0) return;
   SweepState<CPL> S;
-  S.loss = 0.f;
   S.nc = nc;
   S.gmask = (a.group < B) ? a.group - 1 : -1;   // groups nest: a power of two below B
 #pragma unroll
   for (int c = 0; c < CPL; ++c) {
-    const int col = L * CPL + c;
+    const int col = 16 * c + L;
     S.w[c] = (row_ok && col < nc) ? a.Wf[row * a.ldw + a.i0 + col] : 0.f;
     S.ev[c] = 0.f;
-    S.qv[c] = 0;
+    S.qv[c] = 0.f;
   }
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     const int e4 = tid + 256 * v;
     const int r = e4 / (B / 4), c0 = 4 * (e4 % (B / 4));
 #pragma unroll
-    for (int q = 0; q < 4; ++q) sU[r][c0 + q] = (c0 + q > r) ? ut[v][q] : 0.f;
+    for (int q = 0; q < 4; ++q) {
+      const int col = c0 + q;
+      sU[upos<CPL>(r, col / 16, col % 16)] = (col > r) ? ut[v][q] : 0.f;
+    }
   }
   if (tid < B) sInv[tid] = tid < nc ? 1.f / diag : 0.f;
   __syncthreads();
 
   if ((a.i0 % a.group) == 0) {
-    start_group<CPL>(S, a, L, row, row_ok, 0, maxq);
+    start_group<CPL, 0>(S, a, L, row, row_ok, maxq);
   } else {
     const int64_t gi = a.gbase;
     S.s = row_ok ? a.scales[row * a.ngroups + gi] : 1.f;
     S.z = row_ok ? (float)a.zeros[row * a.ngroups + gi] : 0.f;
     S.inv_s = 1.f / S.s;
+    S.nz = -S.z;
+    S.mz = maxq - S.z;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      S.gs[c] = S.s;
+      S.gz[c] = S.z;
+    }
   }
 
-  load_urow<CPL, 0>(S, sU, sInv, L, 0);
+  load_urow<CPL, 0, 0>(S, sU, sInv, L, 0);
+  load_urow<CPL, 1, 0>(S, sU, sInv, L, 1);
   sweep_all<CPL>(S, a, sU, sInv, L, row, row_ok, maxq, std::make_integer_sequence<int, B>{});
 
+  float loss = 0.f;
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) loss = fmaf(S.ev[c], S.ev[c], loss);
+  loss = row_sum16(loss);
   if (row_ok) {
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
-      const int col = L * CPL + c;
+      const int col = 16 * c + L;
       if (col < nc) {
-        a.Wf[row * a.ldw + a.i0 + col] = S.w[c];
+        a.Wf[row * a.ldw + a.i0 + col] = S.gs[c] * (S.qv[c] - S.gz[c]);
         a.codes[row * a.n_quant + a.i0 + col] = (uint8_t)S.qv[c];
       }
       a.E[row * a.lde + col] = S.ev[c];
     }
-    if (L == 0) a.row_loss[row] += S.loss;
+    if (L == 0) a.row_loss[row] = loss0 + loss;
   }
 }
 
