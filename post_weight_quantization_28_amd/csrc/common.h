@@ -54,6 +54,9 @@ hipError_t launch_status_init(hipStream_t s, DevStatus* st);
 constexpr int kLeaf = 64;
 hipError_t launch_leaf(hipStream_t s, float* A, float* X, int64_t n, int64_t off, int64_t m,
                        const int32_t* perm, DevStatus* st);
+// L21 = A21 D^T in place for a 64-column panel (r rows, row pitch ld).
+hipError_t launch_panel_solve(hipStream_t s, float* A21, const float* D, int64_t ld, int64_t r,
+                              const DevStatus* st);
 // The next diagonal block's update and leaf, run beside a trailing update.
 struct LeafTask {
   const float* L21;      // rows k1.., columns of panel k (row pitch n)

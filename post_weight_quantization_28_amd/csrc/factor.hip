@@ -8,7 +8,9 @@
 //
 // Phase 1, right-looking Cholesky in 64-column panels p = [k0, k1):
 //   leaf:    L11 = chol(A11), D = L11^{-1} -> X[p, p]   (one workgroup)
-//   panel:   A[k1:, p] = A[k1:, p] D^T                 (= L21, in place)
+//   panel:   A[k1:, p] = A[k1:, p] D^T                 (= L21, in place;
+//            full 64-column panels only: a panel narrower than 64 is the
+//            last one and has no rows below it)
 //   update:  A[k1:, k1:] -= L21 L21^T                   (lower part)
 // The next panel's leaf runs inside the update launch (see slab.hip).
 // Phase 2, X = L^{-1} by recursive doubling over the diagonal blocks: with
@@ -39,6 +41,62 @@ k_leaf(const float* __restrict__ A, float* __restrict__ X, int64_t n, int64_t k0
 hipError_t launch_leaf(hipStream_t s, float* A, float* X, int64_t n, int64_t off, int64_t m,
                        const int32_t* perm, DevStatus* st) {
   hipLaunchKernelGGL(k_leaf, dim3(1), dim3(256), 0, s, A, X, n, off, (int)m, perm, st);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- panel solve
+// L21 = A21 D^T in place (A21: the r x 64 panel rows below the diagonal
+// block, D = L11^{-1} lower, both row pitch ld). A workgroup owns 16 rows;
+// wave w computes columns 16w..16w+15 with v_mfma_f32_16x16x4f32 and its
+// operands are read straight from memory: for MFMA t of a group of four,
+// lane group g = lane / 16 feeds k = 16p + 4g + t to both operands, so each
+// lane reads 16-byte pieces of one row of A21 and one row of D. Every read
+// of the workgroup's rows completes before any write (the MFMAs consume
+// them before the barrier), so the result can overwrite its input.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float4 row4(const float* p, bool ok, bool vec) {
+  if (!ok) return make_float4(0.f, 0.f, 0.f, 0.f);
+  if (vec) return *reinterpret_cast<const float4*>(p);
+  return make_float4(p[0], p[1], p[2], p[3]);
+}
+
+__global__ void __launch_bounds__(256)
+k_panel_solve(float* A21, const float* __restrict__ D, int64_t ld, int64_t r, const DevStatus* st) {
+  if (st->flags != 0) return;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int li = lane & 15, g = lane >> 4;
+  const int64_t r0 = (int64_t)blockIdx.x * 16;
+  const bool vec = ((ld & 3) == 0) && (((uintptr_t)A21 & 15) == 0) && (((uintptr_t)D & 15) == 0);
+  const bool rok = r0 + li < r;
+  const float* pa = A21 + (rok ? r0 + li : 0) * ld + 4 * g;
+  const float* pb = D + (int64_t)(16 * w + li) * ld + 4 * g;
+  float4 a[4], b[4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    a[p] = row4(pa + 16 * p, rok, vec);
+    b[p] = row4(pb + 16 * p, true, vec);
+  }
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[p].x, b[p].x, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[p].y, b[p].y, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[p].z, b[p].z, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[p].w, b[p].w, acc, 0, 0, 0);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int64_t row = r0 + 4 * g + v;
+    if (row < r) A21[row * ld + 16 * w + li] = acc[v];
+  }
+}
+
+hipError_t launch_panel_solve(hipStream_t s, float* A21, const float* D, int64_t ld, int64_t r,
+                              const DevStatus* st) {
+  if (r <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_panel_solve, dim3((unsigned)ceil_div(r, 16)), dim3(256), 0, s, A21, D, ld, r, st);
   return hipGetLastError();
 }
 

@@ -185,9 +185,8 @@ hipError_t factor_panels(hipStream_t s, float* A, float* X, int64_t n, const int
     if (r == 0) break;
     const float* D = X + k0 * n + k0;    // L11^{-1}, lower
     float* L21 = A + k1 * n + k0;
-    // L21 = A21 D^T in place (overwrites its own A operand: one workgroup per slab)
-    SlabArgs g2{r, m, m, L21, n, D, n, 1, L21, n, 1.f, 0.f, 0, 0, st};
-    if ((e = launch_slab(s, g2, 1)) != hipSuccess) return e;
+    // L21 = A21 D^T in place (m == 64 whenever rows remain below the panel)
+    if ((e = launch_panel_solve(s, L21, D, n, r, st)) != hipSuccess) return e;
     // One launch: the next diagonal block (m2 rows) is updated and factored
     // by its own workgroup while the rest runs
     //   A[k1+m2:, k1:] -= L21[m2:] L21^T   (lower, i.e. j <= i + m2)
