@@ -93,9 +93,10 @@ hipError_t launch_gemm_pair(hipStream_t s, const GemmArgs& a, const GemmArgs* b)
 hipError_t launch_rotate(hipStream_t s, const float* X, float* U, int64_t n);
 
 // ---- slab.hip
-// C[M x N] = alpha A[M x K] B + beta C for K <= 128 (B: K x N, or N x K when
-// tb). Columns are split over at most max_split workgroups per 128-row slab;
-// pass max_split = 1 when C aliases A.
+// C[M x N] = alpha A[M x K] B + beta C for 1 <= K <= 128 (B: K x N, or N x K
+// when tb). With lower_only, only columns j <= i + lower_off are needed
+// (whole 16-column pieces above that band are skipped). C must not alias A
+// or B.
 struct SlabArgs {
   int64_t M, N, K;
   const float* A; int64_t lda;
@@ -103,16 +104,12 @@ struct SlabArgs {
   float* C; int64_t ldc;
   float alpha, beta;
   int lower_only;
-  int nsplit;            // set by the launcher
+  int64_t lower_off;
   const DevStatus* st;
-  int bvec;              // set by the launcher: B rows 16-byte aligned
-  int64_t lower_off;     // with lower_only: keep columns j <= i + lower_off
 };
-hipError_t launch_slab(hipStream_t s, SlabArgs g, int max_split);
-hipError_t launch_slab_pair(hipStream_t s, SlabArgs a, int split_a, const SlabArgs* b, int split_b);
-// launch_slab_pair plus one more workgroup (dispatched first) running `lt`.
-hipError_t launch_slab_pair_leaf(hipStream_t s, SlabArgs a, int split_a, const SlabArgs* b,
-                                 int split_b, const LeafTask& lt);
+hipError_t launch_slab(hipStream_t s, const SlabArgs& g);
+// launch_slab (K <= 64) plus one more workgroup (dispatched first) running `lt`.
+hipError_t launch_slab_leaf(hipStream_t s, const SlabArgs& g, const LeafTask& lt);
 
 // ---- trail.hip
 // C[M x N] -= (Ahi + Alo)(Bhi + Blo) without the lo*lo term: split-bf16

@@ -176,7 +176,6 @@ gptq_status check_ws(void* ws, size_t have, size_t need) {
 hipError_t factor_panels(hipStream_t s, float* A, float* X, int64_t n, const int32_t* perm,
                          DevStatus* st) {
   hipError_t e;
-  constexpr int kAny = 1 << 30;
   // ---- phase 1: Cholesky, leaves write D = L11^{-1} into X's diagonal
   if ((e = launch_leaf(s, A, X, n, 0, std::min<int64_t>(kLeaf, n), perm, st)) != hipSuccess) return e;
   for (int64_t k0 = 0; k0 < n; k0 += kLeaf) {
@@ -191,10 +190,15 @@ hipError_t factor_panels(hipStream_t s, float* A, float* X, int64_t n, const int
     // by its own workgroup while the rest runs
     //   A[k1+m2:, k1:] -= L21[m2:] L21^T   (lower, i.e. j <= i + m2)
     const int64_t m2 = std::min<int64_t>(kLeaf, r);
-    SlabArgs g3{r - m2, r, m, L21 + m2 * n, n, L21, n, 1, A + (k1 + m2) * n + k1, n, -1.f, 1.f, 1, 0, st};
-    g3.lower_off = m2;
+    SlabArgs g3{};
+    g3.M = r - m2; g3.N = r; g3.K = m;
+    g3.A = L21 + m2 * n; g3.lda = n;
+    g3.B = L21; g3.ldb = n; g3.tb = 1;
+    g3.C = A + (k1 + m2) * n + k1; g3.ldc = n;
+    g3.alpha = -1.f; g3.beta = 1.f;
+    g3.lower_only = 1; g3.lower_off = m2; g3.st = st;
     LeafTask lt{L21, A, X, n, k1, (int)m2, (int)m, perm, st};
-    if ((e = launch_slab_pair_leaf(s, g3, kAny, nullptr, 0, lt)) != hipSuccess) return e;
+    if ((e = launch_slab_leaf(s, g3, lt)) != hipSuccess) return e;
   }
   // ---- phase 2: off-diagonal blocks of X = L^{-1}
   for (int64_t h = kLeaf; h < n; h *= 2) {
@@ -457,8 +461,13 @@ gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int
       const int64_t i1 = i0 + nc;
       const int64_t near_end = two ? s1 : n;
       if (i1 < near_end) {
-        SlabArgs g{d_out, near_end - i1, nc, Eb, sw, U + i0 * n + i1, n, 0, Wf + i1, n, -1.f, 1.f, 0, 0, dst};
-        HIP_TRY(launch_slab(s, g, 1 << 30), "near-field update");
+        SlabArgs g{};
+        g.M = d_out; g.N = near_end - i1; g.K = nc;
+        g.A = Eb; g.lda = sw;
+        g.B = U + i0 * n + i1; g.ldb = n; g.tb = 0;
+        g.C = Wf + i1; g.ldc = n;
+        g.alpha = -1.f; g.beta = 1.f; g.st = dst;
+        HIP_TRY(launch_slab(s, g), "near-field update");
       }
     }
     if (two && s1 < n) {

@@ -164,12 +164,15 @@ __device__ __forceinline__ void leaf_run(const float* src, int64_t lds, float* _
 // accumulator layout.
 typedef float leaf_f32x16 __attribute__((ext_vector_type(16)));
 
+// The three phases reuse one region: lrow is last read by the MFMAs
+// (barrier before blk2 is written), blk2 is last read by the leaf's
+// register load (barrier before the leaf's first LDS write).
 struct LeafTaskSmem {
   union {
     float lrow[64][68];   // L21[i][k], zero outside m2 x mk
+    float blk2[64][65];   // the updated block, input of the leaf
     LeafSmem leaf;
   } u;
-  float blk2[64][65];     // the updated block, input of the leaf
 };
 
 __device__ inline void leaf_task_run(const LeafTask& t, LeafTaskSmem& sm) {
@@ -197,10 +200,10 @@ __device__ inline void leaf_task_run(const LeafTask& t, LeafTaskSmem& sm) {
     sm.u.lrow[i][lane] = (i < m2 && lane < mk) ? lv[v] : 0.f;
   }
   __syncthreads();
-  if (wave < 3) {
-    leaf_f32x16 acc;
+  leaf_f32x16 acc;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+  if (wave < 3) {
 #pragma unroll
     for (int p = 0; p < 8; ++p) {
       const float4 fa = *reinterpret_cast<const float4*>(&sm.u.lrow[32 * ta + lr][8 * p + 4 * lh]);
@@ -210,14 +213,17 @@ __device__ inline void leaf_task_run(const LeafTask& t, LeafTaskSmem& sm) {
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa.z, fb.z, acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_32x32x2f32(fa.w, fb.w, acc, 0, 0, 0);
     }
+  }
+  __syncthreads();   // every read of lrow is done
+  if (wave < 3) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int row = 32 * ta + 8 * (r >> 2) + 4 * lh + (r & 3), col = 32 * tb + lr;
-      sm.blk2[row][col] = (col <= row) ? av[r] - acc[r] : 0.f;
+      sm.u.blk2[row][col] = (col <= row) ? av[r] - acc[r] : 0.f;
     }
   }
   __syncthreads();
-  leaf_run(&sm.blk2[0][0], 65, t.X, n, t.k1, m2, t.perm, t.st, sm.u.leaf);
+  leaf_run(&sm.u.blk2[0][0], 65, t.X, n, t.k1, m2, t.perm, t.st, sm.u.leaf);
 }
 
 }  // namespace gq
