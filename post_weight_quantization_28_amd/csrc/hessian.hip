@@ -253,7 +253,6 @@ k_hessian_bf16(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx
 constexpr int kDK = 32;                  // tokens per stage
 constexpr int kDOpBytes = kDK * 512;     // one operand of one stage
 constexpr int kDSlotBytes = 2 * kDOpBytes;
-constexpr int kDSlots = 4;
 
 typedef int v4i32_t __attribute__((ext_vector_type(4)));
 
@@ -262,10 +261,35 @@ __device__ __forceinline__ void dma16_buf(uint32_t voff, v4i32_t rsrc, uint32_t 
                :: "v"(voff), "s"(rsrc), "s"(lds_base), "s"(soff) : "memory");
 }
 
-__global__ void __launch_bounds__(256)
+// WAVES = 4: one wave per SIMD, each a 128 x 128 block (2 x 2); WAVES = 8:
+// two per SIMD, each 128 x 64 (2 x 4). SLOTS stages of kDK tokens are in
+// the LDS ring (32 KiB each).
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// Wait until at most `stages` stages of this wave's DMA (PER instructions
+// each) are outstanding, then barrier (one asm block: no LDS read can be
+// scheduled in between).
+template <int PER, int MAXS>
+__device__ __forceinline__ void wait_stages_barrier(int stages) {
+  if (stages <= 0) wait_vm_barrier<0>();
+  else if (stages == 1 || MAXS < 2) wait_vm_barrier<PER>();
+  else if (stages == 2 || MAXS < 3) wait_vm_barrier<2 * PER>();
+  else wait_vm_barrier<3 * PER>();
+}
+
+template <int WAVES, int SLOTS>
+__global__ void __launch_bounds__(64 * WAVES)
 k_hessian_dma(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx,
               float* __restrict__ part, int64_t chunk, int splits) {
-  __shared__ __align__(16) uint8_t dsm[kDSlots * kDSlotBytes];
+  static_assert(WAVES == 4 || WAVES == 8, "4 or 8 waves");
+  static_assert(SLOTS >= 2 && SLOTS <= 5, "2..5 slots");
+  constexpr int PER = 32 / WAVES;         // DMA instructions per wave per stage
+  constexpr int WN = WAVES / 2;           // waves across the columns
+  constexpr int NB = 4 / (WN / 2);        // 32-column blocks per wave: 4 or 2
+  __shared__ __align__(16) uint8_t dsm[SLOTS * kDSlotBytes];
   const int nt = (int)ceil_div(n, kHT);
   int tile, split, bi, bj;
   if (!hessian_item(blockIdx.x, nt * (nt + 1) / 2, splits, tile, split)) return;
@@ -278,7 +302,7 @@ k_hessian_dma(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx,
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WN, wn = wave % WN;
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dsm));
 
   // buffer over this chunk's tokens: [kbeg, kend) x ldx bf16
@@ -295,13 +319,13 @@ k_hessian_dma(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx,
     rsrc.z = __builtin_amdgcn_readfirstlane(rsrc.z);
   }
   // DMA plan: a stage is 2 operands x 16 row pairs = 32 wave-instructions;
-  // wave w issues q = 0..7 -> instruction 8w+q: operand (8w+q)/16, rows
-  // 2p, 2p+1 with p = (8w+q)%16; lane l fills row 2p + l/32, slot chunk l%32.
-  // A chunk past the last channel gets an offset beyond the buffer.
-  uint32_t voff[8];
+  // wave w issues q = 0..PER-1 -> instruction PER w + q: operand idx / 16,
+  // rows 2p, 2p+1 with p = idx % 16; lane l fills row 2p + l/32, slot chunk
+  // l%32. A chunk past the last channel gets an offset beyond the buffer.
+  uint32_t voff[PER];
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int idx = 8 * wave + q;
+  for (int q = 0; q < PER; ++q) {
+    const int idx = PER * wave + q;
     const int op = idx >> 4, p = idx & 15;
     const int t = 2 * p + (lane >> 5);
     const int c = (lane & 31) ^ dma_swz(t);
@@ -312,8 +336,8 @@ k_hessian_dma(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx,
   auto issue = [&](int st, int slot) {
     const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)st * stage_bytes);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int idx = 8 * wave + q;
+    for (int q = 0; q < PER; ++q) {
+      const int idx = PER * wave + q;
       const int op = idx >> 4, p = idx & 15;
       dma16_buf(voff[q], rsrc, soff,
                 __builtin_amdgcn_readfirstlane(lds0 + slot * kDSlotBytes + op * kDOpBytes + p * 1024));
@@ -322,63 +346,64 @@ k_hessian_dma(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx,
 
   // Transpose-read addresses (per lane, relative to a slot): group G =
   // lane/16, s = lane%16, token row t = 16 ks + 4 h + 8 (G/2) + s/4 and
-  // chunk (16 w + 4 b + 2 (G%2) + (s/2)%2) ^ dma_swz(t), b = mb or nb.
+  // chunk (c0 + 4 b + 2 (G%2) + (s/2)%2) ^ dma_swz(t), with c0 = 16 wm for
+  // the A blocks b = 0..3 and c0 = 4 NB wn for the B blocks b < NB.
   const int G = lane >> 4, sl = lane & 15;
   const int trow_off = 8 * (G >> 1) + (sl >> 2);
   const int cbase = 2 * (G & 1) + ((sl >> 1) & 1);
   const int swz = dma_swz(trow_off);           // t % 4 == trow_off % 4
   const int half8 = (sl & 1) * 8;
-  // per-lane read offsets of the 4 A and 4 B fragments at ks = 0, h = 0;
-  // a stage adds its slot base once per fragment, and (ks, h) move by
+  // per-lane read offsets of the A and B fragments at ks = 0, h = 0; a
+  // stage adds its slot base once per fragment, and (ks, h) move by
   // constants that fit the instructions' 16-bit offset field
-  uint32_t off[8];
+  uint32_t off[4 + NB];
 #pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    off[b] = trow_off * 512 + (((16 * wm + 4 * b + cbase) ^ swz) * 16) + half8;
-    off[4 + b] = kDOpBytes + trow_off * 512 + (((16 * wn + 4 * b + cbase) ^ swz) * 16) + half8;
-  }
+  for (int b = 0; b < 4; ++b) off[b] = trow_off * 512 + (((16 * wm + 4 * b + cbase) ^ swz) * 16) + half8;
+#pragma unroll
+  for (int b = 0; b < NB; ++b)
+    off[4 + b] = kDOpBytes + trow_off * 512 + (((4 * NB * wn + 4 * b + cbase) ^ swz) * 16) + half8;
 
-  f32x16_t acc[4][4];
+  f32x16_t acc[4][NB];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
 
   const int nstage = kend > kbeg ? (int)ceil_div(kend - kbeg, kDK) : 0;
 #pragma unroll
-  for (int ps = 0; ps < kDSlots - 1; ++ps)
+  for (int ps = 0; ps < SLOTS - 1; ++ps)
     if (ps < nstage) issue(ps, ps);
   for (int st = 0; st < nstage; ++st) {
-    wait_dma_barrier(min(kDSlots - 2, nstage - 1 - st));
-    if (st + kDSlots - 1 < nstage) issue(st + kDSlots - 1, (st + kDSlots - 1) % kDSlots);
-    const uint32_t sbase = lds0 + (uint32_t)(st % kDSlots) * kDSlotBytes;
-    uint32_t bs[8];
+    wait_stages_barrier<PER, SLOTS - 2>(min(SLOTS - 2, nstage - 1 - st));
+    if (st + SLOTS - 1 < nstage) issue(st + SLOTS - 1, (st + SLOTS - 1) % SLOTS);
+    const uint32_t sbase = lds0 + (uint32_t)(st % SLOTS) * kDSlotBytes;
+    uint32_t bs[4 + NB];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) bs[b] = off[b] + sbase;
+    for (int b = 0; b < 4 + NB; ++b) bs[b] = off[b] + sbase;
 #pragma unroll
     for (int ks = 0; ks < kDK / 16; ++ks) {
-      v4i16_t ra[2][4], rb[2][4];
+      v4i16_t ra[2][4], rb[2][NB];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const uint32_t row = (16 * ks + 4 * h) * 512;
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          ra[h][b] = lds_tr16(bs[b] + row);
-          rb[h][b] = lds_tr16(bs[4 + b] + row);
-        }
-      }
-      bf16x8_t af[4], bfr[4];
+        for (int b = 0; b < 4; ++b) ra[h][b] = lds_tr16(bs[b] + row);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        af[b] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(ra[0][b], ra[1][b], 0, 1, 2, 3, 4, 5, 6, 7));
-        bfr[b] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(rb[0][b], rb[1][b], 0, 1, 2, 3, 4, 5, 6, 7));
+        for (int b = 0; b < NB; ++b) rb[h][b] = lds_tr16(bs[4 + b] + row);
       }
+      bf16x8_t af[4], bfr[NB];
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+        af[b] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(ra[0][b], ra[1][b], 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+      for (int b = 0; b < NB; ++b)
+        bfr[b] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(rb[0][b], rb[1][b], 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
       for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int nb = 0; nb < NB; ++nb)
           acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
     }
   }
@@ -386,14 +411,17 @@ k_hessian_dma(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx,
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t i = iA + 128 * wm + 32 * mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int64_t j = iB + 128 * wn + 32 * nb + (lane & 31);
+        const int64_t j = iB + 32 * NB * wn + 32 * nb + (lane & 31);
         if (i < n && j < n) P[i * n + j] = acc[mb][nb][r];
       }
 }
+
+constexpr int kDWaves = 8;
+constexpr int kDSlotsUsed = 4;
 
 hipError_t launch_hessian_partials_bf16(hipStream_t s, const uint16_t* X, int64_t T, int64_t n,
                                         int64_t ldx, float* part, int splits) {
@@ -403,8 +431,8 @@ hipError_t launch_hessian_partials_bf16(hipStream_t s, const uint16_t* X, int64_
   const bool aligned = (n % 8 == 0) && (ldx % 8 == 0) && ((uintptr_t)X % 16 == 0);
   // 32-bit buffer offsets: a token chunk must span less than 2^31 bytes
   if (aligned && chunk * ldx * 2 < ((int64_t)1 << 31))
-    hipLaunchKernelGGL(k_hessian_dma, dim3(8 * ((items + 7) / 8)), dim3(256), 0, s, X, T, n, ldx, part,
-                       chunk, splits);
+    hipLaunchKernelGGL((k_hessian_dma<kDWaves, kDSlotsUsed>), dim3(8 * ((items + 7) / 8)), dim3(64 * kDWaves), 0,
+                       s, X, T, n, ldx, part, chunk, splits);
   else
     hipLaunchKernelGGL(k_hessian_bf16<false>, dim3(items), dim3(256), 0, s, X, T, n, ldx, part, chunk);
   return hipGetLastError();

@@ -195,19 +195,52 @@ k_trail_x3(TrailArgs g) {
   }
 
   // C -= acc: lane holds D[i][j], j = lane % 32, i = 8 (r / 4) + 4 (lane / 32) + r % 4.
-  // Every C value is loaded before the first store: a store followed by a
-  // load the compiler cannot prove disjoint would serialise the 128
-  // read-modify-writes on memory latency.
+  // Every C value is loaded, unconditionally (indices clamped into the
+  // matrix), before the first store: predicated loads would each end in a
+  // wait, and a store followed by a load the compiler cannot prove disjoint
+  // would serialise the read-modify-writes on memory latency.
+  const int64_t ib = m0 + 128 * wm + 4 * (lane >> 5);
+  const int64_t jb = n0 + 64 * wn + (lane & 31);
   float cv[4][2][16];
+  if (m0 + kTM <= g.M && n0 + kTN <= g.N && g.ldc < ((int64_t)1 << 22)) {
+    // whole tile: a buffer over this wave's 128 rows, a fixed 32-bit lane
+    // offset and a scalar offset per row, so no access needs vector
+    // address arithmetic
+    const uint64_t cwa = (uint64_t)(uintptr_t)(g.C + (m0 + 128 * wm) * g.ldc + n0 + 64 * wn);
+    float* cw = reinterpret_cast<float*>(
+        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(cwa >> 32)) << 32) |
+        (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)cwa));   // uniform
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        cw, 0, __builtin_amdgcn_readfirstlane((int)(128 * g.ldc * 4)), 0x00020000);
+    const int ldc4 = __builtin_amdgcn_readfirstlane((int)(g.ldc * 4));
+    const int lob = (4 * (lane >> 5)) * ldc4 + (lane & 31) * 4;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          cv[mb][nb][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+              rc, lob, (32 * mb + 8 * (r >> 2) + (r & 3)) * ldc4 + 128 * nb, 0));
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(cv[mb][nb][r] - acc[mb][nb][r]), rc, lob,
+                                                (32 * mb + 8 * (r >> 2) + (r & 3)) * ldc4 + 128 * nb, 0);
+    return;
+  }
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t i = m0 + 128 * wm + 32 * mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int64_t j = n0 + 64 * wn + 32 * nb + (lane & 31);
-        cv[mb][nb][r] = (i < g.M && j < g.N) ? g.C[i * g.ldc + j] : 0.f;
+        const int64_t i = min(ib + 32 * mb + 8 * (r >> 2) + (r & 3), g.M - 1);
+        const int64_t j = min(jb + 32 * nb, g.N - 1);
+        cv[mb][nb][r] = g.C[i * g.ldc + j];
       }
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
@@ -215,8 +248,8 @@ k_trail_x3(TrailArgs g) {
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int64_t i = m0 + 128 * wm + 32 * mb + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        const int64_t j = n0 + 64 * wn + 32 * nb + (lane & 31);
+        const int64_t i = ib + 32 * mb + 8 * (r >> 2) + (r & 3);
+        const int64_t j = jb + 32 * nb;
         if (i < g.M && j < g.N) g.C[i * g.ldc + j] = cv[mb][nb][r] - acc[mb][nb][r];
       }
 }
