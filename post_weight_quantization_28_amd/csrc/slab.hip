@@ -7,20 +7,22 @@
 // of the block's errors at once (W[:, rest] -= E U[block, rest]).
 //
 // Layout (MI355X): with K this short, every output element is read and
-// written once for only 2K flops, so the kernel is built to stream C with
-// as little per-element work as possible and enough waves to fill the chip:
-//  * a workgroup covers 32 rows x 64 columns; wave w owns columns
-//    16w..16w+15 as two 16 x 16 v_mfma_f32_16x16x4f32 tiles, independently
-//    of the other waves (no LDS, no barrier);
-//  * operands are read straight from memory: for MFMA t of a group of four,
-//    lane group g = lane / 16 feeds k = 16p + 4g + t to both operands, so A
-//    (and B when stored N x K) arrive as one 16-byte read per lane per 16 k;
-//    B stored K x N arrives as four 4-byte reads of consecutive k rows;
-//  * every load of a wave (A, B and the C tile) is issued before the first
-//    MFMA; rows and columns past the edge are clamped to valid addresses
-//    and never stored.
+// written once for only 2K flops, so the kernel streams C with little
+// per-element work and keeps operand traffic low:
+//  * a workgroup covers 64 x 64 outputs; its A rows and B columns (K <= KT
+//    deep) are loaded once, with 16-byte coalesced reads, into LDS as
+//    [row][k] / [column][k] (pitch KT + 4 floats) and shared by the four
+//    waves, so each output costs 8K/64 bytes of operand reads instead of
+//    the 24K/64 of per-wave loading;
+//  * wave (wm, wn) owns the 32 x 32 block at (32 wm, 32 wn) as 2 x 2
+//    v_mfma_f32_16x16x4f32 tiles; for MFMA t of a group of four, lane group
+//    g = lane / 16 feeds k = 16p + 4g + t to both operands, so each operand
+//    fragment is one 16-byte LDS read;
+//  * the C block is requested before the operands are staged, so its
+//    latency overlaps the staging; rows and columns past the edge are
+//    clamped to valid addresses and never stored.
 // The factorisation's update needs only the lower band (j <= i + lower_off);
-// waves whose columns lie wholly above it exit at once.
+// workgroups wholly above it exit at once, waves above it after staging.
 #include "common.h"
 #include "leaf.h"
 
@@ -30,110 +32,162 @@ namespace gq {
 
 typedef float kp_f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kPM = 32;   // rows per workgroup
-constexpr int kPN = 64;   // columns per workgroup (16 per wave)
+constexpr int kPN = 64;   // columns per workgroup
 
-template <bool TB, int KT>
-__device__ __forceinline__ void kprod_wave(const SlabArgs& g, int64_t r0, int64_t c0, int lane) {
-  constexpr int P = KT / 16;
+// RM rows per workgroup: 64 (waves 2 x 2, each 32 x 32) or 32 (waves 1 x 4,
+// each 32 x 16, for products too narrow to fill the chip with 64-row tiles)
+template <int KT, int RM>
+struct KprodSmem {
+  float a[RM][KT + 4];    // A[r0 + m][k]
+  float b[kPN][KT + 4];   // B(k, c0 + n), stored [n][k]
+};
+
+template <int KT, int RM>
+__device__ __forceinline__ void kprod_tile(const SlabArgs& g, int64_t b, KprodSmem<KT, RM>& sm) {
+  constexpr int kPM = RM;
+  constexpr int WC = RM == 64 ? 2 : 4;       // waves across the columns
+  constexpr int CT = 2 / (WC / 2);           // 16-column tiles per wave: 2 or 1
+  constexpr int Q = KT / 4;                  // float4 per operand row
+  constexpr int VA = kPM * Q / 256;          // float4 per thread of A
+  constexpr int VB = kPN * Q / 256;          // float4 per thread of B
+  const int64_t ncb = ceil_div(g.N, kPN);
+  const int64_t r0 = (b / ncb) * kPM, c0 = (b % ncb) * kPN;
+  if (g.lower_only && c0 > r0 + kPM - 1 + g.lower_off) return;   // whole workgroup
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w / WC, wn = w % WC;
   const int li = lane & 15, gq = lane >> 4;
   const int64_t M = g.M, N = g.N;
   const int K = (int)g.K;
-  const float* pa0 = g.A + std::min<int64_t>(r0 + li, M - 1) * g.lda + 4 * gq;
-  const float* pa1 = g.A + std::min<int64_t>(r0 + 16 + li, M - 1) * g.lda + 4 * gq;
-  const int64_t col = std::min<int64_t>(c0 + li, N - 1);
-  float4 a0[P], a1[P], b[P];
-  const bool vec = K == KT && ((g.lda & 3) == 0) && (((uintptr_t)g.A & 15) == 0) &&
-                   (!TB || (((g.ldb & 3) == 0) && (((uintptr_t)g.B & 15) == 0)));
-  if (vec) {
+
+  // the wave's C block first (clamped, unconditional: no wait per load)
+  float cv[2][CT][4];
+  const bool beta = g.beta != 0.f;
+  if (beta) {
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-      a0[p] = *reinterpret_cast<const float4*>(pa0 + 16 * p);
-      a1[p] = *reinterpret_cast<const float4*>(pa1 + 16 * p);
-      if constexpr (TB) {
-        b[p] = *reinterpret_cast<const float4*>(g.B + col * g.ldb + 16 * p + 4 * gq);
-      } else {
-        const float* q = g.B + (int64_t)(16 * p + 4 * gq) * g.ldb + col;
-        b[p] = make_float4(q[0], q[g.ldb], q[2 * g.ldb], q[3 * g.ldb]);
-      }
-    }
-  } else {
-    // K below the template width (or unaligned rows): 4-byte reads, k >= K
-    // read as zero (the addresses stay inside row k = K - 1)
+    for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
-      float va0[4], va1[4], vb[4];
+      for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int k = 16 * p + 4 * gq + t;
-        const int kc = std::min(k, K - 1) - 4 * gq;   // offset from the lane's base
-        const bool ok = k < K;
-        va0[t] = ok ? pa0[kc] : 0.f;
-        va1[t] = ok ? pa1[kc] : 0.f;
-        const int kk = std::min(k, K - 1);
-        if constexpr (TB) vb[t] = ok ? g.B[col * g.ldb + kk] : 0.f;
-        else vb[t] = ok ? g.B[(int64_t)kk * g.ldb + col] : 0.f;
-      }
-      a0[p] = make_float4(va0[0], va0[1], va0[2], va0[3]);
-      a1[p] = make_float4(va1[0], va1[1], va1[2], va1[3]);
-      b[p] = make_float4(vb[0], vb[1], vb[2], vb[3]);
+        for (int v = 0; v < 4; ++v) {
+          const int64_t row = std::min<int64_t>(r0 + 32 * wm + 16 * rt + 4 * gq + v, M - 1);
+          const int64_t col = std::min<int64_t>(c0 + 16 * CT * wn + 16 * ct + li, N - 1);
+          cv[rt][ct][v] = g.C[row * g.ldc + col];
+        }
+  }
+
+  // stage A rows and B columns
+  const bool avec = K == KT && ((g.lda & 3) == 0) && (((uintptr_t)g.A & 15) == 0);
+  const bool bvec = K == KT && ((g.ldb & 3) == 0) && (((uintptr_t)g.B & 15) == 0);
+  float4 xa[VA], xb[VB];
+#pragma unroll
+  for (int v = 0; v < VA; ++v) {
+    const int idx = tid + 256 * v;
+    const int m = idx / Q, k4 = 4 * (idx % Q);
+    const float* pa = g.A + std::min<int64_t>(r0 + m, M - 1) * g.lda;
+    if (avec) {
+      xa[v] = *reinterpret_cast<const float4*>(pa + k4);
+    } else {
+      float t[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[e] = (k4 + e < K) ? pa[std::min(k4 + e, K - 1)] : 0.f;
+      xa[v] = make_float4(t[0], t[1], t[2], t[3]);
     }
   }
-  float cv[2][4];
-  if (g.beta != 0.f) {
+#pragma unroll
+  for (int v = 0; v < VB; ++v) {
+    const int idx = tid + 256 * v;
+    if (g.tb) {            // B stored N x K: rows of k
+      const int m = idx / Q, k4 = 4 * (idx % Q);
+      const float* pb = g.B + std::min<int64_t>(c0 + m, N - 1) * g.ldb;
+      if (bvec) {
+        xb[v] = *reinterpret_cast<const float4*>(pb + k4);
+      } else {
+        float t[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t[e] = (k4 + e < K) ? pb[std::min(k4 + e, K - 1)] : 0.f;
+        xb[v] = make_float4(t[0], t[1], t[2], t[3]);
+      }
+    } else {               // B stored K x N: row k, 4 consecutive columns
+      const int kr = idx / (kPN / 4), n4 = 4 * (idx % (kPN / 4));
+      const float* pb = g.B + (int64_t)std::min(kr, K - 1) * g.ldb;
+      if (bvec && c0 + kPN <= N) {
+        xb[v] = *reinterpret_cast<const float4*>(pb + c0 + n4);
+      } else {
+        float t[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t[e] = (kr < K) ? pb[std::min<int64_t>(c0 + n4 + e, N - 1)] : 0.f;
+        xb[v] = make_float4(t[0], t[1], t[2], t[3]);
+      }
+    }
+  }
+#pragma unroll
+  for (int v = 0; v < VA; ++v) {
+    const int idx = tid + 256 * v;
+    const int m = idx / Q, k4 = 4 * (idx % Q);
+    *reinterpret_cast<float4*>(&sm.a[m][k4]) = xa[v];
+  }
+#pragma unroll
+  for (int v = 0; v < VB; ++v) {
+    const int idx = tid + 256 * v;
+    if (g.tb) {
+      const int m = idx / Q, k4 = 4 * (idx % Q);
+      *reinterpret_cast<float4*>(&sm.b[m][k4]) = xb[v];
+    } else {
+      const int kr = idx / (kPN / 4), n4 = 4 * (idx % (kPN / 4));
+      sm.b[n4][kr] = xb[v].x;
+      sm.b[n4 + 1][kr] = xb[v].y;
+      sm.b[n4 + 2][kr] = xb[v].z;
+      sm.b[n4 + 3][kr] = xb[v].w;
+    }
+  }
+  __syncthreads();
+  if (g.lower_only && c0 + 16 * CT * wn > r0 + 32 * wm + 31 + g.lower_off) return;   // this wave's block
+
+  kp_f32x4_t acc[2][CT];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) acc[rt][ct] = (kp_f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < KT / 16; ++p) {
+    float4 fa[2], fb[CT];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      fa[t] = *reinterpret_cast<const float4*>(&sm.a[32 * wm + 16 * t + li][16 * p + 4 * gq]);
+#pragma unroll
+    for (int t = 0; t < CT; ++t)
+      fb[t] = *reinterpret_cast<const float4*>(&sm.b[16 * CT * wn + 16 * t + li][16 * p + 4 * gq]);
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[rt].x, fb[ct].x, acc[rt][ct], 0, 0, 0);
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[rt].y, fb[ct].y, acc[rt][ct], 0, 0, 0);
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[rt].z, fb[ct].z, acc[rt][ct], 0, 0, 0);
+        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[rt].w, fb[ct].w, acc[rt][ct], 0, 0, 0);
+      }
+  }
+  const float al = g.alpha, be = g.beta;
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int64_t col = c0 + 16 * CT * wn + 16 * ct + li;
+    if (col >= N) continue;
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int64_t row = std::min<int64_t>(r0 + 16 * rt + 4 * gq + v, M - 1);
-        cv[rt][v] = g.C[row * g.ldc + col];
+        const int64_t row = r0 + 32 * wm + 16 * rt + 4 * gq + v;
+        if (row < M) g.C[row * g.ldc + col] = fmaf(al, acc[rt][ct][v], beta ? be * cv[rt][ct][v] : 0.f);
       }
-  } else {
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) cv[rt][v] = 0.f;
-  }
-  kp_f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int p = 0; p < P; ++p) {
-    acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[p].x, b[p].x, acc0, 0, 0, 0);
-    acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[p].x, b[p].x, acc1, 0, 0, 0);
-    acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[p].y, b[p].y, acc0, 0, 0, 0);
-    acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[p].y, b[p].y, acc1, 0, 0, 0);
-    acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[p].z, b[p].z, acc0, 0, 0, 0);
-    acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[p].z, b[p].z, acc1, 0, 0, 0);
-    acc0 = __builtin_amdgcn_mfma_f32_16x16x4f32(a0[p].w, b[p].w, acc0, 0, 0, 0);
-    acc1 = __builtin_amdgcn_mfma_f32_16x16x4f32(a1[p].w, b[p].w, acc1, 0, 0, 0);
-  }
-  if (c0 + li >= N) return;
-  const float al = g.alpha, be = g.beta;
-#pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int64_t row = r0 + 4 * gq + v;
-    if (row < M) g.C[row * g.ldc + col] = fmaf(al, acc0[v], be * cv[0][v]);
-    if (row + 16 < M) g.C[(row + 16) * g.ldc + col] = fmaf(al, acc1[v], be * cv[1][v]);
   }
 }
 
-// Tile b of the product (row-major over 32 x 64 workgroup tiles).
-template <int KT>
-__device__ __forceinline__ void kprod_tile(const SlabArgs& g, int64_t b) {
-  const int64_t ncb = ceil_div(g.N, kPN);
-  const int64_t r0 = (b / ncb) * kPM;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t c0 = (b % ncb) * kPN + 16 * w;
-  if (c0 >= g.N) return;
-  if (g.lower_only && c0 > r0 + kPM - 1 + g.lower_off) return;
-  if (g.tb) kprod_wave<true, KT>(g, r0, c0, lane);
-  else kprod_wave<false, KT>(g, r0, c0, lane);
-}
-
-template <int KT>
+template <int KT, int RM>
 __global__ void __launch_bounds__(256)
 k_kprod(SlabArgs g) {
+  __shared__ __align__(16) KprodSmem<KT, RM> sm;
   if (g.st != nullptr && g.st->flags != 0) return;
-  kprod_tile<KT>(g, blockIdx.x);
+  kprod_tile<KT, RM>(g, blockIdx.x, sm);
 }
 
 // The factorisation's trailing update plus, in workgroup 0 (dispatched
@@ -141,35 +195,43 @@ k_kprod(SlabArgs g) {
 // the trailing update streams.
 __global__ void __launch_bounds__(256)
 k_kprod_leaf(SlabArgs g, LeafTask lt) {
-  __shared__ __align__(16) LeafTaskSmem sm;
+  __shared__ __align__(16) union {
+    LeafTaskSmem leaf;
+    KprodSmem<64, 64> prod;
+  } sm;
   if (lt.st != nullptr && lt.st->flags != 0) return;
   if (blockIdx.x == 0) {
-    leaf_task_run(lt, sm);
+    leaf_task_run(lt, sm.leaf);
     return;
   }
-  kprod_tile<64>(g, (int64_t)blockIdx.x - 1);
+  kprod_tile<64, 64>(g, (int64_t)blockIdx.x - 1, sm.prod);
 }
 
-static int64_t kprod_tiles(const SlabArgs& g) {
+static int64_t kprod_tiles(const SlabArgs& g, int rm) {
   if (g.M <= 0 || g.N <= 0) return 0;
-  return ceil_div(g.M, kPM) * ceil_div(g.N, kPN);
+  return ceil_div(g.M, rm) * ceil_div(g.N, kPN);
 }
 
 hipError_t launch_slab(hipStream_t s, const SlabArgs& g) {
   if (g.K < 1 || g.K > 128) return hipErrorInvalidValue;
-  const int64_t nt = kprod_tiles(g);
+  // 64-row tiles unless they leave the 256 CUs with under two workgroups each
+  const int rm = kprod_tiles(g, 64) >= 512 ? 64 : 32;
+  const int64_t nt = kprod_tiles(g, rm);
   if (nt == 0) return hipSuccess;
   if (nt >= (int64_t)1 << 31) return hipErrorInvalidValue;
-  if (g.K <= 64)
-    hipLaunchKernelGGL(k_kprod<64>, dim3((unsigned)nt), dim3(256), 0, s, g);
-  else
-    hipLaunchKernelGGL(k_kprod<128>, dim3((unsigned)nt), dim3(256), 0, s, g);
+  if (g.K <= 64) {
+    if (rm == 64) hipLaunchKernelGGL((k_kprod<64, 64>), dim3((unsigned)nt), dim3(256), 0, s, g);
+    else hipLaunchKernelGGL((k_kprod<64, 32>), dim3((unsigned)nt), dim3(256), 0, s, g);
+  } else {
+    if (rm == 64) hipLaunchKernelGGL((k_kprod<128, 64>), dim3((unsigned)nt), dim3(256), 0, s, g);
+    else hipLaunchKernelGGL((k_kprod<128, 32>), dim3((unsigned)nt), dim3(256), 0, s, g);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_slab_leaf(hipStream_t s, const SlabArgs& g, const LeafTask& lt) {
   if (g.K < 1 || g.K > 64 || lt.mk > 64 || lt.m2 > 64 || lt.m2 < 1 || lt.mk < 1) return hipErrorInvalidValue;
-  const int64_t nt = kprod_tiles(g);
+  const int64_t nt = kprod_tiles(g, 64);
   if (nt + 1 >= (int64_t)1 << 31) return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_kprod_leaf, dim3((unsigned)(1 + nt)), dim3(256), 0, s, g, lt);
   return hipGetLastError();

@@ -14,13 +14,16 @@
 //
 // Layout (MI355X): 256 x 128 output tile per workgroup of 4 waves (2 x 2,
 // each 128 x 64 = 4 x 2 accumulators). K streams through a 3-slot LDS ring
-// of 32-deep stages (48 KiB each) filled by buffer LDS-DMA: A_hi, A_lo as
-// [row][k] (64-byte rows, chunk index XOR-swizzled with (row / 4) % 4) read
-// with ds_read_b128, and B_hi, B_lo as [k][column] (256-byte rows, swizzled
-// like the Hessian tile) read with transposing ds_read_b64_tr_b16. The
-// buffer descriptors end at the last row of A and at row K of B, so rows
-// past M and k past K read as zeros; B chunks past N get an offset outside
-// the buffer. Each wave issues 12 of the 48 DMA instructions of a stage.
+// of 16-deep stages (24 KiB each) filled by buffer LDS-DMA, so a workgroup
+// needs 72 KiB and two independent workgroups share a CU: one's barrier and
+// DMA waits are covered by the other's MFMAs. A_hi, A_lo are stored
+// [row][k] (32-byte rows, 16-byte chunk index XOR-swizzled with (row / 8) %
+// 2) and read with ds_read_b128; B_hi, B_lo as [k][column] (256-byte rows,
+// swizzled like the Hessian tile) and read with transposing
+// ds_read_b64_tr_b16. The buffer descriptors end at the last row of A and at
+// row K of B, so rows past M and k past K read as zeros; B chunks past N get
+// an offset outside the buffer. Each wave issues 6 of the 24 DMA
+// instructions of a stage.
 #include "common.h"
 #include "dma.h"
 
@@ -31,16 +34,17 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef int v4i32_t __attribute__((ext_vector_type(4)));
 
 constexpr int kTM = 256, kTN = 128;        // workgroup tile
-constexpr int kTK = 32;                    // k per stage
+constexpr int kTK = 16;                    // k per stage
 constexpr int kTSlots = 3;
-constexpr int kTA = kTM * kTK * 2;         // bytes of A_hi (or A_lo) per stage: 16 KiB
-constexpr int kTB = kTK * kTN * 2;         // bytes of B_hi (or B_lo) per stage: 8 KiB
-constexpr int kTSlot = 2 * kTA + 2 * kTB;  // 48 KiB
+constexpr int kTA = kTM * kTK * 2;         // bytes of A_hi (or A_lo) per stage: 8 KiB
+constexpr int kTB = kTK * kTN * 2;         // bytes of B_hi (or B_lo) per stage: 4 KiB
+constexpr int kTSlot = 2 * kTA + 2 * kTB;  // 24 KiB
+constexpr int kTDma = 6;                   // DMA instructions per wave per stage
 
-// A rows are 64 bytes: rows r and r + 4 share banks, so the 16-byte chunk
-// index is XORed with (r / 4) % 4 (16 consecutive rows of one chunk column
+// A rows are 32 bytes: rows r and r + 8 share banks, so the 16-byte chunk
+// index is XORed with (r / 8) % 2 (16 consecutive rows of one chunk column
 // then cover all 64 banks)
-__device__ __forceinline__ int swz_a(int row) { return (row >> 2) & 3; }
+__device__ __forceinline__ int swz_a(int row) { return (row >> 3) & 1; }
 
 __device__ __forceinline__ void dma16_rsrc(uint32_t voff, v4i32_t rsrc, uint32_t soff, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
@@ -57,14 +61,14 @@ __device__ __forceinline__ v4i32_t make_rsrc(const void* base, int64_t bytes) {
   return r;
 }
 
-// Wait until at most `stages` stages of 12 DMA instructions of this wave are
-// outstanding, then barrier (one asm block, as in dma.h).
-__device__ __forceinline__ void wait_dma12_barrier(int stages) {
+// Wait until at most `stages` stages of kTDma DMA instructions of this wave
+// are outstanding, then barrier (one asm block, as in dma.h).
+__device__ __forceinline__ void wait_dma6_barrier(int stages) {
   if (stages <= 0) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-  else asm volatile("s_waitcnt vmcnt(12)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
 }
 
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, 2)
 k_trail_x3(TrailArgs g) {
   __shared__ __align__(16) uint8_t sm[kTSlots * kTSlot];
   if (g.st != nullptr && g.st->flags != 0) return;
@@ -90,20 +94,20 @@ k_trail_x3(TrailArgs g) {
   const v4i32_t rBh = make_rsrc(g.Bhi + n0, bbytes);
   const v4i32_t rBl = make_rsrc(g.Blo + n0, bbytes);
 
-  // DMA plan: instruction idx = 12 w + q, q = 0..11:
-  //   0..15 A_hi, 16..31 A_lo: rows 16p .. 16p+15, 4 chunks of 8 k each
-  //   32..39 B_hi, 40..47 B_lo: k rows 4p .. 4p+3, 16 chunks of 8 columns
-  uint32_t voff[12];
+  // DMA plan: instruction idx = 6 w + q, q = 0..5:
+  //   0..7 A_hi, 8..15 A_lo: rows 32p .. 32p+31, 2 chunks of 8 k each
+  //   16..19 B_hi, 20..23 B_lo: k rows 4p .. 4p+3, 16 chunks of 8 columns
+  uint32_t voff[kTDma];
 #pragma unroll
-  for (int q = 0; q < 12; ++q) {
-    const int idx = 12 * wave + q;
-    if (idx < 32) {
-      const int p = idx & 15;
-      const int r = 16 * p + (lane >> 2);
-      const int c = (lane & 3) ^ swz_a(r);
+  for (int q = 0; q < kTDma; ++q) {
+    const int idx = kTDma * wave + q;
+    if (idx < 16) {
+      const int p = idx & 7;
+      const int r = 32 * p + (lane >> 1);
+      const int c = (lane & 1) ^ swz_a(r);
       voff[q] = (uint32_t)((r * g.lda + 8 * c) * 2);
     } else {
-      const int p = idx & 7;
+      const int p = idx & 3;
       const int kr = 4 * p + (lane >> 4);
       const int c = (lane & 15) ^ dma_swz(kr);
       voff[q] = (n0 + 8 * c < g.N) ? (uint32_t)((kr * g.ldb + 8 * c) * 2) : 0x80000000u;
@@ -113,26 +117,23 @@ k_trail_x3(TrailArgs g) {
     const uint32_t sa = __builtin_amdgcn_readfirstlane((uint32_t)(st * kTK * 2));
     const uint32_t sb = __builtin_amdgcn_readfirstlane((uint32_t)(st * kTK * g.ldb * 2));
 #pragma unroll
-    for (int q = 0; q < 12; ++q) {
-      const int idx = 12 * wave + q;
+    for (int q = 0; q < kTDma; ++q) {
+      const int idx = kTDma * wave + q;
       const uint32_t dst = __builtin_amdgcn_readfirstlane(
           lds0 + slot * kTSlot +
-          (idx < 16 ? (idx & 15) * 1024
-                    : idx < 32 ? kTA + (idx & 15) * 1024
-                               : idx < 40 ? 2 * kTA + (idx & 7) * 1024 : 2 * kTA + kTB + (idx & 7) * 1024));
-      const v4i32_t r = idx < 16 ? rAh : idx < 32 ? rAl : idx < 40 ? rBh : rBl;
-      dma16_rsrc(voff[q], r, idx < 32 ? sa : sb, dst);
+          (idx < 8 ? (idx & 7) * 1024
+                   : idx < 16 ? kTA + (idx & 7) * 1024
+                              : idx < 20 ? 2 * kTA + (idx & 3) * 1024 : 2 * kTA + kTB + (idx & 3) * 1024));
+      const v4i32_t r = idx < 8 ? rAh : idx < 16 ? rAl : idx < 20 ? rBh : rBl;
+      dma16_rsrc(voff[q], r, idx < 16 ? sa : sb, dst);
     }
   };
 
   // fragment bases (per lane, relative to a slot)
-  //  A: row 128 wm + 32 mb + lane % 32, k chunk (2 ks + lane / 32) ^ swz_a(row)
-  //  B: k row 16 ks + 4 h + 8 (G/2) + s/4, column chunk (8 wn + 4 nb + 2 (G%2) + (s/2)%2) ^ dma_swz
+  //  A: row 128 wm + 32 mb + lane % 32, k chunk (lane / 32) ^ swz_a(row)
+  //  B: k row 4 h + 8 (G/2) + s/4, column chunk (8 wn + 4 nb + 2 (G%2) + (s/2)%2) ^ dma_swz
   const int arow = 128 * wm + (lane & 31);
-  const int sa_l = swz_a(arow);                  // same for every mb (32 mb adds 8 to row / 4)
-  uint32_t offA[2];
-#pragma unroll
-  for (int ks = 0; ks < 2; ++ks) offA[ks] = arow * 64 + (((2 * ks + (lane >> 5)) ^ sa_l) * 16);
+  const uint32_t offA = arow * 32 + (((lane >> 5) ^ swz_a(arow)) * 16);   // swz_a is the same for every mb
   const int G = lane >> 4, sl = lane & 15;
   const int trow = 8 * (G >> 1) + (sl >> 2);
   const int swzb = dma_swz(trow);
@@ -155,53 +156,45 @@ k_trail_x3(TrailArgs g) {
   for (int ps = 0; ps < kTSlots - 1; ++ps)
     if (ps < nstage) issue(ps, ps);
   for (int st = 0; st < nstage; ++st) {
-    wait_dma12_barrier(min(kTSlots - 2, nstage - 1 - st));
+    wait_dma6_barrier(min(kTSlots - 2, nstage - 1 - st));
     if (st + kTSlots - 1 < nstage) issue(st + kTSlots - 1, (st + kTSlots - 1) % kTSlots);
     const uint32_t sbase = lds0 + (uint32_t)(st % kTSlots) * kTSlot;
-    uint32_t bA[2], bB[2];
+    const uint32_t bA = offA + sbase;
+    bf16x8_t ah[4], al[4], bh[2], bl[2];
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      bA[q] = offA[q] + sbase;
-      bB[q] = offB[q] + sbase;
+    for (int mb = 0; mb < 4; ++mb) {
+      const uint32_t o = bA + mb * 32 * 32;
+      ah[mb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const __attribute__((address_space(3))) uint4*>(
+                                                (uintptr_t)o));
+      al[mb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const __attribute__((address_space(3))) uint4*>(
+                                                (uintptr_t)(o + kTA)));
     }
 #pragma unroll
-    for (int ks = 0; ks < kTK / 16; ++ks) {
-      bf16x8_t ah[4], al[4], bh[2], bl[2];
+    for (int nb = 0; nb < 2; ++nb) {
+      const uint32_t o = offB[nb] + sbase;
+      const v4i16_t h0 = lds_tr16(o), h1 = lds_tr16(o + 4 * 256);
+      const v4i16_t l0 = lds_tr16(o + kTB), l1 = lds_tr16(o + kTB + 4 * 256);
+      bh[nb] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
+      bl[nb] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const uint32_t o = bA[ks] + mb * 32 * 64;
-        ah[mb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const __attribute__((address_space(3))) uint4*>(
-                                                  (uintptr_t)o));
-        al[mb] = __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const __attribute__((address_space(3))) uint4*>(
-                                                  (uintptr_t)(o + kTA)));
-      }
+    for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        const uint32_t o = bB[nb] + 16 * ks * 256;
-        const v4i16_t h0 = lds_tr16(o), h1 = lds_tr16(o + 4 * 256);
-        const v4i16_t l0 = lds_tr16(o + kTB), l1 = lds_tr16(o + kTB + 4 * 256);
-        bh[nb] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(h0, h1, 0, 1, 2, 3, 4, 5, 6, 7));
-        bl[nb] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(l0, l1, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mb], bh[nb], acc[mb][nb], 0, 0, 0);
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mb], bl[nb], acc[mb][nb], 0, 0, 0);
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[mb], bh[nb], acc[mb][nb], 0, 0, 0);
       }
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mb], bh[nb], acc[mb][nb], 0, 0, 0);
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[mb], bl[nb], acc[mb][nb], 0, 0, 0);
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[mb], bh[nb], acc[mb][nb], 0, 0, 0);
-        }
-    }
   }
 
   // C -= acc: lane holds D[i][j], j = lane % 32, i = 8 (r / 4) + 4 (lane / 32) + r % 4.
-  // Every C value is loaded, unconditionally (indices clamped into the
-  // matrix), before the first store: predicated loads would each end in a
-  // wait, and a store followed by a load the compiler cannot prove disjoint
-  // would serialise the read-modify-writes on memory latency.
+  // In two halves (mb = 0..1, then 2..3; 64 registers of C next to the 128
+  // accumulators), each loading all of its C values, unconditionally (indices
+  // clamped into the matrix), before its first store: predicated loads would
+  // each end in a wait, and a store followed by a load the compiler cannot
+  // prove disjoint would serialise the read-modify-writes on memory latency.
   const int64_t ib = m0 + 128 * wm + 4 * (lane >> 5);
   const int64_t jb = n0 + 64 * wn + (lane & 31);
-  float cv[4][2][16];
   if (m0 + kTM <= g.M && n0 + kTN <= g.N && g.ldc < ((int64_t)1 << 22)) {
     // whole tile: a buffer over this wave's 128 rows, a fixed 32-bit lane
     // offset and a scalar offset per row, so no access needs vector
@@ -215,43 +208,46 @@ k_trail_x3(TrailArgs g) {
     const int ldc4 = __builtin_amdgcn_readfirstlane((int)(g.ldc * 4));
     const int lob = (4 * (lane >> 5)) * ldc4 + (lane & 31) * 4;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int half = 0; half < 2; ++half) {
+      float cv[2][2][16];
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          cv[mb][nb][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
-              rc, lob, (32 * mb + 8 * (r >> 2) + (r & 3)) * ldc4 + 128 * nb, 0));
+        for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+          for (int r = 0; r < 16; ++r)
+            cv[m][nb][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                rc, lob, (32 * (2 * half + m) + 8 * (r >> 2) + (r & 3)) * ldc4 + 128 * nb, 0));
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(cv[mb][nb][r] - acc[mb][nb][r]), rc, lob,
-                                                (32 * mb + 8 * (r >> 2) + (r & 3)) * ldc4 + 128 * nb, 0);
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            __builtin_amdgcn_raw_buffer_store_b32(
+                __float_as_uint(cv[m][nb][r] - acc[2 * half + m][nb][r]), rc, lob,
+                (32 * (2 * half + m) + 8 * (r >> 2) + (r & 3)) * ldc4 + 128 * nb, 0);
+    }
     return;
   }
+  // edge tiles: one 32 x 32 block at a time
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int nb = 0; nb < 2; ++nb) {
+      float cv[16];
+      const int64_t j = jb + 32 * nb;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t i = min(ib + 32 * mb + 8 * (r >> 2) + (r & 3), g.M - 1);
-        const int64_t j = min(jb + 32 * nb, g.N - 1);
-        cv[mb][nb][r] = g.C[i * g.ldc + j];
+        cv[r] = g.C[i * g.ldc + min(j, g.N - 1)];
       }
-#pragma unroll
-  for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int64_t i = ib + 32 * mb + 8 * (r >> 2) + (r & 3);
-        const int64_t j = jb + 32 * nb;
-        if (i < g.M && j < g.N) g.C[i * g.ldc + j] = cv[mb][nb][r] - acc[mb][nb][r];
+        if (i < g.M && j < g.N) g.C[i * g.ldc + j] = cv[r] - acc[mb][nb][r];
       }
+    }
 }
 
 hipError_t launch_trail_x3(hipStream_t s, const TrailArgs& g) {
