@@ -155,6 +155,16 @@ struct GemmPair {
 template <int R, bool KC>
 struct Operand {
   static constexpr int L = R * kGBK / 4 / 256;   // float4 per thread
+  // whole chunk inside the operand, 16-byte aligned rows: no predicates
+  __device__ static float4 load_full(const float* p, int64_t ld, int64_t r0, int64_t k0, int idx) {
+    if constexpr (KC) {
+      const int r = idx / (kGBK / 4), k4 = idx % (kGBK / 4);
+      return *reinterpret_cast<const float4*>(p + (r0 + r) * ld + k0 + 4 * k4);
+    } else {
+      const int k = idx / (R / 4), r4 = idx % (R / 4);
+      return *reinterpret_cast<const float4*>(p + (k0 + k) * ld + r0 + 4 * r4);
+    }
+  }
   __device__ static float4 load(const float* p, int64_t ld, int64_t r0, int64_t k0, int64_t RN,
                                 int64_t K, int idx) {
     if constexpr (KC) {
@@ -220,7 +230,18 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int tm, int tn, Gem
       }
 
   float4 ra[OA::L], rb[OB::L];
+  // interior chunks (the common case) take unpredicated 16-byte loads, so
+  // all of a chunk's loads are in flight at once
+  const bool vec = ((g.lda & 3) == 0) && ((g.ldb & 3) == 0) && (((uintptr_t)g.A & 15) == 0) &&
+                   (((uintptr_t)g.B & 15) == 0) && m0 + BM <= g.M && n0 + BN <= g.N;
   auto gload = [&](int64_t k0) {
+    if (vec && k0 + kGBK <= g.K) {
+#pragma unroll
+      for (int v = 0; v < OA::L; ++v) ra[v] = OA::load_full(g.A, g.lda, m0, k0, tid + 256 * v);
+#pragma unroll
+      for (int v = 0; v < OB::L; ++v) rb[v] = OB::load_full(g.B, g.ldb, n0, k0, tid + 256 * v);
+      return;
+    }
 #pragma unroll
     for (int v = 0; v < OA::L; ++v) ra[v] = OA::load(g.A, g.lda, m0, k0, g.M, g.K, tid + 256 * v);
 #pragma unroll
