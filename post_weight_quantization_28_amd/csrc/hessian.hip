@@ -333,12 +333,17 @@ k_hessian_dma(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx,
     voff[q] = ch < n ? (uint32_t)((t * ldx + ch) * 2) : 0x80000000u;
   }
   const uint32_t stage_bytes = (uint32_t)(kDK * ldx * 2);
+  // A diagonal tile needs one channel strip: the B operand is read from the
+  // A region and its DMA is skipped (waves whose instructions are all B
+  // then issue none; their stage waits are trivially met).
+  const bool diag = bi == bj;
   auto issue = [&](int st, int slot) {
     const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)st * stage_bytes);
 #pragma unroll
     for (int q = 0; q < PER; ++q) {
       const int idx = PER * wave + q;
       const int op = idx >> 4, p = idx & 15;
+      if (op == 1 && diag) continue;
       dma16_buf(voff[q], rsrc, soff,
                 __builtin_amdgcn_readfirstlane(lds0 + slot * kDSlotBytes + op * kDOpBytes + p * 1024));
     }
@@ -361,7 +366,10 @@ k_hessian_dma(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx,
   for (int b = 0; b < 4; ++b) off[b] = trow_off * 512 + (((16 * wm + 4 * b + cbase) ^ swz) * 16) + half8;
 #pragma unroll
   for (int b = 0; b < NB; ++b)
-    off[4 + b] = kDOpBytes + trow_off * 512 + (((4 * NB * wn + 4 * b + cbase) ^ swz) * 16) + half8;
+    off[4 + b] = (diag ? 0 : kDOpBytes) + trow_off * 512 + (((4 * NB * wn + 4 * b + cbase) ^ swz) * 16) + half8;
+  // on a diagonal tile, a wave whose block lies wholly below the diagonal
+  // only takes part in the DMA and the barriers (that half is never read)
+  const bool idle = diag && 4 * NB * wn * 8 + 32 * NB - 1 < 128 * wm;
 
   f32x16_t acc[4][NB];
 #pragma unroll
@@ -378,6 +386,7 @@ k_hessian_dma(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx,
   for (int st = 0; st < nstage; ++st) {
     wait_stages_barrier<PER, SLOTS - 2>(min(SLOTS - 2, nstage - 1 - st));
     if (st + SLOTS - 1 < nstage) issue(st + SLOTS - 1, (st + SLOTS - 1) % SLOTS);
+    if (idle) continue;
     const uint32_t sbase = lds0 + (uint32_t)(st % SLOTS) * kDSlotBytes;
     uint32_t bs[4 + NB];
 #pragma unroll
@@ -408,6 +417,7 @@ k_hessian_dma(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx,
     }
   }
 
+  if (idle) return;
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
