@@ -139,6 +139,10 @@ struct SweepArgs {
   float* scales; uint8_t* zeros; int64_t ngroups;
   uint8_t* codes; int64_t n_quant;   // processing order, d_out x n_quant
   float* E; int64_t lde;        // d_out x B block errors (row pitch lde)
+  // fused near field (B = 128 only): W_blk -= Esb[:, :kb] U[i0 - kb : i0, blk]
+  // before the sweep; Esb is the super-block's error matrix (pitch lde),
+  // kb a multiple of 32, at most 384; 0 = none
+  const float* Esb; int64_t kb;
   float* row_loss;
   const DevStatus* st;
 };

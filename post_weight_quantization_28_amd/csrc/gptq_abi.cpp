@@ -441,7 +441,11 @@ gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int
   // the super-block's later columns at once (fp32, K = B); when the
   // super-block is done, all of its errors update the columns right of it
   // in one split-bf16 product (K = s1 - s0). Without the split path the
-  // super-block is the block itself and the far field is fp32.
+  // super-block is the block itself and the far field is fp32. With B = 128,
+  // whole blocks and groups inside a block, the in-super-block update is
+  // taken left-looking by the sweep kernel itself (each block first applies
+  // the errors of the super-block's earlier blocks to its own columns).
+  const bool fused = two && B == 128 && p->group <= B && nq % B == 0 && sw == 512;
   for (int64_t s0 = 0; s0 < nq; s0 += sw) {
     const int64_t s1 = std::min<int64_t>(s0 + sw, nq);
     for (int64_t i0 = s0; i0 < s1; i0 += B) {
@@ -457,10 +461,11 @@ gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int
           if ((1 << sh) == p->group) a.gshift = sh;
       a.scales = out->scales; a.zeros = out->zeros; a.ngroups = nq / p->group;
       a.codes = codes; a.n_quant = nq; a.E = Eb; a.lde = sw; a.row_loss = loss; a.st = dst;
+      a.Esb = E; a.kb = fused ? i0 - s0 : 0;
       HIP_TRY(launch_sweep(s, a), "sweep");
       const int64_t i1 = i0 + nc;
       const int64_t near_end = two ? s1 : n;
-      if (i1 < near_end) {
+      if (!fused && i1 < near_end) {
         SlabArgs g{};
         g.M = d_out; g.N = near_end - i1; g.K = nc;
         g.A = Eb; g.lda = sw;

@@ -26,6 +26,12 @@
 // constants) and branch-free, so the U row for step j + 2 is in flight
 // while step j computes. Codes and errors are kept by a select with a
 // constant lane mask; w_hat and the row loss are formed once at the end.
+//
+// With B = 128 the block's share of the lazy-batch update inside its
+// super-block can be taken here, left-looking: before the sweep, W_blk -=
+// E[:, :kb] U[i0 - kb : i0, blk] for the kb columns of the super-block
+// already quantized (fp32 MFMA, see near_update). That replaces the
+// separate right-looking near-field launches.
 #include "common.h"
 #include <utility>
 
@@ -219,17 +225,112 @@ __device__ __forceinline__ void sweep_all(SweepState<CPL>& S, const SweepArgs& a
   (sweep_step<CPL, Js>(S, a, sU, sInv, L, row, row_ok, maxq), ...);
 }
 
+
+// ---------------------------------------------------------------- near field
+// upd[16][128] = E[rows, :kb] U[i0 - kb : i0, i0 : i0 + 128] for this
+// workgroup's 16 rows (kb a multiple of 32, at most 384). E's rows are
+// staged in LDS once; U streams through a double buffer of 32-row chunks.
+// Wave w computes columns 32w..32w+31 as two v_mfma_f32_16x16x4f32 tiles;
+// for MFMA t of a group of four, lane group g = lane / 16 feeds k = 16p +
+// 4g + t to both operands (E as one 16-byte read, U as four 4-byte reads).
+constexpr int kNearMax = 384;   // largest kb: a 512-column super-block
+constexpr int kNearEP = kNearMax + 4;
+constexpr int kNearUP = 128 + 4;
+constexpr int kNearLds = 16 * kNearEP + 2 * 32 * kNearUP;   // floats (fits the U tile's region)
+constexpr int kUpdP = 128 + 4;
+
+typedef float nf_f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void near_update(const SweepArgs& a, float* stage, float* upd) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int li = lane & 15, g = lane >> 4;
+  const int kb = (int)a.kb;
+  const int64_t r0 = (int64_t)blockIdx.x * 16;
+  float* sE = stage;                        // [16][kNearEP]
+  float* sUc = stage + 16 * kNearEP;        // [2][32][kNearUP]
+  const float* Ub = a.U + (a.i0 - kb) * a.ldu + a.i0;
+  // E rows (clamped to the last row; those results are never used)
+  {
+    const int q4 = kb / 4;                  // float4 per E row
+#pragma unroll
+    for (int v = 0; v < kNearMax * 16 / 4 / 256; ++v) {
+      const int idx = tid + 256 * v;
+      if (idx < 16 * q4) {
+        const int rr = idx / q4, k4 = idx % q4;
+        const int64_t row = min(r0 + rr, a.d_out - 1);
+        *reinterpret_cast<float4*>(&sE[rr * kNearEP + 4 * k4]) =
+            *reinterpret_cast<const float4*>(a.Esb + row * a.lde + 4 * k4);
+      }
+    }
+  }
+  // U chunk c: 32 rows x 128 columns, four 16-byte pieces per thread
+  float4 u0, u1, u2, u3;
+#define NEAR_LOAD(c)                                                                       \
+  do {                                                                                     \
+    const float* src_ = Ub + (int64_t)(32 * (c) + (tid >> 5)) * a.ldu + 4 * (tid & 31);    \
+    u0 = *reinterpret_cast<const float4*>(src_);                                           \
+    u1 = *reinterpret_cast<const float4*>(src_ + 8 * a.ldu);                               \
+    u2 = *reinterpret_cast<const float4*>(src_ + 16 * a.ldu);                              \
+    u3 = *reinterpret_cast<const float4*>(src_ + 24 * a.ldu);                              \
+  } while (0)
+#define NEAR_STORE(buf)                                                                    \
+  do {                                                                                     \
+    float* dst_ = &sUc[((buf) * 32 + (tid >> 5)) * kNearUP + 4 * (tid & 31)];              \
+    *reinterpret_cast<float4*>(dst_) = u0;                                                 \
+    *reinterpret_cast<float4*>(dst_ + 8 * kNearUP) = u1;                                   \
+    *reinterpret_cast<float4*>(dst_ + 16 * kNearUP) = u2;                                  \
+    *reinterpret_cast<float4*>(dst_ + 24 * kNearUP) = u3;                                  \
+  } while (0)
+  NEAR_LOAD(0);
+  NEAR_STORE(0);
+  __syncthreads();
+  nf_f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+  const int nch = kb / 32;
+  for (int c = 0; c < nch; ++c) {
+    const int cur = c & 1;
+    if (c + 1 < nch) NEAR_LOAD(c + 1);
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const float4 fa = *reinterpret_cast<const float4*>(&sE[li * kNearEP + 32 * c + 16 * p + 4 * g]);
+      const float* ub = &sUc[(cur * 32 + 16 * p + 4 * g) * kNearUP + 32 * w + li];
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const float* q = ub + 16 * ct;
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.x, q[0], acc[ct], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.y, q[kNearUP], acc[ct], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.z, q[2 * kNearUP], acc[ct], 0, 0, 0);
+        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.w, q[3 * kNearUP], acc[ct], 0, 0, 0);
+      }
+    }
+    if (c + 1 < nch) NEAR_STORE(cur ^ 1);
+    __syncthreads();
+  }
+#undef NEAR_LOAD
+#undef NEAR_STORE
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) upd[(4 * g + v) * kUpdP + 32 * w + 16 * ct + li] = acc[ct][v];
+}
+
 // One wave per SIMD is all a d_out = 4096 layer provides (16 lanes per row),
 // so the scheduler is told to favour latency over occupancy.
 template <int CPL>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 k_sweep(SweepArgs a) {
   constexpr int B = 16 * CPL;
+  constexpr bool kNear = CPL == 8;   // the fused near field (B = 128)
+  static_assert(!kNear || kNearLds <= B * B, "near-field staging must fit the U tile's region");
   // one array, 1 / U_jj first: the per-step diagonal read then takes a
   // constant offset from a single base register
-  __shared__ float smem[B + B * B];
+  __shared__ float smem[B + B * B + (kNear ? 16 * kUpdP : 0)];
   float* sInv = smem;
   float* sU = smem + B;
+  float* upd = smem + B + B * B;
+  const bool near = kNear && a.kb > 0;
+  if (near) {
+    near_update(a, sU, upd);   // ends with a barrier: sU is free again
+  }
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -292,6 +393,11 @@ k_sweep(SweepArgs a) {
   }
   if (tid < B) sInv[tid] = tid < nc ? 1.f / diag : 0.f;
   __syncthreads();
+  if (near) {
+    const float* ur = upd + (wave * 4 + (lane >> 4)) * kUpdP + L;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) S.w[c] -= ur[16 * c];
+  }
 
   if ((a.i0 % a.group) == 0) {
     start_group<CPL, 0>(S, a, L, row, row_ok, maxq);
