@@ -426,7 +426,8 @@ gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int
   float* loss = out->row_loss ? out->row_loss : reinterpret_cast<float*>(ws + L.loss);
 
   if ((st = enqueue_factor(s, H, n, p, ws, L)) != GPTQ_OK) return st;
-  HIP_TRY(launch_w_prep(s, W, wdt == GPTQ_BF16, d_out, n, ldw, perm, Wf, dst), "w prep");
+  HIP_TRY(launch_w_prep(s, W, wdt == GPTQ_BF16, d_out, n, ldw, p->act_order ? perm : nullptr, Wf, dst),
+          "w prep");
   HIP_TRY(launch_fill_f32(s, loss, (size_t)d_out, 0.f), "fill");
   const int64_t nq = p->n_quant;
   const int B = p->block;
@@ -487,7 +488,10 @@ gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int
   }
   HIP_TRY(launch_finish(s, Wf, codes, invperm, d_out, n, nq, p->group, out->w_hat, out->codes, out->g_idx),
           "finish");
-  if (out->qweight) HIP_TRY(launch_pack(s, codes, nq, invperm, d_out, nq, p->bits, out->qweight), "pack");
+  // the processing order is the identity without act-order
+  if (out->qweight)
+    HIP_TRY(launch_pack(s, codes, nq, p->act_order ? invperm : nullptr, d_out, nq, p->bits, out->qweight),
+            "pack");
   }
   return read_status(s, dst, perm, fail_col);
 }

@@ -7,28 +7,54 @@
 // straddling into the next word when needed (3-bit: 32 codes per 3 words).
 #include "common.h"
 
+#include <algorithm>
+
 namespace gq {
 
-// One thread per output word; codes gathered through invperm (processing
-// order -> original order) when given.
+// One thread per output word (grid: words of a row in x, rows in y, so no
+// 64-bit division); codes gathered through invperm (processing order ->
+// original order) when given. Without invperm and with b = 2, 4 or 8 the
+// word's codes are one aligned 16-, 8- or 4-byte read.
 __global__ void __launch_bounds__(256)
 k_pack(const uint8_t* __restrict__ codes, int64_t ldc, const int32_t* __restrict__ invperm,
        int64_t d_out, int64_t nq, int bits, int64_t wpr, uint32_t* __restrict__ qw) {
-  const int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (id >= d_out * wpr) return;
-  const int64_t r = id / wpr, w = id % wpr;
+  const int64_t w = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (w >= wpr) return;
   const uint32_t mask = (1u << bits) - 1u;
   const int64_t bit0 = 32 * w;
   const int64_t k0 = bit0 / bits;
   const int64_t k1 = min(nq - 1, (bit0 + 31) / bits);
-  uint32_t word = 0;
-  for (int64_t k = k0; k <= k1; ++k) {
-    const int64_t src = invperm ? invperm[k] : k;
-    const uint32_t c = codes[r * ldc + src] & mask;
-    const int64_t o = k * bits - bit0;
-    word |= (o < 0) ? (c >> (-o)) : (c << o);
+  for (int64_t r = blockIdx.y; r < d_out; r += gridDim.y) {
+    const uint8_t* row = codes + r * ldc;
+    uint32_t word = 0;
+    const bool direct = invperm == nullptr && (bits == 2 || bits == 4 || bits == 8) &&
+                        (((uintptr_t)row & 15) == 0) && k0 + 32 / bits <= nq;
+    if (direct && bits == 4) {
+      const uint2 v = *reinterpret_cast<const uint2*>(row + k0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        word |= ((v.x >> (8 * i)) & 15u) << (4 * i);
+        word |= ((v.y >> (8 * i)) & 15u) << (4 * i + 16);
+      }
+    } else if (direct && bits == 2) {
+      const uint4 v = *reinterpret_cast<const uint4*>(row + k0);
+      const uint32_t q[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) word |= ((q[j] >> (8 * i)) & 3u) << (2 * (4 * j + i));
+    } else if (direct) {   // 8-bit
+      word = *reinterpret_cast<const uint32_t*>(row + k0);
+    } else {
+      for (int64_t k = k0; k <= k1; ++k) {
+        const int64_t src = invperm ? invperm[k] : k;
+        const uint32_t c = row[src] & mask;
+        const int64_t o = k * bits - bit0;
+        word |= (o < 0) ? (c >> (-o)) : (c << o);
+      }
+    }
+    qw[r * wpr + w] = word;
   }
-  qw[id] = word;
 }
 
 hipError_t launch_pack(hipStream_t s, const uint8_t* codes, int64_t ldc, const int32_t* invperm,
@@ -36,7 +62,9 @@ hipError_t launch_pack(hipStream_t s, const uint8_t* codes, int64_t ldc, const i
   const int64_t wpr = ceil_div(n_quant * bits, 32);
   const int64_t total = d_out * wpr;
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_pack, dim3((unsigned)ceil_div(total, 256)), dim3(256), 0, s, codes, ldc,
+  // rows run along the grid's y dimension (at most 65535, looped beyond)
+  hipLaunchKernelGGL(k_pack, dim3((unsigned)ceil_div(wpr, 256), (unsigned)std::min<int64_t>(d_out, 65535)),
+                     dim3(256), 0, s, codes, ldc,
                      invperm, d_out, n_quant, bits, wpr, qweight);
   return hipGetLastError();
 }

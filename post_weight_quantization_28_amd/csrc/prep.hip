@@ -145,18 +145,49 @@ template <bool kBF16>
 __global__ void __launch_bounds__(256)
 k_w_prep(const void* __restrict__ Wv, int64_t n, int64_t ldw, const int32_t* __restrict__ perm,
          float* __restrict__ Wf, DevStatus* st) {
+  // four consecutive outputs per thread and pass; all loads of a pass are
+  // issued before its stores. perm == nullptr: the identity order, read and
+  // written as 8/16-byte vectors when the rows allow.
   const int64_t r = blockIdx.x;
-  for (int64_t p = threadIdx.x; p < n; p += 256) {
-    const int64_t c = perm[p];
-    float v;
-    if (kBF16) {
-      const uint16_t u = reinterpret_cast<const uint16_t*>(Wv)[r * ldw + c];
-      v = __uint_as_float((uint32_t)u << 16);
+  const bool vec = perm == nullptr && (n & 3) == 0 && (ldw & 3) == 0 && (((uintptr_t)Wv & 15) == 0) &&
+                   (((uintptr_t)Wf & 15) == 0);
+  for (int64_t p0 = 4 * threadIdx.x; p0 < n; p0 += 4 * 256) {
+    int64_t c[4];
+    float v[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c[e] = perm ? perm[min(p0 + e, n - 1)] : min(p0 + e, n - 1);
+    if (vec) {
+      if (kBF16) {
+        const uint2 u = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(Wv) + r * ldw + p0);
+        v[0] = __uint_as_float(u.x << 16);
+        v[1] = __uint_as_float(u.x & 0xFFFF0000u);
+        v[2] = __uint_as_float(u.y << 16);
+        v[3] = __uint_as_float(u.y & 0xFFFF0000u);
+      } else {
+        const float4 f = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(Wv) + r * ldw + p0);
+        v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+      }
     } else {
-      v = reinterpret_cast<const float*>(Wv)[r * ldw + c];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (kBF16) {
+          const uint16_t u = reinterpret_cast<const uint16_t*>(Wv)[r * ldw + c[e]];
+          v[e] = __uint_as_float((uint32_t)u << 16);
+        } else {
+          v[e] = reinterpret_cast<const float*>(Wv)[r * ldw + c[e]];
+        }
+      }
     }
-    if (!isfinite(v)) raise_status(st, kNonFinite, c);
-    Wf[r * n + p] = v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (p0 + e < n && !isfinite(v[e])) raise_status(st, kNonFinite, c[e]);
+    if (vec) {
+      *reinterpret_cast<float4*>(Wf + r * n + p0) = make_float4(v[0], v[1], v[2], v[3]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (p0 + e < n) Wf[r * n + p0 + e] = v[e];
+    }
   }
 }
 
