@@ -42,6 +42,7 @@ struct LeafSmem {
 struct LeafState {
   float a[4][4];        // A[lane][16q + 4w + c] -> Schur complement / L columns
   float x[4][4];        // X[16q + 4w + c][lane]
+  int bad;              // first failed pivot of this wave (64: none), wave-uniform
 };
 
 __device__ __forceinline__ int leaf_pos(int i) { return 16 * ((i >> 2) & 3) + 4 * (i >> 4) + (i & 3); }
@@ -50,27 +51,38 @@ __device__ __forceinline__ float lane_val(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
+// Pivot C of block BLK on its owner wave: L's column K = 4 BLK + C from
+// the current Schur column, and its rank-1 update of the block's later
+// columns. A failed pivot (not positive or not finite) is recorded as a
+// wave-uniform minimum, off the dependent chain; what follows it is then
+// garbage and the caller discards the result.
+template <int BLK, int C>
+__device__ __forceinline__ void leaf_pivot(LeafState& S, float (&invs)[4]) {
+  constexpr int qb = BLK / 4, K0 = 4 * BLK, K = K0 + C;
+  const float d2 = lane_val(S.a[qb][C], K);
+  if (!(d2 > 0.f && isfinite(d2))) S.bad = min(S.bad, K);
+  const float inv = __builtin_amdgcn_rsqf(d2);   // 1 / sqrt(d2)
+  const float d = d2 * inv;
+  const int lane = threadIdx.x & 63;
+  float l = (lane > K) ? S.a[qb][C] * inv : 0.f;
+  l = (lane == K) ? d : l;
+
+  S.a[qb][C] = l;
+  invs[C] = inv;
+#pragma unroll
+  for (int c2 = C + 1; c2 < 4; ++c2) S.a[qb][c2] = fmaf(-l, lane_val(l, K0 + c2), S.a[qb][c2]);
+}
+
 template <int BLK>
 __device__ __forceinline__ void leaf_block(LeafState& S, LeafSmem& sm, int w, int lane) {
   constexpr int qb = BLK / 4, ob = BLK % 4, K0 = 4 * BLK;
   if (w == ob) {
     // ---- the block's 4 pivots
     float invs[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int K = K0 + c;
-      const float d2 = lane_val(S.a[qb][c], K);
-      const bool ok = d2 > 0.f && isfinite(d2);
-      if (!ok && lane == 0) atomicMin(&sm.bad, K);
-      const float inv = ok ? __builtin_amdgcn_rsqf(d2) : 1.f;   // 1 / sqrt(d2)
-      const float d = ok ? d2 * inv : 1.f;
-      float l = (lane > K) ? S.a[qb][c] * inv : 0.f;
-      l = (lane == K) ? d : l;
-      S.a[qb][c] = l;
-      invs[c] = inv;
-#pragma unroll
-      for (int c2 = c + 1; c2 < 4; ++c2) S.a[qb][c2] = fmaf(-l, lane_val(l, K0 + c2), S.a[qb][c2]);
-    }
+    leaf_pivot<BLK, 0>(S, invs);
+    leaf_pivot<BLK, 1>(S, invs);
+    leaf_pivot<BLK, 2>(S, invs);
+    leaf_pivot<BLK, 3>(S, invs);
     // ---- rows K0..K0+3 of X: forward substitution inside the block
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
@@ -84,6 +96,8 @@ __device__ __forceinline__ void leaf_block(LeafState& S, LeafSmem& sm, int w, in
       sm.colw[K0 + c][pl] = S.a[qb][c];
       sm.xrow[K0 + c][lane] = S.x[qb][c];
     }
+    // the wave's last block: publish its first failure before the barrier
+    if (BLK >= 12 && lane == 0 && S.bad < 64) atomicMin(&sm.bad, S.bad);
   }
   __syncthreads();
   // ---- rank-4 updates of the later blocks of every wave. Blocks with
@@ -128,6 +142,7 @@ __device__ __forceinline__ void leaf_run(const float* src, int64_t lds, float* _
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   LeafState S;
+  S.bad = 64;
   if (threadIdx.x == 0) sm.bad = 64;
 #pragma unroll
   for (int q = 0; q < 4; ++q)

@@ -13,8 +13,8 @@ namespace gq {
 
 // One thread per output word (grid: words of a row in x, rows in y, so no
 // 64-bit division); codes gathered through invperm (processing order ->
-// original order) when given. Without invperm and with b = 2, 4 or 8 the
-// word's codes are one aligned 16-, 8- or 4-byte read.
+// original order) when given. Without invperm and with b = 2 or 4 the
+// word's codes are one aligned 16- or 8-byte read.
 __global__ void __launch_bounds__(256)
 k_pack(const uint8_t* __restrict__ codes, int64_t ldc, const int32_t* __restrict__ invperm,
        int64_t d_out, int64_t nq, int bits, int64_t wpr, uint32_t* __restrict__ qw) {
@@ -27,7 +27,7 @@ k_pack(const uint8_t* __restrict__ codes, int64_t ldc, const int32_t* __restrict
   for (int64_t r = blockIdx.y; r < d_out; r += gridDim.y) {
     const uint8_t* row = codes + r * ldc;
     uint32_t word = 0;
-    const bool direct = invperm == nullptr && (bits == 2 || bits == 4 || bits == 8) &&
+    const bool direct = invperm == nullptr && (bits == 2 || bits == 4) &&
                         (((uintptr_t)row & 15) == 0) && k0 + 32 / bits <= nq;
     if (direct && bits == 4) {
       const uint2 v = *reinterpret_cast<const uint2*>(row + k0);
@@ -43,8 +43,6 @@ k_pack(const uint8_t* __restrict__ codes, int64_t ldc, const int32_t* __restrict
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) word |= ((q[j] >> (8 * i)) & 3u) << (2 * (4 * j + i));
-    } else if (direct) {   // 8-bit
-      word = *reinterpret_cast<const uint32_t*>(row + k0);
     } else {
       for (int64_t k = k0; k <= k1; ++k) {
         const int64_t src = invperm ? invperm[k] : k;

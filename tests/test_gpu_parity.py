@@ -91,6 +91,8 @@ CASES = [
     ("c2", dict(d_out=72, n=300, T=4096), dict(n_quant=256, group=64)),
     # several super-blocks of 512 columns, the last one partial
     ("c2", dict(d_out=96, n=1408, T=4096), dict()),
+    # groups spanning two 128-column blocks: the separate near-field launches
+    ("c2", dict(d_out=64, n=1024, T=4096), dict(group=256)),
 ]
 
 
