@@ -55,8 +55,7 @@ constexpr int kLeaf = 64;
 hipError_t launch_leaf(hipStream_t s, float* A, float* X, int64_t n, int64_t off, int64_t m,
                        const int32_t* perm, DevStatus* st);
 // L21 = A21 D^T in place for a 64-column panel (r rows, row pitch ld).
-hipError_t launch_panel_solve(hipStream_t s, float* A21, const float* D, int64_t ld, int64_t r,
-                              const DevStatus* st);
+hipError_t launch_panel_solve(hipStream_t s, float* A21, const float* D, int64_t ld, int64_t r);
 // The next diagonal block's update and leaf, run beside a trailing update.
 struct LeafTask {
   const float* L21;      // rows k1.., columns of panel k (row pitch n)
@@ -84,7 +83,6 @@ struct GemmArgs {
   float* C; int64_t ldc;
   float alpha, beta;
   int kmode, lower_only;
-  const DevStatus* st;   // if non-null and flagged, the kernel returns at once
   int batch;
   int64_t sA, sB, sC;
 };
@@ -105,9 +103,28 @@ struct SlabArgs {
   float alpha, beta;
   int lower_only;
   int64_t lower_off;
-  const DevStatus* st;
 };
 hipError_t launch_slab(hipStream_t s, const SlabArgs& g);
+// The 64 x 64 tiles of C that the lower band needs, row-major: row tile rt
+// holds column tiles 0 .. min(nct, rt + d) - 1, d = (63 + lower_off) / 64 + 1
+// (d = nct without the band); rows from rs on are full, ps tiles precede
+// them.
+struct BandTiles {
+  int nrt, nct, d, rs;
+  int64_t ps, total;
+};
+inline BandTiles band_tiles(int64_t M, int64_t N, int lower_only, int64_t lower_off) {
+  BandTiles b;
+  b.nrt = (int)ceil_div(M, 64);
+  b.nct = (int)ceil_div(N, 64);
+  const int64_t d = lower_only ? (63 + lower_off) / 64 + 1 : (int64_t)b.nct;
+  b.d = (int)(d < b.nct ? d : b.nct);
+  const int rs = b.nct - b.d;
+  b.rs = rs < 0 ? 0 : (rs > b.nrt ? b.nrt : rs);
+  b.ps = (int64_t)b.rs * (b.rs - 1) / 2 + (int64_t)b.d * b.rs;
+  b.total = b.ps + (int64_t)(b.nrt - b.rs) * b.nct;
+  return b;
+}
 // launch_slab (K <= 64) plus one more workgroup (dispatched first) running `lt`.
 hipError_t launch_slab_leaf(hipStream_t s, const SlabArgs& g, const LeafTask& lt);
 
@@ -121,7 +138,6 @@ struct TrailArgs {
   const uint16_t *Ahi, *Alo; int64_t lda;
   const uint16_t *Bhi, *Blo; int64_t ldb;
   float* C; int64_t ldc;
-  const DevStatus* st;
 };
 hipError_t launch_trail_x3(hipStream_t s, const TrailArgs& g);
 // hi = bf16(x), lo = bf16(x - hi), elementwise over count floats.

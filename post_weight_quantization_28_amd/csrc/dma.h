@@ -1,5 +1,6 @@
 // LDS-DMA staging and transposing LDS reads on gfx950, shared by the
-// streaming MFMA kernels (Hessian Gram and split-bf16 trailing update).
+// streaming MFMA kernels (Hessian Gram, split-bf16 trailing update and the
+// factorisation's trailing update).
 //
 //  * global_load_lds_dwordx4: each lane moves 16 bytes from its own global
 //    address to LDS at M0 + 16 * lane, without passing through VGPRs. It is
@@ -41,6 +42,24 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds_base) {
 }
 
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef int v4i32_t __attribute__((ext_vector_type(4)));
+
+// Buffer form of the DMA: lane offset voff plus scalar offset soff into the
+// buffer rsrc; offsets at or past the buffer's size read as zeros.
+__device__ __forceinline__ void dma16_rsrc(uint32_t voff, v4i32_t rsrc, uint32_t soff, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
+               :: "v"(voff), "s"(rsrc), "s"(lds_base), "s"(soff) : "memory");
+}
+
+__device__ __forceinline__ v4i32_t make_rsrc(const void* base, int64_t bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  v4i32_t r;
+  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));   // stride 0
+  r.z = __builtin_amdgcn_readfirstlane((int)(uint32_t)(bytes > 0 ? bytes : 0));
+  r.w = 0x00020000;                                                    // raw, 32-bit format
+  return r;
+}
 
 __device__ __forceinline__ v4i16_t lds_tr16(uint32_t byte_off) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(

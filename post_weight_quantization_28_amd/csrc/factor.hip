@@ -55,27 +55,27 @@ hipError_t launch_leaf(hipStream_t s, float* A, float* X, int64_t n, int64_t off
 // them before the barrier), so the result can overwrite its input.
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ float4 row4(const float* p, bool ok, bool vec) {
-  if (!ok) return make_float4(0.f, 0.f, 0.f, 0.f);
+__device__ __forceinline__ float4 row4(const float* p, bool vec) {
   if (vec) return *reinterpret_cast<const float4*>(p);
   return make_float4(p[0], p[1], p[2], p[3]);
 }
 
 __global__ void __launch_bounds__(256)
-k_panel_solve(float* A21, const float* __restrict__ D, int64_t ld, int64_t r, const DevStatus* st) {
-  if (st->flags != 0) return;
+k_panel_solve(float* A21, const float* __restrict__ D, int64_t ld, int64_t r) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int li = lane & 15, g = lane >> 4;
   const int64_t r0 = (int64_t)blockIdx.x * 16;
   const bool vec = ((ld & 3) == 0) && (((uintptr_t)A21 & 15) == 0) && (((uintptr_t)D & 15) == 0);
   const bool rok = r0 + li < r;
-  const float* pa = A21 + (rok ? r0 + li : 0) * ld + 4 * g;
+  // rows past the end read the last row (always valid); zeroed below
+  const float* pa = A21 + min(r0 + li, r - 1) * ld + 4 * g;
   const float* pb = D + (int64_t)(16 * w + li) * ld + 4 * g;
   float4 a[4], b[4];
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    a[p] = row4(pa + 16 * p, rok, vec);
-    b[p] = row4(pb + 16 * p, true, vec);
+    a[p] = row4(pa + 16 * p, vec);
+    b[p] = row4(pb + 16 * p, vec);
+    if (!rok) a[p] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -93,10 +93,9 @@ k_panel_solve(float* A21, const float* __restrict__ D, int64_t ld, int64_t r, co
   }
 }
 
-hipError_t launch_panel_solve(hipStream_t s, float* A21, const float* D, int64_t ld, int64_t r,
-                              const DevStatus* st) {
+hipError_t launch_panel_solve(hipStream_t s, float* A21, const float* D, int64_t ld, int64_t r) {
   if (r <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_panel_solve, dim3((unsigned)ceil_div(r, 16)), dim3(256), 0, s, A21, D, ld, r, st);
+  hipLaunchKernelGGL(k_panel_solve, dim3((unsigned)ceil_div(r, 16)), dim3(256), 0, s, A21, D, ld, r);
   return hipGetLastError();
 }
 
@@ -306,7 +305,6 @@ k_gemm_f32(GemmPair gp) {
   const int which = (int)blockIdx.x >= gp.nt0;
   int t = (int)blockIdx.x - (which ? gp.nt0 : 0);
   GemmArgs g = gp.p[which];
-  if (g.st != nullptr && g.st->flags != 0) return;
   const int per = gp.per[which];          // tiles of one batch instance
   const int b = t / per;
   t -= b * per;

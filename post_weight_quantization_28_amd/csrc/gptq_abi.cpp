@@ -185,7 +185,7 @@ hipError_t factor_panels(hipStream_t s, float* A, float* X, int64_t n, const int
     const float* D = X + k0 * n + k0;    // L11^{-1}, lower
     float* L21 = A + k1 * n + k0;
     // L21 = A21 D^T in place (m == 64 whenever rows remain below the panel)
-    if ((e = launch_panel_solve(s, L21, D, n, r, st)) != hipSuccess) return e;
+    if ((e = launch_panel_solve(s, L21, D, n, r)) != hipSuccess) return e;
     // One launch: the next diagonal block (m2 rows) is updated and factored
     // by its own workgroup while the rest runs
     //   A[k1+m2:, k1:] -= L21[m2:] L21^T   (lower, i.e. j <= i + m2)
@@ -196,7 +196,7 @@ hipError_t factor_panels(hipStream_t s, float* A, float* X, int64_t n, const int
     g3.B = L21; g3.ldb = n; g3.tb = 1;
     g3.C = A + (k1 + m2) * n + k1; g3.ldc = n;
     g3.alpha = -1.f; g3.beta = 1.f;
-    g3.lower_only = 1; g3.lower_off = m2; g3.st = st;
+    g3.lower_only = 1; g3.lower_off = m2;
     LeafTask lt{L21, A, X, n, k1, (int)m2, (int)m, perm, st};
     if ((e = launch_slab_leaf(s, g3, lt)) != hipSuccess) return e;
   }
@@ -214,7 +214,7 @@ hipError_t factor_panels(hipStream_t s, float* A, float* X, int64_t n, const int
       g1.A = X + ap * n + ap; g1.lda = n; g1.ta = 1;
       g1.B = A + bp * n + ap; g1.ldb = n; g1.tb = 1;
       g1.C = A + ap * n + bp; g1.ldc = n;
-      g1.alpha = 1.f; g1.beta = 0.f; g1.kmode = 4; g1.st = st;
+      g1.alpha = 1.f; g1.beta = 0.f; g1.kmode = 4;
       g1.batch = batch; g1.sA = step; g1.sB = step; g1.sC = step;
       // g2: X_ji (hj x h) = -X_jj T
       g2 = GemmArgs{};
@@ -222,7 +222,7 @@ hipError_t factor_panels(hipStream_t s, float* A, float* X, int64_t n, const int
       g2.A = X + bp * n + bp; g2.lda = n; g2.ta = 0;
       g2.B = A + ap * n + bp; g2.ldb = n; g2.tb = 1;
       g2.C = X + bp * n + ap; g2.ldc = n;
-      g2.alpha = -1.f; g2.beta = 0.f; g2.kmode = 3; g2.st = st;
+      g2.alpha = -1.f; g2.beta = 0.f; g2.kmode = 3;
       g2.batch = batch; g2.sA = step; g2.sB = step; g2.sC = step;
     };
     GemmArgs f1{}, f2{}, p1{}, p2{};
@@ -472,7 +472,7 @@ gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int
         g.A = Eb; g.lda = sw;
         g.B = U + i0 * n + i1; g.ldb = n; g.tb = 0;
         g.C = Wf + i1; g.ldc = n;
-        g.alpha = -1.f; g.beta = 1.f; g.st = dst;
+        g.alpha = -1.f; g.beta = 1.f;
         HIP_TRY(launch_slab(s, g), "near-field update");
       }
     }
@@ -482,7 +482,7 @@ gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int
       t.M = d_out; t.N = n - s1; t.K = s1 - s0;
       t.Ahi = Ehi; t.Alo = Elo; t.lda = sw;
       t.Bhi = Uhi + s0 * n + s1; t.Blo = Ulo + s0 * n + s1; t.ldb = n;
-      t.C = Wf + s1; t.ldc = n; t.st = dst;
+      t.C = Wf + s1; t.ldc = n;
       HIP_TRY(launch_trail_x3(s, t), "far-field update");
     }
   }

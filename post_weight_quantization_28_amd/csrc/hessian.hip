@@ -458,7 +458,7 @@ hipError_t launch_hessian_partials_f32(hipStream_t s, const float* X, int64_t T,
     g.A = X + kb * ldx; g.lda = ldx; g.ta = 1;     // A(m,k) = X[k][m]
     g.B = X + kb * ldx; g.ldb = ldx; g.tb = 0;     // B(k,n) = X[k][n]
     g.C = part + (int64_t)sp * n * n; g.ldc = n;
-    g.alpha = 1.f; g.beta = 0.f; g.kmode = 0; g.lower_only = 0; g.st = nullptr;
+    g.alpha = 1.f; g.beta = 0.f; g.kmode = 0; g.lower_only = 0;
     hipError_t e = launch_gemm_f32(s, g);
     if (e != hipSuccess) return e;
   }

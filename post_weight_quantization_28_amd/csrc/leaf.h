@@ -155,7 +155,8 @@ __device__ __forceinline__ void leaf_run(const float* src, int64_t lds, float* _
     }
   __syncthreads();   // sm.bad initialised before any pivot can fail
   leaf_blocks(S, sm, w, lane, std::make_integer_sequence<int, 16>{});
-  if (threadIdx.x == 0 && sm.bad < m) raise_status(st, kNotPD, perm[n - 1 - (k0 + sm.bad)]);
+  // only the first failing block reports (later ones run on garbage)
+  if (threadIdx.x == 0 && sm.bad < m && st->flags == 0) raise_status(st, kNotPD, perm[n - 1 - (k0 + sm.bad)]);
   float* xcol = X + k0 * n + k0 + lane;
 #pragma unroll
   for (int q = 0; q < 4; ++q)

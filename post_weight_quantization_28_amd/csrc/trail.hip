@@ -31,7 +31,6 @@ namespace gq {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef int v4i32_t __attribute__((ext_vector_type(4)));
 
 constexpr int kTM = 256, kTN = 128;        // workgroup tile
 constexpr int kTK = 16;                    // k per stage
@@ -46,21 +45,6 @@ constexpr int kTDma = 6;                   // DMA instructions per wave per stag
 // then cover all 64 banks)
 __device__ __forceinline__ int swz_a(int row) { return (row >> 3) & 1; }
 
-__device__ __forceinline__ void dma16_rsrc(uint32_t voff, v4i32_t rsrc, uint32_t soff, uint32_t lds_base) {
-  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, %3 offen lds"
-               :: "v"(voff), "s"(rsrc), "s"(lds_base), "s"(soff) : "memory");
-}
-
-__device__ __forceinline__ v4i32_t make_rsrc(const void* base, int64_t bytes) {
-  const uint64_t b = (uint64_t)(uintptr_t)base;
-  v4i32_t r;
-  r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-  r.y = __builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));   // stride 0
-  r.z = __builtin_amdgcn_readfirstlane((int)(uint32_t)(bytes > 0 ? bytes : 0));
-  r.w = 0x00020000;                                                    // raw, 32-bit format
-  return r;
-}
-
 // Wait until at most `stages` stages of kTDma DMA instructions of this wave
 // are outstanding, then barrier (one asm block, as in dma.h).
 __device__ __forceinline__ void wait_dma6_barrier(int stages) {
@@ -71,7 +55,6 @@ __device__ __forceinline__ void wait_dma6_barrier(int stages) {
 __global__ void __launch_bounds__(256, 2)
 k_trail_x3(TrailArgs g) {
   __shared__ __align__(16) uint8_t sm[kTSlots * kTSlot];
-  if (g.st != nullptr && g.st->flags != 0) return;
   // XCD-contiguous tile order: block b runs on XCD b % 8; give each XCD a
   // contiguous run of row-major tiles, so the rows of A it needs stay in its
   // L2 and each column tile of B is fetched once per XCD
