@@ -88,7 +88,10 @@ struct GemmArgs {
 };
 hipError_t launch_gemm_f32(hipStream_t s, const GemmArgs& g);
 hipError_t launch_gemm_pair(hipStream_t s, const GemmArgs& a, const GemmArgs* b);
-hipError_t launch_rotate(hipStream_t s, const float* X, float* U, int64_t n);
+// U = X with both indices reversed; if hi is non-null, also U's split-bf16
+// parts hi = bf16(U), lo = bf16(U - hi).
+hipError_t launch_rotate(hipStream_t s, const float* X, float* U, int64_t n, uint16_t* hi = nullptr,
+                         uint16_t* lo = nullptr);
 
 // ---- slab.hip
 // C[M x N] = alpha A[M x K] B + beta C for 1 <= K <= 128 (B: K x N, or N x K
@@ -140,8 +143,6 @@ struct TrailArgs {
   float* C; int64_t ldc;
 };
 hipError_t launch_trail_x3(hipStream_t s, const TrailArgs& g);
-// hi = bf16(x), lo = bf16(x - hi), elementwise over count floats.
-hipError_t launch_split_bf16(hipStream_t s, const float* x, int64_t count, uint16_t* hi, uint16_t* lo);
 
 // ---- sweep.hip
 struct SweepArgs {
@@ -160,6 +161,8 @@ struct SweepArgs {
   // kb a multiple of 32, at most 384; 0 = none
   const float* Esb; int64_t kb;
   float* row_loss;
+  // if non-null, E's split-bf16 parts are written beside it (same pitch)
+  uint16_t *Ehi, *Elo;
   const DevStatus* st;
 };
 hipError_t launch_sweep(hipStream_t s, const SweepArgs& a);

@@ -22,6 +22,7 @@
 // triangle of A.
 // All products are fp32 v_mfma_f32_32x32x2f32.
 #include "common.h"
+#include "dma.h"
 #include "leaf.h"
 
 #include <algorithm>
@@ -367,18 +368,27 @@ hipError_t launch_gemm_pair(hipStream_t s, const GemmArgs& a, const GemmArgs* b)
 hipError_t launch_gemm_f32(hipStream_t s, const GemmArgs& g) { return launch_gemm_pair(s, g, nullptr); }
 
 // ---------------------------------------------------------------- rotate
-// U[i][j] = X[n-1-i][n-1-j]: the flat array reversed.
-__global__ void k_rotate(const float* __restrict__ X, float* __restrict__ U, int64_t nn) {
+// U[i][j] = X[n-1-i][n-1-j]: the flat array reversed; optionally with U's
+// split-bf16 parts for the far-field update.
+__global__ void k_rotate(const float* __restrict__ X, float* __restrict__ U, int64_t nn, uint16_t* __restrict__ hi,
+                         uint16_t* __restrict__ lo) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < nn; q += stride)
-    U[q] = X[nn - 1 - q];
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < nn; q += stride) {
+    const float v = X[nn - 1 - q];
+    U[q] = v;
+    if (hi) {
+      const uint16_t h = f32_to_bf16_rne(v);
+      hi[q] = h;
+      lo[q] = f32_to_bf16_rne(v - bf16_to_f32(h));
+    }
+  }
 }
 
-hipError_t launch_rotate(hipStream_t s, const float* X, float* U, int64_t n) {
+hipError_t launch_rotate(hipStream_t s, const float* X, float* U, int64_t n, uint16_t* hi, uint16_t* lo) {
   const int64_t nn = n * n;
   int64_t blocks = ceil_div(nn, 256);
   if (blocks > 16384) blocks = 16384;
-  hipLaunchKernelGGL(k_rotate, dim3((unsigned)blocks), dim3(256), 0, s, X, U, nn);
+  hipLaunchKernelGGL(k_rotate, dim3((unsigned)blocks), dim3(256), 0, s, X, U, nn, hi, lo);
   return hipGetLastError();
 }
 

@@ -241,7 +241,7 @@ hipError_t factor_panels(hipStream_t s, float* A, float* X, int64_t n, const int
 // Steps 2-3 shared by quantize_layer and factor_hinv. On return (enqueued)
 // the upper factor U is in the A buffer (processing order).
 gptq_status enqueue_factor(hipStream_t s, const float* H, int64_t n, const gptq_params* p,
-                           char* ws, const QLayout& L) {
+                           char* ws, const QLayout& L, uint16_t* Uhi = nullptr, uint16_t* Ulo = nullptr) {
   DevStatus* st = reinterpret_cast<DevStatus*>(ws + L.status);
   double* lam = reinterpret_cast<double*>(ws + L.lam);
   float* diag = reinterpret_cast<float*>(ws + L.diag);
@@ -257,7 +257,7 @@ gptq_status enqueue_factor(hipStream_t s, const float* H, int64_t n, const gptq_
     HIP_TRY(launch_build_flipped(s, H, n, perm, diag, lam, A, st), "build");
   }
   HIP_TRY(factor_panels(s, A, X, n, perm, st), "factor");
-  HIP_TRY(launch_rotate(s, X, A, n), "rotate");
+  HIP_TRY(launch_rotate(s, X, A, n, Uhi, Ulo), "rotate");
   return GPTQ_OK;
 }
 
@@ -425,10 +425,6 @@ gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int
   uint8_t* codes = reinterpret_cast<uint8_t*>(ws + L.codes);
   float* loss = out->row_loss ? out->row_loss : reinterpret_cast<float*>(ws + L.loss);
 
-  if ((st = enqueue_factor(s, H, n, p, ws, L)) != GPTQ_OK) return st;
-  HIP_TRY(launch_w_prep(s, W, wdt == GPTQ_BF16, d_out, n, ldw, p->act_order ? perm : nullptr, Wf, dst),
-          "w prep");
-  HIP_TRY(launch_fill_f32(s, loss, (size_t)d_out, 0.f), "fill");
   const int64_t nq = p->n_quant;
   const int B = p->block;
   const bool two = use_two_level(n, p);
@@ -437,7 +433,12 @@ gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int
   uint16_t* Elo = reinterpret_cast<uint16_t*>(ws + L.Elo);
   uint16_t* Uhi = reinterpret_cast<uint16_t*>(ws + L.Uhi);
   uint16_t* Ulo = reinterpret_cast<uint16_t*>(ws + L.Ulo);
-  if (two) HIP_TRY(launch_split_bf16(s, U, n * n, Uhi, Ulo), "split U");
+  // the far field's split-bf16 operands are written by the kernels that
+  // produce U (the final rotation) and E (the sweep)
+  if ((st = enqueue_factor(s, H, n, p, ws, L, two ? Uhi : nullptr, two ? Ulo : nullptr)) != GPTQ_OK) return st;
+  HIP_TRY(launch_w_prep(s, W, wdt == GPTQ_BF16, d_out, n, ldw, p->act_order ? perm : nullptr, Wf, dst),
+          "w prep");
+  HIP_TRY(launch_fill_f32(s, loss, (size_t)d_out, 0.f), "fill");
   // Two-level lazy batch. Inside a super-block [s0, s1) each block updates
   // the super-block's later columns at once (fp32, K = B); when the
   // super-block is done, all of its errors update the columns right of it
@@ -463,6 +464,8 @@ gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int
       a.scales = out->scales; a.zeros = out->zeros; a.ngroups = nq / p->group;
       a.codes = codes; a.n_quant = nq; a.E = Eb; a.lde = sw; a.row_loss = loss; a.st = dst;
       a.Esb = E; a.kb = fused ? i0 - s0 : 0;
+      a.Ehi = two && s1 < n ? Ehi + (i0 - s0) : nullptr;
+      a.Elo = two && s1 < n ? Elo + (i0 - s0) : nullptr;
       HIP_TRY(launch_sweep(s, a), "sweep");
       const int64_t i1 = i0 + nc;
       const int64_t near_end = two ? s1 : n;
@@ -477,7 +480,6 @@ gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int
       }
     }
     if (two && s1 < n) {
-      HIP_TRY(launch_split_bf16(s, E, d_out * sw, Ehi, Elo), "split E");
       TrailArgs t{};
       t.M = d_out; t.N = n - s1; t.K = s1 - s0;
       t.Ahi = Ehi; t.Alo = Elo; t.lda = sw;

@@ -33,6 +33,7 @@
 // already quantized (fp32 MFMA, see near_update). That replaces the
 // separate right-looking near-field launches.
 #include "common.h"
+#include "dma.h"
 #include <utility>
 
 namespace gq {
@@ -432,6 +433,11 @@ k_sweep(SweepArgs a) {
         a.codes[row * a.n_quant + a.i0 + col] = (uint8_t)S.qv[c];
       }
       a.E[row * a.lde + col] = S.ev[c];
+      if (a.Ehi) {
+        const uint16_t h = f32_to_bf16_rne(S.ev[c]);
+        a.Ehi[row * a.lde + col] = h;
+        a.Elo[row * a.lde + col] = f32_to_bf16_rne(S.ev[c] - bf16_to_f32(h));
+      }
     }
     if (L == 0) a.row_loss[row] = loss0 + loss;
   }

@@ -247,24 +247,4 @@ hipError_t launch_trail_x3(hipStream_t s, const TrailArgs& g) {
   return hipGetLastError();
 }
 
-// ---- bf16 splitting of fp32 arrays: hi = bf16(x), lo = bf16(x - hi)
-__global__ void k_split_bf16(const float* __restrict__ x, int64_t count, uint16_t* __restrict__ hi,
-                             uint16_t* __restrict__ lo) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < count; q += stride) {
-    const float v = x[q];
-    const uint16_t h = f32_to_bf16_rne(v);
-    hi[q] = h;
-    lo[q] = f32_to_bf16_rne(v - bf16_to_f32(h));
-  }
-}
-
-hipError_t launch_split_bf16(hipStream_t s, const float* x, int64_t count, uint16_t* hi, uint16_t* lo) {
-  if (count <= 0) return hipSuccess;
-  int64_t blocks = ceil_div(count, 256);
-  if (blocks > 16384) blocks = 16384;
-  hipLaunchKernelGGL(k_split_bf16, dim3((unsigned)blocks), dim3(256), 0, s, x, count, hi, lo);
-  return hipGetLastError();
-}
-
 }  // namespace gq
