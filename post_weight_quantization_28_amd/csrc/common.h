@@ -158,7 +158,7 @@ struct SweepArgs {
   float* E; int64_t lde;        // d_out x B block errors (row pitch lde)
   // fused near field (B = 128 only): W_blk -= Esb[:, :kb] U[i0 - kb : i0, blk]
   // before the sweep; Esb is the super-block's error matrix (pitch lde),
-  // kb a multiple of 32, at most 384; 0 = none
+  // kb = 128, 256 or 384; 0 = none
   const float* Esb; int64_t kb;
   float* row_loss;
   // if non-null, E's split-bf16 parts are written beside it (same pitch)

@@ -229,89 +229,110 @@ __device__ __forceinline__ void sweep_all(SweepState<CPL>& S, const SweepArgs& a
 
 // ---------------------------------------------------------------- near field
 // upd[16][128] = E[rows, :kb] U[i0 - kb : i0, i0 : i0 + 128] for this
-// workgroup's 16 rows (kb a multiple of 32, at most 384). E's rows are
-// staged in LDS once; U streams through a double buffer of 32-row chunks.
-// Wave w computes columns 32w..32w+31 as two v_mfma_f32_16x16x4f32 tiles;
-// for MFMA t of a group of four, lane group g = lane / 16 feeds k = 16p +
-// 4g + t to both operands (E as one 16-byte read, U as four 4-byte reads).
+// workgroup's 16 rows (kb = 32 NCH, at most 384). E's rows and the first
+// kNearDepth 32-row chunks of U are requested up front and every later
+// chunk kNearDepth chunks ahead (four 16-byte pieces per thread, held in
+// registers; one wave per SIMD leaves room for them), so the chunks do not
+// each wait a full L2 round trip. They pass through a double buffer in
+// LDS. Wave w computes columns 32w..32w+31 as two v_mfma_f32_16x16x4f32
+// tiles; for MFMA t of a group of four, lane group g = lane / 16 feeds k =
+// 16p + 4g + t to both operands (E as one 16-byte read, U as four 4-byte
+// reads).
 constexpr int kNearMax = 384;   // largest kb: a 512-column super-block
 constexpr int kNearEP = kNearMax + 4;
 constexpr int kNearUP = 128 + 4;
 constexpr int kNearLds = 16 * kNearEP + 2 * 32 * kNearUP;   // floats (fits the U tile's region)
 constexpr int kUpdP = 128 + 4;
+constexpr int kNearDepth = 6;   // U chunks in flight
 
 typedef float nf_f32x4_t __attribute__((ext_vector_type(4)));
 
+struct NearCtx {
+  float* sE;        // [16][kNearEP]
+  float* sUc;       // [2][32][kNearUP]
+  const float* src; // this thread's first piece of chunk 0
+  int64_t ldu;
+  int tid, li, g, w;
+};
+
+// The chunk index C is a template argument, so the ring slot C % kNearDepth
+// is a compile-time index and the ring stays in registers.
+template <int C, int NCH>
+__device__ __forceinline__ void near_chunk(const NearCtx& x, nf_f32x4_t (&uc)[kNearDepth][4], nf_f32x4_t (&acc)[2]) {
+  constexpr int cur = C & 1, slot = C % kNearDepth;
+  float* dst = &x.sUc[(cur * 32 + (x.tid >> 5)) * kNearUP + 4 * (x.tid & 31)];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) *reinterpret_cast<nf_f32x4_t*>(dst + 8 * q * kNearUP) = uc[slot][q];
+  if constexpr (C + kNearDepth < NCH) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      uc[slot][q] = *reinterpret_cast<const nf_f32x4_t*>(x.src + (int64_t)(32 * (C + kNearDepth) + 8 * q) * x.ldu);
+  }
+  __syncthreads();   // chunk C (and, the first time, E) staged; buffer cur ^ 1 no longer read
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const float4 fa = *reinterpret_cast<const float4*>(&x.sE[x.li * kNearEP + 32 * C + 16 * p + 4 * x.g]);
+    const float* ub = &x.sUc[(cur * 32 + 16 * p + 4 * x.g) * kNearUP + 32 * x.w + x.li];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const float* q = ub + 16 * ct;
+      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.x, q[0], acc[ct], 0, 0, 0);
+      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.y, q[kNearUP], acc[ct], 0, 0, 0);
+      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.z, q[2 * kNearUP], acc[ct], 0, 0, 0);
+      acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.w, q[3 * kNearUP], acc[ct], 0, 0, 0);
+    }
+  }
+}
+
+template <int NCH, int... Cs>
+__device__ __forceinline__ void near_chunks(const NearCtx& x, nf_f32x4_t (&uc)[kNearDepth][4], nf_f32x4_t (&acc)[2],
+                                            std::integer_sequence<int, Cs...>) {
+  (near_chunk<Cs, NCH>(x, uc, acc), ...);
+}
+
+template <int NCH>
 __device__ __forceinline__ void near_update(const SweepArgs& a, float* stage, float* upd) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int li = lane & 15, g = lane >> 4;
-  const int kb = (int)a.kb;
+  constexpr int kb = 32 * NCH;
+  const int tid = threadIdx.x, lane = tid & 63;
+  NearCtx x;
+  x.tid = tid;
+  x.w = tid >> 6;
+  x.li = lane & 15;
+  x.g = lane >> 4;
+  x.sE = stage;
+  x.sUc = stage + 16 * kNearEP;
+  x.ldu = a.ldu;
   const int64_t r0 = (int64_t)blockIdx.x * 16;
-  float* sE = stage;                        // [16][kNearEP]
-  float* sUc = stage + 16 * kNearEP;        // [2][32][kNearUP]
   const float* Ub = a.U + (a.i0 - kb) * a.ldu + a.i0;
+  x.src = Ub + (int64_t)(tid >> 5) * a.ldu + 4 * (tid & 31);
   // E rows (clamped to the last row; those results are never used)
-  {
-    const int q4 = kb / 4;                  // float4 per E row
+  constexpr int q4 = kb / 4;                // float4 per E row
+  constexpr int NE = (16 * q4 + 255) / 256;
+  float4 ev[NE];
 #pragma unroll
-    for (int v = 0; v < kNearMax * 16 / 4 / 256; ++v) {
-      const int idx = tid + 256 * v;
-      if (idx < 16 * q4) {
-        const int rr = idx / q4, k4 = idx % q4;
-        const int64_t row = min(r0 + rr, a.d_out - 1);
-        *reinterpret_cast<float4*>(&sE[rr * kNearEP + 4 * k4]) =
-            *reinterpret_cast<const float4*>(a.Esb + row * a.lde + 4 * k4);
-      }
-    }
+  for (int v = 0; v < NE; ++v) {
+    const int idx = min(tid + 256 * v, 16 * q4 - 1);
+    const int rr = idx / q4, k4 = idx % q4;
+    const int64_t row = min(r0 + rr, a.d_out - 1);
+    ev[v] = *reinterpret_cast<const float4*>(a.Esb + row * a.lde + 4 * k4);
   }
-  // U chunk c: 32 rows x 128 columns, four 16-byte pieces per thread
-  float4 u0, u1, u2, u3;
-#define NEAR_LOAD(c)                                                                       \
-  do {                                                                                     \
-    const float* src_ = Ub + (int64_t)(32 * (c) + (tid >> 5)) * a.ldu + 4 * (tid & 31);    \
-    u0 = *reinterpret_cast<const float4*>(src_);                                           \
-    u1 = *reinterpret_cast<const float4*>(src_ + 8 * a.ldu);                               \
-    u2 = *reinterpret_cast<const float4*>(src_ + 16 * a.ldu);                              \
-    u3 = *reinterpret_cast<const float4*>(src_ + 24 * a.ldu);                              \
-  } while (0)
-#define NEAR_STORE(buf)                                                                    \
-  do {                                                                                     \
-    float* dst_ = &sUc[((buf) * 32 + (tid >> 5)) * kNearUP + 4 * (tid & 31)];              \
-    *reinterpret_cast<float4*>(dst_) = u0;                                                 \
-    *reinterpret_cast<float4*>(dst_ + 8 * kNearUP) = u1;                                   \
-    *reinterpret_cast<float4*>(dst_ + 16 * kNearUP) = u2;                                  \
-    *reinterpret_cast<float4*>(dst_ + 24 * kNearUP) = u3;                                  \
-  } while (0)
-  NEAR_LOAD(0);
-  NEAR_STORE(0);
-  __syncthreads();
+  nf_f32x4_t uc[kNearDepth][4];
+#pragma unroll
+  for (int c = 0; c < kNearDepth && c < NCH; ++c)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) uc[c][q] = *reinterpret_cast<const nf_f32x4_t*>(x.src + (int64_t)(32 * c + 8 * q) * a.ldu);
+#pragma unroll
+  for (int v = 0; v < NE; ++v) {
+    const int idx = tid + 256 * v;
+    if (idx < 16 * q4) *reinterpret_cast<float4*>(&x.sE[(idx / q4) * kNearEP + 4 * (idx % q4)]) = ev[v];
+  }
   nf_f32x4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-  const int nch = kb / 32;
-  for (int c = 0; c < nch; ++c) {
-    const int cur = c & 1;
-    if (c + 1 < nch) NEAR_LOAD(c + 1);
-#pragma unroll
-    for (int p = 0; p < 2; ++p) {
-      const float4 fa = *reinterpret_cast<const float4*>(&sE[li * kNearEP + 32 * c + 16 * p + 4 * g]);
-      const float* ub = &sUc[(cur * 32 + 16 * p + 4 * g) * kNearUP + 32 * w + li];
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct) {
-        const float* q = ub + 16 * ct;
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.x, q[0], acc[ct], 0, 0, 0);
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.y, q[kNearUP], acc[ct], 0, 0, 0);
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.z, q[2 * kNearUP], acc[ct], 0, 0, 0);
-        acc[ct] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa.w, q[3 * kNearUP], acc[ct], 0, 0, 0);
-      }
-    }
-    if (c + 1 < nch) NEAR_STORE(cur ^ 1);
-    __syncthreads();
-  }
-#undef NEAR_LOAD
-#undef NEAR_STORE
+  near_chunks<NCH>(x, uc, acc, std::make_integer_sequence<int, NCH>{});
 #pragma unroll
   for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-    for (int v = 0; v < 4; ++v) upd[(4 * g + v) * kUpdP + 32 * w + 16 * ct + li] = acc[ct][v];
+    for (int v = 0; v < 4; ++v) upd[(4 * x.g + v) * kUpdP + 32 * x.w + 16 * ct + x.li] = acc[ct][v];
+  __syncthreads();   // the staging region is free again
 }
 
 // One wave per SIMD is all a d_out = 4096 layer provides (16 lanes per row),
@@ -330,7 +351,10 @@ k_sweep(SweepArgs a) {
   float* upd = smem + B + B * B;
   const bool near = kNear && a.kb > 0;
   if (near) {
-    near_update(a, sU, upd);   // ends with a barrier: sU is free again
+    // kb is 128, 256 or 384 (a multiple of the 128-column block)
+    if (a.kb == 128) near_update<4>(a, sU, upd);
+    else if (a.kb == 256) near_update<8>(a, sU, upd);
+    else near_update<12>(a, sU, upd);   // each ends with a barrier: sU is free again
   }
 
   const int tid = threadIdx.x;
