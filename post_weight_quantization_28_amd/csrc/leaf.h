@@ -10,9 +10,9 @@
 // consecutive pivots; block b is owned by wave b % 4:
 //  * Cholesky, right-looking: lane i holds row i; wave w holds the columns
 //    of its blocks, j = 16q + 4w + c (q, c = 0..3), in registers a[q][c].
-//    The owner of block b takes its 4 pivots in registers: pivot from lane
-//    K (v_readlane), scale the column, update the block's later columns
-//    with the column's entries read by v_readlane.
+//    The owner of block b takes its 4 pivots in registers: it reads the
+//    block's 4 x 4 lower part once (v_readlane), factors it on wave-uniform
+//    values, and every lane forms its entries of the 4 columns from those.
 //  * Inverse X = L^{-1}, column-oriented forward substitution: lane c holds
 //    column c of X; wave w holds the rows of its blocks, x[q][c'] =
 //    X[16q + 4w + c'][lane]. The owner of block b finalises rows 4b..4b+3
@@ -51,45 +51,61 @@ __device__ __forceinline__ float lane_val(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-// Pivot C of block BLK on its owner wave: L's column K = 4 BLK + C from
-// the current Schur column, and its rank-1 update of the block's later
-// columns. A failed pivot (not positive or not finite) is recorded as a
+// The owner of block BLK takes its 4 pivots. The block's 4 x 4 lower part
+// is read once (10 independent v_readlane) and factored on wave-uniform
+// values; each lane then forms its entries of the 4 columns and of X's 4
+// rows with those values. Every FMA is the one a lane-by-lane pivot
+// sequence would do (same operands, same order), so the results are the
+// same; only the v_readlane between dependent steps are gone from the
+// chain. A failed pivot (not positive or not finite) is recorded as a
 // wave-uniform minimum, off the dependent chain; what follows it is then
 // garbage and the caller discards the result.
-template <int BLK, int C>
-__device__ __forceinline__ void leaf_pivot(LeafState& S, float (&invs)[4]) {
-  constexpr int qb = BLK / 4, K0 = 4 * BLK, K = K0 + C;
-  const float d2 = lane_val(S.a[qb][C], K);
-  if (!(d2 > 0.f && isfinite(d2))) S.bad = min(S.bad, K);
-  const float inv = __builtin_amdgcn_rsqf(d2);   // 1 / sqrt(d2)
-  const float d = d2 * inv;
-  const int lane = threadIdx.x & 63;
-  float l = (lane > K) ? S.a[qb][C] * inv : 0.f;
-  l = (lane == K) ? d : l;
-
-  S.a[qb][C] = l;
-  invs[C] = inv;
+template <int BLK>
+__device__ __forceinline__ void leaf_owner(LeafState& S, int lane) {
+  constexpr int qb = BLK / 4, K0 = 4 * BLK;
+  float b[4][4];   // b[r][c], c <= r: the block's Schur complement, then L
 #pragma unroll
-  for (int c2 = C + 1; c2 < 4; ++c2) S.a[qb][c2] = fmaf(-l, lane_val(l, K0 + c2), S.a[qb][c2]);
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c <= r; ++c) b[r][c] = lane_val(S.a[qb][c], K0 + r);
+  float inv[4];
+#pragma unroll
+  for (int C = 0; C < 4; ++C) {
+    const float d2 = b[C][C];
+    if (!(d2 > 0.f && isfinite(d2))) S.bad = min(S.bad, K0 + C);
+    inv[C] = __builtin_amdgcn_rsqf(d2);   // 1 / sqrt(d2)
+    b[C][C] = d2 * inv[C];
+#pragma unroll
+    for (int r = C + 1; r < 4; ++r) b[r][C] *= inv[C];
+#pragma unroll
+    for (int c2 = C + 1; c2 < 4; ++c2)
+#pragma unroll
+      for (int r = c2; r < 4; ++r) b[r][c2] = fmaf(-b[r][C], b[c2][C], b[r][c2]);
+  }
+  // this lane's entries of the 4 columns (rows above the block: zero)
+#pragma unroll
+  for (int C = 0; C < 4; ++C) {
+    const int K = K0 + C;
+    float l = (lane > K) ? S.a[qb][C] * inv[C] : 0.f;
+    l = (lane == K) ? b[C][C] : l;
+    S.a[qb][C] = l;
+#pragma unroll
+    for (int c2 = C + 1; c2 < 4; ++c2) S.a[qb][c2] = fmaf(-l, b[c2][C], S.a[qb][c2]);
+  }
+  // rows K0..K0+3 of X: forward substitution inside the block
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    S.x[qb][c] *= inv[c];
+#pragma unroll
+    for (int c2 = c + 1; c2 < 4; ++c2) S.x[qb][c2] = fmaf(-b[c2][c], S.x[qb][c], S.x[qb][c2]);
+  }
 }
 
 template <int BLK>
 __device__ __forceinline__ void leaf_block(LeafState& S, LeafSmem& sm, int w, int lane) {
   constexpr int qb = BLK / 4, ob = BLK % 4, K0 = 4 * BLK;
   if (w == ob) {
-    // ---- the block's 4 pivots
-    float invs[4];
-    leaf_pivot<BLK, 0>(S, invs);
-    leaf_pivot<BLK, 1>(S, invs);
-    leaf_pivot<BLK, 2>(S, invs);
-    leaf_pivot<BLK, 3>(S, invs);
-    // ---- rows K0..K0+3 of X: forward substitution inside the block
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      S.x[qb][c] *= invs[c];
-#pragma unroll
-      for (int c2 = c + 1; c2 < 4; ++c2) S.x[qb][c2] = fmaf(-lane_val(S.a[qb][c], K0 + c2), S.x[qb][c], S.x[qb][c2]);
-    }
+    leaf_owner<BLK>(S, lane);
     const int pl = leaf_pos(lane);
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
