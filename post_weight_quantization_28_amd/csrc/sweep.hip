@@ -349,14 +349,6 @@ k_sweep(SweepArgs a) {
   float* sInv = smem;
   float* sU = smem + B;
   float* upd = smem + B + B * B;
-  const bool near = kNear && a.kb > 0;
-  if (near) {
-    // kb is 128, 256 or 384 (a multiple of the 128-column block)
-    if (a.kb == 128) near_update<4>(a, sU, upd);
-    else if (a.kb == 256) near_update<8>(a, sU, upd);
-    else near_update<12>(a, sU, upd);   // each ends with a barrier: sU is free again
-  }
-
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int L = lane & 15;
@@ -393,9 +385,6 @@ k_sweep(SweepArgs a) {
   }
   const float diag = (tid < B && tid < nc) ? Ublk[(int64_t)tid * a.ldu + tid] : 1.f;
   const float loss0 = (row_ok && L == 0) ? a.row_loss[row] : 0.f;
-  // checked after the loads above are issued (they only read valid buffers):
-  // nothing is stored when an earlier step failed
-  if (a.st->flags != 0) return;
   SweepState<CPL> S;
   S.nc = nc;
   S.gmask = (a.group < B) ? a.group - 1 : -1;   // groups nest: a power of two below B
@@ -405,6 +394,17 @@ k_sweep(SweepArgs a) {
     S.w[c] = (row_ok && col < nc) ? a.Wf[row * a.ldw + a.i0 + col] : 0.f;
     S.ev[c] = 0.f;
     S.qv[c] = 0.f;
+  }
+  // checked after the loads above are issued (they only read valid buffers):
+  // nothing is stored when an earlier step failed
+  if (a.st->flags != 0) return;
+  // the in-super-block update runs while those loads are in flight
+  const bool near = kNear && a.kb > 0;
+  if (near) {
+    // kb is 128, 256 or 384 (a multiple of the 128-column block)
+    if (a.kb == 128) near_update<4>(a, sU, upd);
+    else if (a.kb == 256) near_update<8>(a, sU, upd);
+    else near_update<12>(a, sU, upd);   // each ends with a barrier: sU is free again
   }
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
