@@ -307,6 +307,15 @@ k_gemm_f32(GemmPair gp) {
   int t = (int)blockIdx.x - (which ? gp.nt0 : 0);
   GemmArgs g = gp.p[which];
   const int per = gp.per[which];          // tiles of one batch instance
+  // Triangular K ranges make tiles unequal. The tiles are ordered longest
+  // first and dealt to the CUs 256 at a time, so the workgroups that share a
+  // CU are t, t + 256, ...: every other full round is reversed (a serpentine),
+  // which pairs long tiles with short ones on each CU.
+  if (g.kmode != 0) {
+    const int total = which ? (int)gridDim.x - gp.nt0 : gp.nt0;
+    const int q = t >> 8, w = t & 255;
+    if ((q & 1) && (q << 8) + 256 <= total) t = (q << 8) + 255 - w;
+  }
   const int b = t / per;
   t -= b * per;
   g.A += b * g.sA;

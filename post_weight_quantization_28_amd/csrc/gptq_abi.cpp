@@ -420,7 +420,11 @@ gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int
   Timed whole(GPTQ_PROF_QUANTIZE, s);
   int32_t* invperm = reinterpret_cast<int32_t*>(ws + L.invperm);
   float* U = reinterpret_cast<float*>(ws + L.A);
-  float* Wf = reinterpret_cast<float*>(ws + L.Wf);
+  // Without act-order the processing order is the identity, so the working
+  // copy can live in w_hat itself: it ends holding the dequantised weights
+  // (and the updated unquantised columns) and needs no final copy.
+  const bool in_place = !p->act_order && out->w_hat != nullptr;
+  float* Wf = in_place ? out->w_hat : reinterpret_cast<float*>(ws + L.Wf);
   float* E = reinterpret_cast<float*>(ws + L.E);
   uint8_t* codes = reinterpret_cast<uint8_t*>(ws + L.codes);
   float* loss = out->row_loss ? out->row_loss : reinterpret_cast<float*>(ws + L.loss);
@@ -488,7 +492,8 @@ gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int
       HIP_TRY(launch_trail_x3(s, t), "far-field update");
     }
   }
-  HIP_TRY(launch_finish(s, Wf, codes, invperm, d_out, n, nq, p->group, out->w_hat, out->codes, out->g_idx),
+  HIP_TRY(launch_finish(s, Wf, codes, invperm, d_out, n, nq, p->group, in_place ? nullptr : out->w_hat,
+                        out->codes, out->g_idx),
           "finish");
   // the processing order is the identity without act-order
   if (out->qweight)
