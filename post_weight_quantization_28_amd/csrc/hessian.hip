@@ -25,6 +25,8 @@
 #include "common.h"
 #include "dma.h"
 
+#include <utility>
+
 #include <type_traits>
 
 namespace gq {
@@ -468,10 +470,16 @@ hipError_t launch_hessian_partials_f32(hipStream_t s, const float* X, int64_t T,
 // H[i][j] (i <= j) = base + 2 * sum_s part[s][i][j]; H[j][i] = H[i][j].
 // One 64x64 tile on or above the diagonal per workgroup; thread (ty, tx)
 // sums rows ty + 16 q of columns 4 tx .. 4 tx + 3 with 16-byte loads when
-// the row stride allows, so each thread keeps 4 x splits loads in flight.
+// the row stride allows. The split count S is a template argument: a
+// row's S loads are all issued before the sum (in split order, so the
+// result is the same as a sequential sum), one memory round trip per row
+// instead of one per split.
+typedef float red_f32x4_t __attribute__((ext_vector_type(4)));
+
+template <int S>
 __global__ void __launch_bounds__(256)
-k_hessian_reduce(const float* __restrict__ part, int splits, int64_t n, float* __restrict__ H,
-                 int zero_first) {
+k_hessian_reduce(const float* __restrict__ part, int64_t n, float* __restrict__ H, int zero_first) {
+  constexpr int splits = S;
   __shared__ float tile[64][65];
   const int nt = (int)ceil_div(n, 64);
   int a, b;
@@ -487,10 +495,13 @@ k_hessian_reduce(const float* __restrict__ part, int splits, int64_t n, float* _
     float v[4] = {0.f, 0.f, 0.f, 0.f};
     if (i < n) {
       if (vec) {
+        red_f32x4_t x[S];
+#pragma unroll
+        for (int sp = 0; sp < S; ++sp) x[sp] = *reinterpret_cast<const red_f32x4_t*>(part + sp * nn + i * n + j0);
         float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int sp = 0; sp < splits; ++sp) {
-          const float4 x = *reinterpret_cast<const float4*>(part + sp * nn + i * n + j0);
-          sum.x += x.x; sum.y += x.y; sum.z += x.z; sum.w += x.w;
+#pragma unroll
+        for (int sp = 0; sp < S; ++sp) {
+          sum.x += x[sp].x; sum.y += x[sp].y; sum.z += x[sp].z; sum.w += x[sp].w;
         }
         const float s4[4] = {sum.x, sum.y, sum.z, sum.w};
 #pragma unroll
@@ -526,11 +537,24 @@ k_hessian_reduce(const float* __restrict__ part, int splits, int64_t n, float* _
   }
 }
 
+template <int S>
+static void launch_reduce_s(hipStream_t s, dim3 grid, const float* part, int64_t n, float* H, int zero_first) {
+  hipLaunchKernelGGL(k_hessian_reduce<S>, grid, dim3(256), 0, s, part, n, H, zero_first);
+}
+
+template <int... Ss>
+static bool launch_reduce_any(int splits, std::integer_sequence<int, Ss...>, hipStream_t s, dim3 grid,
+                              const float* part, int64_t n, float* H, int zero_first) {
+  return ((splits == Ss + 1 ? (launch_reduce_s<Ss + 1>(s, grid, part, n, H, zero_first), true) : false) || ...);
+}
+
 hipError_t launch_hessian_reduce(hipStream_t s, const float* part, int splits, int64_t n,
                                  float* H, int zero_first) {
   const int nt = (int)ceil_div(n, 64);
-  hipLaunchKernelGGL(k_hessian_reduce, dim3(nt * (nt + 1) / 2), dim3(256), 0, s, part, splits, n,
-                     H, zero_first);
+  const dim3 grid(nt * (nt + 1) / 2);
+  // hessian_splits() returns 1..16
+  if (!launch_reduce_any(splits, std::make_integer_sequence<int, 16>{}, s, grid, part, n, H, zero_first))
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
