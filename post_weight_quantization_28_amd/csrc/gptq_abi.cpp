@@ -254,7 +254,8 @@ gptq_status enqueue_factor(hipStream_t s, const float* H, int64_t n, const gptq_
     HIP_TRY(launch_fill_f32(s, X, (size_t)n * n, 0.f), "fill");
     HIP_TRY(launch_prep_diag(s, H, n, diag, lam, p->damp, st), "prep diag");
     HIP_TRY(launch_order(s, diag, n, p->n_quant, p->act_order, perm, invperm), "order");
-    HIP_TRY(launch_build_flipped(s, H, n, perm, diag, lam, A, st), "build");
+    // the processing order is the identity without act-order
+    HIP_TRY(launch_build_flipped(s, H, n, p->act_order ? perm : nullptr, diag, lam, A, st), "build");
   }
   HIP_TRY(factor_panels(s, A, X, n, perm, st), "factor");
   HIP_TRY(launch_rotate(s, X, A, n, Uhi, Ulo), "rotate");

@@ -112,24 +112,46 @@ hipError_t launch_order(hipStream_t s, const float* diag, int64_t n, int64_t n_q
 }
 
 // A[a][b] = H_d[p][q], p = perm[n-1-a], q = perm[n-1-b]; lower part only
-// (b <= a). The diagonal uses the dead-fixed value plus lambda.
+// (b <= a). The diagonal uses the dead-fixed value plus lambda. perm ==
+// nullptr: the identity order, where a row of A is a row of H read
+// backwards (16-byte loads when n % 4 == 0). Four outputs per thread and
+// pass, all loads of a pass issued before its stores.
 __global__ void __launch_bounds__(256)
 k_build_flipped(const float* __restrict__ H, int64_t n, const int32_t* __restrict__ perm,
                 const float* __restrict__ diag, const double* __restrict__ lam,
                 float* __restrict__ A, DevStatus* st) {
   const int64_t a = blockIdx.x;
-  const int64_t p = perm[n - 1 - a];
+  const int64_t p = perm ? perm[n - 1 - a] : n - 1 - a;
   const float lamf = (float)lam[0];
-  for (int64_t b = threadIdx.x; b <= a; b += 256) {
-    const int64_t q = perm[n - 1 - b];
-    float v;
-    if (b == a) {
-      v = diag[p] + lamf;
-    } else {
-      v = H[p * n + q];
-      if (!isfinite(v)) raise_status(st, kNonFinite, min(p, q));
+  const bool vec = perm == nullptr && (n & 3) == 0 && (((uintptr_t)H & 15) == 0) && (((uintptr_t)A & 15) == 0);
+  for (int64_t b0 = 4 * threadIdx.x; b0 <= a; b0 += 4 * 256) {
+    float v[4];
+    int64_t q[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t b = min(b0 + e, a);
+      q[e] = perm ? perm[n - 1 - b] : n - 1 - b;
     }
-    A[a * n + b] = v;
+    if (vec) {
+      // H[p][n-4-b0 .. n-1-b0] holds q[3], q[2], q[1], q[0] (b0 + 3 may pass a:
+      // those entries are not stored)
+      const float4 h = *reinterpret_cast<const float4*>(H + p * n + (n - 4 - b0));
+      v[0] = h.w; v[1] = h.z; v[2] = h.y; v[3] = h.x;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = H[p * n + q[e]];
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t b = b0 + e;
+      if (b > a) break;
+      if (b == a) {
+        v[e] = diag[p] + lamf;
+      } else if (!isfinite(v[e])) {
+        raise_status(st, kNonFinite, min(p, q[e]));
+      }
+      A[a * n + b] = v[e];
+    }
   }
 }
 
