@@ -61,7 +61,9 @@ def test_hessian_streaming_accumulates():
 
 
 # ---------------------------------------------------------------- factorisation
-@pytest.mark.parametrize("n,act_order", [(64, False), (200, False), (320, True), (1000, False)])
+# n = 202: rows not a multiple of 4 floats, so the trailing updates and the
+# flipped-matrix build take their general (unvectorised) kernels
+@pytest.mark.parametrize("n,act_order", [(64, False), (200, False), (202, False), (320, True), (1000, False)])
 def test_factor_matches_lapack(n, act_order):
     wl = synth.make_workload("c2", d_out=4, n=n, T=4 * n, group=4)
     H64 = O.hessian(wl.X)
@@ -93,6 +95,8 @@ CASES = [
     ("c2", dict(d_out=96, n=1408, T=4096), dict()),
     # groups spanning two 128-column blocks: the separate near-field launches
     ("c2", dict(d_out=64, n=1024, T=4096), dict(group=256)),
+    # n % 4 != 0: the general trailing-update and flipped-build kernels
+    ("c2", dict(d_out=56, n=266, T=4096), dict(n_quant=256, group=64)),
 ]
 
 
