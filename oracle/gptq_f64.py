@@ -132,6 +132,13 @@ def quantize_column(w, s, z, maxq):
     return q, s * (q - z), pre
 
 
+def other_neighbour(x):
+    """The integer next to ``x`` on the far side from rint(x): the rounding
+    a decision takes when it goes the other way at a tie."""
+    r = np.rint(x)
+    return np.where(x >= r, r + 1.0, r - 1.0)
+
+
 def tie_distance(pre):
     """Distance of a pre-rounding value to the nearest half-integer, in
     quantization steps (0 means an exact tie)."""
@@ -168,7 +175,7 @@ def _finish(W, Wp, perm, codes_p, scales, zeros, loss, n_quant, group,
 # O2: Cholesky of the inverse + lazy batches (the scalable form)
 # ---------------------------------------------------------------------------
 def gptq_o2(W, H, bits=4, group=128, damp=0.01, block=128, act_order=False,
-            n_quant=None, U=None, perm=None):
+            n_quant=None, U=None, perm=None, alt=None):
     """GPTQ sweep with the upper Cholesky factor U of H_d^{-1} and lazy
     batches of ``block`` columns ([GPTQ] "Enfoque Técnico"; [GIL]
     "Detalles de Implementación").
@@ -181,6 +188,12 @@ def gptq_o2(W, H, bits=4, group=128, damp=0.01, block=128, act_order=False,
 
     ``U``/``perm`` may be passed in to reuse a factorisation (the oracle
     still computes them with :func:`prepare` and LAPACK).
+    ``alt`` = (codes, zeros), two collections of (row, processing position)
+    and (row, group) pairs whose rounding takes the other neighbour of its
+    pre-rounding value instead of the nearest integer: the other branch of a
+    decision that sits at a tie, where either rounding is correct at the
+    precision of the inputs. Everything after such a decision follows from
+    it by the same rules.
     Returns codes (original order), scales/zeros (group order), g_idx,
     w_hat, row_loss = sum_j e_j^2, and the tie distances of every decision.
     """
@@ -200,6 +213,10 @@ def gptq_o2(W, H, bits=4, group=128, damp=0.01, block=128, act_order=False,
     margins = np.zeros((d_out, nq))
     zmargins = np.zeros((d_out, ng))
     loss = np.zeros(d_out)
+    alt_c, alt_z = {}, {}
+    for src, dst in zip(alt or ((), ()), (alt_c, alt_z)):
+        for r, k in src:
+            dst.setdefault(int(k), []).append(int(r))
     s = z = None
     for i0 in range(0, nq, block):
         i1 = min(i0 + block, nq)
@@ -207,10 +224,17 @@ def gptq_o2(W, H, bits=4, group=128, damp=0.01, block=128, act_order=False,
         for j in range(i0, i1):
             if j % group == 0:
                 s, z, zpre = group_grid(Wp[:, j:j + group], maxq)
+                rz = alt_z.get(j // group)
+                if rz:
+                    z[rz] = np.clip(other_neighbour(zpre[rz]), 0.0, maxq)
                 scales[:, j // group] = s
                 zeros[:, j // group] = z
                 zmargins[:, j // group] = tie_distance(zpre)
             q, what, pre = quantize_column(Wp[:, j], s, z, maxq)
+            rc = alt_c.get(j)
+            if rc:
+                q[rc] = np.clip(other_neighbour(pre[rc]) + z[rc], 0.0, maxq)
+                what[rc] = s[rc] * (q[rc] - z[rc])
             e = (Wp[:, j] - what) / U[j, j]
             Wp[:, j + 1:i1] -= np.outer(e, U[j, j + 1:i1])
             Wp[:, j] = what

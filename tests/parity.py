@@ -10,14 +10,23 @@ sits next to a half-integer):
     order is a tie for the oracle: its pre-rounding value lies within
     TAU = 1e-3 quantization steps of a half-integer. Later differences in
     the same row are the cascade of that tie.
+  * tie branches: at such a tie either rounding is correct, so the oracle is
+    rerun with the other rounding there (its own arithmetic; the GPU only
+    picks which branch a row is held to) and the row must then match
+    exactly, repeating at each further tie: every row of the GPU's output
+    is one of the oracle's valid runs.
   * layer error r within 1e-3 (relative) of the oracle's.
 """
+import time
+
 import numpy as np
 import torch
 
 from oracle import gptq_f64 as O
+from oracle import packing as P
 
 TAU = 1e-3
+LOSS_RTOL = 1e-3
 
 
 def to_dev(wl_vals, bits=None, dtype="f32"):
@@ -67,20 +76,161 @@ def first_mismatch_report(gpu_codes_orig, gpu_zeros, orc, group, tau=TAU):
     return rate, len(rows), bad
 
 
-def check_quant(res, wl, H64, orc, params, nq, report=None):
-    """Apply the acceptance rules to a QuantResult against oracle output."""
+def tie_branch_report(gpu_codes_orig, gpu_zeros, W, H64, orc, params, nq, tau=TAU, max_ties=16):
+    """Follow the oracle's own branches at its ties.
+
+    Where the first decision (processing order) in which a row differs is
+    one the oracle takes at a tie (within tau steps of a half-integer), both
+    roundings are correct at the precision of the inputs: the oracle is run
+    again with that decision's other rounding (gptq_o2's ``alt``) and the
+    row compared again, until it matches or differs somewhere that is not a
+    tie. The oracle computes each branch itself; the GPU's output only
+    selects which of the oracle's branches a row is compared with.
+    Returns (identity against the branched oracle, ties followed per row,
+    bad rows)."""
+    p = params
+    perm = orc["perm"]
+    g = np.asarray(gpu_codes_orig)[:, perm[:nq]]
+    gz = np.asarray(gpu_zeros)
+    U = None
+    alt_c, alt_z = [], []
+    ties = np.zeros(len(g), int)
+    bad = set()
+    o = orc
+    for it in range(max_ties + 1):
+        cm = g != o["codes_proc"]
+        zm = gz != o["zeros"]
+        pending = [int(r) for r in np.nonzero(cm.any(1) | zm.any(1))[0] if int(r) not in bad]
+        if not pending:
+            break
+        if it == max_ties:
+            bad.update(pending)
+            break
+        for r in pending:
+            jc = int(np.argmax(cm[r])) if cm[r].any() else nq
+            zi = int(np.argmax(zm[r])) if zm[r].any() else zm.shape[1]
+            jz = zi * p["group"] if zi < zm.shape[1] else nq
+            if jz <= jc and o["zmargins"][r, zi] < tau:
+                alt_z.append((r, zi))
+            elif jz > jc and o["margins"][r, jc] < tau:
+                alt_c.append((r, jc))
+            else:
+                bad.add(r)
+                continue
+            ties[r] += 1
+        if U is None:
+            Hd, _ = O.prepare(H64, p["damp"], p["act_order"], nq)
+            U = O.upper_chol_of_inverse(Hd)
+            del Hd
+        o = O.gptq_o2(W, None, p["bits"], p["group"], p["damp"], p["block"], p["act_order"], nq,
+                      U=U, perm=perm, alt=(alt_c, alt_z))
+    rate = 1.0 - (g != o["codes_proc"]).mean()
+    return rate, ties, sorted(bad)
+
+
+def check_quant(res, wl, H64, orc, params, nq, report=None, min_identity=0.999):
+    """Apply the acceptance rules to a QuantResult against oracle output:
+    the plain identity (at least ``min_identity``, None: reported only), the
+    first-mismatch tie rule, identity 1 against the oracle's tie branches,
+    the layer error and g_idx."""
     codes = res.codes.cpu().numpy()
     zeros = res.zeros.cpu().numpy()
     rate, nrows, bad = first_mismatch_report(codes, zeros, orc, params["group"])
+    brate, ties, bbad = tie_branch_report(codes, zeros, wl.W, H64, orc, params, nq)
     w_hat = res.w_hat.cpu().numpy().astype(np.float64)
     r_gpu = O.layer_error(wl.W, w_hat, H64)
     r_orc = O.layer_error(wl.W, orc["w_hat"], H64)
-    info = dict(identity=rate, rows_mismatch=nrows, bad_rows=bad[:10], r_gpu=r_gpu, r_oracle=r_orc)
+    info = dict(identity=rate, rows_mismatch=nrows, bad_rows=bad[:10], branched_identity=brate,
+                ties_followed=int(ties.sum()), max_ties_in_row=int(ties.max(initial=0)),
+                branch_bad_rows=bbad[:10], r_gpu=r_gpu, r_oracle=r_orc)
     if report is not None:
         report.update(info)
-    assert rate >= 0.999, info
+    if min_identity is not None:
+        assert rate >= min_identity, info
     assert not bad, info
+    assert not bbad and brate == 1.0, info
     assert abs(r_gpu - r_orc) <= 1e-3 * r_orc, info
     # g_idx is integer work: exact
     assert np.array_equal(res.g_idx.cpu().numpy(), orc["g_idx"]), "g_idx"
     return info
+
+
+def dev64(a):
+    return torch.from_numpy(np.ascontiguousarray(a, np.float64)).cuda()
+
+
+def quad_rows(D, Mt):
+    """Row-wise D_r M D_r^T in float64 on the device (Mt: M as a device tensor)."""
+    Dt = dev64(D)
+    q = ((Dt @ Mt) * Dt).sum(1)
+    return q.cpu().numpy()
+
+
+def check_any_size(wl, H32, res, t0, say=print):
+    """Properties that hold at any size, on every row of a QuantResult:
+
+      * format: codes and zero points in range, positive finite scales,
+        w_hat equal to s (q - z) bit for bit, the packed words equal to the
+        oracle's packing of the GPU's codes, g_idx exact without act-order;
+      * the loss identity: the row loss the sweep reports, sum_j e_j^2,
+        equals delta^T H_d delta for delta = w - w_hat (processing order).
+        In exact arithmetic W_final = W - E U and U H_d U^T = I make the two
+        equal, so the check ties the factorisation, the sweep and both
+        trailing updates together. Tolerance: the relative layer-error bound
+        1e-3 (the identity's right side is the damped layer error itself);
+      * feedback pays: the undamped layer error is below round-to-nearest's
+        on the same grid rules (asserted without appended columns; with
+        them it is reported: on the full 5120-wide augmented 2-bit layer the
+        error lands about 0.5 % above round-to-nearest's while the sampled
+        rows match the oracle's layer error within 1e-6, so there it is an
+        observation about the method at that damping, not a check).
+    H32 is the H the GPU was given."""
+    p = wl.params
+    nq, bits, group = wl.n_quant, p["bits"], p["group"]
+    codes = res.codes.cpu().numpy()
+    zeros = res.zeros.cpu().numpy()
+    scales = res.scales.cpu().numpy()
+    w_hat = res.w_hat.cpu().numpy()
+    g_idx = res.g_idx.cpu().numpy()
+    rl = res.row_loss.cpu().numpy().astype(np.float64)
+
+    # format
+    maxq = (1 << bits) - 1
+    assert codes.max() <= maxq and zeros.max() <= maxq
+    assert np.all(scales > 0) and np.all(np.isfinite(scales))
+    recon = scales[:, g_idx] * (codes.astype(np.float32) - zeros[:, g_idx].astype(np.float32))
+    assert np.array_equal(recon.astype(np.float32), w_hat[:, :nq])
+    assert np.array_equal(res.qweight.cpu().numpy().view(np.uint32), P.pack(codes, bits))
+    if not p["act_order"]:
+        assert np.array_equal(g_idx, np.arange(nq) // group)
+    assert np.all(np.isfinite(w_hat)) and np.all(np.isfinite(rl)) and np.all(rl >= 0)
+
+    # loss identity (processing order)
+    Hd, perm = O.prepare(H32, p["damp"], p["act_order"], nq)
+    Mt = dev64(Hd)
+    del Hd
+    D = (wl.W.astype(np.float64) - w_hat.astype(np.float64))[:, perm]
+    q = quad_rows(D, Mt)
+    del Mt, D
+    dev = np.abs(rl - q) / np.maximum(q, 1e-300)
+    say(f"{wl.name}: loss identity max rel dev {dev.max():.3e} (median {np.median(dev):.3e}) "
+        f"at {time.perf_counter() - t0:.1f} s")
+    assert dev.max() <= LOSS_RTOL
+
+    # feedback pays: undamped layer error vs round-to-nearest (original order)
+    Mt = dev64(H32)
+    rt = O.rtn(wl.W[:, :nq], bits, group)
+    W64 = wl.W.astype(np.float64)
+    Dr = W64.copy()
+    Dr[:, :nq] -= rt["w_hat"]
+    Dr[:, nq:] = 0.0
+    den = quad_rows(W64, Mt).sum()
+    r_gptq = quad_rows(W64 - w_hat.astype(np.float64), Mt).sum() / den
+    r_rtn = quad_rows(Dr, Mt).sum() / den
+    del Mt
+    torch.cuda.empty_cache()
+    say(f"{wl.name}: layer error {r_gptq:.4e} vs round-to-nearest {r_rtn:.4e} "
+        f"at {time.perf_counter() - t0:.1f} s")
+    if nq == wl.n:
+        assert r_gptq < r_rtn
+    return rl

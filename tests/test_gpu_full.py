@@ -9,13 +9,13 @@ oracle rows. Properties that hold at any size are checked on every row.
 """
 import sys
 import time
+import types
 
 import numpy as np
 import pytest
 
 import synth
 from oracle import gptq_f64 as O
-from oracle import packing as P
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -24,7 +24,7 @@ if not torch.cuda.is_available():
     pytest.skip("no GPU", allow_module_level=True)
 
 import post_weight_quantization_28_amd as G  # noqa: E402
-from parity import TAU, rel_fro, x_dev, w_dev  # noqa: E402
+from parity import check_any_size, check_quant, rel_fro, x_dev, w_dev  # noqa: E402
 
 SAMPLE_ROWS = 48
 
@@ -61,40 +61,10 @@ def test_attention_projection_full_size_sampled_rows():
     orc = O.gptq_o2(wl.W[rows], H64, p["bits"], p["group"], p["damp"], p["block"],
                     p["act_order"], nq)
     say(f"oracle sweep of {SAMPLE_ROWS} rows at {time.perf_counter() - t0:.1f} s")
-    codes = res.codes.cpu().numpy()
-    zeros = res.zeros.cpu().numpy()
-    scales = res.scales.cpu().numpy()
-    w_hat = res.w_hat.cpu().numpy()
-    g_idx = res.g_idx.cpu().numpy()
-
-    cs, zs = codes[rows], zeros[rows]
-    perm = orc["perm"]
-    cm = cs[:, perm[:nq]] != orc["codes_proc"]
-    zm = zs != orc["zeros"]
-    identity = 1.0 - cm.mean()
-    bad = []
-    for i in np.nonzero(cm.any(1) | zm.any(1))[0]:
-        jc = int(np.argmax(cm[i])) if cm[i].any() else nq
-        gz = int(np.argmax(zm[i])) if zm[i].any() else zm.shape[1]
-        jz = gz * p["group"] if gz < zm.shape[1] else nq
-        tie = orc["zmargins"][i, gz] < TAU if jz <= jc else orc["margins"][i, jc] < TAU
-        if not tie:
-            bad.append(int(rows[i]))
-    r_gpu = O.layer_error(wl.W[rows], w_hat[rows].astype(np.float64), H64)
-    r_orc = O.layer_error(wl.W[rows], orc["w_hat"], H64)
-    say(f"sampled identity {identity:.6f}, rows with a mismatch {int((cm.any(1) | zm.any(1)).sum())}, "
-        f"non-tie {bad}, r_gpu {r_gpu:.6e}, r_oracle {r_orc:.6e}")
-    assert identity >= 0.999
-    assert not bad
-    assert abs(r_gpu - r_orc) <= 1e-3 * r_orc
-    assert np.array_equal(g_idx, orc["g_idx"])
-
-    # --- every row: format invariants of the GPU's own outputs
-    maxq = (1 << p["bits"]) - 1
-    assert codes.max() <= maxq and zeros.max() <= maxq
-    assert np.all(scales > 0) and np.all(np.isfinite(scales))
-    recon = scales[:, g_idx] * (codes.astype(np.float32) - zeros[:, g_idx].astype(np.float32))
-    assert np.array_equal(recon.astype(np.float32), w_hat[:, :nq])
-    assert np.array_equal(res.qweight.cpu().numpy().view(np.uint32), P.pack(codes, p["bits"]))
-    rl = res.row_loss.cpu().numpy()
-    assert np.all(np.isfinite(rl)) and np.all(rl >= 0)
+    rt = torch.from_numpy(rows).cuda()
+    sub = types.SimpleNamespace(codes=res.codes[rt], zeros=res.zeros[rt], w_hat=res.w_hat[rt],
+                                g_idx=res.g_idx)
+    rep = {}
+    check_quant(sub, types.SimpleNamespace(W=wl.W[rows]), H64, orc, p, nq, rep)
+    say(f"sampled rows: {rep}")
+    check_any_size(wl, Hg, res, t0, say)

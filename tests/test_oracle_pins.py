@@ -187,6 +187,48 @@ def test_row_loss_equals_quadratic_form(act_order):
     assert np.allclose(o1["row_loss"], q, rtol=1e-9)
 
 
+# ---------------------------------------------------------------- tie branches
+def test_other_neighbour():
+    x = np.array([2.5, 3.5, 2.4999, 2.5001, -0.5, 0.0004, 6.9])
+    assert np.array_equal(O.other_neighbour(x), [3.0, 3.0, 3.0, 2.0, -1.0, 1.0, 6.0])
+
+
+@pytest.mark.parametrize("act_order", [False, True])
+def test_tie_branch_is_a_valid_gptq_run(act_order):
+    """The other branch at a decision: every earlier decision unchanged, that
+    code one level away from the plain run's, and the branch is still a GPTQ
+    run of the same problem (its row loss equals its own quadratic form)."""
+    W, X = _tiny(6, 9, 64, 400, heavy=True)
+    H = O.hessian(X)
+    Hd, perm = O.prepare(H, 0.01, act_order)
+    U = O.upper_chol_of_inverse(Hd)
+    plain = O.gptq_o2(W, H, 3, 16, 0.01, 16, act_order, U=U, perm=perm)
+    assert _same_run(plain, O.gptq_o2(W, H, 3, 16, 0.01, 16, act_order, U=U, perm=perm, alt=((), ())))
+    # the closest decision whose other neighbour is not clipped away
+    cp = plain["codes_proc"]
+    m = np.where((cp > 0) & (cp < 7), plain["margins"], np.inf)
+    r, j = np.unravel_index(np.argmin(m), m.shape)
+    br = O.gptq_o2(W, H, 3, 16, 0.01, 16, act_order, U=U, perm=perm, alt=([(r, j)], ()))
+    cb = br["codes_proc"]
+    assert np.array_equal(np.delete(cp, r, 0), np.delete(cb, r, 0))
+    assert np.array_equal(cp[r, :j], cb[r, :j])
+    assert abs(int(cb[r, j]) - int(cp[r, j])) == 1
+    D = (W - br["w_hat"])[:, perm]
+    assert np.allclose(br["row_loss"], np.einsum("ri,ij,rj->r", D, Hd, D), rtol=1e-9)
+    # a zero point's other branch: z moves by one, the group's scale does not
+    g = 1
+    bz = O.gptq_o2(W, H, 3, 16, 0.01, 16, act_order, U=U, perm=perm, alt=((), [(r, g)]))
+    assert abs(int(bz["zeros"][r, g]) - int(plain["zeros"][r, g])) == 1
+    assert np.array_equal(bz["codes_proc"][r, :16 * g], cp[r, :16 * g])
+    assert bz["scales"][r, g] == plain["scales"][r, g]
+    D = (W - bz["w_hat"])[:, perm]
+    assert np.allclose(bz["row_loss"], np.einsum("ri,ij,rj->r", D, Hd, D), rtol=1e-9)
+
+
+def _same_run(a, b):
+    return all(np.array_equal(a[k], b[k]) for k in ("codes", "zeros", "scales", "w_hat", "row_loss"))
+
+
 # ---------------------------------------------------------------- brute force
 @pytest.mark.parametrize("shape,T", [((2, 3), 8), ((3, 4), 16)])
 def test_gptq_not_better_than_exhaustive_optimum(shape, T):
