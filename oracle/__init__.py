@@ -11,6 +11,7 @@ Modules
 gptq_f64   the method itself (Hessian, damping/ordering, the O1 and O2 sweeps,
            round-to-nearest, brute force, layer error)
 packing    the LSB-first code bitstream and its inverse
+dequant    the dequantising product Y = X W_hat^T of a packed layer
 memory     storage accounting used by the pages' worked examples
 
 Every function names the passage of the pages it follows. The pages are:
