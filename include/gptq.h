@@ -148,6 +148,34 @@ gptq_status gptq_unpack_codes(void *stream, const uint32_t *qweight,
                               int64_t d_out, int64_t n_quant, int32_t bits,
                               uint8_t *codes);
 
+/* ---- Inference: dequantising product of a packed layer ---------------------
+ * Y (M x d_out fp32, row pitch ldy >= d_out) = X W_hat^T for X (M x n, bf16
+ * only: xdt must be GPTQ_BF16, row pitch ldx >= n with ldx % 8 == 0, 16-byte
+ * aligned base) and W_hat[o][k] = scales[o][k/group] * (q[o][k] -
+ * zeros[o][k/group]), the codes q read from qweight in the layout above
+ * (d_out x n*bits/32 words: n_quant = n, contiguous groups, i.e. a layer
+ * quantized without act-order, or whose g_idx is k / group). group must be a
+ * positive multiple of 32 that divides n. Products of bf16 activations and
+ * the integers q - z are exact in fp32 and each group's sum is scaled once
+ * (the weights are never rounded to bf16); sums are fp32 in a fixed order,
+ * so results are bitwise reproducible. Workspace:
+ * gptq_dequant_matmul_workspace_bytes (0 when one pass covers the whole
+ * product; otherwise fp32 partials of a split over the groups).
+ * Asynchronous on ``stream``. M == 0 or d_out == 0 enqueues nothing; n == 0
+ * writes zeros.
+ * ("El balance de errores de la inferencia de pocos bits", section 6: the
+ * saving is realised by a kernel that unpacks, dequantises and multiplies;
+ * decode and prefill are separate regimes. Section 1: reconstruction
+ * s (q - z).) */
+gptq_status gptq_dequant_matmul_workspace_bytes(int64_t M, int64_t n, int64_t d_out,
+                                                int32_t bits, int32_t group,
+                                                size_t *bytes);
+gptq_status gptq_dequant_matmul(void *stream, const void *X, int32_t xdt, int64_t M,
+                                int64_t n, int64_t ldx, const uint32_t *qweight,
+                                const float *scales, const uint8_t *zeros,
+                                int64_t d_out, int32_t bits, int32_t group, float *Y,
+                                int64_t ldy, void *workspace, size_t ws_bytes);
+
 /* ---- Diagnostics ------------------------------------------------------------ */
 const char *gptq_status_string(int status);
 const char *gptq_last_error(void); /* thread-local detail of the last failure */

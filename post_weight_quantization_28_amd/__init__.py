@@ -1,13 +1,15 @@
 """MI355X (gfx950) GPTQ layer quantizer: Hessian accumulation, damped
 Cholesky factor of the inverse, blocked column sweep with error feedback and
 lazy-batch trailing updates, and code packing, in hand-written HIP kernels
-behind a C ABI (include/gptq.h). This package is its Python binding."""
-from .gptq import (BF16, F32, GPTQError, QuantResult, accumulate_hessian, factor_hinv,
-                   hessian_workspace_bytes, load, make_params, pack_codes, profile_collect,
+behind a C ABI (include/gptq.h); and, for inference, the dequantising product
+of a packed layer. This package is its Python binding."""
+from .gptq import (BF16, F32, GPTQError, QuantResult, accumulate_hessian, dequant_matmul,
+                   dequant_matmul_workspace_bytes, factor_hinv, hessian_workspace_bytes, load, make_params, pack_codes, profile_collect,
                    profile_enable, quantize_layer, unpack_codes, workspace_bytes, LIB_PATH,
                    PROF_CLASSES)
 
-__all__ = ["BF16", "F32", "GPTQError", "QuantResult", "accumulate_hessian", "factor_hinv",
+__all__ = ["BF16", "F32", "GPTQError", "QuantResult", "accumulate_hessian", "dequant_matmul",
+           "dequant_matmul_workspace_bytes", "factor_hinv",
            "hessian_workspace_bytes", "load", "make_params", "pack_codes", "profile_collect",
            "profile_enable", "quantize_layer", "unpack_codes", "workspace_bytes", "LIB_PATH",
            "PROF_CLASSES"]

@@ -522,4 +522,51 @@ gptq_status gptq_unpack_codes(void* stream, const uint32_t* qweight, int64_t d_o
   return GPTQ_OK;
 }
 
+// ---------------------------------------------------------------- inference
+static gptq_status dq_check(int64_t M, int64_t n, int64_t d_out, int32_t bits, int32_t group) {
+  if (bits < 2 || bits > 4) return fail(GPTQ_EINVAL, "bits must be 2, 3 or 4");
+  if (M < 0 || n < 0 || d_out < 0) return fail(GPTQ_EINVAL, "negative size");
+  if (group <= 0 || group % 32 != 0) return fail(GPTQ_EINVAL, "group must be a positive multiple of 32");
+  if (n % group != 0) return fail(GPTQ_EINVAL, "group must divide n");
+  return GPTQ_OK;
+}
+
+gptq_status gptq_dequant_matmul_workspace_bytes(int64_t M, int64_t n, int64_t d_out, int32_t bits,
+                                                int32_t group, size_t* bytes) {
+  if (!bytes) return fail(GPTQ_EINVAL, "NULL pointer");
+  const gptq_status st = dq_check(M, n, d_out, bits, group);
+  if (st != GPTQ_OK) return st;
+  const DqPlan p = dequant_mm_plan(M, n, d_out, group);
+  *bytes = (p.part_bytes + 255) / 256 * 256;
+  return GPTQ_OK;
+}
+
+gptq_status gptq_dequant_matmul(void* stream, const void* X, int32_t xdt, int64_t M, int64_t n, int64_t ldx,
+                                const uint32_t* qweight, const float* scales, const uint8_t* zeros,
+                                int64_t d_out, int32_t bits, int32_t group, float* Y, int64_t ldy,
+                                void* workspace, size_t ws_bytes) {
+  gptq_status st = dq_check(M, n, d_out, bits, group);
+  if (st != GPTQ_OK) return st;
+  if (xdt != GPTQ_BF16) return fail(GPTQ_EINVAL, "dequant_matmul takes bf16 activations");
+  if (M == 0 || d_out == 0) return GPTQ_OK;
+  if (ldy < d_out) return fail(GPTQ_EINVAL, "ldy < d_out");
+  if (!Y) return fail(GPTQ_EINVAL, "NULL pointer");
+  if (n > 0) {
+    if (!X || !qweight || !scales || !zeros) return fail(GPTQ_EINVAL, "NULL pointer");
+    if (ldx < n || ldx % 8 != 0 || ((uintptr_t)X & 15) != 0)
+      return fail(GPTQ_EINVAL, "X rows must be 16-byte aligned (ldx % 8 == 0, ldx >= n)");
+  }
+  const DqPlan p = dequant_mm_plan(M, n, d_out, group);
+  if (p.mtiles > 65535 || p.splits > 65535 || p.otiles > ((int64_t)1 << 31) - 1)
+    return fail(GPTQ_EINVAL, "dequant_matmul: M or d_out too large for one launch");
+  if (p.part_bytes > 0) {
+    if (!workspace || ((uintptr_t)workspace & 255) != 0) return fail(GPTQ_EINVAL, "workspace: NULL or unaligned");
+    if (ws_bytes < p.part_bytes) return fail(GPTQ_EWORKSPACE, "workspace too small");
+  }
+  HIP_TRY(launch_dequant_mm((hipStream_t)stream, p, static_cast<const uint16_t*>(X), M, n, ldx, qweight, scales,
+                            zeros, d_out, bits, group, Y, ldy, static_cast<float*>(workspace)),
+          "dequant_matmul");
+  return GPTQ_OK;
+}
+
 }  // extern "C"

@@ -66,6 +66,10 @@ def load():
                              ctypes.POINTER(c_i64)],
         "gptq_pack_codes": [c_vp, c_vp, c_i64, c_i64, ctypes.c_int32, c_vp],
         "gptq_unpack_codes": [c_vp, c_vp, c_i64, c_i64, ctypes.c_int32, c_vp],
+        "gptq_dequant_matmul_workspace_bytes": [c_i64, c_i64, c_i64, ctypes.c_int32, ctypes.c_int32,
+                                                ctypes.POINTER(c_sz)],
+        "gptq_dequant_matmul": [c_vp, c_vp, ctypes.c_int32, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_i64,
+                                ctypes.c_int32, ctypes.c_int32, c_vp, c_i64, c_vp, c_sz],
         "gptq_profile_enable": [ctypes.c_int],
         "gptq_profile_collect": [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i64)],
     }
@@ -225,6 +229,35 @@ def factor_hinv(H, damp=0.01, act_order=False, n_quant=None, workspace=None):
                               _dev(perm, "perm"), ctypes.byref(fail))
     _check(st, fail.value)
     return U, perm
+
+
+# ---------------------------------------------------------------- inference
+def dequant_matmul_workspace_bytes(M, n, d_out, bits, group):
+    lib = load()
+    out = ctypes.c_size_t(0)
+    _check(lib.gptq_dequant_matmul_workspace_bytes(int(M), int(n), int(d_out), int(bits), int(group),
+                                                   ctypes.byref(out)))
+    return out.value
+
+
+def dequant_matmul(X, qweight, scales, zeros, bits, group, out=None, workspace=None):
+    """Y = X W_hat^T (M x d_out fp32) from a packed layer: X (M x n bf16),
+    qweight (d_out x n*bits/32 int32/uint32 words), scales (d_out x n/group
+    fp32), zeros (d_out x n/group uint8)."""
+    lib = load()
+    _dev(X, "X")
+    if X.dtype != torch.bfloat16:
+        raise TypeError("X must be bfloat16")
+    M, n = X.shape
+    d_out = qweight.shape[0]
+    Y = out if out is not None else torch.empty((M, d_out), dtype=torch.float32, device=X.device)
+    _dev(Y, "Y")
+    need = dequant_matmul_workspace_bytes(M, n, d_out, bits, group)
+    ws, wsp = _workspace(need, X.device, workspace)
+    _check(lib.gptq_dequant_matmul(_stream(), _dev(X, "X"), BF16, M, n, n, _dev(qweight, "qweight"),
+                                   _dev(scales, "scales"), _dev(zeros, "zeros"), d_out, int(bits), int(group),
+                                   _dev(Y, "Y"), d_out, wsp, need))
+    return Y
 
 
 # ---------------------------------------------------------------- packing

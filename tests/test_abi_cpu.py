@@ -28,7 +28,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for must in ("gptq_accumulate_hessian", "gptq_quantize_layer", "gptq_workspace_bytes",
                  "gptq_hessian_workspace_bytes", "gptq_pack_codes", "gptq_unpack_codes",
-                 "gptq_status_string", "gptq_factor_hinv"):
+                 "gptq_status_string", "gptq_factor_hinv", "gptq_dequant_matmul",
+                 "gptq_dequant_matmul_workspace_bytes"):
         assert must in names
 
 
@@ -74,6 +75,30 @@ def test_workspace_and_validation_on_host():
     assert st == G.gptq.EINVAL
     st = lib.gptq_pack_codes(None, None, 1, 8, 7, None)
     assert st == G.gptq.EINVAL
+
+
+def test_dequant_matmul_validation_on_host():
+    """Argument checks of the inference product run on the host, before
+    anything is enqueued (NULL device pointers are never dereferenced)."""
+    G, lib = _lib()
+    import ctypes
+    # decode: few output blocks split the groups, fp32 partials in the workspace
+    assert G.dequant_matmul_workspace_bytes(16, 4096, 4096, 4, 128) == 8 * 16 * 4096 * 4
+    # prefill: one pass, no workspace
+    assert G.dequant_matmul_workspace_bytes(4096, 4096, 4096, 4, 128) == 0
+    for bits, group, n in ((5, 128, 256), (4, 48, 96), (4, 128, 200), (4, 0, 128)):
+        with pytest.raises(G.GPTQError) as e:
+            G.dequant_matmul_workspace_bytes(4, n, 64, bits, group)
+        assert e.value.status == -1
+    null = ctypes.c_void_p(0)
+    # fp32 activations are refused; so is a NULL X with work to do
+    assert lib.gptq_dequant_matmul(null, null, 1, 4, 128, 128, null, null, null, 64, 4, 128,
+                                   null, 64, null, 0) == -1
+    assert lib.gptq_dequant_matmul(null, null, 0, 4, 128, 128, null, null, null, 64, 4, 128,
+                                   null, 64, null, 0) == -1
+    # nothing to do: M == 0
+    assert lib.gptq_dequant_matmul(null, null, 0, 0, 128, 128, null, null, null, 64, 4, 128,
+                                   null, 64, null, 0) == 0
 
 
 def test_python_binding_refuses_host_tensors():
