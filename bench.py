@@ -8,6 +8,11 @@ region; every step recomputes everything from X and W.
 
 Prints one JSON line: the step throughput, the Hessian kernel against the bf16
 MFMA roofline, and the float64 oracle timed on the host cores.
+
+`--workload dequant_matmul --tokens M` instead times the inference product
+Y = X W_hat^T of a packed 4096 x 4096 4-bit g128 layer for M tokens (decode:
+M = 16, bound by reading the packed weights; prefill: M = 4096, bound by the
+matrix cores) and prints one JSON line for it.
 """
 import argparse
 import hashlib
@@ -82,6 +87,98 @@ def cpu_baseline(wl, X_vals, p, sample_tokens=4096, sample_rows=64):
     }
 
 
+def bench_dequant(args):
+    """The inference product on the 4096 x 4096 4-bit g128 layer (seeded
+    random codes, zero points and scales; Student-t(4) bf16 activations)."""
+    import numpy as np
+    import torch
+
+    import post_weight_quantization_28_amd as G
+    import synth
+
+    if not os.path.exists(G.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    G.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    M, n, d_out, bits, group = args.tokens, 4096, 4096, 4, 128
+    r = np.random.default_rng(2024)
+    codes = r.integers(0, 2 ** bits, (d_out, n)).astype(np.uint8)
+    scales = r.uniform(0.002, 0.05, (d_out, n // group)).astype(np.float32)
+    zeros = r.integers(0, 2 ** bits, (d_out, n // group)).astype(np.uint8)
+    xv = r.standard_t(4, (M, n)).astype(np.float32)
+    xb = synth.f32_to_bf16_bits(xv)
+    qw_dev = G.pack_codes(torch.from_numpy(codes).to(dev), bits)
+    sc_dev = torch.from_numpy(scales).to(dev)
+    z_dev = torch.from_numpy(zeros).to(dev)
+    X = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).to(dev)
+    Y = torch.empty((M, d_out), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(G.dequant_matmul_workspace_bytes(M, n, d_out, bits, group), 1), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        G.dequant_matmul(X, qw_dev, sc_dev, z_dev, bits, group, out=Y, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    # events on the stream the library launches on (torch's current stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    w_bytes = d_out * n * bits // 8 + d_out * (n // group) * 5          # codes, fp32 scales, uint8 zeros
+    io_bytes = M * n * 2 + M * d_out * 4
+    flops = 2.0 * M * n * d_out
+    if M <= 64:
+        ach = (w_bytes + io_bytes) / (ms / 1e3) / 1e9
+        roof = {"bound": "hbm", "kernel": "k_dequant_mm (+ k_dequant_mm_reduce)", "achieved": ach,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": None,
+                "work": "packed codes + scales + zeros + X + Y bytes per call"}
+    else:
+        ach = flops / (ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "kernel": "k_dequant_mm", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
+                "work": "2 M n d_out flop per call"}
+    line = {
+        "metric": f"packed-layer product Y = X W_hat^T (4096², 4-bit g128), {M} tokens",
+        "value": M / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "wall_ms_per_step": 1e3 * elapsed / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"inference product of a packed 4096x4096 4-bit g128 layer, {M} bf16 tokens "
+                               f"({'decode' if M <= 64 else 'prefill'})",
+                   "tokens": M, "d_in": n, "d_out": d_out, "bits": bits, "group": group,
+                   "parallelism": "single GPU"},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import dequant as D
+        from oracle import packing as P
+        try:
+            from threadpoolctl import threadpool_info
+            cores = sum(i.get("num_threads", 0) for i in threadpool_info()
+                        if i.get("user_api") == "blas") or None
+        except Exception:
+            cores = None
+        ms_rows = min(M, 16)
+        qw_host = P.pack(codes, bits)
+        xs = synth.bf16_bits_to_f32(xb[:ms_rows])
+        t0 = time.perf_counter()
+        D.dequant_matmul(xs, qw_host, scales, zeros, bits, group)
+        t = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": ms_rows / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                                "sample": f"{ms_rows} of {M} tokens: float64 unpack, dequantise and product "
+                                          "(numpy)"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -91,12 +188,17 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before warm-up, run one plain 1 GiB device copy and one 1 GiB fill "
                          "(known bytes) for calibrating HBM byte counters")
+    ap.add_argument("--workload", choices=["gptq_layer", "dequant_matmul"], default="gptq_layer")
+    ap.add_argument("--tokens", type=int, default=16, help="tokens M for --workload dequant_matmul")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: --gpus {args.gpus} is not supported; the library and this benchmark "
               "run on one GPU (a token-sharded Hessian and row-sharded sweep are not implemented)",
               file=sys.stderr)
         sys.exit(2)
+    if args.workload == "dequant_matmul":
+        bench_dequant(args)
+        return
 
     import numpy as np
     import torch

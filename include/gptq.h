@@ -153,7 +153,8 @@ gptq_status gptq_unpack_codes(void *stream, const uint32_t *qweight,
  * only: xdt must be GPTQ_BF16, row pitch ldx >= n with ldx % 8 == 0, 16-byte
  * aligned base) and W_hat[o][k] = scales[o][k/group] * (q[o][k] -
  * zeros[o][k/group]), the codes q read from qweight in the layout above
- * (d_out x n*bits/32 words: n_quant = n, contiguous groups, i.e. a layer
+ * (d_out x n*bits/32 words, 16-byte aligned base: n_quant = n, contiguous
+ * groups, i.e. a layer
  * quantized without act-order, or whose g_idx is k / group). group must be a
  * positive multiple of 32 that divides n. Products of bf16 activations and
  * the integers q - z are exact in fp32 and each group's sum is scaled once

@@ -178,12 +178,13 @@ hipError_t launch_finish(hipStream_t s, const float* Wf, const uint8_t* codes_p,
 
 // ---- dqmm.hip: Y = X W_hat^T from the packed codes (inference)
 struct DqPlan {
+  int decode;                // 1: the 16-token kernel (16 x 16 x 32 MFMA, 8 chunks in flight)
   int mb;                    // 32-row blocks of X per workgroup: 1, 2 or 4
   int64_t mtiles, otiles;    // workgroups along M and along d_out
   int64_t groups_per_split, splits;
   size_t part_bytes;         // fp32 partials when splits > 1
 };
-DqPlan dequant_mm_plan(int64_t M, int64_t n, int64_t d_out, int group);
+DqPlan dequant_mm_plan(int64_t M, int64_t n, int64_t d_out, int bits, int group);
 hipError_t launch_dequant_mm(hipStream_t s, const DqPlan& p, const uint16_t* X, int64_t M, int64_t n,
                              int64_t ldx, const uint32_t* qw, const float* scales, const uint8_t* zeros,
                              int64_t d_out, int bits, int group, float* Y, int64_t ldy, float* part);

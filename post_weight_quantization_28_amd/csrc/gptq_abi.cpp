@@ -536,7 +536,7 @@ gptq_status gptq_dequant_matmul_workspace_bytes(int64_t M, int64_t n, int64_t d_
   if (!bytes) return fail(GPTQ_EINVAL, "NULL pointer");
   const gptq_status st = dq_check(M, n, d_out, bits, group);
   if (st != GPTQ_OK) return st;
-  const DqPlan p = dequant_mm_plan(M, n, d_out, group);
+  const DqPlan p = dequant_mm_plan(M, n, d_out, bits, group);
   *bytes = (p.part_bytes + 255) / 256 * 256;
   return GPTQ_OK;
 }
@@ -555,8 +555,9 @@ gptq_status gptq_dequant_matmul(void* stream, const void* X, int32_t xdt, int64_
     if (!X || !qweight || !scales || !zeros) return fail(GPTQ_EINVAL, "NULL pointer");
     if (ldx < n || ldx % 8 != 0 || ((uintptr_t)X & 15) != 0)
       return fail(GPTQ_EINVAL, "X rows must be 16-byte aligned (ldx % 8 == 0, ldx >= n)");
+    if (((uintptr_t)qweight & 15) != 0) return fail(GPTQ_EINVAL, "qweight must be 16-byte aligned");
   }
-  const DqPlan p = dequant_mm_plan(M, n, d_out, group);
+  const DqPlan p = dequant_mm_plan(M, n, d_out, bits, group);
   if (p.mtiles > 65535 || p.splits > 65535 || p.otiles > ((int64_t)1 << 31) - 1)
     return fail(GPTQ_EINVAL, "dequant_matmul: M or d_out too large for one launch");
   if (p.part_bytes > 0) {

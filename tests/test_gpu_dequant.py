@@ -62,8 +62,10 @@ def check(Y, x, qw, scales, zeros, bits, group):
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("M,d_out,n,group", [
-    (1, 100, 256, 32),       # one token, ragged output block
-    (5, 300, 384, 64),       # decode-sized, split over groups
+    (1, 100, 256, 32),       # one token, ragged output block (16-token kernel, 8 groups a step)
+    (16, 200, 1024, 128),    # 16-token kernel, 4 splits of 2 groups
+    (3, 70, 768, 256),       # 16-token kernel, one 256-code group a step
+    (5, 300, 384, 64),       # 6 groups of 2 chunks: not whole 8-chunk steps, general kernel
     (33, 128, 512, 128),     # two 32-row blocks, second ragged
     (70, 257, 1024, 128),    # 64-row blocks, ragged both ways
     (200, 130, 640, 32),     # 128-row blocks, ragged tails, many groups
