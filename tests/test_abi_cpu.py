@@ -82,10 +82,13 @@ def test_dequant_matmul_validation_on_host():
     anything is enqueued (NULL device pointers are never dereferenced)."""
     G, lib = _lib()
     import ctypes
-    # decode: few output blocks split the groups, fp32 partials in the workspace
-    assert G.dequant_matmul_workspace_bytes(16, 4096, 4096, 4, 128) == 8 * 16 * 4096 * 4
+    # 16 tokens: one kernel sums its K slices in LDS, no workspace
+    assert G.dequant_matmul_workspace_bytes(16, 4096, 4096, 4, 128) == 0
     # prefill: one pass, no workspace
     assert G.dequant_matmul_workspace_bytes(4096, 4096, 4096, 4, 128) == 0
+    # few output tiles of the general kernel: the 6 groups split over 6
+    # passes, fp32 partials 6 x 5 x 300 (rounded up to 256 bytes)
+    assert G.dequant_matmul_workspace_bytes(5, 384, 300, 4, 64) == (6 * 5 * 300 * 4 + 255) // 256 * 256
     for bits, group, n in ((5, 128, 256), (4, 48, 96), (4, 128, 200), (4, 0, 128)):
         with pytest.raises(G.GPTQError) as e:
             G.dequant_matmul_workspace_bytes(4, n, 64, bits, group)
