@@ -108,13 +108,30 @@ def upper_chol_of_inverse(Hd):
 # ---------------------------------------------------------------------------
 # The quantization grid ([BAL] section 1; R4-R6)
 # ---------------------------------------------------------------------------
-def group_grid(v, maxq):
+def group_grid(v, maxq, sym=False):
     """Per-row (s, z, zpre) from the group's current values ``v`` (rows x g).
 
     zpre = -xmin / s is the value rint() decides the zero point from.
+
+    sym: the symmetric alphabet {-A, ..., A} with A = (maxq - 1) / 2 =
+    2^(b-1) - 1 levels on each side of zero ("Resumen Técnico:
+    GPTQ-intrinsic LoRA", "Límites Inferiores de la Teoría de la
+    Información": a finite integer alphabet of size 2B + 1). Reading: the
+    scale maps the group's largest magnitude to A, s = max|v| / A (a group
+    of zeros takes max|v| = 1, as the affine rule takes the range (-1, 1));
+    codes are stored as q + A, i.e. with the fixed zero point z = A, so the
+    reconstruction s (code - z) and the packing stay those of the affine
+    format. zpre is A itself (no rounding decision).
     """
     xmin = np.minimum(v.min(axis=1), 0.0)
     xmax = np.maximum(v.max(axis=1), 0.0)
+    if sym:
+        A = (maxq - 1.0) / 2.0
+        amax = np.maximum(-xmin, xmax)
+        amax = np.where(amax == 0.0, 1.0, amax)
+        s = amax / A
+        z = np.full_like(s, A)
+        return s, z, z.copy()
     same = xmin == xmax
     xmin = np.where(same, -1.0, xmin)
     xmax = np.where(same, 1.0, xmax)
@@ -175,7 +192,7 @@ def _finish(W, Wp, perm, codes_p, scales, zeros, loss, n_quant, group,
 # O2: Cholesky of the inverse + lazy batches (the scalable form)
 # ---------------------------------------------------------------------------
 def gptq_o2(W, H, bits=4, group=128, damp=0.01, block=128, act_order=False,
-            n_quant=None, U=None, perm=None, alt=None):
+            n_quant=None, U=None, perm=None, alt=None, sym=False):
     """GPTQ sweep with the upper Cholesky factor U of H_d^{-1} and lazy
     batches of ``block`` columns ([GPTQ] "Enfoque Técnico"; [GIL]
     "Detalles de Implementación").
@@ -223,7 +240,7 @@ def gptq_o2(W, H, bits=4, group=128, damp=0.01, block=128, act_order=False,
         E = np.zeros((d_out, i1 - i0))
         for j in range(i0, i1):
             if j % group == 0:
-                s, z, zpre = group_grid(Wp[:, j:j + group], maxq)
+                s, z, zpre = group_grid(Wp[:, j:j + group], maxq, sym)
                 rz = alt_z.get(j // group)
                 if rz:
                     z[rz] = np.clip(other_neighbour(zpre[rz]), 0.0, maxq)
@@ -250,7 +267,7 @@ def gptq_o2(W, H, bits=4, group=128, damp=0.01, block=128, act_order=False,
 # ---------------------------------------------------------------------------
 # O1: the Optimal-Brain definition with explicit inverse downdates
 # ---------------------------------------------------------------------------
-def gptq_o1(W, H, bits=4, group=128, damp=0.01, act_order=False, n_quant=None):
+def gptq_o1(W, H, bits=4, group=128, damp=0.01, act_order=False, n_quant=None, sym=False):
     """Column-by-column OBS form, eager updates ([GPTQ] "Enfoque Técnico").
 
     G is the inverse of H_d restricted to the columns not yet quantized.
@@ -278,7 +295,7 @@ def gptq_o1(W, H, bits=4, group=128, damp=0.01, act_order=False, n_quant=None):
     s = z = None
     for j in range(nq):
         if j % group == 0:
-            s, z, zpre = group_grid(Wp[:, j:j + group], maxq)
+            s, z, zpre = group_grid(Wp[:, j:j + group], maxq, sym)
             scales[:, j // group] = s
             zeros[:, j // group] = z
             zmargins[:, j // group] = tie_distance(zpre)
@@ -298,7 +315,7 @@ def gptq_o1(W, H, bits=4, group=128, damp=0.01, act_order=False, n_quant=None):
 # ---------------------------------------------------------------------------
 # Round-to-nearest and brute force
 # ---------------------------------------------------------------------------
-def rtn(W, bits=4, group=128):
+def rtn(W, bits=4, group=128, sym=False):
     """Round-to-nearest on the same grid rules (R4-R6), no feedback: the
     baseline GPTQ is compared with ([GPTQ] "Rendimiento y Precisión")."""
     W = np.asarray(W, np.float64)
@@ -311,7 +328,7 @@ def rtn(W, bits=4, group=128):
     zeros = np.zeros((d_out, ng))
     for gi in range(ng):
         sl = slice(gi * group, (gi + 1) * group)
-        s, z, _ = group_grid(W[:, sl], maxq)
+        s, z, _ = group_grid(W[:, sl], maxq, sym)
         scales[:, gi] = s
         zeros[:, gi] = z
         for j in range(sl.start, sl.stop):

@@ -76,9 +76,43 @@ def test_grid_hand_worked_3bit():
     assert np.array_equal(res["w_hat"][3], [0.0, 0.0, 0.0, 0.0])
 
 
-# ---------------------------------------------------------------- RTN special case
+# ---------------------------------------------------------------- symmetric alphabet
+def test_symmetric_grid_hand_worked():
+    """4 bits: alphabet {-7 .. 7}, s = max|v| / 7, codes stored as q + 7.
+    Group [-0.7, 0.35, 0.1, 0]: s = 0.1, w / s = [-7, 3.5, 1, 0], rint (half
+    to even) = [-7, 4, 1, 0], codes [0, 11, 8, 7], w_hat [-0.7, 0.4, 0.1, 0].
+    A group of zeros takes s = 1 / 7."""
+    W = np.array([[-0.7, 0.35, 0.1, 0.0, 0.0, 0.0, 0.0, 0.0]])
+    o = O.rtn(W, 4, 4, sym=True)
+    assert np.array_equal(o["codes"][0, :4], [0, 11, 8, 7])
+    assert np.allclose(o["scales"][0], [0.1, 1.0 / 7.0], rtol=0, atol=1e-15)
+    assert np.array_equal(o["zeros"][0], [7, 7])
+    assert np.allclose(o["w_hat"][0, :4], [-0.7, 0.4, 0.1, 0.0], rtol=0, atol=1e-15)
+    assert np.array_equal(o["codes"][0, 4:], [7, 7, 7, 7])
+
+
 @pytest.mark.parametrize("bits", [2, 3, 4])
-def test_diagonal_hessian_is_rtn(bits):
+def test_symmetric_alphabet_levels_and_odd_symmetry(bits):
+    """Codes stay in [0, 2A] (2A + 1 levels, A = 2^(b-1) - 1); the
+    reconstruction is an odd function of the weights (rint to even is
+    odd-symmetric and the scale depends on |v| only)."""
+    r = np.random.default_rng(40 + bits)
+    W = r.standard_normal((12, 64)) * 0.02
+    A = 2 ** (bits - 1) - 1
+    a = O.rtn(W, bits, 16, sym=True)
+    b = O.rtn(-W, bits, 16, sym=True)
+    assert a["codes"].max() <= 2 * A and np.all(a["zeros"] == A)
+    assert np.array_equal(a["w_hat"], -b["w_hat"])
+    assert np.array_equal(a["codes"].astype(int), 2 * A - b["codes"].astype(int))
+    # every group's largest magnitude is reproduced exactly as s * A
+    g = np.abs(W).reshape(12, 4, 16).max(axis=2)
+    assert np.allclose(a["scales"] * A, g, rtol=1e-15, atol=0)
+
+
+# ---------------------------------------------------------------- RTN special case
+@pytest.mark.parametrize("sym", [False, True])
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_diagonal_hessian_is_rtn(bits, sym):
     """P-RTN: with orthonormal-column calibration (one nonzero per token, so
     X^T X is diagonal) there is no feedback and O1, O2 and round-to-nearest
     agree bitwise."""
@@ -89,13 +123,13 @@ def test_diagonal_hessian_is_rtn(bits):
     H = O.hessian(X)
     assert np.count_nonzero(H - np.diag(np.diagonal(H))) == 0
     W = r.standard_normal((d_out, n)) * 0.02
-    ref = O.rtn(W, bits, 16)
-    o2 = O.gptq_o2(W, H, bits, 16, 0.01, 32)
-    o1 = O.gptq_o1(W, H, bits, 16, 0.01)
+    ref = O.rtn(W, bits, 16, sym=sym)
+    o2 = O.gptq_o2(W, H, bits, 16, 0.01, 32, sym=sym)
+    o1 = O.gptq_o1(W, H, bits, 16, 0.01, sym=sym)
     for o in (o1, o2):
         assert np.array_equal(o["codes"], ref["codes"])
         assert np.array_equal(o["w_hat"], ref["w_hat"])
-    o3 = O.gptq_o2(W, 2.0 * np.eye(n), bits, 16, 0.01, 8)
+    o3 = O.gptq_o2(W, 2.0 * np.eye(n), bits, 16, 0.01, 8, sym=sym)
     assert np.array_equal(o3["codes"], ref["codes"])
 
 
@@ -280,15 +314,16 @@ def test_block_size_invariance():
         assert np.allclose(o["w_hat"], base["w_hat"], atol=1e-12)
 
 
+@pytest.mark.parametrize("sym", [False, True])
 @pytest.mark.parametrize("bits", [2, 3, 4])
 @pytest.mark.parametrize("act_order", [False, True])
-def test_o1_equals_o2(bits, act_order):
+def test_o1_equals_o2(bits, act_order, sym):
     """P-O1O2: the OBS inverse-downdate definition and the Cholesky/lazy-batch
     form agree to float64 rounding."""
     W, X = _tiny(20 + bits, 16, 96, 500, heavy=True)
     H = O.hessian(X)
-    o1 = O.gptq_o1(W, H, bits, 32, 0.01, act_order=act_order)
-    o2 = O.gptq_o2(W, H, bits, 32, 0.01, 16, act_order=act_order)
+    o1 = O.gptq_o1(W, H, bits, 32, 0.01, act_order=act_order, sym=sym)
+    o2 = O.gptq_o2(W, H, bits, 32, 0.01, 16, act_order=act_order, sym=sym)
     assert np.array_equal(o1["perm"], o2["perm"])
     ok = (o1["codes"] == o2["codes"]) | (o2["margins"][:, np.argsort(o2["perm"])] < 1e-8)
     assert ok.all()
