@@ -68,13 +68,21 @@ typedef enum {
 typedef enum { GPTQ_BF16 = 0, GPTQ_F32 = 1 } gptq_dtype;
 
 typedef struct {
-  uint32_t struct_size; /* sizeof(gptq_params) */
+  uint32_t struct_size; /* sizeof(gptq_params); at least offsetof(sym) */
   int32_t bits;         /* 2, 3 or 4 */
   int32_t group;        /* g >= 8; n_quant % g == 0; g % block == 0 or block % g == 0 */
   float damp;           /* lambda = damp * mean(diag H); >= 0, finite */
   int32_t block;        /* lazy-batch width B: 32, 64 or 128 */
   int32_t act_order;    /* 0 or 1 */
   int64_t n_quant;      /* 1..n; columns n_quant..n-1 receive feedback only */
+  int32_t sym;          /* 0: affine grid (scale and zero point per group);
+                           1: symmetric alphabet {-A..A}, A = 2^(bits-1) - 1,
+                           s = max|v| / A over the group's current values
+                           (1 / A for a group of zeros), stored as codes
+                           q + A with zeros = A. Read only when struct_size
+                           covers it (older callers: 0). ("Resumen Técnico:
+                           GPTQ-intrinsic LoRA": a finite integer alphabet of
+                           size 2B + 1.) */
 } gptq_params;
 
 typedef struct {

@@ -141,6 +141,13 @@ def group_grid(v, maxq, sym=False):
     return s, z, zpre
 
 
+def code_top(maxq, sym):
+    """Largest code: maxq on the affine grid, 2A = maxq - 1 on the symmetric
+    alphabet (codes q + A for q in {-A..A}; a value pushed past A by the
+    feedback clamps to A)."""
+    return maxq - 1.0 if sym else maxq
+
+
 def quantize_column(w, s, z, maxq):
     """(q, w_hat, pre): q = clamp(rint(w/s) + z, 0, maxq), w_hat = s (q - z),
     pre = w / s (the value the rounding decides on)."""
@@ -219,6 +226,7 @@ def gptq_o2(W, H, bits=4, group=128, damp=0.01, block=128, act_order=False,
     nq = n if n_quant is None else int(n_quant)
     _check_params(n, bits, group, block, nq)
     maxq = float(2 ** bits - 1)
+    qtop = code_top(maxq, sym)
     if U is None:
         Hd, perm = prepare(H, damp, act_order, nq)
         U = upper_chol_of_inverse(Hd)
@@ -243,14 +251,14 @@ def gptq_o2(W, H, bits=4, group=128, damp=0.01, block=128, act_order=False,
                 s, z, zpre = group_grid(Wp[:, j:j + group], maxq, sym)
                 rz = alt_z.get(j // group)
                 if rz:
-                    z[rz] = np.clip(other_neighbour(zpre[rz]), 0.0, maxq)
+                    z[rz] = np.clip(other_neighbour(zpre[rz]), 0.0, qtop)
                 scales[:, j // group] = s
                 zeros[:, j // group] = z
                 zmargins[:, j // group] = tie_distance(zpre)
-            q, what, pre = quantize_column(Wp[:, j], s, z, maxq)
+            q, what, pre = quantize_column(Wp[:, j], s, z, qtop)
             rc = alt_c.get(j)
             if rc:
-                q[rc] = np.clip(other_neighbour(pre[rc]) + z[rc], 0.0, maxq)
+                q[rc] = np.clip(other_neighbour(pre[rc]) + z[rc], 0.0, qtop)
                 what[rc] = s[rc] * (q[rc] - z[rc])
             e = (Wp[:, j] - what) / U[j, j]
             Wp[:, j + 1:i1] -= np.outer(e, U[j, j + 1:i1])
@@ -282,6 +290,7 @@ def gptq_o1(W, H, bits=4, group=128, damp=0.01, act_order=False, n_quant=None, s
     nq = n if n_quant is None else int(n_quant)
     _check_params(n, bits, group, None, nq)
     maxq = float(2 ** bits - 1)
+    qtop = code_top(maxq, sym)
     Hd, perm = prepare(H, damp, act_order, nq)
     G = np.linalg.inv(Hd)
     Wp = W[:, perm].copy()
@@ -299,7 +308,7 @@ def gptq_o1(W, H, bits=4, group=128, damp=0.01, act_order=False, n_quant=None, s
             scales[:, j // group] = s
             zeros[:, j // group] = z
             zmargins[:, j // group] = tie_distance(zpre)
-        q, what, pre = quantize_column(Wp[:, j], s, z, maxq)
+        q, what, pre = quantize_column(Wp[:, j], s, z, qtop)
         g00 = G[0, 0]
         delta = Wp[:, j] - what
         Wp[:, j + 1:] -= np.outer(delta / g00, G[0, 1:])
@@ -321,6 +330,7 @@ def rtn(W, bits=4, group=128, sym=False):
     W = np.asarray(W, np.float64)
     d_out, n = W.shape
     maxq = float(2 ** bits - 1)
+    qtop = code_top(maxq, sym)
     ng = n // group
     codes = np.zeros((d_out, n), np.uint8)
     w_hat = np.zeros_like(W)
@@ -332,7 +342,7 @@ def rtn(W, bits=4, group=128, sym=False):
         scales[:, gi] = s
         zeros[:, gi] = z
         for j in range(sl.start, sl.stop):
-            q, what, _ = quantize_column(W[:, j], s, z, maxq)
+            q, what, _ = quantize_column(W[:, j], s, z, qtop)
             codes[:, j] = q.astype(np.uint8)
             w_hat[:, j] = what
     return dict(codes=codes, w_hat=w_hat, scales=scales,

@@ -151,6 +151,7 @@ struct SweepArgs {
   int64_t d_out, i0, ncols;     // block [i0, i0 + ncols)
   int block;                    // B
   int group, bits;
+  int sym;                      // 1: symmetric alphabet {-A..A}, z = A = 2^(bits-1) - 1
   int64_t gbase;                // group index of column i0
   int gshift;                   // log2(group) when groups split a block, else 31
   float* scales; uint8_t* zeros; int64_t ngroups;

@@ -5,6 +5,8 @@
 #include "../../include/gptq.h"
 #include "common.h"
 
+#include <cstddef>
+
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -133,9 +135,16 @@ QLayout q_layout(int64_t d_out, int64_t n, const gptq_params* p) {
   return L;
 }
 
+// The parameter block grows at its end; fields past a caller's struct_size
+// take their defaults.
+constexpr size_t kParamsMin = offsetof(gptq_params, sym);
+int params_sym(const gptq_params* p) {
+  return p->struct_size >= offsetof(gptq_params, sym) + sizeof(int32_t) ? p->sym : 0;
+}
+
 gptq_status check_params(int64_t d_out, int64_t n, const gptq_params* p) {
   if (!p) return fail(GPTQ_EINVAL, "params is NULL");
-  if (p->struct_size < sizeof(gptq_params)) return fail(GPTQ_EINVAL, "params.struct_size too small");
+  if (p->struct_size < kParamsMin) return fail(GPTQ_EINVAL, "params.struct_size too small");
   if (d_out < 0 || n < 1) return fail(GPTQ_EINVAL, "need d_out >= 0 and n >= 1");
   if (n > (int64_t)1 << 30 || d_out > (int64_t)1 << 30) return fail(GPTQ_EINVAL, "dimension too large");
   if (p->bits < 2 || p->bits > 4) return fail(GPTQ_EINVAL, "bits must be 2, 3 or 4");
@@ -148,13 +157,15 @@ gptq_status check_params(int64_t d_out, int64_t n, const gptq_params* p) {
     return fail(GPTQ_EINVAL, "group and block must nest (one divides the other)");
   if (!(p->damp >= 0.f) || !std::isfinite(p->damp)) return fail(GPTQ_EINVAL, "damp must be finite and >= 0");
   if (p->act_order != 0 && p->act_order != 1) return fail(GPTQ_EINVAL, "act_order must be 0 or 1");
+  const int sym = params_sym(p);
+  if (sym != 0 && sym != 1) return fail(GPTQ_EINVAL, "sym must be 0 or 1");
   return GPTQ_OK;
 }
 
 // gptq_factor_hinv only uses n, damp, act_order and n_quant.
 gptq_status check_factor_params(int64_t n, const gptq_params* p) {
   if (!p) return fail(GPTQ_EINVAL, "params is NULL");
-  if (p->struct_size < sizeof(gptq_params)) return fail(GPTQ_EINVAL, "params.struct_size too small");
+  if (p->struct_size < kParamsMin) return fail(GPTQ_EINVAL, "params.struct_size too small");
   if (n < 1 || n > (int64_t)1 << 30) return fail(GPTQ_EINVAL, "need 1 <= n <= 2^30");
   if (p->n_quant < 1 || p->n_quant > n) return fail(GPTQ_EINVAL, "n_quant must be in [1, n]");
   if (!(p->damp >= 0.f) || !std::isfinite(p->damp)) return fail(GPTQ_EINVAL, "damp must be finite and >= 0");
@@ -460,7 +471,7 @@ gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int
       float* Eb = E + (i0 - s0);
       SweepArgs a{};
       a.Wf = Wf; a.ldw = n; a.U = U; a.ldu = n; a.d_out = d_out; a.i0 = i0; a.ncols = nc;
-      a.block = B; a.group = p->group; a.bits = p->bits;
+      a.block = B; a.group = p->group; a.bits = p->bits; a.sym = params_sym(p);
       a.gbase = i0 / p->group;
       a.gshift = 31;
       if (p->group < B)

@@ -9,7 +9,9 @@
 //
 // For block [i0, i0+ncols) and every row independently, in column order j:
 //   at a group start: (s, z) from the group's current values
-//   q_j = clamp(rint(w_j / s) + z, 0, maxq), w_hat_j = s (q_j - z)
+//   q_j = clamp(rint(w_j / s) + z, 0, top), w_hat_j = s (q_j - z)
+// (top = maxq; on the symmetric alphabet {-A..A} of the GPTQ-intrinsic LoRA
+// page's finite-alphabet bounds, s = max|v| / A, z = A and top = 2A)
 //   e_j = (w_j - w_hat_j) / U_jj
 //   w_k -= e_j U_jk for the later columns k of the block
 // E (d_out x B) collects e_j for the trailing update of the later blocks.
@@ -137,13 +139,22 @@ __device__ __forceinline__ Grid group_start(const float (&w)[CPL], const SweepAr
   mn = row_min16(mn);
   mx = row_max16(mx);
   float xmin = fminf(mn, 0.f), xmax = fmaxf(mx, 0.f);
-  if (xmin == xmax) {
-    xmin = -1.f;
-    xmax = 1.f;
-  }
   Grid g;
-  g.s = (xmax - xmin) / maxq;
-  g.z = rintf(-xmin / g.s);
+  if (a.sym) {
+    // symmetric alphabet {-A..A}: s = max|v| / A, codes q + A (z = A)
+    const float A = 0.5f * (maxq - 1.f);
+    float amax = fmaxf(-xmin, xmax);
+    if (amax == 0.f) amax = 1.f;
+    g.s = amax / A;
+    g.z = A;
+  } else {
+    if (xmin == xmax) {
+      xmin = -1.f;
+      xmax = 1.f;
+    }
+    g.s = (xmax - xmin) / maxq;
+    g.z = rintf(-xmin / g.s);
+  }
   g.inv_s = 1.f / g.s;
   if (row_ok && L == 0) {
     const int64_t gi = a.gbase + (LO >> a.gshift);
@@ -162,7 +173,7 @@ __device__ __forceinline__ void start_group(SweepState<CPL>& S, const SweepArgs&
   S.z = g.z;
   S.inv_s = g.inv_s;
   S.nz = -g.z;
-  S.mz = maxq - g.z;
+  S.mz = (a.sym ? maxq - 1.f : maxq) - g.z;   // the largest code: 2A on the symmetric alphabet
 #pragma unroll
   for (int c = LO / 16; c < CPL; ++c) {
     const int col = 16 * c + L;
@@ -432,7 +443,7 @@ k_sweep(SweepArgs a) {
     S.z = row_ok ? (float)a.zeros[row * a.ngroups + gi] : 0.f;
     S.inv_s = 1.f / S.s;
     S.nz = -S.z;
-    S.mz = maxq - S.z;
+    S.mz = (a.sym ? maxq - 1.f : maxq) - S.z;
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       S.gs[c] = S.s;

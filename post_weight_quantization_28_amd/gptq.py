@@ -31,7 +31,7 @@ class _Params(ctypes.Structure):
     _fields_ = [("struct_size", ctypes.c_uint32), ("bits", ctypes.c_int32),
                 ("group", ctypes.c_int32), ("damp", ctypes.c_float),
                 ("block", ctypes.c_int32), ("act_order", ctypes.c_int32),
-                ("n_quant", ctypes.c_int64)]
+                ("n_quant", ctypes.c_int64), ("sym", ctypes.c_int32)]
 
 
 class _Outputs(ctypes.Structure):
@@ -123,10 +123,10 @@ def _workspace(nbytes, device, workspace):
     return ws, _dev(ws, "workspace")
 
 
-def make_params(bits=4, group=128, damp=0.01, block=128, act_order=False, n_quant=None, n=None):
+def make_params(bits=4, group=128, damp=0.01, block=128, act_order=False, n_quant=None, n=None, sym=False):
     nq = n if n_quant is None else n_quant
     return _Params(ctypes.sizeof(_Params), int(bits), int(group), float(damp), int(block),
-                   int(bool(act_order)), int(nq))
+                   int(bool(act_order)), int(nq), int(bool(sym)))
 
 
 # ---------------------------------------------------------------- Hessian
@@ -174,7 +174,7 @@ def workspace_bytes(d_out, n, params):
 
 
 def quantize_layer(W, H=None, X=None, bits=4, group=128, damp=0.01, block=128, act_order=False,
-                   n_quant=None, want_codes=False, workspace=None, outputs=None):
+                   n_quant=None, want_codes=False, workspace=None, outputs=None, sym=False):
     """GPTQ of W (d_out x n, bf16 or fp32) against H = 2 X^T X (given, or
     accumulated from X first). Returns a QuantResult of device tensors.
     ``outputs`` may hold preallocated tensors (same names as QuantResult)."""
@@ -186,7 +186,7 @@ def quantize_layer(W, H=None, X=None, bits=4, group=128, damp=0.01, block=128, a
         H = accumulate_hessian(X)
     _dev(H, "H")
     d_out, n = W.shape
-    p = make_params(bits, group, damp, block, act_order, n_quant, n)
+    p = make_params(bits, group, damp, block, act_order, n_quant, n, sym)
     nq = p.n_quant
     dev = W.device
     o = outputs or {}

@@ -123,7 +123,7 @@ def tie_branch_report(gpu_codes_orig, gpu_zeros, W, H64, orc, params, nq, tau=TA
             U = O.upper_chol_of_inverse(Hd)
             del Hd
         o = O.gptq_o2(W, None, p["bits"], p["group"], p["damp"], p["block"], p["act_order"], nq,
-                      U=U, perm=perm, alt=(alt_c, alt_z))
+                      U=U, perm=perm, alt=(alt_c, alt_z), sym=p.get("sym", False))
     rate = 1.0 - (g != o["codes_proc"]).mean()
     return rate, ties, sorted(bad)
 

@@ -77,6 +77,24 @@ def test_workspace_and_validation_on_host():
     assert st == G.gptq.EINVAL
 
 
+def test_params_versioning_and_sym_on_host():
+    """The parameter block grows at its end: a caller that knows only the
+    fields before `sym` (struct_size 32) gets the affine grid; sym must be 0
+    or 1 when given; a block shorter than the first version is refused."""
+    G, lib = _lib()
+    import ctypes
+    p = G.make_params(4, 128, 0.01, 128, False, None, 512, sym=True)
+    assert p.struct_size == ctypes.sizeof(p) and p.sym == 1
+    out = ctypes.c_size_t(0)
+    assert lib.gptq_workspace_bytes(64, 512, ctypes.byref(p), ctypes.byref(out)) == 0
+    p.sym = 2
+    assert lib.gptq_workspace_bytes(64, 512, ctypes.byref(p), ctypes.byref(out)) == -1
+    p.struct_size = 32                       # older callers: sym is not read
+    assert lib.gptq_workspace_bytes(64, 512, ctypes.byref(p), ctypes.byref(out)) == 0
+    p.struct_size = 28
+    assert lib.gptq_workspace_bytes(64, 512, ctypes.byref(p), ctypes.byref(out)) == -1
+
+
 def test_dequant_matmul_validation_on_host():
     """Argument checks of the inference product run on the host, before
     anything is enqueued (NULL device pointers are never dereferenced)."""

@@ -97,6 +97,12 @@ CASES = [
     ("c2", dict(d_out=64, n=1024, T=4096), dict(group=256)),
     # n % 4 != 0: the general trailing-update and flipped-build kernels
     ("c2", dict(d_out=56, n=266, T=4096), dict(n_quant=256, group=64)),
+    # the symmetric alphabet {-A..A}: 4, 3 (act-order) and 2 bits, and groups
+    # spanning two blocks (the second block reads the grid back)
+    ("c2", dict(d_out=200, n=640, T=8192), dict(sym=True)),
+    ("c3", dict(d_out=256, n=1024, T=8192), dict(sym=True)),
+    ("c3", dict(d_out=40, n=384, T=4096), dict(bits=2, group=64, block=128, sym=True)),
+    ("c2", dict(d_out=64, n=1024, T=4096), dict(group=256, sym=True)),
 ]
 
 
@@ -106,15 +112,19 @@ def test_quantize_parity(name, kw, over):
     p = dict(wl.params)
     p.update(over)
     nq = p.pop("n_quant", wl.n_quant)
+    sym = p.setdefault("sym", False)
     say("quantize", name, kw, p, "n_quant", nq)
     H64 = O.hessian(wl.X)
     H32 = torch.from_numpy(H64.astype(np.float32)).cuda()
     res = G.quantize_layer(w_dev(wl), H32, bits=p["bits"], group=p["group"], damp=p["damp"],
                            block=p["block"], act_order=p["act_order"], n_quant=nq,
-                           want_codes=True)
+                           want_codes=True, sym=sym)
     torch.cuda.synchronize()
     orc = O.gptq_o2(wl.W, H64.astype(np.float32), p["bits"], p["group"], p["damp"], p["block"],
-                    p["act_order"], nq)
+                    p["act_order"], nq, sym=sym)
+    if sym:
+        A = 2 ** (p["bits"] - 1) - 1
+        assert res.codes.max().item() <= 2 * A and bool((res.zeros == A).all())
     rep = {}
     check_quant(res, wl, H64, orc, p, nq, rep)
     say("  ", rep)

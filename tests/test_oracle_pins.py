@@ -109,6 +109,19 @@ def test_symmetric_alphabet_levels_and_odd_symmetry(bits):
     assert np.allclose(a["scales"] * A, g, rtol=1e-15, atol=0)
 
 
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_symmetric_alphabet_holds_under_feedback(bits):
+    """With feedback the later columns of a group can move past the scale's
+    range; their codes clamp to the alphabet's end, never to 2A + 1."""
+    W, X = _tiny(50 + bits, 24, 128, 600, heavy=True)
+    o = O.gptq_o2(W, O.hessian(X), bits, 64, 0.01, 32, sym=True)
+    A = 2 ** (bits - 1) - 1
+    assert o["codes"].max() <= 2 * A and np.all(o["zeros"] == A)
+    assert o["codes"].max() == 2 * A          # the clamp is reached on this input
+    q = o["w_hat"] / o["scales"][:, np.arange(128) // 64]
+    assert np.allclose(q, np.rint(q), atol=1e-9) and np.abs(np.rint(q)).max() <= A
+
+
 # ---------------------------------------------------------------- RTN special case
 @pytest.mark.parametrize("sym", [False, True])
 @pytest.mark.parametrize("bits", [2, 3, 4])
