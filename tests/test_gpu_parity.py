@@ -174,6 +174,21 @@ def test_pack_unpack_bit_exact(bits):
         assert np.array_equal(back.cpu().numpy(), c)
 
 
+def test_packed_zero_points():
+    """Packed zero points (a format variant): the quantizer's zero points
+    through the same packing call as the codes equal the oracle's packing of
+    them, and unpack back exactly."""
+    wl = synth.make_workload("c3", d_out=48, n=512, T=4096, group=32)
+    p = wl.params
+    res = G.quantize_layer(w_dev(wl), G.accumulate_hessian(x_dev(wl)), bits=p["bits"], group=32,
+                           damp=p["damp"], block=p["block"], act_order=p["act_order"])
+    ng = 512 // 32
+    qz = G.pack_codes(res.zeros, p["bits"])
+    assert qz.shape == (48, (ng * p["bits"] + 31) // 32)
+    assert np.array_equal(qz.cpu().numpy().view(np.uint32), P.pack(res.zeros.cpu().numpy(), p["bits"]))
+    assert torch.equal(G.unpack_codes(qz, ng, p["bits"]), res.zeros)
+
+
 # ---------------------------------------------------------------- edge cases
 def test_edge_cases():
     wl = synth.make_workload("c2", d_out=32, n=256, T=2048, group=64)
