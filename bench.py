@@ -42,13 +42,28 @@ HESSIAN_TRAFFIC = {
 }
 HESSIAN_SRC = os.path.join(ROOT, "post_weight_quantization_28_amd", "csrc", "hessian.hip")
 
+# The same record for the 16-token dequantising product (k_dequant_mv on the
+# packed 4096 x 4096 4-bit g128 layer), from `bench.py --workload
+# dequant_matmul --tokens 16 --steps 20 --warmup 2 --no-cpu-baseline
+# --copy-calibration` under the two counter passes.
+DEQUANT16_TRAFFIC = {
+    "bytes": 10424073,
+    "source_sha256": "4e040a0d7c7cb337fdaeeabd87e58871e6835fcb9332e109cdd5ed21e132202f",
+    "profile": "profiles/k_dequant_mv_4096x4096_4bit_16tok_hbm_traffic.md",
+}
+DEQUANT_SRC = os.path.join(ROOT, "post_weight_quantization_28_amd", "csrc", "dqmm.hip")
+
+
+def recorded_traffic(record, src):
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if record["bytes"] is None or sha != record["source_sha256"]:
+        return None
+    return record["bytes"]
+
 
 def hessian_traffic():
-    with open(HESSIAN_SRC, "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
-    if HESSIAN_TRAFFIC["bytes"] is None or sha != HESSIAN_TRAFFIC["source_sha256"]:
-        return None
-    return HESSIAN_TRAFFIC["bytes"]
+    return recorded_traffic(HESSIAN_TRAFFIC, HESSIAN_SRC)
 
 
 def log(*a):
@@ -117,6 +132,14 @@ def bench_dequant(args):
     ws = torch.empty(max(G.dequant_matmul_workspace_bytes(M, n, d_out, bits, group), 1), dtype=torch.uint8,
                      device=dev)
 
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        a.fill_(1)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
     def step():
         G.dequant_matmul(X, qw_dev, sc_dev, z_dev, bits, group, out=Y, workspace=ws)
 
@@ -138,12 +161,15 @@ def bench_dequant(args):
     flops = 2.0 * M * n * d_out
     if M <= 64:
         ach = (w_bytes + io_bytes) / (ms / 1e3) / 1e9
-        roof = {"bound": "hbm", "kernel": "k_dequant_mm (+ k_dequant_mm_reduce)", "achieved": ach,
-                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": None,
-                "work": "packed codes + scales + zeros + X + Y bytes per call"}
+        kern = "k_dequant_mv" if M <= 16 else "k_dequant_mm"
+        traffic = recorded_traffic(DEQUANT16_TRAFFIC, DEQUANT_SRC) if M == 16 else None
+        roof = {"bound": "hbm", "kernel": kern, "achieved": ach,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": traffic,
+                "work": "packed codes + scales + zeros + X + Y bytes per call; time between HIP events "
+                        "around back-to-back calls (launch gaps included)"}
     else:
         ach = flops / (ms / 1e3) / 1e12
-        roof = {"bound": "mfma", "kernel": "k_dequant_mm", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+        roof = {"bound": "mfma", "kernel": "k_dequant_mm_x", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS, "traffic": None,
                 "work": "2 M n d_out flop per call"}
     line = {
