@@ -116,3 +116,22 @@ def test_edges():
     a = G.dequant_matmul(X, *args, 4, 32)
     b = G.dequant_matmul(X, *args, 4, 32)
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("bits,sym", [(4, False), (3, False), (2, True)])
+def test_product_of_the_quantizers_own_output(bits, sym):
+    """Property over the whole chain on the GPU: the product of the packed
+    layer that quantize_layer emits equals X w_hat^T of that call's own
+    w_hat (float64 on the host), within the summation bound; so packing,
+    scales and zero points carry exactly the reconstruction the sweep used."""
+    wl = synth.make_workload("c2", d_out=160, n=768, T=4096)
+    Wd = torch.from_numpy(np.ascontiguousarray(wl.W_bits).view(np.int16)).view(torch.bfloat16).cuda()
+    Xd = torch.from_numpy(np.ascontiguousarray(wl.X_bits).view(np.int16)).view(torch.bfloat16).cuda()
+    res = G.quantize_layer(Wd, X=Xd, bits=bits, group=128, sym=sym)
+    x = wl.X[:24]
+    Y = G.dequant_matmul(Xd[:24].contiguous(), res.qweight, res.scales, res.zeros, bits, 128)
+    w_hat = res.w_hat.cpu().numpy().astype(np.float64)
+    ref = x.astype(np.float64) @ w_hat.T
+    mag = np.abs(x.astype(np.float64)) @ np.abs(w_hat).T
+    bound = (128 + 768 // 128 + 1) * 2.0 ** -24 * mag
+    assert np.all(np.abs(Y.cpu().numpy() - ref) <= bound)
