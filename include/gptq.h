@@ -178,12 +178,37 @@ gptq_status gptq_unpack_codes(void *stream, const uint32_t *qweight,
  * s (q - z).) */
 gptq_status gptq_dequant_matmul_workspace_bytes(int64_t M, int64_t n, int64_t d_out,
                                                 int32_t bits, int32_t group,
-                                                size_t *bytes);
+                                                int32_t permuted, size_t *bytes);
+/* perm: NULL, or n int32 column indices (see gptq_repack_act_order): the
+ * product is then X[:, perm] W_hat^T with qweight, scales and zeros in that
+ * column order; X is gathered into the workspace (permuted = 1 in the size
+ * call), so its rows need no alignment then. */
 gptq_status gptq_dequant_matmul(void *stream, const void *X, int32_t xdt, int64_t M,
                                 int64_t n, int64_t ldx, const uint32_t *qweight,
                                 const float *scales, const uint8_t *zeros,
-                                int64_t d_out, int32_t bits, int32_t group, float *Y,
-                                int64_t ldy, void *workspace, size_t ws_bytes);
+                                const int32_t *perm, int64_t d_out, int32_t bits,
+                                int32_t group, float *Y, int64_t ldy, void *workspace,
+                                size_t ws_bytes);
+
+/* ---- Act-order layers for the product ---------------------------------------
+ * A layer quantized with act-order has, in the original column order, groups
+ * that are not contiguous (g_idx). The product is invariant to one
+ * permutation of the columns of both X and W_hat, so such a layer is used
+ * through the order perm that lists group 0's columns, then group 1's, ...
+ * (a stable sort of g_idx): perm_out (n int32) receives it, qweight_out (same
+ * size as qweight) the codes repacked in that order, whose groups are then
+ * contiguous and match scales and zeros as quantize_layer wrote them. g_idx
+ * must give every group exactly `group` columns (as quantize_layer's does);
+ * otherwise perm is not a permutation and the product is wrong (entries of a
+ * short group stay 0; nothing is read out of bounds). Workspace:
+ * gptq_repack_act_order_workspace_bytes (d_out x n bytes of codes).
+ * Asynchronous. ("El balance de errores de la inferencia de pocos bits",
+ * section 1: the grouping direction is part of the format.) */
+gptq_status gptq_repack_act_order_workspace_bytes(int64_t d_out, int64_t n, size_t *bytes);
+gptq_status gptq_repack_act_order(void *stream, const uint32_t *qweight,
+                                  const int32_t *g_idx, int64_t d_out, int64_t n,
+                                  int32_t bits, int32_t group, uint32_t *qweight_out,
+                                  int32_t *perm_out, void *workspace, size_t ws_bytes);
 
 /* ---- Diagnostics ------------------------------------------------------------ */
 const char *gptq_status_string(int status);

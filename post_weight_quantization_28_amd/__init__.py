@@ -5,11 +5,11 @@ behind a C ABI (include/gptq.h); and, for inference, the dequantising product
 of a packed layer. This package is its Python binding."""
 from .gptq import (BF16, F32, GPTQError, QuantResult, accumulate_hessian, dequant_matmul,
                    dequant_matmul_workspace_bytes, factor_hinv, hessian_workspace_bytes, load, make_params, pack_codes, profile_collect,
-                   profile_enable, quantize_layer, unpack_codes, workspace_bytes, LIB_PATH,
+                   profile_enable, quantize_layer, repack_act_order, unpack_codes, workspace_bytes, LIB_PATH,
                    PROF_CLASSES)
 
 __all__ = ["BF16", "F32", "GPTQError", "QuantResult", "accumulate_hessian", "dequant_matmul",
            "dequant_matmul_workspace_bytes", "factor_hinv",
            "hessian_workspace_bytes", "load", "make_params", "pack_codes", "profile_collect",
-           "profile_enable", "quantize_layer", "unpack_codes", "workspace_bytes", "LIB_PATH",
+           "profile_enable", "quantize_layer", "repack_act_order", "unpack_codes", "workspace_bytes", "LIB_PATH",
            "PROF_CLASSES"]

@@ -186,6 +186,9 @@ struct DqPlan {
   size_t part_bytes;         // fp32 partials when splits > 1
 };
 DqPlan dequant_mm_plan(int64_t M, int64_t n, int64_t d_out, int bits, int group);
+hipError_t launch_group_order(hipStream_t s, const int32_t* g_idx, int64_t n, int group, int32_t* perm);
+hipError_t launch_gather_cols(hipStream_t s, const uint16_t* X, int64_t M, int64_t ldx, int64_t n,
+                              const int32_t* perm, uint16_t* Xp);
 hipError_t launch_dequant_mm(hipStream_t s, const DqPlan& p, const uint16_t* X, int64_t M, int64_t n,
                              int64_t ldx, const uint32_t* qw, const float* scales, const uint8_t* zeros,
                              int64_t d_out, int bits, int group, float* Y, int64_t ldy, float* part);

@@ -32,6 +32,7 @@
 //    so results do not depend on timing.
 #include "common.h"
 
+#include <algorithm>
 #include <type_traits>
 
 namespace gq {
@@ -469,6 +470,56 @@ k_dequant_mm_reduce(const float* __restrict__ part, int splits, int64_t M, int64
   float v = 0.f;
   for (int sp = 0; sp < splits; ++sp) v += part[(int64_t)sp * M * d_out + i];
   Y[(i / d_out) * ldy + i % d_out] = v;
+}
+
+// ---- act-order layers
+//
+// The product is invariant to one permutation applied to the columns of both
+// X and W_hat, so a layer whose groups are not contiguous in the original
+// column order (act-order) is used through any order that makes them
+// contiguous: pi lists the columns of group 0, then of group 1, ..., each
+// group's members in original order (a stable sort of g_idx).
+
+// perm[g * group + r] = the r-th column k (in original order) with
+// g_idx[k] == g; one thread per group. Entries of a group with fewer than
+// `group` members keep their prior (zero) value.
+__global__ void __launch_bounds__(256)
+k_group_order(const int32_t* __restrict__ g_idx, int64_t n, int group, int64_t ngroups,
+              int32_t* __restrict__ perm) {
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (g >= ngroups) return;
+  int64_t r = 0;
+  for (int64_t k = 0; k < n && r < group; ++k)
+    if (g_idx[k] == g) perm[g * group + r++] = (int32_t)k;
+}
+
+hipError_t launch_group_order(hipStream_t s, const int32_t* g_idx, int64_t n, int group, int32_t* perm) {
+  const int64_t ngroups = n / group;
+  if (ngroups == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_group_order, dim3((unsigned)ceil_div(ngroups, 256)), dim3(256), 0, s, g_idx, n, group,
+                     ngroups, perm);
+  return hipGetLastError();
+}
+
+// Xp[m][p] = X[m][perm[p]] (bf16 bits), Xp dense with row pitch n.
+__global__ void __launch_bounds__(256)
+k_gather_cols(const uint16_t* __restrict__ X, int64_t ldx, int64_t n, const int32_t* __restrict__ perm,
+              uint16_t* __restrict__ Xp) {
+  const int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t m = blockIdx.y;
+  if (p >= n) return;
+  Xp[m * n + p] = X[m * ldx + perm[p]];
+}
+
+hipError_t launch_gather_cols(hipStream_t s, const uint16_t* X, int64_t M, int64_t ldx, int64_t n,
+                              const int32_t* perm, uint16_t* Xp) {
+  if (M <= 0 || n <= 0) return hipSuccess;
+  for (int64_t m0 = 0; m0 < M; m0 += 65535) {
+    const int64_t rows = std::min<int64_t>(65535, M - m0);
+    hipLaunchKernelGGL(k_gather_cols, dim3((unsigned)ceil_div(n, 256), (unsigned)rows), dim3(256), 0, s,
+                       X + m0 * ldx, ldx, n, perm, Xp + m0 * n);
+  }
+  return hipGetLastError();
 }
 
 DqPlan dequant_mm_plan(int64_t M, int64_t n, int64_t d_out, int bits, int group) {

@@ -542,20 +542,53 @@ static gptq_status dq_check(int64_t M, int64_t n, int64_t d_out, int32_t bits, i
   return GPTQ_OK;
 }
 
+// bytes of the gathered activations (permuted product), then the partials
+static size_t dq_xp_bytes(int64_t M, int64_t n, int permuted) {
+  return permuted ? ((size_t)M * n * sizeof(uint16_t) + 255) / 256 * 256 : 0;
+}
+
 gptq_status gptq_dequant_matmul_workspace_bytes(int64_t M, int64_t n, int64_t d_out, int32_t bits,
-                                                int32_t group, size_t* bytes) {
+                                                int32_t group, int32_t permuted, size_t* bytes) {
   if (!bytes) return fail(GPTQ_EINVAL, "NULL pointer");
   const gptq_status st = dq_check(M, n, d_out, bits, group);
   if (st != GPTQ_OK) return st;
   const DqPlan p = dequant_mm_plan(M, n, d_out, bits, group);
-  *bytes = (p.part_bytes + 255) / 256 * 256;
+  *bytes = dq_xp_bytes(M, n, permuted) + (p.part_bytes + 255) / 256 * 256;
+  return GPTQ_OK;
+}
+
+gptq_status gptq_repack_act_order_workspace_bytes(int64_t d_out, int64_t n, size_t* bytes) {
+  if (!bytes) return fail(GPTQ_EINVAL, "NULL pointer");
+  if (d_out < 0 || n < 0) return fail(GPTQ_EINVAL, "negative size");
+  *bytes = ((size_t)d_out * n + 255) / 256 * 256;
+  return GPTQ_OK;
+}
+
+gptq_status gptq_repack_act_order(void* stream, const uint32_t* qweight, const int32_t* g_idx, int64_t d_out,
+                                  int64_t n, int32_t bits, int32_t group, uint32_t* qweight_out,
+                                  int32_t* perm_out, void* workspace, size_t ws_bytes) {
+  gptq_status st = dq_check(1, n, d_out, bits, group);
+  if (st != GPTQ_OK) return st;
+  if (n == 0) return GPTQ_OK;
+  if (!g_idx || !perm_out) return fail(GPTQ_EINVAL, "NULL pointer");
+  hipStream_t s = (hipStream_t)stream;
+  HIP_TRY(launch_fill_f32(s, reinterpret_cast<float*>(perm_out), (size_t)n, 0.f), "fill");   // int32 zeros
+  HIP_TRY(launch_group_order(s, g_idx, n, group, perm_out), "group order");
+  if (d_out == 0) return GPTQ_OK;
+  if (!qweight || !qweight_out) return fail(GPTQ_EINVAL, "NULL pointer");
+  size_t need = 0;
+  gptq_repack_act_order_workspace_bytes(d_out, n, &need);
+  if ((st = check_ws(workspace, ws_bytes, need)) != GPTQ_OK) return st;
+  uint8_t* codes = static_cast<uint8_t*>(workspace);
+  HIP_TRY(launch_unpack(s, qweight, d_out, n, bits, codes), "unpack");
+  HIP_TRY(launch_pack(s, codes, n, perm_out, d_out, n, bits, qweight_out), "pack");
   return GPTQ_OK;
 }
 
 gptq_status gptq_dequant_matmul(void* stream, const void* X, int32_t xdt, int64_t M, int64_t n, int64_t ldx,
                                 const uint32_t* qweight, const float* scales, const uint8_t* zeros,
-                                int64_t d_out, int32_t bits, int32_t group, float* Y, int64_t ldy,
-                                void* workspace, size_t ws_bytes) {
+                                const int32_t* perm, int64_t d_out, int32_t bits, int32_t group, float* Y,
+                                int64_t ldy, void* workspace, size_t ws_bytes) {
   gptq_status st = dq_check(M, n, d_out, bits, group);
   if (st != GPTQ_OK) return st;
   if (xdt != GPTQ_BF16) return fail(GPTQ_EINVAL, "dequant_matmul takes bf16 activations");
@@ -564,19 +597,32 @@ gptq_status gptq_dequant_matmul(void* stream, const void* X, int32_t xdt, int64_
   if (!Y) return fail(GPTQ_EINVAL, "NULL pointer");
   if (n > 0) {
     if (!X || !qweight || !scales || !zeros) return fail(GPTQ_EINVAL, "NULL pointer");
-    if (ldx < n || ldx % 8 != 0 || ((uintptr_t)X & 15) != 0)
+    if (perm == nullptr && (ldx < n || ldx % 8 != 0 || ((uintptr_t)X & 15) != 0))
       return fail(GPTQ_EINVAL, "X rows must be 16-byte aligned (ldx % 8 == 0, ldx >= n)");
+    if (perm != nullptr && ldx < n) return fail(GPTQ_EINVAL, "ldx < n");
     if (((uintptr_t)qweight & 15) != 0) return fail(GPTQ_EINVAL, "qweight must be 16-byte aligned");
   }
   const DqPlan p = dequant_mm_plan(M, n, d_out, bits, group);
   if (p.mtiles > 65535 || p.splits > 65535 || p.otiles > ((int64_t)1 << 31) - 1)
     return fail(GPTQ_EINVAL, "dequant_matmul: M or d_out too large for one launch");
-  if (p.part_bytes > 0) {
+  const int permuted = perm != nullptr && n > 0;
+  const size_t xp = dq_xp_bytes(M, n, permuted);
+  const size_t need = xp + (p.part_bytes + 255) / 256 * 256;
+  if (need > 0) {
     if (!workspace || ((uintptr_t)workspace & 255) != 0) return fail(GPTQ_EINVAL, "workspace: NULL or unaligned");
-    if (ws_bytes < p.part_bytes) return fail(GPTQ_EWORKSPACE, "workspace too small");
+    if (ws_bytes < need) return fail(GPTQ_EWORKSPACE, "workspace too small");
   }
-  HIP_TRY(launch_dequant_mm((hipStream_t)stream, p, static_cast<const uint16_t*>(X), M, n, ldx, qweight, scales,
-                            zeros, d_out, bits, group, Y, ldy, static_cast<float*>(workspace)),
+  hipStream_t s = (hipStream_t)stream;
+  const uint16_t* Xs = static_cast<const uint16_t*>(X);
+  int64_t ldxs = ldx;
+  if (permuted) {
+    uint16_t* Xp = static_cast<uint16_t*>(workspace);
+    HIP_TRY(launch_gather_cols(s, Xs, M, ldx, n, perm, Xp), "gather columns");
+    Xs = Xp;
+    ldxs = n;
+  }
+  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + xp);
+  HIP_TRY(launch_dequant_mm(s, p, Xs, M, n, ldxs, qweight, scales, zeros, d_out, bits, group, Y, ldy, part),
           "dequant_matmul");
   return GPTQ_OK;
 }

@@ -67,9 +67,12 @@ def load():
         "gptq_pack_codes": [c_vp, c_vp, c_i64, c_i64, ctypes.c_int32, c_vp],
         "gptq_unpack_codes": [c_vp, c_vp, c_i64, c_i64, ctypes.c_int32, c_vp],
         "gptq_dequant_matmul_workspace_bytes": [c_i64, c_i64, c_i64, ctypes.c_int32, ctypes.c_int32,
-                                                ctypes.POINTER(c_sz)],
-        "gptq_dequant_matmul": [c_vp, c_vp, ctypes.c_int32, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_i64,
-                                ctypes.c_int32, ctypes.c_int32, c_vp, c_i64, c_vp, c_sz],
+                                                ctypes.c_int32, ctypes.POINTER(c_sz)],
+        "gptq_dequant_matmul": [c_vp, c_vp, ctypes.c_int32, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp,
+                                c_i64, ctypes.c_int32, ctypes.c_int32, c_vp, c_i64, c_vp, c_sz],
+        "gptq_repack_act_order_workspace_bytes": [c_i64, c_i64, ctypes.POINTER(c_sz)],
+        "gptq_repack_act_order": [c_vp, c_vp, c_vp, c_i64, c_i64, ctypes.c_int32, ctypes.c_int32, c_vp, c_vp,
+                                  c_vp, c_sz],
         "gptq_profile_enable": [ctypes.c_int],
         "gptq_profile_collect": [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i64)],
     }
@@ -232,18 +235,19 @@ def factor_hinv(H, damp=0.01, act_order=False, n_quant=None, workspace=None):
 
 
 # ---------------------------------------------------------------- inference
-def dequant_matmul_workspace_bytes(M, n, d_out, bits, group):
+def dequant_matmul_workspace_bytes(M, n, d_out, bits, group, permuted=False):
     lib = load()
     out = ctypes.c_size_t(0)
     _check(lib.gptq_dequant_matmul_workspace_bytes(int(M), int(n), int(d_out), int(bits), int(group),
-                                                   ctypes.byref(out)))
+                                                   int(bool(permuted)), ctypes.byref(out)))
     return out.value
 
 
-def dequant_matmul(X, qweight, scales, zeros, bits, group, out=None, workspace=None):
+def dequant_matmul(X, qweight, scales, zeros, bits, group, perm=None, out=None, workspace=None):
     """Y = X W_hat^T (M x d_out fp32) from a packed layer: X (M x n bf16),
     qweight (d_out x n*bits/32 int32/uint32 words), scales (d_out x n/group
-    fp32), zeros (d_out x n/group uint8)."""
+    fp32), zeros (d_out x n/group uint8). With perm (from repack_act_order)
+    the layer is in that column order and X's columns are gathered by it."""
     lib = load()
     _dev(X, "X")
     if X.dtype != torch.bfloat16:
@@ -252,12 +256,28 @@ def dequant_matmul(X, qweight, scales, zeros, bits, group, out=None, workspace=N
     d_out = qweight.shape[0]
     Y = out if out is not None else torch.empty((M, d_out), dtype=torch.float32, device=X.device)
     _dev(Y, "Y")
-    need = dequant_matmul_workspace_bytes(M, n, d_out, bits, group)
+    need = dequant_matmul_workspace_bytes(M, n, d_out, bits, group, perm is not None)
     ws, wsp = _workspace(need, X.device, workspace)
+    pp = _dev(perm, "perm") if perm is not None else ctypes.c_void_p(0)
     _check(lib.gptq_dequant_matmul(_stream(), _dev(X, "X"), BF16, M, n, n, _dev(qweight, "qweight"),
-                                   _dev(scales, "scales"), _dev(zeros, "zeros"), d_out, int(bits), int(group),
-                                   _dev(Y, "Y"), d_out, wsp, need))
+                                   _dev(scales, "scales"), _dev(zeros, "zeros"), pp, d_out, int(bits),
+                                   int(group), _dev(Y, "Y"), d_out, wsp, need))
     return Y
+
+
+def repack_act_order(qweight, g_idx, n, bits, group, workspace=None):
+    """(qweight in group-contiguous column order, perm): see gptq_repack_act_order."""
+    lib = load()
+    d_out = qweight.shape[0]
+    out = torch.empty_like(qweight)
+    perm = torch.empty((n,), dtype=torch.int32, device=qweight.device)
+    c = ctypes.c_size_t(0)
+    _check(lib.gptq_repack_act_order_workspace_bytes(d_out, n, ctypes.byref(c)))
+    ws, wsp = _workspace(c.value, qweight.device, workspace)
+    _check(lib.gptq_repack_act_order(_stream(), _dev(qweight, "qweight"), _dev(g_idx, "g_idx"), d_out, n,
+                                     int(bits), int(group), _dev(out, "qweight_out"), _dev(perm, "perm"),
+                                     wsp, c.value))
+    return out, perm
 
 
 # ---------------------------------------------------------------- packing

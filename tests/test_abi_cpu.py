@@ -29,7 +29,8 @@ def test_header_declares_the_boundary():
     for must in ("gptq_accumulate_hessian", "gptq_quantize_layer", "gptq_workspace_bytes",
                  "gptq_hessian_workspace_bytes", "gptq_pack_codes", "gptq_unpack_codes",
                  "gptq_status_string", "gptq_factor_hinv", "gptq_dequant_matmul",
-                 "gptq_dequant_matmul_workspace_bytes"):
+                 "gptq_dequant_matmul_workspace_bytes", "gptq_repack_act_order",
+                 "gptq_repack_act_order_workspace_bytes"):
         assert must in names
 
 
@@ -113,13 +114,18 @@ def test_dequant_matmul_validation_on_host():
         assert e.value.status == -1
     null = ctypes.c_void_p(0)
     # fp32 activations are refused; so is a NULL X with work to do
-    assert lib.gptq_dequant_matmul(null, null, 1, 4, 128, 128, null, null, null, 64, 4, 128,
+    assert lib.gptq_dequant_matmul(null, null, 1, 4, 128, 128, null, null, null, null, 64, 4, 128,
                                    null, 64, null, 0) == -1
-    assert lib.gptq_dequant_matmul(null, null, 0, 4, 128, 128, null, null, null, 64, 4, 128,
+    assert lib.gptq_dequant_matmul(null, null, 0, 4, 128, 128, null, null, null, null, 64, 4, 128,
                                    null, 64, null, 0) == -1
     # nothing to do: M == 0
-    assert lib.gptq_dequant_matmul(null, null, 0, 0, 128, 128, null, null, null, 64, 4, 128,
+    assert lib.gptq_dequant_matmul(null, null, 0, 0, 128, 128, null, null, null, null, 64, 4, 128,
                                    null, 64, null, 0) == 0
+    # a permuted product gathers X into the workspace first
+    assert G.dequant_matmul_workspace_bytes(16, 4096, 4096, 4, 128, permuted=True) == 16 * 4096 * 2
+    out = ctypes.c_size_t(0)
+    assert lib.gptq_repack_act_order_workspace_bytes(4096, 11008, ctypes.byref(out)) == 0
+    assert out.value == (4096 * 11008 + 255) // 256 * 256
 
 
 def test_python_binding_refuses_host_tensors():

@@ -135,3 +135,33 @@ def test_product_of_the_quantizers_own_output(bits, sym):
     mag = np.abs(x.astype(np.float64)) @ np.abs(w_hat).T
     bound = (128 + 768 // 128 + 1) * 2.0 ** -24 * mag
     assert np.all(np.abs(Y.cpu().numpy() - ref) <= bound)
+
+
+@pytest.mark.parametrize("M", [16, 300])
+def test_act_order_layer(M):
+    """An act-order layer (groups not contiguous in the original column
+    order): repacked once into group-contiguous order, the product with X's
+    columns gathered through that order equals the oracle's product with
+    g_idx. The repacked codes are the original codes in that order, and the
+    order lists every group's columns in original order."""
+    wl = synth.make_workload("c3", d_out=96, n=1024, T=4096)
+    p = wl.params
+    assert p["act_order"]
+    o = O.gptq_o2(wl.W, O.hessian(wl.X), p["bits"], p["group"], p["damp"], p["block"], True)
+    qw = P.pack(o["codes"], p["bits"])
+    sc = o["scales"].astype(np.float32)
+    gi = o["g_idx"]
+    qd, perm = G.repack_act_order(torch.from_numpy(qw.view(np.int32)).cuda(), torch.from_numpy(gi).cuda(),
+                                  1024, p["bits"], p["group"])
+    perm = perm.cpu().numpy()
+    assert np.array_equal(perm, np.argsort(gi, kind="stable"))
+    assert np.array_equal(qd.cpu().numpy().view(np.uint32), P.pack(o["codes"][:, perm], p["bits"]))
+    x, xb = activations(900 + M, M, 1024)
+    X = torch.from_numpy(np.ascontiguousarray(xb).view(np.int16)).view(torch.bfloat16).cuda()
+    Y = G.dequant_matmul(X, qd, torch.from_numpy(sc).cuda(), torch.from_numpy(o["zeros"]).cuda(), p["bits"],
+                         p["group"], perm=torch.from_numpy(perm.astype(np.int32)).cuda())
+    ref = D.dequant_matmul(x, qw, sc, o["zeros"], p["bits"], p["group"], g_idx=gi)
+    mag = np.abs(x.astype(np.float64)) @ np.abs(D.dequantize(qw, sc, o["zeros"], p["bits"], p["group"], 1024,
+                                                             g_idx=gi)).T
+    bound = (p["group"] + 1024 // p["group"] + 1) * 2.0 ** -24 * mag
+    assert np.all(np.abs(Y.cpu().numpy() - ref) <= bound)
