@@ -47,8 +47,8 @@ HESSIAN_SRC = os.path.join(ROOT, "post_weight_quantization_28_amd", "csrc", "hes
 # dequant_matmul --tokens 16 --steps 20 --warmup 2 --no-cpu-baseline
 # --copy-calibration` under the two counter passes.
 DEQUANT16_TRAFFIC = {
-    "bytes": 10424073,
-    "source_sha256": "4e040a0d7c7cb337fdaeeabd87e58871e6835fcb9332e109cdd5ed21e132202f",
+    "bytes": 10424147,
+    "source_sha256": "fd34db3af77fbf5b2cc1c7e18a3f37d1c7d6cdfd05fe5ff447e2adfd781df555",
     "profile": "profiles/k_dequant_mv_4096x4096_4bit_16tok_hbm_traffic.md",
 }
 DEQUANT_SRC = os.path.join(ROOT, "post_weight_quantization_28_amd", "csrc", "dqmm.hip")
