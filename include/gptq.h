@@ -161,15 +161,16 @@ gptq_status gptq_unpack_codes(void *stream, const uint32_t *qweight,
  * only: xdt must be GPTQ_BF16, row pitch ldx >= n with ldx % 8 == 0, 16-byte
  * aligned base) and W_hat[o][k] = scales[o][k/group] * (q[o][k] -
  * zeros[o][k/group]), the codes q read from qweight in the layout above
- * (d_out x n*bits/32 words, 16-byte aligned base: n_quant = n, contiguous
- * groups, i.e. a layer
- * quantized without act-order, or whose g_idx is k / group). group must be a
- * positive multiple of 32 that divides n. Products of bf16 activations and
- * the integers q - z are exact in fp32 and each group's sum is scaled once
- * (the weights are never rounded to bf16); sums are fp32 in a fixed order,
- * so results are bitwise reproducible. Workspace:
- * gptq_dequant_matmul_workspace_bytes (0 when one pass covers the whole
- * product; otherwise fp32 partials of a split over the groups).
+ * (d_out x n*bits/32 words, 16-byte aligned base, n_quant = n). Groups must
+ * be contiguous in qweight's column order: a layer quantized without
+ * act-order as it is, an act-order layer after gptq_repack_act_order (then
+ * pass its perm). group must be a positive multiple of 32 that divides n.
+ * Products of bf16 activations and the integers q - z are exact in fp32 and
+ * each group's sum is scaled once (the weights are never rounded to bf16);
+ * sums are fp32 in a fixed order, so results are bitwise reproducible.
+ * Workspace: gptq_dequant_matmul_workspace_bytes (the gathered activations
+ * when permuted, and fp32 partials when few output tiles split the groups;
+ * 0 when neither applies).
  * Asynchronous on ``stream``. M == 0 or d_out == 0 enqueues nothing; n == 0
  * writes zeros.
  * ("El balance de errores de la inferencia de pocos bits", section 6: the
