@@ -102,8 +102,51 @@ def pin_block_inv(O):
     assert np.allclose(a["w_hat"], b["w_hat"], atol=1e-12)
 
 
+def pin_tie_distance(O):
+    x = np.array([0.5, 1.0, -0.5, 2.49, 3.0, -1.25, -0.75, 7.5, -2.0, -2.51])
+    want = [0.0, 0.5, 0.0, 0.01, 0.5, 0.25, 0.25, 0.0, 0.5, 0.01]
+    assert np.allclose(O.tie_distance(x), want, atol=1e-12, rtol=0)
+
+
+def pin_layer_error(O):
+    r = np.random.default_rng(12)
+    X = r.standard_t(4, (300, 24))
+    W = r.standard_normal((7, 24)) * 0.02
+    Wh = O.rtn(W, 3, 8)["w_hat"]
+    ref = np.linalg.norm(X @ (W - Wh).T) ** 2 / np.linalg.norm(X @ W.T) ** 2
+    assert abs(O.layer_error(W, Wh, O.hessian(X)) - ref) <= 1e-12 * ref
+
+
+def pin_dead_column(O):
+    r = np.random.default_rng(33)
+    n, j = 16, 5
+    X = r.standard_normal((200, n))
+    X[:, j] = 0.0
+    W = r.standard_normal((6, n)) * 0.02
+    W[:, j] = 0.5 * W[:, 0]
+    H = O.hessian(X)
+    keep = np.delete(np.arange(n), j)
+    d = np.diag(H)
+    lam = 0.01 * (d.sum() + 1.0) / n
+    full = O.gptq_o2(W, H, 4, n, 0.01, n)
+    red = O.gptq_o2(W[:, keep], H[np.ix_(keep, keep)], 4, n - 1, lam / (d[keep].sum() / (n - 1)), n - 1)
+    assert np.allclose(full["w_hat"][:, keep], red["w_hat"], atol=1e-13, rtol=0)
+    extra = (W[:, j] - full["w_hat"][:, j]) ** 2 * (1.0 + lam)
+    assert np.allclose(full["row_loss"], red["row_loss"] + extra, rtol=1e-10, atol=0)
+
+
+def pin_chol_reversal(O):
+    r = np.random.default_rng(9)
+    A = r.standard_normal((80, 24))
+    Hd = 2.0 * A.T @ A + 0.1 * np.eye(24)
+    U = O.upper_chol_of_inverse_by_reversal(Hd)
+    assert np.array_equal(U, np.triu(U)) and np.all(np.diag(U) > 0)
+    assert np.abs(U.T @ U @ Hd - np.eye(24)).max() < 1e-10
+
+
 BATTERY = [pin_hessian, pin_grid, pin_o1_o2, pin_loss, pin_n2, pin_perm,
-           pin_rtn_special, pin_block_inv]
+           pin_rtn_special, pin_block_inv, pin_tie_distance, pin_layer_error, pin_dead_column,
+           pin_chol_reversal]
 
 
 def _caught(O):
@@ -138,6 +181,19 @@ MUTATIONS = [
     ("O1 update without 1/G00", "Wp[:, j + 1:] -= np.outer(delta / g00, G[0, 1:])",
      "Wp[:, j + 1:] -= np.outer(delta, G[0, 1:])"),
     ("group start off by one", "if j % group == 0:", "if j % group == 1 or j == 0:"),
+    ("tie distance without floor", "f = pre - np.floor(pre)", "f = pre - np.trunc(pre)"),
+    ("tie distance to the integer", "return np.abs(f - 0.5)", "return np.minimum(f, 1.0 - f)"),
+    ("tie distance signed", "return np.abs(f - 0.5)", "return f - 0.5"),
+    ("layer error on damped H", "num = row_objective(W, W_hat, H).sum()",
+     "num = row_objective(W, W_hat, H + 0.01 * np.mean(np.diag(H)) * np.eye(len(H))).sum()"),
+    ("layer error over the weight norm", "den = row_objective(W, np.zeros_like(W), H).sum()",
+     "den = float((W * W).sum())"),
+    ("dead-column fix skipped", "H[dead, dead] = 1.0", "H[dead, dead] = 0.0"),
+    ("dead-column value 2", "H[dead, dead] = 1.0", "H[dead, dead] = 2.0"),
+    ("reversal route without the reversal", "A = np.array(np.asarray(Hd, np.float64)[::-1, ::-1], order=",
+     "A = np.array(np.asarray(Hd, np.float64), order="),
+    ("reversal route returns the lower factor", "return np.ascontiguousarray(Li[::-1, ::-1]).reshape(n, n)",
+     "return np.ascontiguousarray(Li).reshape(n, n)"),
 ]
 
 

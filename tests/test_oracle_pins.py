@@ -354,6 +354,22 @@ def test_cholesky_factor_of_inverse():
     assert np.abs(U.T @ U @ Hd - np.eye(64)).max() < 1e-10
 
 
+@pytest.mark.parametrize("n", [1, 7, 64, 333])
+def test_cholesky_factor_by_reversal(n):
+    """P-CHOL for the route used on the widest layer (one Cholesky of the
+    index-reversed H_d and a triangular inverse): U upper, positive
+    diagonal, U^T U H_d = I, and equal to the explicit-inverse route."""
+    _, X = _tiny(35 + n, 1, n, 4 * n + 8)
+    Hd, _ = O.prepare(O.hessian(X), 0.01)
+    U = O.upper_chol_of_inverse_by_reversal(Hd)
+    assert np.array_equal(U, np.triu(U))
+    assert np.all(np.diag(U) > 0)
+    assert np.abs(U.T @ U @ Hd - np.eye(n)).max() < 1e-10
+    assert np.abs(U - O.upper_chol_of_inverse(Hd)).max() <= 1e-12 * np.abs(U).max()
+    with pytest.raises(np.linalg.LinAlgError):
+        O.upper_chol_of_inverse_by_reversal(-Hd)
+
+
 def test_act_order_is_permuted_problem():
     """P-PERM: act-order = plain GPTQ on the problem permuted by descending
     diag(H) (stable), un-permuted afterwards."""
@@ -371,8 +387,9 @@ def test_act_order_is_permuted_problem():
 
 
 def test_dead_column_reading():
-    """R3: a zero diagonal entry behaves as a column of unit curvature that
-    no other column couples to; its code is plain RTN on its current value."""
+    """R3 end to end on a tiny layer: the result is finite and O1 and O2 agree
+    (the decoupling and the round-to-nearest code of the dead column are
+    asserted by test_dead_column_is_decoupled_unit_curvature)."""
     W, X = _tiny(32, 4, 16, 100)
     X[:, 5] = 0.0
     H = O.hessian(X)
@@ -514,3 +531,121 @@ def test_storage_examples_from_pages():
     assert M.gb(M.raw_weight_bytes(ll["n_params"], 16)) == ll["fp16_gb_approx"]
     assert M.gb(M.raw_weight_bytes(ll["n_params"], 4)) < ll["int4_total_gb_approx"]
     assert M.bits_per_weight(4, 128) == 4.28125
+
+
+# ---------------------------------------------------------------- tie distance
+def test_tie_distance_hand_values():
+    """The distance of a pre-rounding value to the nearest half-integer, in
+    steps, worked by hand: exact half-integers (positive, negative, a
+    zero-point value) are 0, integers are 0.5, and a value 0.01 below a
+    half-integer is 0.01, on either side of zero."""
+    x = np.array([0.5, 1.0, -0.5, 2.49, 3.0, -1.25, -0.75, 7.5, -2.0, 0.0, -2.51, 14.5])
+    want = np.array([0.0, 0.5, 0.0, 0.01, 0.5, 0.25, 0.25, 0.0, 0.5, 0.5, 0.01, 0.0])
+    assert np.allclose(O.tie_distance(x), want, atol=1e-12, rtol=0)
+
+
+def test_tie_distance_is_distance_to_the_rounding_boundary():
+    """Brute force: the distance equals min over k of |x - (k + 1/2)|, and it
+    is the decision's margin: moving x by less than it never changes rint(x),
+    moving it slightly past it (towards the nearest half-integer) does."""
+    r = np.random.default_rng(3)
+    x = np.concatenate([r.uniform(-20, 20, 4000), np.arange(-12, 12) + 0.5 + r.uniform(-1e-3, 1e-3, 24)])
+    halves = np.arange(-40, 41) + 0.5
+    ref = np.abs(x[:, None] - halves[None, :]).min(1)
+    d = O.tie_distance(x)
+    assert np.allclose(d, ref, atol=1e-12, rtol=0)
+    keep = d > 1e-6
+    xs, ds = x[keep], d[keep]
+    near = np.where(xs - np.floor(xs) < 0.5, 1.0, -1.0)   # direction of the nearest half-integer
+    assert np.array_equal(np.rint(xs + near * ds * 0.999), np.rint(xs))
+    assert np.array_equal(np.rint(xs - near * ds * 0.999), np.rint(xs))
+    assert np.all(np.rint(xs + near * (ds + 1e-7)) != np.rint(xs))
+
+
+def test_zero_point_margin_hand_worked():
+    """The margin of a zero-point decision: 3-bit (maxq 7), a row whose range
+    is [-0.625, 1.125] gives s = 0.25 and -xmin/s = 2.5 exactly (a tie, z =
+    rint(2.5) = 2, half to even); a row with range [-0.25, 1.5] gives
+    -xmin/s = 1 (margin 0.5). H = 2I: no feedback, the grid is the input's."""
+    W = np.array([[-0.625, 1.125, 0.0, 0.5], [1.5, -0.25, 0.125, 0.375]])
+    o = O.gptq_o2(W, 2.0 * np.eye(4), 3, 4, 0.01, 4)
+    assert np.array_equal(o["scales"][:, 0], [0.25, 0.25])
+    assert np.array_equal(o["zeros"][:, 0], [2, 1])
+    assert np.allclose(o["zmargins"][:, 0], [0.0, 0.5], atol=1e-15)
+    # code margins: row 1 is w / s = 6, -1, 0.5, 1.5
+    assert np.allclose(o["margins"][1], [0.5, 0.5, 0.0, 0.0], atol=1e-15)
+
+
+# ---------------------------------------------------------------- layer error
+def test_layer_error_hand_worked():
+    """r = ||X (W - W_hat)^T||^2 / ||X W^T||^2 ("Resumen Técnico:
+    GPTQ-intrinsic LoRA", "Declaración del Problema"), by hand:
+    X = [[1, 0], [1, 1]], W = [1, 2], W_hat = [1, 1]: X W^T = (1, 3), norm^2
+    10; X (W - W_hat)^T = (0, 1), norm^2 1; r = 0.1. Any positive scale of H
+    gives the same r."""
+    X = np.array([[1.0, 0.0], [1.0, 1.0]])
+    W = np.array([[1.0, 2.0]])
+    Wh = np.array([[1.0, 1.0]])
+    assert O.layer_error(W, Wh, O.hessian(X)) == pytest.approx(0.1, rel=1e-15)
+    assert O.layer_error(W, Wh, X.T @ X) == pytest.approx(0.1, rel=1e-15)
+
+
+def test_layer_error_from_activations():
+    """The same ratio formed from X directly, on a random layer: the
+    undamped H, all rows, the output-space norm."""
+    r = np.random.default_rng(12)
+    X = r.standard_t(4, (300, 24))
+    W = r.standard_normal((7, 24)) * 0.02
+    o = O.gptq_o2(W, O.hessian(X), 3, 8, 0.01, 8)
+    ref = np.linalg.norm(X @ (W - o["w_hat"]).T) ** 2 / np.linalg.norm(X @ W.T) ** 2
+    assert O.layer_error(W, o["w_hat"], O.hessian(X)) == pytest.approx(ref, rel=1e-12)
+
+
+# ---------------------------------------------------------------- dead columns (R3)
+def _dead_problem(seed, n=16, j=5):
+    r = np.random.default_rng(seed)
+    X = r.standard_normal((200, n))
+    X[:, j] = 0.0
+    W = r.standard_normal((6, n)) * 0.02
+    W[:, j] = 0.5 * W[:, 0]          # inside every row's range: the grid does not depend on it
+    return W, O.hessian(X), j
+
+
+@pytest.mark.parametrize("damp", [0.0, 0.01])
+def test_dead_column_is_decoupled_unit_curvature(damp):
+    """R3: a column no token activates (H_jj = 0) takes H_jj := 1 before
+    damping. Then it couples to no other column: the other columns' codes
+    and w_hat equal GPTQ on the problem with that column removed (with the
+    damping matched: lambda = damp * mean of the diagonal including the 1);
+    its own code is round-to-nearest of its original value on its group's
+    grid; and the row loss gains exactly (w_j - w_hat_j)^2 (1 + lambda)."""
+    W, H, j = _dead_problem(33)
+    n = H.shape[0]
+    keep = np.delete(np.arange(n), j)
+    d = np.diag(H)
+    lam = damp * (d.sum() + 1.0) / n
+    damp_red = lam / (d[keep].sum() / (n - 1))
+    for run in (lambda W_, H_, g, dm: O.gptq_o2(W_, H_, 4, g, dm, g),
+                lambda W_, H_, g, dm: O.gptq_o1(W_, H_, 4, g, dm)):
+        full = run(W, H, n, damp)
+        red = run(W[:, keep], H[np.ix_(keep, keep)], n - 1, damp_red)
+        assert np.array_equal(full["codes"][:, keep], red["codes"])
+        assert np.allclose(full["w_hat"][:, keep], red["w_hat"], atol=1e-13, rtol=0)
+        s, z = full["scales"][:, 0], full["zeros"][:, 0].astype(np.float64)
+        assert np.array_equal(full["scales"][:, 0], red["scales"][:, 0])
+        q = np.clip(np.rint(W[:, j] / s) + z, 0, 15)
+        assert np.array_equal(full["codes"][:, j], q.astype(np.uint8))
+        assert np.array_equal(full["w_hat"][:, j], s * (q - z))
+        extra = (W[:, j] - full["w_hat"][:, j]) ** 2 * (1.0 + lam)
+        assert np.allclose(full["row_loss"], red["row_loss"] + extra, rtol=1e-10, atol=0)
+
+
+def test_dead_column_in_act_order():
+    """With act-order the fixed diagonal value 1 takes its place in the
+    stable descending sort like any other entry."""
+    W, H, j = _dead_problem(34)
+    d = np.diag(H).copy()
+    d[j] = 1.0
+    want = sorted(range(len(d)), key=lambda i: (-d[i], i))
+    _, perm = O.prepare(H, 0.01, act_order=True)
+    assert list(perm) == want
