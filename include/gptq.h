@@ -124,7 +124,20 @@ gptq_status gptq_accumulate_hessian(void *stream, const void *X, gptq_dtype xdt,
  * Synchronises ``stream`` before returning to read the device status:
  * GPTQ_ENOTPD / GPTQ_ENONFINITE set *fail_col (if fail_col != NULL) to the
  * first offending ORIGINAL column (-1 if unknown); outputs are then
- * unspecified. d_out == 0 is a no-op. */
+ * unspecified. d_out == 0 is a no-op.
+ * Workspace: gptq_workspace_bytes(d_out, n, p) bytes, 256-byte aligned,
+ * owned by the caller, not read before it is written (its contents on entry
+ * do not matter). It holds the factorisation (two n x n fp32 matrices and
+ * U's split-bf16 parts), the fp32 working weights, one super-block of
+ * errors and the processing-order codes.
+ * ("GPTQ" (wikiprompt.org), "Enfoque Técnico": the columns are quantized in
+ * turn and the columns not yet quantized get the closed-form Optimal Brain
+ * Quantization correction, with groups of weights sharing a scale;
+ * "El balance de errores de la inferencia de pocos bits", section 1: scale,
+ * zero point, rounding and packing fields of the format; "Resumen Técnico:
+ * GPTQ-intrinsic LoRA", "Detalles de Implementación": the Cholesky
+ * factorisation of the lambda-regularised Hessian; "Metodología" 2: appended
+ * columns n_quant..n-1 that absorb the feedback unrounded.) */
 gptq_status gptq_workspace_bytes(int64_t d_out, int64_t n, const gptq_params *p,
                                  size_t *bytes);
 gptq_status gptq_quantize_layer(void *stream, const void *W, gptq_dtype wdt,

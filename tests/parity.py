@@ -76,7 +76,7 @@ def first_mismatch_report(gpu_codes_orig, gpu_zeros, orc, group, tau=TAU):
     return rate, len(rows), bad
 
 
-def tie_branch_report(gpu_codes_orig, gpu_zeros, W, H64, orc, params, nq, tau=TAU, max_ties=16):
+def tie_branch_report(gpu_codes_orig, gpu_zeros, W, H64, orc, params, nq, tau=TAU, max_ties=16, U=None):
     """Follow the oracle's own branches at its ties.
 
     Where the first decision (processing order) in which a row differs is
@@ -85,58 +85,74 @@ def tie_branch_report(gpu_codes_orig, gpu_zeros, W, H64, orc, params, nq, tau=TA
     again with that decision's other rounding (gptq_o2's ``alt``) and the
     row compared again, until it matches or differs somewhere that is not a
     tie. The oracle computes each branch itself; the GPU's output only
-    selects which of the oracle's branches a row is compared with.
+    selects which of the oracle's branches a row is compared with. The sweep
+    is independent per row given U, so only the rows that took a new branch
+    are run again (U: the oracle's factor, computed here when not given).
     Returns (identity against the branched oracle, ties followed per row,
     bad rows)."""
     p = params
     perm = orc["perm"]
     g = np.asarray(gpu_codes_orig)[:, perm[:nq]]
     gz = np.asarray(gpu_zeros)
-    U = None
-    alt_c, alt_z = [], []
+    W = np.asarray(W)
+    codes_o = orc["codes_proc"].copy()
+    zeros_o = orc["zeros"].copy()
+    margins = orc["margins"].copy()
+    zmargins = orc["zmargins"].copy()
+    alts = {}
     ties = np.zeros(len(g), int)
     bad = set()
-    o = orc
     for it in range(max_ties + 1):
-        cm = g != o["codes_proc"]
-        zm = gz != o["zeros"]
+        cm = g != codes_o
+        zm = gz != zeros_o
         pending = [int(r) for r in np.nonzero(cm.any(1) | zm.any(1))[0] if int(r) not in bad]
         if not pending:
             break
         if it == max_ties:
             bad.update(pending)
             break
+        rerun = []
         for r in pending:
             jc = int(np.argmax(cm[r])) if cm[r].any() else nq
             zi = int(np.argmax(zm[r])) if zm[r].any() else zm.shape[1]
             jz = zi * p["group"] if zi < zm.shape[1] else nq
-            if jz <= jc and o["zmargins"][r, zi] < tau:
-                alt_z.append((r, zi))
-            elif jz > jc and o["margins"][r, jc] < tau:
-                alt_c.append((r, jc))
+            ac, az = alts.setdefault(r, ([], []))
+            if jz <= jc and zmargins[r, zi] < tau:
+                az.append(zi)
+            elif jz > jc and margins[r, jc] < tau:
+                ac.append(jc)
             else:
                 bad.add(r)
                 continue
             ties[r] += 1
+            rerun.append(r)
+        if not rerun:
+            continue
         if U is None:
             Hd, _ = O.prepare(H64, p["damp"], p["act_order"], nq)
             U = O.upper_chol_of_inverse(Hd)
             del Hd
-        o = O.gptq_o2(W, None, p["bits"], p["group"], p["damp"], p["block"], p["act_order"], nq,
+        alt_c = [(i, k) for i, r in enumerate(rerun) for k in alts[r][0]]
+        alt_z = [(i, k) for i, r in enumerate(rerun) for k in alts[r][1]]
+        o = O.gptq_o2(W[rerun], None, p["bits"], p["group"], p["damp"], p["block"], p["act_order"], nq,
                       U=U, perm=perm, alt=(alt_c, alt_z), sym=p.get("sym", False))
-    rate = 1.0 - (g != o["codes_proc"]).mean()
+        codes_o[rerun] = o["codes_proc"]
+        zeros_o[rerun] = o["zeros"]
+        margins[rerun] = o["margins"]
+        zmargins[rerun] = o["zmargins"]
+    rate = 1.0 - (g != codes_o).mean()
     return rate, ties, sorted(bad)
 
 
-def check_quant(res, wl, H64, orc, params, nq, report=None, min_identity=0.999):
+def check_quant(res, wl, H64, orc, params, nq, report=None, min_identity=0.999, U=None):
     """Apply the acceptance rules to a QuantResult against oracle output:
-    the plain identity (at least ``min_identity``, None: reported only), the
-    first-mismatch tie rule, identity 1 against the oracle's tie branches,
-    the layer error and g_idx."""
+    the plain identity (at least ``min_identity``), the first-mismatch tie
+    rule, identity 1 against the oracle's tie branches, the layer error and
+    g_idx. U: the oracle's factor when the caller already has it."""
     codes = res.codes.cpu().numpy()
     zeros = res.zeros.cpu().numpy()
     rate, nrows, bad = first_mismatch_report(codes, zeros, orc, params["group"])
-    brate, ties, bbad = tie_branch_report(codes, zeros, wl.W, H64, orc, params, nq)
+    brate, ties, bbad = tie_branch_report(codes, zeros, wl.W, H64, orc, params, nq, U=U)
     w_hat = res.w_hat.cpu().numpy().astype(np.float64)
     r_gpu = O.layer_error(wl.W, w_hat, H64)
     r_orc = O.layer_error(wl.W, orc["w_hat"], H64)
@@ -145,8 +161,7 @@ def check_quant(res, wl, H64, orc, params, nq, report=None, min_identity=0.999):
                 branch_bad_rows=bbad[:10], r_gpu=r_gpu, r_oracle=r_orc)
     if report is not None:
         report.update(info)
-    if min_identity is not None:
-        assert rate >= min_identity, info
+    assert rate >= min_identity, info
     assert not bad, info
     assert not bbad and brate == 1.0, info
     assert abs(r_gpu - r_orc) <= 1e-3 * r_orc, info

@@ -4,14 +4,18 @@
   * the augmented layer, 5120 x (5120 + 64), 2-bit, n_quant 5120 (X given);
   * the large 2-bit layer, 8192 x 28672, g64, with H given.
 
-Where the float64 oracle can afford it (the first two), it recomputes H from
-the same seeded X and runs its sweep on a seeded sample of rows (the sweep is
-independent per row given U, so sampled rows are exact oracle rows; with
-act-order, see test_given_x_full_size). On every row of every shape,
-properties that hold at any size are checked (parity.check_any_size:
-format, the loss identity sum_j e_j^2 = delta^T H_d delta, and a layer error
-below round-to-nearest's), and a second call must give bit-identical
-outputs.
+For the first two the float64 oracle recomputes H from the same seeded X and
+runs its sweep on every row of the layer; the acceptance rules (at least
+99.9 % identical codes over the whole layer, every row's first difference an
+oracle tie, identity 1 against the oracle's tie branches, layer error within
+1e-3) apply to all rows (with act-order, see test_given_x_full_size). For
+the large layer the oracle factorises the full 28672-wide damped H itself
+(float64, LAPACK) and sweeps a seeded sample of rows: the sweep is
+independent per row given U, so sampled rows are exact oracle rows. On every
+row of every shape, properties that hold at any size are checked
+(parity.check_any_size: format, the loss identity sum_j e_j^2 = delta^T H_d
+delta, and a layer error below round-to-nearest's), and a second call must
+give bit-identical outputs.
 
 The large layer's H is an input (float64 accumulation of its Gaussian-plus-
 spike X, rounded once to fp32); the test forms it with a float64 GEMM on the
@@ -48,18 +52,31 @@ def run_layer(wl, H):
                             want_codes=True)
 
 
-def check_sampled_rows(wl, H64, res, nrows, seed, t0, min_identity=0.999):
-    """Exact oracle rows: the acceptance rules of the reduced-size parity tests."""
+def oracle_factor(wl, H64, reversal=False):
     p = wl.params
-    rows = np.sort(np.random.default_rng(seed).choice(wl.d_out, nrows, replace=False))
-    orc = O.gptq_o2(wl.W[rows], H64, p["bits"], p["group"], p["damp"], p["block"],
-                    p["act_order"], wl.n_quant)
-    rt = torch.from_numpy(rows).cuda()
-    sub = types.SimpleNamespace(codes=res.codes[rt], zeros=res.zeros[rt], w_hat=res.w_hat[rt],
-                                g_idx=res.g_idx)
+    Hd, perm = O.prepare(H64, p["damp"], p["act_order"], wl.n_quant)
+    U = O.upper_chol_of_inverse_by_reversal(Hd) if reversal else O.upper_chol_of_inverse(Hd)
+    return U, perm
+
+
+def check_rows(wl, H64, res, rows, t0, U, perm):
+    """Exact oracle rows (all, or a seeded sample): the acceptance rules of
+    the reduced-size parity tests, the 99.9 % identity included."""
+    p = wl.params
+    orc = O.gptq_o2(wl.W[rows], None, p["bits"], p["group"], p["damp"], p["block"],
+                    p["act_order"], wl.n_quant, U=U, perm=perm)
+    say(f"{wl.name}: oracle sweep of {len(rows)} rows at {time.perf_counter() - t0:.1f} s")
+    if len(rows) == wl.d_out:
+        sub, wsub = res, wl
+    else:
+        rt = torch.from_numpy(rows).cuda()
+        sub = types.SimpleNamespace(codes=res.codes[rt], zeros=res.zeros[rt], w_hat=res.w_hat[rt],
+                                    g_idx=res.g_idx)
+        wsub = types.SimpleNamespace(W=wl.W[rows])
     rep = {}
-    check_quant(sub, types.SimpleNamespace(W=wl.W[rows]), H64, orc, p, wl.n_quant, rep, min_identity)
-    say(f"{wl.name}: {nrows} oracle rows at {time.perf_counter() - t0:.1f} s: {rep}")
+    check_quant(sub, wsub, H64, orc, p, wl.n_quant, rep, U=U)
+    say(f"{wl.name}: {len(rows)} oracle rows at {time.perf_counter() - t0:.1f} s: {rep}")
+    return rep
 
 
 def check_deterministic(wl, H, res):
@@ -89,33 +106,32 @@ def check_order(wl, H64, Hg, t0):
     assert np.array_equal(np.sort(perm), np.arange(wl.n_quant))
 
 
-def check_layer_error_rows(wl, H64, res, nrows, seed, t0):
-    """Sampled rows, oracle on its own float64 H: relative layer error within 1e-3."""
+def check_layer_error_all_rows(wl, H64, res, t0):
+    """Every row, oracle on its own float64 H and its own order: relative
+    layer error within 1e-3."""
     p = wl.params
-    rows = np.sort(np.random.default_rng(seed).choice(wl.d_out, nrows, replace=False))
-    orc = O.gptq_o2(wl.W[rows], H64, p["bits"], p["group"], p["damp"], p["block"],
-                    p["act_order"], wl.n_quant)
-    r_gpu = O.layer_error(wl.W[rows], res.w_hat.cpu().numpy()[rows].astype(np.float64), H64)
-    r_orc = O.layer_error(wl.W[rows], orc["w_hat"], H64)
-    say(f"{wl.name}: {nrows} rows, layer error {r_gpu:.6e} vs oracle {r_orc:.6e} "
+    orc = O.gptq_o2(wl.W, H64, p["bits"], p["group"], p["damp"], p["block"], p["act_order"], wl.n_quant)
+    r_gpu = O.layer_error(wl.W, res.w_hat.cpu().numpy().astype(np.float64), H64)
+    r_orc = O.layer_error(wl.W, orc["w_hat"], H64)
+    say(f"{wl.name}: all {wl.d_out} rows, layer error {r_gpu:.6e} vs oracle {r_orc:.6e} "
         f"at {time.perf_counter() - t0:.1f} s")
     assert abs(r_gpu - r_orc) <= 1e-3 * r_orc
 
 
-@pytest.mark.parametrize("name,nrows", [("c3", 16), ("c5", 32)])
-def test_given_x_full_size(name, nrows):
+@pytest.mark.parametrize("name", ["c3", "c5"])
+def test_given_x_full_size(name):
     """X -> H on the GPU -> quantize_layer on the GPU, as a user runs it.
 
-    Without act-order, sampled rows are exact oracle rows (oracle H from X).
-    With act-order the processing order depends on near-equal diagonal
+    Without act-order every row is compared with the oracle (oracle H from
+    X). With act-order the processing order depends on near-equal diagonal
     entries (see check_order), so the end-to-end run is held to the order's
-    validity, the layer error and the any-size properties, and exact code
-    parity is checked on a second run whose H input is the oracle's float64
-    H rounded once to fp32, given to both sides (same keys, same order)."""
+    validity, the layer error over all rows and the any-size properties, and
+    exact code parity over all rows is checked on a second run whose H input
+    is the oracle's float64 H rounded once to fp32, given to both sides (same
+    keys, same order)."""
     t0 = time.perf_counter()
     wl = synth.make_workload(name)
     p = wl.params
-    seed = 20240605 + wl.recipe["index"]
     say(f"{name}: inputs {wl.d_out}x{wl.n} (n_quant {wl.n_quant}), T={wl.T} "
         f"ready in {time.perf_counter() - t0:.1f} s")
     X = x_dev(wl)
@@ -133,19 +149,21 @@ def test_given_x_full_size(name, nrows):
     assert err <= 1e-5
     assert np.array_equal(Hg, Hg.T)
     wl.X = wl.X_bits = None
+    rows = np.arange(wl.d_out)
 
     if not p["act_order"]:
-        check_sampled_rows(wl, H64, res, nrows, seed, t0)
+        U, perm = oracle_factor(wl, H64)
+        check_rows(wl, H64, res, rows, t0, U, perm)
+        del U
     else:
         check_order(wl, H64, Hg, t0)
-        check_layer_error_rows(wl, H64, res, nrows, seed, t0)
+        check_layer_error_all_rows(wl, H64, res, t0)
         H32 = H64.astype(np.float32)
         res_given = run_layer(wl, torch.from_numpy(H32).cuda())
-        # 3-bit rows 11008 long: one tie cascades over thousands of later
-        # codes of its row, so the plain identity of a small row sample is
-        # reported, and the rows are held to the tie-branch rule instead
-        check_sampled_rows(wl, H32.astype(np.float64), res_given, nrows, seed, t0, min_identity=None)
-        del res_given
+        Hq = H32.astype(np.float64)
+        U, perm = oracle_factor(wl, Hq)
+        check_rows(wl, Hq, res_given, rows, t0, U, perm)
+        del res_given, U, Hq
     check_any_size(wl, Hg, res, t0, say)
 
 
@@ -164,7 +182,14 @@ def gram_f64_on_device(chunks):
     return out
 
 
+C4_ORACLE_ROWS = 256
+
+
 def test_large_2bit_given_hessian_full_size():
+    """8192 x 28672, 2-bit g64, fp32 H given (rank-32 spike): the oracle
+    factorises the full damped H in float64 and sweeps a seeded sample of
+    rows, which must meet every acceptance rule; every row is held to the
+    any-size properties and to determinism."""
     t0 = time.perf_counter()
     wl = synth.make_workload("c4", H_fn=gram_f64_on_device)
     say(f"c4: inputs {wl.d_out}x{wl.n}, H given from T={wl.T}, "
@@ -177,3 +202,9 @@ def test_large_2bit_given_hessian_full_size():
     del H
     torch.cuda.empty_cache()
     check_any_size(wl, wl.H, res, t0, say)
+
+    H64 = wl.H.astype(np.float64)
+    U, perm = oracle_factor(wl, H64, reversal=True)
+    say(f"c4: oracle factor of the 28672-wide damped H at {time.perf_counter() - t0:.1f} s")
+    rows = np.sort(np.random.default_rng(20240609).choice(wl.d_out, C4_ORACLE_ROWS, replace=False))
+    check_rows(wl, H64, res, rows, t0, U, perm)

@@ -76,7 +76,7 @@ def test_factor_matches_lapack(n, act_order):
     assert np.array_equal(Ug, np.triu(Ug))
     err = rel_fro(Ug, Uo)
     say("factor", n, act_order, "rel fro", err)
-    assert err < 2e-4
+    assert err < 5e-6
 
 
 # ---------------------------------------------------------------- quantize_layer
@@ -226,5 +226,94 @@ def test_dead_column_matches_oracle():
     assert H64[17, 17] == 0.0
     res = G.quantize_layer(w_dev(wl), torch.from_numpy(H64.astype(np.float32)).cuda(), group=64,
                            want_codes=True)
-    orc = O.gptq_o2(wl.W, H64, 4, 64, 0.01, 128)
-    check_quant(res, wl, H64, orc, dict(group=64), wl.n_quant)
+    p = dict(wl.params)
+    assert (p["bits"], p["group"], p["damp"], p["block"], p["act_order"]) == (4, 64, 0.01, 128, False)
+    orc = O.gptq_o2(wl.W, H64, p["bits"], p["group"], p["damp"], p["block"])
+    check_quant(res, wl, H64, orc, p, wl.n_quant)
+
+
+@pytest.mark.parametrize("act_order", [False, True])
+def test_degenerate_groups_match_oracle(act_order):
+    """Groups whose current values are all zero at their first column take
+    the range (-1, 1): rows whose first group (processing order) is zero and
+    rows that are zero throughout, against the oracle."""
+    wl = synth.make_workload("c2", d_out=64, n=512, T=4096, group=64, act_order=act_order)
+    # both sides take the same fp32 H, so the act-order keys are the same
+    H32 = O.hessian(wl.X).astype(np.float32)
+    H64 = H32.astype(np.float64)
+    _, perm = O.prepare(H64, wl.params["damp"], act_order)
+    first = perm[:64]
+    for r in range(0, 64, 4):
+        wl.W[r, first] = 0.0
+        wl.W_bits[r, first] = 0
+    wl.W[5] = 0.0
+    wl.W_bits[5] = 0
+    p = dict(wl.params)
+    res = G.quantize_layer(w_dev(wl), torch.from_numpy(H32).cuda(), bits=p["bits"],
+                           group=p["group"], damp=p["damp"], block=p["block"], act_order=act_order,
+                           want_codes=True)
+    orc = O.gptq_o2(wl.W, H64, p["bits"], p["group"], p["damp"], p["block"], act_order)
+    # -xmin/s = maxq/2 exactly: every zero point of a degenerate group is a
+    # tie, and the group's codes all equal its zero point, so whichever
+    # rounding a side takes there, every code of the group follows it. The
+    # plain identity is therefore taken over the other groups; the tie rule
+    # and identity 1 against the oracle's tie branches cover all of them.
+    deg = np.zeros((64, 512 // 64), bool)
+    deg[0::4, 0] = True
+    deg[5, :] = True
+    assert np.all(orc["zmargins"][deg] < 1e-12)
+    check_quant(res, wl, H64, orc, p, wl.n_quant, min_identity=0.0)
+    gcodes = res.codes.cpu().numpy()[:, perm]
+    other = ~np.repeat(deg, 64, axis=1)
+    assert (gcodes == orc["codes_proc"])[other].mean() >= 0.999
+    zeros = res.zeros.cpu().numpy()
+    assert np.array_equal(gcodes[np.repeat(deg, 64, axis=1)].reshape(-1, 64).min(1),
+                          zeros[deg])                       # codes of a degenerate group = its z
+    maxq = (1 << p["bits"]) - 1
+    # either neighbour of maxq / 2 is correct at a tie; the codes equal z and w_hat is 0
+    assert np.all(np.isin(zeros[0::4, 0], [maxq // 2, maxq // 2 + 1]))
+    assert np.all(np.isin(zeros[5], [maxq // 2, maxq // 2 + 1]))
+    assert np.all(res.w_hat.cpu().numpy()[5] == 0.0)
+    assert np.allclose(res.scales.cpu().numpy()[5], 2.0 / maxq, rtol=1e-6, atol=0)
+
+
+@pytest.mark.parametrize("act_order", [False, True])
+def test_nonfinite_inputs_report_original_column(act_order):
+    """NaN or Inf in H or W: GPTQ_ENONFINITE, and fail_col is the smallest
+    ORIGINAL column involved, with act-order too."""
+    wl = synth.make_workload("c2", d_out=32, n=256, T=2048, group=64)
+    W = w_dev(wl)
+    H = G.accumulate_hessian(x_dev(wl))
+    kw = dict(group=64, act_order=act_order)
+    for (i, j, v) in [(40, 201, float("nan")), (133, 133, float("inf")), (90, 7, float("-inf"))]:
+        Hb = H.clone()
+        Hb[i, j] = v
+        Hb[j, i] = v
+        with pytest.raises(G.GPTQError) as e:
+            G.quantize_layer(W, Hb, **kw)
+        assert e.value.status == -3 and e.value.fail_col == min(i, j), (i, j, e.value.fail_col)
+    Wn = W.clone()
+    Wn[3, 150] = float("nan")
+    Wn[9, 211] = float("inf")
+    with pytest.raises(G.GPTQError) as e:
+        G.quantize_layer(Wn, H, **kw)
+    assert e.value.status == -3 and e.value.fail_col == 150
+    # the library still works afterwards
+    res = G.quantize_layer(W, H, **kw)
+    assert torch.isfinite(res.w_hat).all()
+
+
+def test_not_pd_reports_original_column_under_act_order():
+    """An indefinite damped Hessian: GPTQ_ENOTPD at the first failing pivot,
+    reported as its ORIGINAL column. H = diag(d) with one negative entry
+    large enough to survive the damping: with act-order that column is
+    processed last, and its original index is reported."""
+    n = 256
+    d = np.linspace(2.0, 1.0, n)
+    d[37] = -50.0
+    H = torch.from_numpy(np.diag(d).astype(np.float32)).cuda()
+    wl = synth.make_workload("c2", d_out=16, n=n, T=1024, group=64)
+    for ao in (False, True):
+        with pytest.raises(G.GPTQError) as e:
+            G.quantize_layer(w_dev(wl), H, group=64, act_order=ao)
+        assert e.value.status == -2 and e.value.fail_col == 37, (ao, e.value.fail_col)
