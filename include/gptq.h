@@ -204,6 +204,30 @@ gptq_status gptq_dequant_matmul(void *stream, const void *X, int32_t xdt, int64_
                                 int32_t group, float *Y, int64_t ldy, void *workspace,
                                 size_t ws_bytes);
 
+/* ---- The product without a workspace -----------------------------------------
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, serving loops that must not call hipMalloc, harnesses that
+ * forbid it. Same arguments, result and errors as gptq_dequant_matmul (the
+ * same kernels, bit-identical Y), but its scratch (the gathered activations
+ * of a permuted product, the fp32 partials of a split product) lives in a
+ * static device array of GPTQ_NOALLOC_SCRATCH_BYTES that the library holds
+ * on every GPU it runs on until the process ends; nothing is allocated or
+ * freed. A product whose scratch, gptq_dequant_matmul_workspace_bytes(M, n,
+ * d_out, bits, group, perm != NULL), exceeds that size returns GPTQ_EINVAL
+ * before anything is enqueued. The array belongs to the current device
+ * (hipGetDevice): ``stream`` must be a stream of that device. Every call on
+ * one GPU shares that GPU's array, so calls that may overlap on one GPU
+ * (concurrent streams, several host threads) race and give wrong results:
+ * serialise them. The array keeps the last call's contents; every value a
+ * call reads from it was written by the same call. */
+#define GPTQ_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+gptq_status gptq_dequant_matmul_noalloc(void *stream, const void *X, int32_t xdt,
+                                        int64_t M, int64_t n, int64_t ldx,
+                                        const uint32_t *qweight, const float *scales,
+                                        const uint8_t *zeros, const int32_t *perm,
+                                        int64_t d_out, int32_t bits, int32_t group,
+                                        float *Y, int64_t ldy);
+
 /* ---- Act-order layers for the product ---------------------------------------
  * A layer quantized with act-order has, in the original column order, groups
  * that are not contiguous (g_idx). The product is invariant to one

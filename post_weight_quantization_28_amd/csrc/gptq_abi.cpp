@@ -585,10 +585,23 @@ gptq_status gptq_repack_act_order(void* stream, const uint32_t* qweight, const i
   return GPTQ_OK;
 }
 
-gptq_status gptq_dequant_matmul(void* stream, const void* X, int32_t xdt, int64_t M, int64_t n, int64_t ldx,
-                                const uint32_t* qweight, const float* scales, const uint8_t* zeros,
-                                const int32_t* perm, int64_t d_out, int32_t bits, int32_t group, float* Y,
-                                int64_t ldy, void* workspace, size_t ws_bytes) {
+}  // extern "C"
+
+namespace {
+
+// Bytes of scratch one gptq_dequant_matmul call needs (the gathered
+// activations when permuted, then the fp32 partials); valid arguments only.
+size_t dq_need(int64_t M, int64_t n, int64_t d_out, int32_t bits, int32_t group, int permuted) {
+  const DqPlan p = dequant_mm_plan(M, n, d_out, bits, group);
+  return dq_xp_bytes(M, n, permuted) + (p.part_bytes + 255) / 256 * 256;
+}
+
+// Argument checks shared by both dequant_matmul entry points (host only,
+// nothing enqueued). *run = 0 when there is nothing to launch.
+gptq_status dq_validate(const void* X, int32_t xdt, int64_t M, int64_t n, int64_t ldx, const uint32_t* qweight,
+                        const float* scales, const uint8_t* zeros, const int32_t* perm, int64_t d_out,
+                        int32_t bits, int32_t group, float* Y, int64_t ldy, int* run) {
+  *run = 0;
   gptq_status st = dq_check(M, n, d_out, bits, group);
   if (st != GPTQ_OK) return st;
   if (xdt != GPTQ_BF16) return fail(GPTQ_EINVAL, "dequant_matmul takes bf16 activations");
@@ -605,26 +618,96 @@ gptq_status gptq_dequant_matmul(void* stream, const void* X, int32_t xdt, int64_
   const DqPlan p = dequant_mm_plan(M, n, d_out, bits, group);
   if (p.mtiles > 65535 || p.splits > 65535 || p.otiles > ((int64_t)1 << 31) - 1)
     return fail(GPTQ_EINVAL, "dequant_matmul: M or d_out too large for one launch");
+  *run = 1;
+  return GPTQ_OK;
+}
+
+// The launches of one product, with `scratch` (at least dq_need bytes,
+// 256-byte aligned) already checked by the caller.
+gptq_status dq_enqueue(hipStream_t s, const void* X, int64_t M, int64_t n, int64_t ldx, const uint32_t* qweight,
+                       const float* scales, const uint8_t* zeros, const int32_t* perm, int64_t d_out,
+                       int32_t bits, int32_t group, float* Y, int64_t ldy, void* scratch) {
+  const DqPlan p = dequant_mm_plan(M, n, d_out, bits, group);
   const int permuted = perm != nullptr && n > 0;
   const size_t xp = dq_xp_bytes(M, n, permuted);
-  const size_t need = xp + (p.part_bytes + 255) / 256 * 256;
-  if (need > 0) {
-    if (!workspace || ((uintptr_t)workspace & 255) != 0) return fail(GPTQ_EINVAL, "workspace: NULL or unaligned");
-    if (ws_bytes < need) return fail(GPTQ_EWORKSPACE, "workspace too small");
-  }
-  hipStream_t s = (hipStream_t)stream;
   const uint16_t* Xs = static_cast<const uint16_t*>(X);
   int64_t ldxs = ldx;
   if (permuted) {
-    uint16_t* Xp = static_cast<uint16_t*>(workspace);
+    uint16_t* Xp = static_cast<uint16_t*>(scratch);
     HIP_TRY(launch_gather_cols(s, Xs, M, ldx, n, perm, Xp), "gather columns");
     Xs = Xp;
     ldxs = n;
   }
-  float* part = reinterpret_cast<float*>(static_cast<char*>(workspace) + xp);
+  float* part = reinterpret_cast<float*>(static_cast<char*>(scratch) + xp);
   HIP_TRY(launch_dequant_mm(s, p, Xs, M, n, ldxs, qweight, scales, zeros, d_out, bits, group, Y, ldy, part),
           "dequant_matmul");
   return GPTQ_OK;
+}
+
+// ---- the allocation-free variant's scratch: one array per GPU, in the code
+// object's device memory (each device that loads the library holds its own
+// copy until the process ends). Host code never uses the array's name as an
+// address: the device address comes from hipGetSymbolAddress, once per
+// device, and only that address is passed to kernels.
+static __device__ __align__(256) unsigned char scratch[GPTQ_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;   // indexed by device ordinal; nullptr = not looked up yet
+
+gptq_status scratch_for_current_device(void** out) {
+  int dev = -1;
+  HIP_TRY(hipGetDevice(&dev), "hipGetDevice");
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if ((size_t)dev >= g_scratch_ptr.size()) g_scratch_ptr.resize((size_t)dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+    if (!p || ((uintptr_t)p & 255) != 0) return fail(GPTQ_EHIP, "static scratch address is NULL or unaligned");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return GPTQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gptq_status gptq_dequant_matmul(void* stream, const void* X, int32_t xdt, int64_t M, int64_t n, int64_t ldx,
+                                const uint32_t* qweight, const float* scales, const uint8_t* zeros,
+                                const int32_t* perm, int64_t d_out, int32_t bits, int32_t group, float* Y,
+                                int64_t ldy, void* workspace, size_t ws_bytes) {
+  int run = 0;
+  gptq_status st = dq_validate(X, xdt, M, n, ldx, qweight, scales, zeros, perm, d_out, bits, group, Y, ldy, &run);
+  if (st != GPTQ_OK || !run) return st;
+  const size_t need = dq_need(M, n, d_out, bits, group, perm != nullptr && n > 0);
+  if (need > 0) {
+    if (!workspace || ((uintptr_t)workspace & 255) != 0) return fail(GPTQ_EINVAL, "workspace: NULL or unaligned");
+    if (ws_bytes < need) return fail(GPTQ_EWORKSPACE, "workspace too small");
+  }
+  return dq_enqueue((hipStream_t)stream, X, M, n, ldx, qweight, scales, zeros, perm, d_out, bits, group, Y, ldy,
+                    workspace);
+}
+
+gptq_status gptq_dequant_matmul_noalloc(void* stream, const void* X, int32_t xdt, int64_t M, int64_t n,
+                                        int64_t ldx, const uint32_t* qweight, const float* scales,
+                                        const uint8_t* zeros, const int32_t* perm, int64_t d_out, int32_t bits,
+                                        int32_t group, float* Y, int64_t ldy) {
+  int run = 0;
+  gptq_status st = dq_validate(X, xdt, M, n, ldx, qweight, scales, zeros, perm, d_out, bits, group, Y, ldy, &run);
+  if (st != GPTQ_OK || !run) return st;
+  const size_t need = dq_need(M, n, d_out, bits, group, perm != nullptr && n > 0);
+  if (need > (size_t)GPTQ_NOALLOC_SCRATCH_BYTES) {
+    char msg[160];
+    snprintf(msg, sizeof msg, "dequant_matmul_noalloc: this product needs %zu bytes of scratch; the static "
+             "scratch holds %zu (use gptq_dequant_matmul with a workspace)", need,
+             (size_t)GPTQ_NOALLOC_SCRATCH_BYTES);
+    return fail(GPTQ_EINVAL, msg);
+  }
+  void* ws = nullptr;
+  if (need > 0 && (st = scratch_for_current_device(&ws)) != GPTQ_OK) return st;
+  return dq_enqueue((hipStream_t)stream, X, M, n, ldx, qweight, scales, zeros, perm, d_out, bits, group, Y, ldy,
+                    ws);
 }
 
 }  // extern "C"

@@ -70,6 +70,8 @@ def load():
                                                 ctypes.c_int32, ctypes.POINTER(c_sz)],
         "gptq_dequant_matmul": [c_vp, c_vp, ctypes.c_int32, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp, c_vp,
                                 c_i64, ctypes.c_int32, ctypes.c_int32, c_vp, c_i64, c_vp, c_sz],
+        "gptq_dequant_matmul_noalloc": [c_vp, c_vp, ctypes.c_int32, c_i64, c_i64, c_i64, c_vp, c_vp, c_vp,
+                                        c_vp, c_i64, ctypes.c_int32, ctypes.c_int32, c_vp, c_i64],
         "gptq_repack_act_order_workspace_bytes": [c_i64, c_i64, ctypes.POINTER(c_sz)],
         "gptq_repack_act_order": [c_vp, c_vp, c_vp, c_i64, c_i64, ctypes.c_int32, ctypes.c_int32, c_vp, c_vp,
                                   c_vp, c_sz],
@@ -262,6 +264,30 @@ def dequant_matmul(X, qweight, scales, zeros, bits, group, perm=None, out=None, 
     _check(lib.gptq_dequant_matmul(_stream(), _dev(X, "X"), BF16, M, n, n, _dev(qweight, "qweight"),
                                    _dev(scales, "scales"), _dev(zeros, "zeros"), pp, d_out, int(bits),
                                    int(group), _dev(Y, "Y"), d_out, wsp, need))
+    return Y
+
+
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
+
+
+def dequant_matmul_noalloc(X, qweight, scales, zeros, bits, group, perm=None, out=None):
+    """dequant_matmul without a workspace: the library's static per-GPU
+    scratch holds the gathered activations and partials (at most
+    NOALLOC_SCRATCH_BYTES; larger products raise). ``out`` (M x d_out fp32)
+    lets a caller that cannot allocate pass Y as well. Calls that may overlap
+    on one GPU race."""
+    lib = load()
+    _dev(X, "X")
+    if X.dtype != torch.bfloat16:
+        raise TypeError("X must be bfloat16")
+    M, n = X.shape
+    d_out = qweight.shape[0]
+    Y = out if out is not None else torch.empty((M, d_out), dtype=torch.float32, device=X.device)
+    _dev(Y, "Y")
+    pp = _dev(perm, "perm") if perm is not None else ctypes.c_void_p(0)
+    _check(lib.gptq_dequant_matmul_noalloc(_stream(), _dev(X, "X"), BF16, M, n, n, _dev(qweight, "qweight"),
+                                           _dev(scales, "scales"), _dev(zeros, "zeros"), pp, d_out, int(bits),
+                                           int(group), _dev(Y, "Y"), d_out))
     return Y
 
 

@@ -133,3 +133,28 @@ def test_python_binding_refuses_host_tensors():
     import torch
     with pytest.raises(TypeError):
         G.pack_codes(torch.zeros((2, 8), dtype=torch.uint8), 4)
+
+
+def test_noalloc_product_rejects_oversized_scratch_on_host():
+    """The allocation-free product checks its scratch need against the static
+    array's size on the host and returns GPTQ_EINVAL before any HIP call:
+    a permuted 8192 x 8192 product needs 128 MiB of gathered activations.
+    (Pointers are never dereferenced on this path; they only need the
+    alignment the argument checks ask for.)"""
+    G, lib = _lib()
+    fake = ctypes.c_void_p(1 << 20)
+    need = G.dequant_matmul_workspace_bytes(8192, 8192, 4096, 4, 128, permuted=True)
+    assert need > G.NOALLOC_SCRATCH_BYTES
+    st = lib.gptq_dequant_matmul_noalloc(None, fake, 0, 8192, 8192, 8192, fake, fake, fake, fake, 4096, 4, 128,
+                                         fake, 4096)
+    assert st == -1
+    assert b"scratch" in lib.gptq_last_error()
+    # nothing to do: no launch, no scratch lookup
+    assert lib.gptq_dequant_matmul_noalloc(None, fake, 0, 0, 8192, 8192, fake, fake, fake, fake, 4096, 4, 128,
+                                           fake, 4096) == 0
+    # the same argument checks as the workspace entry point
+    assert lib.gptq_dequant_matmul_noalloc(None, fake, 1, 16, 4096, 4096, fake, fake, fake, None, 4096, 4, 128,
+                                           fake, 4096) == -1
+    assert G.NOALLOC_SCRATCH_BYTES == 64 * 1024 * 1024
+    hdr = open(HEADER).read()
+    assert "#define GPTQ_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)" in hdr
