@@ -7,7 +7,13 @@ at 4 bits, group 128, block 128. Inputs are resident in HBM before the timed
 region; every step recomputes everything from X and W.
 
 Prints one JSON line: the step throughput, the Hessian kernel against the bf16
-MFMA roofline, and the float64 oracle timed on the host cores.
+MFMA roofline, the phases of quantize_layer (factorisation, sweep, far-field
+update) with the sweep's HBM rate and the far field's MFMA rate, the copy and
+GEMM rates this box measures, and the float64 oracle timed on the host cores.
+
+`--config c3|c4|c5` times the other layer shapes the same way: 4096 x 11008
+3-bit act-order, 8192 x 28672 2-bit with H given (the step is quantize_layer
+alone; its roofline is the far-field update's), 5120 x 5184 augmented 2-bit.
 
 `--workload dequant_matmul --tokens M` instead times the inference product
 Y = X W_hat^T of a packed 4096 x 4096 4-bit g128 layer for M tokens (decode:
@@ -70,34 +76,74 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(wl, X_vals, p, sample_tokens=4096, sample_rows=64):
-    """The float64 oracle, untuned, on a bounded sample of the same workload,
-    scaled to the whole layer step."""
-    import numpy as np
-    from oracle import gptq_f64 as O
+def host_blas():
+    """(threads, description) of the BLAS numpy uses on this host, and the CPU model."""
+    import numpy  # noqa: F401  (loads the BLAS so that threadpoolctl sees it)
+    threads, blas = None, "unknown BLAS"
     try:
         from threadpoolctl import threadpool_info
-        cores = sum(i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas") or None
+        libs = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+        if libs:
+            threads = sum(i.get("num_threads", 0) for i in libs) or None
+            blas = ", ".join(f"{i.get('internal_api')} {i.get('version')} ({i.get('architecture')}, "
+                             f"{i.get('num_threads')} threads)" for i in libs)
     except Exception:
-        cores = None
-    T, n = X_vals.shape
+        pass
+    cpu = "unknown CPU"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return threads, f"{cpu}; {os.cpu_count()} logical CPUs; {blas}"
+
+
+def cpu_baseline(wl, X_vals, p, sample_tokens=4096, sample_rows=64, given_h=False, sub_n=8192):
+    """The float64 oracle, untuned, on a bounded sample of the same workload,
+    scaled to the whole layer step. With H given (the 28672-wide layer) the
+    step has no Hessian, and the factorisation and the sweep run on the
+    leading sub_n columns, scaled by (n / sub_n)^3 and (n / sub_n)^2."""
+    import numpy as np
+    from oracle import gptq_f64 as O
+    cores, host = host_blas()
+    if given_h:
+        n = wl.H.shape[0]
+        m = min(sub_n, n)
+        Hs = wl.H[:m, :m].astype(np.float64)
+        Ws = wl.W[:sample_rows, :m]
+        t_h = 0.0
+        f_scale, s_scale = (n / m) ** 3, (wl.d_out / sample_rows) * (n / m) ** 2
+        nq_s = m
+    else:
+        T, n = X_vals.shape
+        t0 = time.perf_counter()
+        Hs = O.hessian(X_vals[:sample_tokens])
+        t_h = (time.perf_counter() - t0) * (T / sample_tokens)
+        Ws = wl.W[:sample_rows]
+        f_scale, s_scale = 1.0, wl.d_out / sample_rows
+        nq_s = wl.n_quant
     t0 = time.perf_counter()
-    Hs = O.hessian(X_vals[:sample_tokens])
-    t_h = (time.perf_counter() - t0) * (T / sample_tokens)
-    t0 = time.perf_counter()
-    Hd, perm = O.prepare(Hs, p["damp"], p["act_order"], wl.n_quant)
+    Hd, perm = O.prepare(Hs, p["damp"], p["act_order"], nq_s)
     U = O.upper_chol_of_inverse(Hd)
-    t_f = time.perf_counter() - t0
+    t_f = (time.perf_counter() - t0) * f_scale
     t0 = time.perf_counter()
-    O.gptq_o2(wl.W[:sample_rows], Hs, p["bits"], p["group"], p["damp"], p["block"], p["act_order"],
-              wl.n_quant, U=U, perm=perm)
-    t_s = (time.perf_counter() - t0) * (wl.d_out / sample_rows)
+    O.gptq_o2(Ws, Hs, p["bits"], p["group"], p["damp"], p["block"], p["act_order"], nq_s, U=U, perm=perm)
+    t_s = (time.perf_counter() - t0) * s_scale
     total = t_h + t_f + t_s
+    if given_h:
+        sample = (f"H given: factorisation of the leading {m}x{m} block (time x(n/{m})^3) and the sweep of "
+                  f"{sample_rows} of {wl.d_out} rows over those {m} columns (time x{wl.d_out // sample_rows}"
+                  f" x(n/{m})^2); float64 numpy")
+    else:
+        sample = (f"Hessian on {sample_tokens} of {T} tokens (time x{T // sample_tokens}); "
+                  f"factorisation at full n={n}; sweep on {sample_rows} of {wl.d_out} rows "
+                  f"(time x{wl.d_out // sample_rows}); float64 numpy")
     return {
         "value": wl.d_out * wl.n_quant / total, "unit": "weights/s", "cores": cores, "kind": "oracle",
-        "sample": (f"Hessian on {sample_tokens} of {T} tokens (time x{T // sample_tokens}); "
-                   f"factorisation at full n={n}; sweep on {sample_rows} of {wl.d_out} rows "
-                   f"(time x{wl.d_out // sample_rows}); float64 numpy"),
+        "sample": sample, "host": host,
         "seconds_est": {"hessian": t_h, "factor": t_f, "sweep": t_s, "step": total},
     }
 
@@ -187,12 +233,7 @@ def bench_dequant(args):
     if not args.no_cpu_baseline:
         from oracle import dequant as D
         from oracle import packing as P
-        try:
-            from threadpoolctl import threadpool_info
-            cores = sum(i.get("num_threads", 0) for i in threadpool_info()
-                        if i.get("user_api") == "blas") or None
-        except Exception:
-            cores = None
+        cores, host = host_blas()
         ms_rows = min(M, 16)
         qw_host = P.pack(codes, bits)
         xs = synth.bf16_bits_to_f32(xb[:ms_rows])
@@ -201,8 +242,87 @@ def bench_dequant(args):
         t = time.perf_counter() - t0
         line["cpu_baseline"] = {"value": ms_rows / t, "unit": "tokens/s", "cores": cores, "kind": "oracle",
                                 "sample": f"{ms_rows} of {M} tokens: float64 unpack, dequantise and product "
-                                          "(numpy)"}
+                                          "(numpy)", "host": host}
     print(json.dumps(line), flush=True)
+
+
+CONFIG_TEXT = {
+    "c2": "attention-projection GPTQ layer: W 4096x4096 bf16, X 131072x4096 bf16 Student-t(4) with 41 "
+          "outlier channels x30; 4-bit asymmetric, group 128, block 128, damp 0.01, act-order off",
+    "c3": "MLP down-projection GPTQ layer: W 4096x11008 bf16, X 65536x11008 bf16 x*sigmoid(x)*y gated; "
+          "3-bit asymmetric, group 128, block 128, damp 0.01, act-order on",
+    "c4": "large 2-bit GPTQ layer: W 8192x28672 bf16, fp32 H given (2 X^T X of 32768x28672 Gaussian X with "
+          "a rank-32 spike x10); 2-bit asymmetric, group 64, block 128, damp 0.01",
+    "c5": "GPTQ-intrinsic augmented layer: W 5120x5120 bf16 -> [W, 0] 5120x5184, X~ = [X, X V_64] "
+          "65536x5184 bf16 Student-t(4); 2-bit asymmetric, group 128, block 128, damp 0.01, 5120 columns "
+          "quantized, 64 kept in fp32",
+}
+
+
+def far_field_flops(d_out, n, nq, group, block=128):
+    """Algorithmic flops of the far-field updates per quantize call: every
+    512-column super-block's errors (K = its width) applied to all columns
+    right of it (the library's two-level split for groups <= block)."""
+    sw = 512 if group <= block else (group * (512 // group) if group <= 512 else group)
+    f = 0.0
+    for s0 in range(0, nq, sw):
+        s1 = min(s0 + sw, nq)
+        if s1 < n:
+            f += 2.0 * d_out * (s1 - s0) * (n - s1)
+    return f
+
+
+def measured_peaks(dev):
+    """What this machine delivers on two plain reference operations, beside the
+    nominal peaks: a 1 GiB device-to-device copy (torch, read + write bytes)
+    and an 8192^3 bf16 GEMM (torch -> hipBLASLt)."""
+    import torch
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    a.fill_(1)
+    x = torch.randn((8192, 8192), device=dev).to(torch.bfloat16)
+    y = torch.randn((8192, 8192), device=dev).to(torch.bfloat16)
+    for _ in range(3):
+        b.copy_(a)
+        torch.matmul(x, y)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2.0 * (1 << 30) * 10 / (e0.elapsed_time(e1) / 1e3) / 1e9
+    e0.record()
+    for _ in range(10):
+        torch.matmul(x, y)
+    e1.record()
+    torch.cuda.synchronize()
+    gemm_tf = 2.0 * 8192 ** 3 * 10 / (e0.elapsed_time(e1) / 1e3) / 1e12
+    del a, b, x, y
+    torch.cuda.empty_cache()
+    return {"hbm_copy_GBps": copy_gbs, "bf16_gemm_hipblaslt_TFLOPs": gemm_tf,
+            "nominal_hbm_GBps": PEAK_HBM_GBS, "nominal_bf16_TFLOPs": PEAK_BF16_TFLOPS,
+            "how": "1 GiB device copy (read + write bytes) and an 8192^3 bf16 matmul through torch, "
+                   "10 timed repetitions each"}
+
+
+def gram_f64_on_device(chunks):
+    """2 X^T X in float64 over the token chunks of the large layer's X, on the
+    device: the recipe's given H (an input of the benchmark, formed before
+    the timed region and rounded once to fp32 by the recipe)."""
+    import torch
+    H = None
+    for _, x, _ in chunks:
+        xt = torch.from_numpy(x).to("cuda", torch.float64)
+        g = xt.T.contiguous() @ xt
+        H = g if H is None else H.add_(g)
+        del xt, g
+    H.mul_(2.0)
+    out = H.cpu().numpy()
+    del H
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -215,6 +335,10 @@ def main():
                     help="before warm-up, run one plain 1 GiB device copy and one 1 GiB fill "
                          "(known bytes) for calibrating HBM byte counters")
     ap.add_argument("--workload", choices=["gptq_layer", "dequant_matmul"], default="gptq_layer")
+    ap.add_argument("--config", choices=sorted(CONFIG_TEXT), default="c2",
+                    help="layer workload: c2 4096x4096 4-bit (the metric's), c3 4096x11008 3-bit act-order, "
+                         "c4 8192x28672 2-bit with H given, c5 5120x5184 augmented 2-bit")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the copy / GEMM peak measurement")
     ap.add_argument("--tokens", type=int, default=16, help="tokens M for --workload dequant_matmul")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -239,19 +363,26 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    log("bench: generating the 4096x4096 layer and 131072x4096 bf16 calibration tokens")
+    cfg = args.config
+    log(f"bench: generating the {cfg} workload")
     t0 = time.perf_counter()
-    wl = synth.make_workload("c2")
+    wl = synth.make_workload(cfg, H_fn=gram_f64_on_device if cfg == "c4" else None)
     p = wl.params
     log(f"bench: inputs ready in {time.perf_counter() - t0:.1f} s")
     W = torch.from_numpy(wl.W_bits.view(np.int16)).view(torch.bfloat16).to(dev)
-    X = torch.from_numpy(wl.X_bits.view(np.int16)).view(torch.bfloat16).to(dev)
-    T, n = X.shape
-    d_out = W.shape[0]
+    d_out, n = W.shape
     nq = wl.n_quant
-
-    H = torch.empty((n, n), dtype=torch.float32, device=dev)
-    ws_h = torch.empty(G.hessian_workspace_bytes(T, n, torch.bfloat16), dtype=torch.uint8, device=dev)
+    given_h = wl.H is not None
+    if given_h:
+        X = None
+        T = wl.T
+        H = torch.from_numpy(wl.H).to(dev)
+        ws_h = None
+    else:
+        X = torch.from_numpy(wl.X_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        T = X.shape[0]
+        H = torch.empty((n, n), dtype=torch.float32, device=dev)
+        ws_h = torch.empty(G.hessian_workspace_bytes(T, n, torch.bfloat16), dtype=torch.uint8, device=dev)
     params = G.make_params(p["bits"], p["group"], p["damp"], p["block"], p["act_order"], nq, n)
     ws_q = torch.empty(G.workspace_bytes(d_out, n, params), dtype=torch.uint8, device=dev)
     outs = {
@@ -273,7 +404,8 @@ def main():
         log("bench: ran the 1 GiB fill and copy for counter calibration")
 
     def step():
-        G.accumulate_hessian(X, H=H, zero_first=True, workspace=ws_h)
+        if not given_h:
+            G.accumulate_hessian(X, H=H, zero_first=True, workspace=ws_h)
         G.quantize_layer(W, H, bits=p["bits"], group=p["group"], damp=p["damp"], block=p["block"],
                          act_order=p["act_order"], n_quant=nq, workspace=ws_q, outputs=outs)
 
@@ -293,14 +425,33 @@ def main():
     G.profile_enable(False)
     log(f"bench: {args.steps} steps in {elapsed:.3f} s")
 
+    # one more, untimed step with the phases of quantize_layer timed
+    G.profile_enable(True, phases=True)
+    step()
+    torch.cuda.synchronize()
+    ph = G.profile_collect()
+    G.profile_enable(False)
+
     ms_step = 1e3 * elapsed / args.steps
     per_class = {k: (v[0] / args.steps) for k, v in prof.items()}
-    syrk_ms, syrk_n = prof["hessian_syrk"]
-    syrk_avg_s = syrk_ms / max(syrk_n, 1) / 1e3
-    hess_flops = float(T) * n * (n + 1)        # symmetric count per launch
-    achieved = hess_flops / syrk_avg_s / 1e12
-    hess_ms = per_class["hessian_syrk"] + per_class["hessian_reduce"]
     quant_ms = per_class["quantize"]
+    sweep_ms, sweep_n = ph["sweep"]
+    far_ms, far_n = ph["far_field"]
+    sweep_bytes = 13.0 * d_out * nq        # read W 4, write w_hat 4 and E 4, code 1 per weight
+    sweep_gbs = sweep_bytes / (sweep_ms / 1e3) / 1e9 if sweep_ms > 0 else None
+    ff = far_field_flops(d_out, n, nq, p["group"], p["block"])
+    ff_tf = ff / (far_ms / 1e3) / 1e12 if far_ms > 0 else None
+    phases = {
+        "factor_ms": ph["factor"][0], "sweep_ms": sweep_ms, "sweep_launches": sweep_n,
+        "far_field_ms": far_ms, "far_field_launches": far_n, "prep_finish_ms": ph["prep_finish"][0],
+        "quantize_ms_with_phase_events": ph["quantize"][0],
+        "sweep_GBps": sweep_gbs, "sweep_hbm_frac": sweep_gbs / PEAK_HBM_GBS if sweep_gbs else None,
+        "far_field_TFLOPs": ff_tf, "far_field_mfma_frac": ff_tf / PEAK_BF16_TFLOPS if ff_tf else None,
+        "far_field_mfma_frac_3_products": 3 * ff_tf / PEAK_BF16_TFLOPS if ff_tf else None,
+        "how": "one extra untimed step with an event pair around every phase launch; sweep bytes "
+               "13 per weight (read W, write w_hat and E fp32, code), far-field flops "
+               "sum 2 d_out K N over the super-blocks",
+    }
     line = {
         "metric": METRIC,
         "value": d_out * nq / (ms_step / 1e3),
@@ -314,24 +465,38 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "attention-projection GPTQ layer: W 4096x4096 bf16, X 131072x4096 bf16 "
-                               "Student-t(4) with 41 outlier channels x30; 4-bit asymmetric, group 128, "
-                               "block 128, damp 0.01, act-order off",
-                   "d_out": d_out, "d_in": n, "tokens": T, "bits": p["bits"], "group": p["group"],
-                   "block": p["block"], "damp": p["damp"], "act_order": p["act_order"],
-                   "parallelism": "single GPU"},
-        "hessian_tflops": hess_flops / (hess_ms / 1e3) / 1e12,
-        "hessian_ms": hess_ms,
+        "config": {"workload": CONFIG_TEXT[cfg], "name": cfg,
+                   "d_out": d_out, "d_in": n, "n_quant": nq, "tokens": T, "bits": p["bits"],
+                   "group": p["group"], "block": p["block"], "damp": p["damp"], "act_order": p["act_order"],
+                   "hessian_given": given_h, "parallelism": "single GPU"},
         "quantize_ms": quant_ms,
         "layer_weights_per_s_quantize_only": d_out * nq / (quant_ms / 1e3),
-        "roofline": {"bound": "mfma", "kernel": "k_hessian_dma", "achieved": achieved,
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                     "traffic": hessian_traffic(),
-                     "work": "T*n*(n+1) flop per launch (upper triangle of 2 X^T X)"},
+        "phases": phases,
     }
+    if not given_h:
+        syrk_ms, syrk_n = prof["hessian_syrk"]
+        syrk_avg_s = syrk_ms / max(syrk_n, 1) / 1e3
+        hess_flops = float(T) * n * (n + 1)        # symmetric count per launch
+        achieved = hess_flops / syrk_avg_s / 1e12
+        hess_ms = per_class["hessian_syrk"] + per_class["hessian_reduce"]
+        line["hessian_tflops"] = hess_flops / (hess_ms / 1e3) / 1e12
+        line["hessian_ms"] = hess_ms
+        line["roofline"] = {"bound": "mfma", "kernel": "k_hessian_dma", "achieved": achieved,
+                            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
+                            "traffic": hessian_traffic() if cfg == "c2" else None,
+                            "work": "T*n*(n+1) flop per launch (upper triangle of 2 X^T X)"}
+    else:
+        # H given: the far-field update is the largest part of the layer
+        line["roofline"] = {"bound": "mfma", "kernel": "k_trail_x3", "achieved": ff_tf,
+                            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                            "frac": ff_tf / PEAK_BF16_TFLOPS if ff_tf else None, "traffic": None,
+                            "work": "sum over super-blocks of 2 d_out K N flop per call (fp32-accurate "
+                                    "product taken as three bf16 products; frac counts one)"}
+    if not args.no_peaks:
+        line["measured_peaks"] = measured_peaks(dev)
     if not args.no_cpu_baseline:
         log("bench: timing the float64 oracle on a bounded sample (cpu_baseline)")
-        line["cpu_baseline"] = cpu_baseline(wl, wl.X, p)
+        line["cpu_baseline"] = cpu_baseline(wl, wl.X, p, given_h=given_h)
     print(json.dumps(line), flush=True)
 
 

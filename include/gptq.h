@@ -256,15 +256,24 @@ const char *gptq_last_error(void); /* thread-local detail of the last failure */
  * Hessian Gram kernel, around the Hessian reduction, and around a whole
  * quantize_layer call (events are deliberately coarse: an event record
  * between every pair of small kernels costs microseconds of GPU time).
- * enable != 0 starts recording (and clears what was recorded);
- * gptq_profile_collect synchronises the recorded events and returns, for
- * class c in [0, GPTQ_PROF_NCLASSES), the summed milliseconds and the
- * number of timed intervals, then clears. */
+ * enable == 1 starts recording those (and clears what was recorded);
+ * enable >= 2 also records the phases of quantize_layer: the factorisation
+ * (preparation of H included), the W preparation and the final un-permute /
+ * pack, every sweep launch (with its near-field update), every far-field
+ * update; that adds a few microseconds per launch and is meant for one
+ * untimed breakdown pass. enable == 0 stops. gptq_profile_collect
+ * synchronises the recorded events and returns, for class c in
+ * [0, GPTQ_PROF_NCLASSES), the summed milliseconds and the number of timed
+ * intervals, then clears. */
 enum {
   GPTQ_PROF_HESSIAN_SYRK = 0,
   GPTQ_PROF_HESSIAN_REDUCE = 1,
   GPTQ_PROF_QUANTIZE = 2,
-  GPTQ_PROF_NCLASSES = 3
+  GPTQ_PROF_FACTOR = 3,
+  GPTQ_PROF_PREP_FINISH = 4,
+  GPTQ_PROF_SWEEP = 5,
+  GPTQ_PROF_FARFIELD = 6,
+  GPTQ_PROF_NCLASSES = 7
 };
 gptq_status gptq_profile_enable(int enable);
 gptq_status gptq_profile_collect(double *ms, int64_t *count);

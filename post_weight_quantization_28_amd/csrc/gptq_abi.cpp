@@ -43,7 +43,7 @@ struct ProfRec {
   hipEvent_t a, b;
 };
 std::mutex g_prof_mu;
-bool g_prof_on = false;
+int g_prof_level = 0;   // 0 off, 1 the coarse classes, 2 also the phases of quantize_layer
 std::vector<ProfRec> g_prof_recs;
 std::vector<hipEvent_t> g_prof_pool;
 
@@ -59,11 +59,11 @@ hipEvent_t prof_event() {
 }
 
 // Records a start event on construction and a stop event on destruction
-// when timing is enabled.
+// when timing is enabled at `level` or above.
 class Timed {
  public:
-  Timed(int cls, hipStream_t s) : cls_(cls), s_(s) {
-    if (!g_prof_on) return;
+  Timed(int cls, hipStream_t s, int level = 1) : cls_(cls), s_(s) {
+    if (g_prof_level < level) return;
     std::lock_guard<std::mutex> lk(g_prof_mu);
     a_ = prof_event();
     b_ = prof_event();
@@ -309,7 +309,7 @@ gptq_status gptq_profile_enable(int enable) {
     g_prof_pool.push_back(r.b);
   }
   g_prof_recs.clear();
-  g_prof_on = enable != 0;
+  g_prof_level = enable <= 0 ? 0 : (enable == 1 ? 1 : 2);
   return GPTQ_OK;
 }
 
@@ -451,10 +451,16 @@ gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int
   uint16_t* Ulo = reinterpret_cast<uint16_t*>(ws + L.Ulo);
   // the far field's split-bf16 operands are written by the kernels that
   // produce U (the final rotation) and E (the sweep)
-  if ((st = enqueue_factor(s, H, n, p, ws, L, two ? Uhi : nullptr, two ? Ulo : nullptr)) != GPTQ_OK) return st;
-  HIP_TRY(launch_w_prep(s, W, wdt == GPTQ_BF16, d_out, n, ldw, p->act_order ? perm : nullptr, Wf, dst),
-          "w prep");
-  HIP_TRY(launch_fill_f32(s, loss, (size_t)d_out, 0.f), "fill");
+  {
+    Timed ph(GPTQ_PROF_FACTOR, s, 2);
+    if ((st = enqueue_factor(s, H, n, p, ws, L, two ? Uhi : nullptr, two ? Ulo : nullptr)) != GPTQ_OK) return st;
+  }
+  {
+    Timed ph(GPTQ_PROF_PREP_FINISH, s, 2);
+    HIP_TRY(launch_w_prep(s, W, wdt == GPTQ_BF16, d_out, n, ldw, p->act_order ? perm : nullptr, Wf, dst),
+            "w prep");
+    HIP_TRY(launch_fill_f32(s, loss, (size_t)d_out, 0.f), "fill");
+  }
   // Two-level lazy batch. Inside a super-block [s0, s1) each block updates
   // the super-block's later columns at once (fp32, K = B); when the
   // super-block is done, all of its errors update the columns right of it
@@ -482,6 +488,7 @@ gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int
       a.Esb = E; a.kb = fused ? i0 - s0 : 0;
       a.Ehi = two && s1 < n ? Ehi + (i0 - s0) : nullptr;
       a.Elo = two && s1 < n ? Elo + (i0 - s0) : nullptr;
+      Timed ph(GPTQ_PROF_SWEEP, s, 2);
       HIP_TRY(launch_sweep(s, a), "sweep");
       const int64_t i1 = i0 + nc;
       const int64_t near_end = two ? s1 : n;
@@ -501,9 +508,11 @@ gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int
       t.Ahi = Ehi; t.Alo = Elo; t.lda = sw;
       t.Bhi = Uhi + s0 * n + s1; t.Blo = Ulo + s0 * n + s1; t.ldb = n;
       t.C = Wf + s1; t.ldc = n;
+      Timed ph(GPTQ_PROF_FARFIELD, s, 2);
       HIP_TRY(launch_trail_x3(s, t), "far-field update");
     }
   }
+  Timed ph(GPTQ_PROF_PREP_FINISH, s, 2);
   HIP_TRY(launch_finish(s, Wf, codes, invperm, d_out, n, nq, p->group, in_place ? nullptr : out->w_hat,
                         out->codes, out->g_idx),
           "finish");

@@ -286,12 +286,14 @@ k_kprod_leaf_pipe(SlabArgs g, LeafTask lt, BandTiles bt) {
   if (wave >= 4) {
     // ---------------- data movers
     // A rows [0, M), B rows [0, N): 64 floats each; C rows [0, M), columns
-    // [0, N). Past the ends: loads read zeros, stores are dropped.
-    const v4i32_t ra = make_rsrc(g.A, ((M - 1) * g.lda + 64) * 4);
-    const v4i32_t rb = make_rsrc(g.B, ((N - 1) * g.ldb + 64) * 4);
-    const v4i32_t rcl = make_rsrc(g.C, ((M - 1) * g.ldc + N) * 4);
-    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
-        g.C, 0, __builtin_amdgcn_readfirstlane((int)(((M - 1) * g.ldc + N) * 4)), 0x00020000);
+    // [0, N). Past the ends: loads read zeros, stores are dropped. Every
+    // buffer resource starts at its tile (A's and B's first row, C's first
+    // element) and spans at most one tile, so the lane offsets stay below
+    // 2^31 bytes whatever the size of the matrix.
+    const int64_t a_end = ((M - 1) * g.lda + 64) * 4, b_end = ((N - 1) * g.ldb + 64) * 4;
+    const int64_t c_end = ((M - 1) * g.ldc + N) * 4;
+    const int64_t a_span = (63 * g.lda + 64) * 4, b_span = (63 * g.ldb + 64) * 4;
+    const int64_t c_span = (63 * g.ldc + 64) * 4;
     // instruction q of this wave moves tile rows 16 w4 + 4 q + lane / 16;
     // a lane's 16-byte chunk is lane % 16
     const int ch = lane & 15;
@@ -309,23 +311,27 @@ k_kprod_leaf_pipe(SlabArgs g, LeafTask lt, BandTiles bt) {
     auto issue = [&](int i, int st) {
       int rt = 0, ct = 0;
       band_tile(bt, t0 + G * min(i, nt - 1), rt, ct);   // past the end: the last tile again
-      const uint32_t sa = __builtin_amdgcn_readfirstlane((uint32_t)((int64_t)rt * 64 * g.lda * 4));
-      const uint32_t sb = __builtin_amdgcn_readfirstlane((uint32_t)((int64_t)ct * 64 * g.ldb * 4));
-      const uint32_t sc =
-          __builtin_amdgcn_readfirstlane((uint32_t)(((int64_t)rt * 64 * g.ldc + (int64_t)ct * 64) * 4));
+      const int64_t oa = (int64_t)rt * 64 * g.lda, ob = (int64_t)ct * 64 * g.ldb;
+      const int64_t oc = (int64_t)rt * 64 * g.ldc + (int64_t)ct * 64;
+      const v4i32_t ra = make_rsrc(g.A + oa, min(a_end - 4 * oa, a_span));
+      const v4i32_t rb = make_rsrc(g.B + ob, min(b_end - 4 * ob, b_span));
+      const v4i32_t rcl = make_rsrc(g.C + oc, min(c_end - 4 * oc, c_span));
       const uint32_t base = lds0 + (uint32_t)st * kPStage + (uint32_t)(4 * w4) * 1024;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dma16_rsrc(voa[q], ra, sa, base + q * 1024);
+      for (int q = 0; q < 4; ++q) dma16_rsrc(voa[q], ra, 0u, base + q * 1024);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dma16_rsrc(vob[q], rb, sb, base + kPA + q * 1024);
+      for (int q = 0; q < 4; ++q) dma16_rsrc(vob[q], rb, 0u, base + kPA + q * 1024);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) dma16_rsrc(voc[q], rcl, sc, base + 2 * kPA + q * 1024);
+      for (int q = 0; q < 4; ++q) dma16_rsrc(voc[q], rcl, 0u, base + 2 * kPA + q * 1024);
     };
     // tile i's results (stage st) to C; i < 0 stores nothing (offsets past
     // the buffer) but issues the same 4 stores, keeping the wait counts fixed
     auto store = [&](int i, int st) {
       int rt = 0, ct = 0;
       if (i >= 0) band_tile(bt, t0 + G * i, rt, ct);
+      const int64_t oc = (int64_t)rt * 64 * g.ldc + (int64_t)ct * 64;
+      const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+          g.C + oc, 0, __builtin_amdgcn_readfirstlane((int)min(c_end - 4 * oc, c_span)), 0x00020000);
       const uint32_t sbase = lds0 + (uint32_t)st * kPStage;
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -333,7 +339,8 @@ k_kprod_leaf_pipe(SlabArgs g, LeafTask lt, BandTiles bt) {
             (uintptr_t)(sbase + lcs[q]));
         const int64_t row = (int64_t)rt * 64 + rowq[q];
         const int64_t col = (int64_t)ct * 64 + 4 * (ch ^ pipe_c_swz(rowq[q]));
-        const uint32_t off = (i >= 0 && row < M && col < N) ? (uint32_t)((row * g.ldc + col) * 4) : 0x80000000u;
+        // voc[q] is this lane's offset inside the tile; 2^31 lies past every tile's span
+        const uint32_t off = (i >= 0 && row < M && col < N) ? voc[q] : 0x80000000u;
         __builtin_amdgcn_raw_buffer_store_b128(v, rc, off, 0, 0);
       }
     };
@@ -434,12 +441,13 @@ hipError_t launch_slab(hipStream_t s, const SlabArgs& g) {
 
 hipError_t launch_slab_leaf(hipStream_t s, const SlabArgs& g, const LeafTask& lt) {
   if (g.K < 1 || g.K > 64 || lt.mk > 64 || lt.m2 > 64 || lt.m2 < 1 || lt.mk < 1) return hipErrorInvalidValue;
-  // the pipelined kernel: full panels, 16-byte rows, 32-bit buffer offsets
+  // the pipelined kernel: full panels, 16-byte rows, one tile's span of
+  // each operand below 2^31 bytes (its buffer resources start at the tile)
   const bool pipe = g.K == 64 && g.tb && g.M > 0 && g.N > 0 && (g.N & 3) == 0 && (g.ldc & 3) == 0 &&
                     ((uintptr_t)g.C & 15) == 0 && (g.lda & 3) == 0 && (g.ldb & 3) == 0 &&
                     ((uintptr_t)g.A & 15) == 0 && ((uintptr_t)g.B & 15) == 0 &&
-                    (g.M * g.lda + 64) * 4 < ((int64_t)1 << 32) && (g.N * g.ldb + 64) * 4 < ((int64_t)1 << 32) &&
-                    ((g.M - 1) * g.ldc + g.N) * 4 < ((int64_t)1 << 31);
+                    (63 * g.lda + 64) * 4 < ((int64_t)1 << 31) && (63 * g.ldb + 64) * 4 < ((int64_t)1 << 31) &&
+                    (63 * g.ldc + 64) * 4 < ((int64_t)1 << 31);
   if (pipe) {
     const BandTiles bt = band_tiles(g.M, g.N, g.lower_only, g.lower_off);
     if (bt.total >= ((int64_t)1 << 31)) return hipErrorInvalidValue;

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libgptq.so")
 
 OK, EINVAL, ENOTPD, ENONFINITE, EHIP, EWORKSPACE = 0, -1, -2, -3, -4, -5
 BF16, F32 = 0, 1
-PROF_CLASSES = ["hessian_syrk", "hessian_reduce", "quantize"]
+PROF_CLASSES = ["hessian_syrk", "hessian_reduce", "quantize", "factor", "prep_finish", "sweep", "far_field"]
 
 
 class GPTQError(RuntimeError):
@@ -327,8 +327,10 @@ def unpack_codes(qweight, n_quant, bits):
 
 
 # ---------------------------------------------------------------- timing
-def profile_enable(on=True):
-    _check(load().gptq_profile_enable(int(on)))
+def profile_enable(on=True, phases=False):
+    """Start (clearing) or stop event timing; phases=True also times the
+    phases of quantize_layer (for an untimed breakdown pass)."""
+    _check(load().gptq_profile_enable(0 if not on else (2 if phases else 1)))
 
 
 def profile_collect():
