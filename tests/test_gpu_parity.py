@@ -63,7 +63,11 @@ def test_hessian_streaming_accumulates():
 # ---------------------------------------------------------------- factorisation
 # n = 202: rows not a multiple of 4 floats, so the trailing updates and the
 # flipped-matrix build take their general (unvectorised) kernels
-@pytest.mark.parametrize("n,act_order", [(64, False), (200, False), (202, False), (320, True), (1000, False)])
+# n >= 6144: the two-level factorisation (256-column super-panels, the last
+# one partial; n = 6150 also has a last panel of 6 columns and rows that are
+# not a multiple of 4 floats)
+@pytest.mark.parametrize("n,act_order", [(64, False), (200, False), (202, False), (320, True), (1000, False),
+                                         (6208, False), (6150, True)])
 def test_factor_matches_lapack(n, act_order):
     wl = synth.make_workload("c2", d_out=4, n=n, T=4 * n, group=4)
     H64 = O.hessian(wl.X)
