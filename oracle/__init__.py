@@ -12,6 +12,7 @@ gptq_f64   the method itself (Hessian, damping/ordering, the O1 and O2 sweeps,
            round-to-nearest, brute force, layer error)
 packing    the LSB-first code bitstream and its inverse
 dequant    the dequantising product Y = X W_hat^T of a packed layer
+eora       the EoRA low-rank adapter of the compression error
 memory     storage accounting used by the pages' worked examples
 
 Every function names the passage of the pages it follows. The pages are:
@@ -21,5 +22,6 @@ Every function names the passage of the pages it follows. The pages are:
            (auturnal.com), sections 1-6 and "Ejemplo resuelto"
   [GIL]    "Resumen Técnico: GPTQ-intrinsic LoRA" (gist.science 2606.01412),
            "Declaración del Problema" and "Metodología" item 2
-  [EORA]   "Aumento de la precisión de LLM de 2 bits con EoRA" (7minutos.es)
+  [EORA]   "Aumento de la precisión de LLM de 2 bits con EoRA" (7minutos.es),
+           section "Bucear en el espacio propio en busca de un adaptador"
 """
