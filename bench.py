@@ -11,6 +11,10 @@ MFMA roofline, the phases of quantize_layer (factorisation, sweep, far-field
 update) with the sweep's HBM rate and the far field's MFMA rate, the copy and
 GEMM rates this box measures, and the float64 oracle timed on the host cores.
 
+`--workload eora` times the EoRA rank-64 adapter of that layer's 4-bit
+GPTQ output (the compensation of the quantization error in the eigenspace of
+H) and times the float64 oracle beside it.
+
 `--config c3|c4|c5` times the other layer shapes the same way: 4096 x 11008
 3-bit act-order, 8192 x 28672 2-bit with H given (the step is quantize_layer
 alone; its roofline is the far-field update's), 5120 x 5184 augmented 2-bit.
@@ -325,6 +329,84 @@ def gram_f64_on_device(chunks):
     return out
 
 
+def bench_eora(args):
+    """EoRA adapter of the 4096 x 4096 attention projection: the layer's own
+    4-bit GPTQ output on the GPU (untimed, as are H and the quantization),
+    then gptq_eora at rank 64 timed between HIP events."""
+    import numpy as np
+    import torch
+
+    import post_weight_quantization_28_amd as G
+    import synth
+
+    if not os.path.exists(G.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    G.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    rank = args.rank
+    log("bench: generating the c2 workload")
+    wl = synth.make_workload("c2")
+    p = wl.params
+    W = torch.from_numpy(wl.W_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    X = torch.from_numpy(wl.X_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    H = G.accumulate_hessian(X)
+    del X
+    q = G.quantize_layer(W, H, bits=p["bits"], group=p["group"], damp=p["damp"], block=p["block"])
+    d_out, n = W.shape
+    ws = torch.empty(G.eora_workspace_bytes(d_out, n, rank), dtype=torch.uint8, device=dev)
+
+    def step():
+        return G.eora(W, q.w_hat, H, rank=rank, iters=args.iters, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        B, A, sig = step()
+    e1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    k = min(rank + 64, 128, d_out)
+    k += k & 1
+    iters = args.iters or 24
+    flops = (2.0 * d_out * n * n + 2.0 * d_out * d_out * n                 # D H, then (D H) D^T
+             + (iters + 3) * (2.0 * d_out * d_out * k + 4.0 * d_out * k * k)   # G Q, Y^T Y, Y U^T
+             + 2.0 * d_out * k * k + 2.0 * d_out * k * rank + 2.0 * rank * d_out * n)
+    ach = flops / (ms / 1e3) / 1e12
+    line = {
+        "metric": f"EoRA rank-{rank} adapter of a GPTQ layer (4096², 4-bit g128)",
+        "value": d_out * n / (ms / 1e3), "unit": "weights/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "wall_ms_per_step": 1e3 * elapsed / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "EoRA adapter of the 4096x4096 attention-projection layer after 4-bit g128 GPTQ, "
+                               f"H = 2 X^T X of 131072 Student-t(4) tokens, rank {rank}, {iters} subspace steps",
+                   "d_out": d_out, "d_in": n, "rank": rank, "iters": iters, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": "gptq_eora (k_gemm_f32 products)", "achieved": ach,
+                     "peak": 157.3, "unit": "TFLOP/s", "frac": ach / 157.3, "traffic": None,
+                     "work": "2 d n^2 + 2 d^2 n (G = D H D^T) + per subspace step 2 d^2 k + 4 d k^2, plus the "
+                             "final U_r and A products, per call; fp32 MFMA peak"},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import eora as E
+        cores, host = host_blas()
+        Wv = wl.W.astype(np.float64)
+        Wh = q.w_hat.cpu().numpy().astype(np.float64)
+        Hn = H.cpu().numpy().astype(np.float64)
+        t0 = time.perf_counter()
+        E.eora(Wv, Wh, Hn, rank)
+        t = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": d_out * n / t, "unit": "weights/s", "cores": cores, "kind": "oracle",
+                                "sample": "the whole layer: float64 eigh of H, projection, SVD, back-projection "
+                                          "(numpy)", "host": host, "seconds": t}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -334,7 +416,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before warm-up, run one plain 1 GiB device copy and one 1 GiB fill "
                          "(known bytes) for calibrating HBM byte counters")
-    ap.add_argument("--workload", choices=["gptq_layer", "dequant_matmul"], default="gptq_layer")
+    ap.add_argument("--workload", choices=["gptq_layer", "dequant_matmul", "eora"], default="gptq_layer")
+    ap.add_argument("--rank", type=int, default=64, help="adapter rank for --workload eora")
+    ap.add_argument("--iters", type=int, default=0, help="subspace steps for --workload eora (0: 24)")
     ap.add_argument("--config", choices=sorted(CONFIG_TEXT), default="c2",
                     help="layer workload: c2 4096x4096 4-bit (the metric's), c3 4096x11008 3-bit act-order, "
                          "c4 8192x28672 2-bit with H given, c5 5120x5184 augmented 2-bit")
@@ -348,6 +432,9 @@ def main():
         sys.exit(2)
     if args.workload == "dequant_matmul":
         bench_dequant(args)
+        return
+    if args.workload == "eora":
+        bench_eora(args)
         return
 
     import numpy as np

@@ -248,6 +248,33 @@ gptq_status gptq_repack_act_order(void *stream, const uint32_t *qweight,
                                   int32_t bits, int32_t group, uint32_t *qweight_out,
                                   int32_t *perm_out, void *workspace, size_t ws_bytes);
 
+/* ---- EoRA: rank-r compensation of the compression error ----------------------
+ * B (d_out x rank fp32, row-major) and A (rank x n fp32, row-major) such that
+ * W_hat + B A is the best rank-r correction of W_hat in the layer loss
+ * tr((W - W_hat - B A) H (W - W_hat - B A)^T), and sigma (rank fp32,
+ * descending) the singular values of the error projected into the
+ * eigenspace of H. H == NULL: the plain SVD of W - W_hat (B = U_r Sigma_r,
+ * A = V_r^T). W: d_out x n, dtype wdt, row stride ldw >= n; W_hat: d_out x n
+ * fp32 (e.g. quantize_layer's w_hat); H: n x n fp32 symmetric (e.g. the
+ * Hessian 2 X^T X). 1 <= rank <= min(64, d_out). The r largest eigenpairs of
+ * D H D^T (D = W - W_hat) come from iters steps of block subspace iteration
+ * (0: 24) on a block of min(rank + 64, 128) columns and a Rayleigh-Ritz
+ * step; B A = U_r U_r^T D, B = U_r diag(sigma), A = diag(1/sigma) U_r^T D
+ * (a zero sigma gives zero rows of A). Workspace:
+ * gptq_eora_workspace_bytes(d_out, n, rank, H != NULL). Synchronises the
+ * stream; GPTQ_ENONFINITE if W - W_hat or H is not finite.
+ * ("Aumento de la precisión de LLM de 2 bits con EoRA" (7minutos.es), "Bucear
+ * en el espacio propio en busca de un adaptador": the error projected by the
+ * eigendecomposition of the activation covariance, truncated by SVD and
+ * projected back; the plain-SVD adapter B = U Sigma, A = V^T beside it. Any
+ * square root of H gives the same product B A as Q Lambda^{1/2}.) */
+gptq_status gptq_eora_workspace_bytes(int64_t d_out, int64_t n, int32_t rank, int32_t with_h,
+                                      size_t *bytes);
+gptq_status gptq_eora(void *stream, const void *W, gptq_dtype wdt, const float *W_hat,
+                      int64_t d_out, int64_t n, int64_t ldw, const float *H, int32_t rank,
+                      int32_t iters, float *B, float *A, float *sigma, void *workspace,
+                      size_t workspace_bytes);
+
 /* ---- Diagnostics ------------------------------------------------------------ */
 const char *gptq_status_string(int status);
 const char *gptq_last_error(void); /* thread-local detail of the last failure */

@@ -193,4 +193,15 @@ hipError_t launch_dequant_mm(hipStream_t s, const DqPlan& p, const uint16_t* X, 
                              int64_t ldx, const uint32_t* qw, const float* scales, const uint8_t* zeros,
                              int64_t d_out, int bits, int group, float* Y, int64_t ldy, float* part);
 
+// ---- eora.hip: rank-r compensation of a layer's error
+hipError_t launch_eora_delta(hipStream_t s, const void* W, int wbf16, int64_t ldw, const float* Wh,
+                             int64_t d_out, int64_t n, float* D, DevStatus* st);
+hipError_t launch_eora_start(hipStream_t s, float* Om, int64_t d, int k);
+hipError_t launch_col_normalize(hipStream_t s, float* Y, int64_t d, int k);
+// eigenvalues (descending) and eigenvectors (columns, same order) of the
+// symmetric part of the k x k matrix S; k even, 2 <= k <= 128
+hipError_t launch_sym_eig_jacobi(hipStream_t s, const float* S, int k, float* theta, float* V);
+hipError_t launch_eora_finish(hipStream_t s, const float* theta, int r, float* sigma, float* B, int64_t d,
+                              int64_t ldb, float* A, int64_t n);
+
 }  // namespace gq

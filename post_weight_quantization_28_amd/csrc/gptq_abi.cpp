@@ -284,6 +284,87 @@ gptq_status read_status(hipStream_t s, const DevStatus* st, const int32_t* perm,
   return fail(GPTQ_ENOTPD, "damped Hessian is not positive definite");
 }
 
+// ---------------------------------------------------------------- EoRA
+// Top-r eigenpairs of G = D H D^T (D = W - W_hat) by block subspace
+// iteration: Y = G Q, Q = orth(Y) by CholeskyQR on unit columns (Y's
+// columns scaled to length 1, C = Y^T Y with a unit diagonal, U with
+// U^T U = (C + lambda I)^{-1} from this library's factorisation, Q = Y U^T;
+// lambda = 1e-5 keeps a nearly rank-deficient block factorable in fp32),
+// then Rayleigh-Ritz: S = Q^T G Q, S = V Theta V^T (Jacobi), U_r = Q V_r.
+constexpr int kEoraMaxRank = 64;
+constexpr int kEoraOversample = 64;
+constexpr int kEoraDefaultIters = 24;
+
+int eora_block(int64_t d_out, int rank) {
+  int64_t k = std::min<int64_t>(rank + kEoraOversample, 128);
+  if (k > d_out) k = d_out;
+  if (k & 1) k += 1;            // Jacobi pairs indices: k even (at most one direction past d_out)
+  return (int)k;
+}
+
+struct ELayout {
+  size_t status, D, T, G, Y, Q, C, S, V, theta, fac, total;
+  QLayout fl;
+  int k;
+};
+
+gptq_params eora_factor_params(int k) {
+  gptq_params fp{};
+  fp.struct_size = sizeof(gptq_params);
+  fp.bits = 4; fp.group = 8; fp.block = 32;
+  fp.damp = 1e-5f; fp.act_order = 0; fp.n_quant = k; fp.sym = 0;
+  return fp;
+}
+
+ELayout e_layout(int64_t d_out, int64_t n, int rank, int with_h) {
+  ELayout L{};
+  Carver c;
+  L.k = eora_block(d_out, rank);
+  const int64_t k = L.k;
+  const gptq_params fp = eora_factor_params(L.k);
+  L.fl = q_layout(0, k, &fp);
+  L.status = c.take(sizeof(DevStatus));
+  L.D = c.take(sizeof(float) * d_out * n);
+  L.T = c.take(with_h ? sizeof(float) * d_out * n : 0);
+  L.G = c.take(sizeof(float) * d_out * d_out);
+  L.Y = c.take(sizeof(float) * d_out * k);
+  L.Q = c.take(sizeof(float) * d_out * k);
+  L.C = c.take(sizeof(float) * k * k);
+  L.S = c.take(sizeof(float) * k * k);
+  L.V = c.take(sizeof(float) * k * k);
+  L.theta = c.take(sizeof(float) * k);
+  L.fac = c.take(L.fl.total);
+  L.total = c.off;
+  return L;
+}
+
+GemmArgs gemm(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, int ta, const float* B, int64_t ldb,
+              int tb, float* C, int64_t ldc) {
+  GemmArgs g{};
+  g.M = M; g.N = N; g.K = K;
+  g.A = A; g.lda = lda; g.ta = ta;
+  g.B = B; g.ldb = ldb; g.tb = tb;
+  g.C = C; g.ldc = ldc;
+  g.alpha = 1.f; g.beta = 0.f; g.batch = 1;
+  return g;
+}
+
+// Q = Y U^T with U^T U = (Y^T Y + lambda I)^{-1} after Y's columns are
+// scaled to unit length (in place): columns of Q orthonormal (up to
+// lambda) and spanning Y's columns.
+gptq_status eora_orth(hipStream_t s, float* Y, float* Q, int64_t d, const ELayout& L, char* ws) {
+  const int64_t k = L.k;
+  float* C = reinterpret_cast<float*>(ws + L.C);
+  HIP_TRY(launch_col_normalize(s, Y, d, (int)k), "eora normalize");
+  HIP_TRY(launch_gemm_f32(s, gemm(k, k, d, Y, k, 1, Y, k, 0, C, k)), "eora gram");
+  const gptq_params fp = eora_factor_params(L.k);
+  gptq_status st = enqueue_factor(s, C, k, &fp, ws + L.fac, L.fl);
+  if (st != GPTQ_OK) return st;
+  const float* U = reinterpret_cast<const float*>(ws + L.fac + L.fl.A);
+  HIP_TRY(launch_gemm_f32(s, gemm(d, k, k, Y, k, 0, U, k, 1, Q, k)), "eora orth");
+  return GPTQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -719,4 +800,72 @@ gptq_status gptq_dequant_matmul_noalloc(void* stream, const void* X, int32_t xdt
                     ws);
 }
 
+
+// ---------------------------------------------------------------- EoRA
+gptq_status gptq_eora_workspace_bytes(int64_t d_out, int64_t n, int32_t rank, int32_t with_h, size_t* bytes) {
+  if (!bytes) return fail(GPTQ_EINVAL, "bytes is NULL");
+  if (d_out < 1 || n < 1 || d_out > ((int64_t)1 << 30) || n > ((int64_t)1 << 30))
+    return fail(GPTQ_EINVAL, "need 1 <= d_out, n <= 2^30");
+  if (rank < 1 || rank > kEoraMaxRank || rank > d_out) return fail(GPTQ_EINVAL, "rank must be in [1, min(64, d_out)]");
+  *bytes = e_layout(d_out, n, rank, with_h != 0).total;
+  return GPTQ_OK;
+}
+
+gptq_status gptq_eora(void* stream, const void* W, gptq_dtype wdt, const float* W_hat, int64_t d_out, int64_t n,
+                      int64_t ldw, const float* H, int32_t rank, int32_t iters, float* B, float* A, float* sigma,
+                      void* workspace, size_t workspace_bytes) {
+  size_t need = 0;
+  gptq_status st = gptq_eora_workspace_bytes(d_out, n, rank, H != nullptr, &need);
+  if (st != GPTQ_OK) return st;
+  if (wdt != GPTQ_BF16 && wdt != GPTQ_F32) return fail(GPTQ_EINVAL, "bad dtype");
+  if (!W || !W_hat || !B || !A || !sigma) return fail(GPTQ_EINVAL, "NULL pointer");
+  if (ldw < n) return fail(GPTQ_EINVAL, "ldw < n");
+  if (iters < 0 || iters > 1000) return fail(GPTQ_EINVAL, "iters must be in [0, 1000]");
+  if ((st = check_ws(workspace, workspace_bytes, need)) != GPTQ_OK) return st;
+  const int it_n = iters == 0 ? kEoraDefaultIters : iters;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = reinterpret_cast<char*>(workspace);
+  const ELayout L = e_layout(d_out, n, rank, H != nullptr);
+  const int64_t k = L.k, d = d_out;
+  DevStatus* dst = reinterpret_cast<DevStatus*>(ws + L.status);
+  float* D = reinterpret_cast<float*>(ws + L.D);
+  float* T = reinterpret_cast<float*>(ws + L.T);
+  float* G = reinterpret_cast<float*>(ws + L.G);
+  float* Y = reinterpret_cast<float*>(ws + L.Y);
+  float* Q = reinterpret_cast<float*>(ws + L.Q);
+  float* S = reinterpret_cast<float*>(ws + L.S);
+  float* V = reinterpret_cast<float*>(ws + L.V);
+  float* theta = reinterpret_cast<float*>(ws + L.theta);
+  HIP_TRY(launch_status_init(s, dst), "status init");
+  HIP_TRY(launch_eora_delta(s, W, wdt == GPTQ_BF16, ldw, W_hat, d, n, D, dst), "eora delta");
+  // G = D H D^T (plain SVD of D when H is NULL: G = D D^T)
+  if (H) {
+    HIP_TRY(launch_gemm_f32(s, gemm(d, n, n, D, n, 0, H, n, 0, T, n)), "eora D H");
+    HIP_TRY(launch_gemm_f32(s, gemm(d, d, n, T, n, 0, D, n, 1, G, d)), "eora G");
+  } else {
+    HIP_TRY(launch_gemm_f32(s, gemm(d, d, n, D, n, 0, D, n, 1, G, d)), "eora G");
+  }
+  // start block and subspace iteration
+  HIP_TRY(launch_eora_start(s, Q, d, (int)k), "eora start");
+  HIP_TRY(launch_gemm_f32(s, gemm(d, k, d, G, d, 0, Q, k, 0, Y, k)), "eora G Q");
+  for (int it = 0; it < it_n; ++it) {
+    if ((st = eora_orth(s, Y, Q, d, L, ws)) != GPTQ_OK) return st;
+    HIP_TRY(launch_gemm_f32(s, gemm(d, k, d, G, d, 0, Q, k, 0, Y, k)), "eora G Q");
+  }
+  // CholeskyQR2 for the final basis, then Rayleigh-Ritz
+  if ((st = eora_orth(s, Y, Q, d, L, ws)) != GPTQ_OK) return st;
+  if ((st = eora_orth(s, Q, Y, d, L, ws)) != GPTQ_OK) return st;       // Y holds the basis now
+  HIP_TRY(launch_gemm_f32(s, gemm(d, k, d, G, d, 0, Y, k, 0, Q, k)), "eora G Q");
+  HIP_TRY(launch_gemm_f32(s, gemm(k, k, d, Y, k, 1, Q, k, 0, S, k)), "eora Rayleigh quotient");
+  HIP_TRY(launch_sym_eig_jacobi(s, S, (int)k, theta, V), "eora Jacobi");
+  // U_r = basis V[:, :r] into B, A = U_r^T D, then the singular-value scaling
+  HIP_TRY(launch_gemm_f32(s, gemm(d, rank, k, Y, k, 0, V, k, 0, B, rank)), "eora U_r");
+  HIP_TRY(launch_gemm_f32(s, gemm(rank, n, d, B, rank, 1, D, n, 0, A, n)), "eora A");
+  HIP_TRY(launch_eora_finish(s, theta, rank, sigma, B, d, rank, A, n), "eora finish");
+  // device status: the difference, then the last factorisation (NaN in H
+  // reaches the Gram matrix it factors)
+  int64_t col = -1;
+  if ((st = read_status(s, dst, nullptr, &col)) != GPTQ_OK) return st;
+  return read_status(s, reinterpret_cast<DevStatus*>(ws + L.fac + L.fl.status), nullptr, nullptr);
+}
 }  // extern "C"

@@ -75,6 +75,9 @@ def load():
         "gptq_repack_act_order_workspace_bytes": [c_i64, c_i64, ctypes.POINTER(c_sz)],
         "gptq_repack_act_order": [c_vp, c_vp, c_vp, c_i64, c_i64, ctypes.c_int32, ctypes.c_int32, c_vp, c_vp,
                                   c_vp, c_sz],
+        "gptq_eora_workspace_bytes": [c_i64, c_i64, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(c_sz)],
+        "gptq_eora": [c_vp, c_vp, ctypes.c_int, c_vp, c_i64, c_i64, c_i64, c_vp, ctypes.c_int32, ctypes.c_int32,
+                      c_vp, c_vp, c_vp, c_vp, c_sz],
         "gptq_profile_enable": [ctypes.c_int],
         "gptq_profile_collect": [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i64)],
     }
@@ -304,6 +307,40 @@ def repack_act_order(qweight, g_idx, n, bits, group, workspace=None):
                                      int(bits), int(group), _dev(out, "qweight_out"), _dev(perm, "perm"),
                                      wsp, c.value))
     return out, perm
+
+
+# ---------------------------------------------------------------- EoRA
+def eora_workspace_bytes(d_out, n, rank, with_h=True):
+    lib = load()
+    out = ctypes.c_size_t(0)
+    _check(lib.gptq_eora_workspace_bytes(int(d_out), int(n), int(rank), int(bool(with_h)), ctypes.byref(out)))
+    return out.value
+
+
+def eora(W, W_hat, H=None, rank=32, iters=0, workspace=None):
+    """(B, A, sigma): the rank-r EoRA adapter of W - W_hat in the eigenspace
+    of H (plain SVD of W - W_hat when H is None); W_hat + B A is the
+    compensated layer. W bf16 or fp32 (d_out x n), W_hat fp32, H fp32 n x n."""
+    lib = load()
+    _dev(W, "W")
+    _dev(W_hat, "W_hat")
+    if W_hat.dtype != torch.float32:
+        raise TypeError("W_hat must be float32")
+    d_out, n = W.shape
+    if H is not None:
+        _dev(H, "H")
+        if H.dtype != torch.float32:
+            raise TypeError("H must be float32")
+    dev = W.device
+    B = torch.empty((d_out, rank), dtype=torch.float32, device=dev)
+    A = torch.empty((rank, n), dtype=torch.float32, device=dev)
+    sigma = torch.empty((rank,), dtype=torch.float32, device=dev)
+    need = eora_workspace_bytes(d_out, n, rank, H is not None)
+    ws, wsp = _workspace(need, dev, workspace)
+    _check(lib.gptq_eora(_stream(), _dev(W, "W"), _dtype_code(W), _dev(W_hat, "W_hat"), d_out, n, W.stride(0),
+                         _dev(H, "H") if H is not None else ctypes.c_void_p(0), int(rank), int(iters),
+                         _dev(B, "B"), _dev(A, "A"), _dev(sigma, "sigma"), wsp, need))
+    return B, A, sigma
 
 
 # ---------------------------------------------------------------- packing
