@@ -198,6 +198,7 @@ hipError_t launch_eora_delta(hipStream_t s, const void* W, int wbf16, int64_t ld
                              int64_t d_out, int64_t n, float* D, DevStatus* st);
 hipError_t launch_eora_start(hipStream_t s, float* Om, int64_t d, int k);
 hipError_t launch_col_normalize(hipStream_t s, float* Y, int64_t d, int k);
+hipError_t launch_sum_partials(hipStream_t s, const float* part, int np, int64_t count, float* C);
 // eigenvalues (descending) and eigenvectors (columns, same order) of the
 // symmetric part of the k x k matrix S; k even, 2 <= k <= 128
 hipError_t launch_sym_eig_jacobi(hipStream_t s, const float* S, int k, float* theta, float* V);

@@ -92,6 +92,21 @@ hipError_t launch_col_normalize(hipStream_t s, float* Y, int64_t d, int k) {
   return hipGetLastError();
 }
 
+// C[i] = sum over p of part[p * count + i], in p order (the split-K sums of
+// the skinny products below).
+__global__ void k_sum_partials(const float* __restrict__ part, int np, int64_t count, float* __restrict__ C) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= count) return;
+  float v = 0.f;
+  for (int p = 0; p < np; ++p) v += part[p * count + i];
+  C[i] = v;
+}
+
+hipError_t launch_sum_partials(hipStream_t s, const float* part, int np, int64_t count, float* C) {
+  hipLaunchKernelGGL(k_sum_partials, dim3((unsigned)ceil_div(count, 256)), dim3(256), 0, s, part, np, count, C);
+  return hipGetLastError();
+}
+
 // ---- Jacobi eigensolver for one small symmetric matrix (k <= 128, even).
 // Cyclic Jacobi in round-robin order: every round rotates k/2 disjoint
 // index pairs at once, (r mod m, k-1) and ((r + j) mod m, (r - j) mod m),
@@ -151,7 +166,8 @@ k_sym_eig_jacobi(const float* __restrict__ Sin, int k, float* __restrict__ theta
     float alls = 0.f;
     for (int w = 0; w < nt / 64; ++w) alls += sm.red[w];
     __syncthreads();
-    if (!(offs > 1e-14f * alls)) break;          // uniform across the workgroup
+    // fp32 rounding leaves off^2 near k eps^2 of the whole once converged
+    if (!(offs > 1e-11f * alls)) break;          // uniform across the workgroup
     for (int r = 0; r < m; ++r) {
       if (tid < half) {
         int a, b;

@@ -303,10 +303,54 @@ int eora_block(int64_t d_out, int rank) {
 }
 
 struct ELayout {
-  size_t status, D, T, G, Y, Q, C, S, V, theta, fac, total;
+  size_t status, D, T, G, Y, Q, C, S, V, theta, fac, part, total;
   QLayout fl;
   int k;
 };
+
+// Split-K for the skinny products of the subspace iteration (few output
+// tiles, long K): the K range is cut into equal chunks run as one batched
+// launch into fp32 partials (and one launch for a ragged rest), then summed
+// in a fixed order. At most kSplitMax + 1 partials.
+constexpr int kSplitMax = 64;
+
+int split_count(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ceil_div(M, 64) * ceil_div(N, 64);
+  if (tiles >= 512 || K < 256) return 1;
+  int64_t sp = std::min<int64_t>(ceil_div(512, tiles), K / 128);
+  return (int)std::max<int64_t>(1, std::min<int64_t>(sp, kSplitMax));
+}
+
+// C (M x N, contiguous) = op(A) op(B) with split K. ta/tb as GemmArgs.
+hipError_t gemm_splitk(hipStream_t s, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, int ta,
+                       const float* B, int64_t ldb, int tb, float* C, float* part) {
+  const int sp = split_count(M, N, K);
+  GemmArgs g{};
+  g.M = M; g.N = N; g.K = K;
+  g.A = A; g.lda = lda; g.ta = ta;
+  g.B = B; g.ldb = ldb; g.tb = tb;
+  g.C = C; g.ldc = N;
+  g.alpha = 1.f; g.beta = 0.f; g.batch = 1;
+  if (sp == 1) return launch_gemm_f32(s, g);
+  const int64_t kc = K / sp, rest = K - kc * sp;
+  g.K = kc; g.batch = sp;
+  g.sA = ta ? kc * lda : kc;         // the chunk's first k: row of a K x M store, column of an M x K one
+  g.sB = tb ? kc : kc * ldb;
+  g.C = part; g.sC = M * N;
+  hipError_t e = launch_gemm_f32(s, g);
+  if (e != hipSuccess) return e;
+  int np = sp;
+  if (rest > 0) {
+    GemmArgs r = g;
+    r.K = rest; r.batch = 1;
+    r.A = A + (ta ? sp * kc * lda : sp * kc);
+    r.B = B + (tb ? sp * kc : sp * kc * ldb);
+    r.C = part + (int64_t)sp * M * N;
+    if ((e = launch_gemm_f32(s, r)) != hipSuccess) return e;
+    ++np;
+  }
+  return launch_sum_partials(s, part, np, M * N, C);
+}
 
 gptq_params eora_factor_params(int k) {
   gptq_params fp{};
@@ -334,6 +378,15 @@ ELayout e_layout(int64_t d_out, int64_t n, int rank, int with_h) {
   L.V = c.take(sizeof(float) * k * k);
   L.theta = c.take(sizeof(float) * k);
   L.fac = c.take(L.fl.total);
+  // split-K partials of the three skinny products (G Q, the k x k Gram and
+  // Rayleigh matrices, A = U_r^T D): (splits + 1) x M x N floats each
+  int64_t mx = 0;
+  const int64_t uses[3][3] = {{d_out, k, d_out}, {k, k, d_out}, {rank, n, d_out}};
+  for (const auto& u : uses) {
+    const int sp = split_count(u[0], u[1], u[2]);
+    if (sp > 1) mx = std::max<int64_t>(mx, (sp + 1) * u[0] * u[1]);
+  }
+  L.part = c.take(sizeof(float) * mx);
   L.total = c.off;
   return L;
 }
@@ -356,7 +409,7 @@ gptq_status eora_orth(hipStream_t s, float* Y, float* Q, int64_t d, const ELayou
   const int64_t k = L.k;
   float* C = reinterpret_cast<float*>(ws + L.C);
   HIP_TRY(launch_col_normalize(s, Y, d, (int)k), "eora normalize");
-  HIP_TRY(launch_gemm_f32(s, gemm(k, k, d, Y, k, 1, Y, k, 0, C, k)), "eora gram");
+  HIP_TRY(gemm_splitk(s, k, k, d, Y, k, 1, Y, k, 0, C, reinterpret_cast<float*>(ws + L.part)), "eora gram");
   const gptq_params fp = eora_factor_params(L.k);
   gptq_status st = enqueue_factor(s, C, k, &fp, ws + L.fac, L.fl);
   if (st != GPTQ_OK) return st;
@@ -847,20 +900,21 @@ gptq_status gptq_eora(void* stream, const void* W, gptq_dtype wdt, const float* 
   }
   // start block and subspace iteration
   HIP_TRY(launch_eora_start(s, Q, d, (int)k), "eora start");
-  HIP_TRY(launch_gemm_f32(s, gemm(d, k, d, G, d, 0, Q, k, 0, Y, k)), "eora G Q");
+  float* part = reinterpret_cast<float*>(ws + L.part);
+  HIP_TRY(gemm_splitk(s, d, k, d, G, d, 0, Q, k, 0, Y, part), "eora G Q");
   for (int it = 0; it < it_n; ++it) {
     if ((st = eora_orth(s, Y, Q, d, L, ws)) != GPTQ_OK) return st;
-    HIP_TRY(launch_gemm_f32(s, gemm(d, k, d, G, d, 0, Q, k, 0, Y, k)), "eora G Q");
+    HIP_TRY(gemm_splitk(s, d, k, d, G, d, 0, Q, k, 0, Y, part), "eora G Q");
   }
   // CholeskyQR2 for the final basis, then Rayleigh-Ritz
   if ((st = eora_orth(s, Y, Q, d, L, ws)) != GPTQ_OK) return st;
   if ((st = eora_orth(s, Q, Y, d, L, ws)) != GPTQ_OK) return st;       // Y holds the basis now
-  HIP_TRY(launch_gemm_f32(s, gemm(d, k, d, G, d, 0, Y, k, 0, Q, k)), "eora G Q");
-  HIP_TRY(launch_gemm_f32(s, gemm(k, k, d, Y, k, 1, Q, k, 0, S, k)), "eora Rayleigh quotient");
+  HIP_TRY(gemm_splitk(s, d, k, d, G, d, 0, Y, k, 0, Q, part), "eora G Q");
+  HIP_TRY(gemm_splitk(s, k, k, d, Y, k, 1, Q, k, 0, S, part), "eora Rayleigh quotient");
   HIP_TRY(launch_sym_eig_jacobi(s, S, (int)k, theta, V), "eora Jacobi");
   // U_r = basis V[:, :r] into B, A = U_r^T D, then the singular-value scaling
   HIP_TRY(launch_gemm_f32(s, gemm(d, rank, k, Y, k, 0, V, k, 0, B, rank)), "eora U_r");
-  HIP_TRY(launch_gemm_f32(s, gemm(rank, n, d, B, rank, 1, D, n, 0, A, n)), "eora A");
+  HIP_TRY(gemm_splitk(s, rank, n, d, B, rank, 1, D, n, 0, A, part), "eora A");
   HIP_TRY(launch_eora_finish(s, theta, rank, sigma, B, d, rank, A, n), "eora finish");
   // device status: the difference, then the last factorisation (NaN in H
   // reaches the Gram matrix it factors)
