@@ -13,6 +13,7 @@ gptq_f64   the method itself (Hessian, damping/ordering, the O1 and O2 sweeps,
 packing    the LSB-first code bitstream and its inverse
 dequant    the dequantising product Y = X W_hat^T of a packed layer
 eora       the EoRA low-rank adapter of the compression error
+intrinsic  OLrC / Bid-Up refinement of a low-precision plus low-rank layer
 memory     storage accounting used by the pages' worked examples
 
 Every function names the passage of the pages it follows. The pages are:
@@ -21,7 +22,7 @@ Every function names the passage of the pages it follows. The pages are:
   [BAL]    "El balance de errores de la inferencia de pocos bits"
            (auturnal.com), sections 1-6 and "Ejemplo resuelto"
   [GIL]    "Resumen Técnico: GPTQ-intrinsic LoRA" (gist.science 2606.01412),
-           "Declaración del Problema" and "Metodología" item 2
+           "Declaración del Problema", "Metodología" items 2 and 4
   [EORA]   "Aumento de la precisión de LLM de 2 bits con EoRA" (7minutos.es),
            section "Bucear en el espacio propio en busca de un adaptador"
 """
