@@ -407,6 +407,66 @@ def bench_eora(args):
     print(json.dumps(line), flush=True)
 
 
+def bench_refine(args):
+    """One OLrC + Bid-Up cycle on the 5120-wide GPTQ-intrinsic layer (the
+    augmented 2-bit sweep's codes and grid, H of the original activations),
+    rank 64, timed between HIP events; the inputs are made untimed."""
+    import numpy as np
+    import torch
+
+    import post_weight_quantization_28_amd as G
+    import synth
+
+    if not os.path.exists(G.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    G.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("bench: generating the c5 workload")
+    wl = synth.make_workload("c5")
+    n0 = wl.n_quant
+    X = torch.from_numpy(wl.X_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    Wa = torch.from_numpy(wl.W_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    q = G.quantize_layer(Wa, G.accumulate_hessian(X), bits=2, group=128, damp=0.01, block=128, n_quant=n0,
+                         want_codes=True)
+    H = G.accumulate_hessian(X[:, :n0].contiguous())
+    del X
+    W = Wa[:, :n0].contiguous()
+    d_out = W.shape[0]
+    rank = 64
+    ws = torch.empty(G.refine_workspace_bytes(d_out, n0, rank), dtype=torch.uint8, device=dev)
+
+    def step():
+        return G.refine_lowrank(W, H, q.codes, q.scales, q.zeros, q.g_idx, 2, 128, rank=rank, cycles=1,
+                                passes=1, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = e0.elapsed_time(e1) / args.steps
+    line = {
+        "metric": "OLrC + Bid-Up refinement cycle of a GPTQ-intrinsic layer (5120x5120, 2-bit g128, rank 64)",
+        "value": d_out * n0 / (ms / 1e3), "unit": "weights/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "wall_ms_per_step": 1e3 * elapsed / args.steps,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": "one OLrC (rank-64 EoRA of W - W_hat) and one Bid-Up pass on the 5120x5120 layer's "
+                               "codes from the augmented 2-bit g128 sweep (X~ = [X, X V_64], 65536 Student-t(4) "
+                               "tokens); H = 2 X^T X of the original columns",
+                   "d_out": d_out, "d_in": n0, "rank": rank, "bits": 2, "group": 128, "parallelism": "single GPU"},
+        "roofline": None,
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -416,7 +476,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before warm-up, run one plain 1 GiB device copy and one 1 GiB fill "
                          "(known bytes) for calibrating HBM byte counters")
-    ap.add_argument("--workload", choices=["gptq_layer", "dequant_matmul", "eora"], default="gptq_layer")
+    ap.add_argument("--workload", choices=["gptq_layer", "dequant_matmul", "eora", "refine"], default="gptq_layer")
     ap.add_argument("--rank", type=int, default=64, help="adapter rank for --workload eora")
     ap.add_argument("--iters", type=int, default=0, help="subspace steps for --workload eora (0: 24)")
     ap.add_argument("--config", choices=sorted(CONFIG_TEXT), default="c2",
@@ -435,6 +495,9 @@ def main():
         return
     if args.workload == "eora":
         bench_eora(args)
+        return
+    if args.workload == "refine":
+        bench_refine(args)
         return
 
     import numpy as np

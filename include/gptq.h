@@ -275,6 +275,32 @@ gptq_status gptq_eora(void *stream, const void *W, gptq_dtype wdt, const float *
                       int32_t iters, float *B, float *A, float *sigma, void *workspace,
                       size_t workspace_bytes);
 
+/* ---- OLrC / Bid-Up refinement of a low-precision plus low-rank layer ---------
+ * W ~ W_hat + B A with W_hat = s (q - z) the codes on a fixed grid: each of
+ * `cycles` cycles first sets B (d_out x rank) and A (rank x n) to the best
+ * rank-r correction of W - W_hat (OLrC: the computation of gptq_eora), then
+ * runs `passes` Bid-Up passes over the codes for the target W - B A: the
+ * columns in order, each code moved to the grid point nearest the minimiser
+ * of tr((W - B A - W_hat) H (...)^T) along it, clamped to [0, 2^bits - 1]
+ * (columns with H_jj <= 0 unchanged). Every step lowers or keeps the layer
+ * error (up to fp32 rounding). codes: d_out x n uint8, in/out (e.g.
+ * quantize_layer's codes); scales / zeros: d_out x (n / group) with g_idx (n
+ * int32) mapping each column to its group, as quantize_layer writes them;
+ * H: n x n fp32; W: d_out x n, dtype wdt, row stride ldw. Outputs B, A and,
+ * if w_hat != NULL, the dequantised codes (d_out x n fp32). bits 2..8,
+ * 1 <= rank <= min(64, d_out), cycles and passes 1..100. Workspace:
+ * gptq_refine_workspace_bytes. Synchronises the stream.
+ * ("Resumen Técnico: GPTQ-intrinsic LoRA", "Refinamiento Bid-Up": OLrC
+ * optimises L and R for a fixed Q, Bid-Up optimises Q on the fixed grid by
+ * coordinate updates; the alternation never increases the layer error.) */
+gptq_status gptq_refine_workspace_bytes(int64_t d_out, int64_t n, int32_t rank, size_t *bytes);
+gptq_status gptq_refine_lowrank(void *stream, const void *W, gptq_dtype wdt, int64_t d_out,
+                                int64_t n, int64_t ldw, const float *H, int32_t bits,
+                                int32_t group, const int32_t *g_idx, const float *scales,
+                                const uint8_t *zeros, uint8_t *codes, int32_t rank,
+                                int32_t cycles, int32_t passes, float *B, float *A,
+                                float *w_hat, void *workspace, size_t workspace_bytes);
+
 /* ---- Diagnostics ------------------------------------------------------------ */
 const char *gptq_status_string(int status);
 const char *gptq_last_error(void); /* thread-local detail of the last failure */

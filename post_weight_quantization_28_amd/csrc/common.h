@@ -205,4 +205,12 @@ hipError_t launch_sym_eig_jacobi(hipStream_t s, const float* S, int k, float* th
 hipError_t launch_eora_finish(hipStream_t s, const float* theta, int r, float* sigma, float* B, int64_t d,
                               int64_t ldb, float* A, int64_t n);
 
+// ---- bidup.hip: coordinate descent over codes on a fixed grid
+hipError_t launch_bidup_block(hipStream_t s, const float* G, int64_t n, const float* H, uint8_t* codes,
+                              const float* scales, const int32_t* g_idx, int64_t ngroups,
+                              int64_t d_out, int64_t j0, int nb, int bits, float* Delta);
+hipError_t launch_bid_residual(hipStream_t s, const float* T, const uint8_t* codes, const float* scales,
+                               const uint8_t* zeros, const int32_t* g_idx, int64_t ngroups, int64_t d_out,
+                               int64_t n, float* D);
+
 }  // namespace gq

@@ -922,4 +922,96 @@ gptq_status gptq_eora(void* stream, const void* W, gptq_dtype wdt, const float* 
   if ((st = read_status(s, dst, nullptr, &col)) != GPTQ_OK) return st;
   return read_status(s, reinterpret_cast<DevStatus*>(ws + L.fac + L.fl.status), nullptr, nullptr);
 }
+
+// ---------------------------------------------------------------- OLrC / Bid-Up refinement
+namespace {
+struct RLayout {
+  size_t Qh, T, D, G, Delta, B0, A0, sig, eora, total;
+};
+
+RLayout r_layout(int64_t d_out, int64_t n, int rank) {
+  RLayout L{};
+  Carver c;
+  L.Qh = c.take(sizeof(float) * d_out * n);
+  L.T = c.take(sizeof(float) * d_out * n);
+  L.D = c.take(sizeof(float) * d_out * n);
+  L.G = c.take(sizeof(float) * d_out * n);
+  L.Delta = c.take(sizeof(float) * d_out * 128);
+  L.sig = c.take(sizeof(float) * 64);
+  L.eora = c.take(e_layout(d_out, n, rank, 1).total);
+  L.total = c.off;
+  return L;
+}
+}  // namespace
+
+gptq_status gptq_refine_workspace_bytes(int64_t d_out, int64_t n, int32_t rank, size_t* bytes) {
+  size_t e = 0;
+  gptq_status st = gptq_eora_workspace_bytes(d_out, n, rank, 1, &e);
+  if (st != GPTQ_OK) return st;
+  *bytes = r_layout(d_out, n, rank).total;
+  return GPTQ_OK;
+}
+
+gptq_status gptq_refine_lowrank(void* stream, const void* W, gptq_dtype wdt, int64_t d_out, int64_t n, int64_t ldw,
+                                const float* H, int32_t bits, int32_t group, const int32_t* g_idx,
+                                const float* scales, const uint8_t* zeros, uint8_t* codes, int32_t rank,
+                                int32_t cycles, int32_t passes, float* B, float* A, float* w_hat,
+                                void* workspace, size_t workspace_bytes) {
+  size_t need = 0;
+  gptq_status st = gptq_refine_workspace_bytes(d_out, n, rank, &need);
+  if (st != GPTQ_OK) return st;
+  if (wdt != GPTQ_BF16 && wdt != GPTQ_F32) return fail(GPTQ_EINVAL, "bad dtype");
+  if (bits < 2 || bits > 8) return fail(GPTQ_EINVAL, "bits must be in [2, 8]");
+  if (group < 1 || n % group != 0) return fail(GPTQ_EINVAL, "group must divide n");
+  if (cycles < 1 || cycles > 100 || passes < 1 || passes > 100) return fail(GPTQ_EINVAL, "cycles and passes in [1, 100]");
+  if (!W || !H || !g_idx || !scales || !zeros || !codes || !B || !A) return fail(GPTQ_EINVAL, "NULL pointer");
+  if (ldw < n) return fail(GPTQ_EINVAL, "ldw < n");
+  if ((st = check_ws(workspace, workspace_bytes, need)) != GPTQ_OK) return st;
+  hipStream_t s = (hipStream_t)stream;
+  char* ws = reinterpret_cast<char*>(workspace);
+  const RLayout L = r_layout(d_out, n, rank);
+  const int64_t ng = n / group;
+  float* Qh = reinterpret_cast<float*>(ws + L.Qh);
+  float* T = reinterpret_cast<float*>(ws + L.T);
+  float* D = reinterpret_cast<float*>(ws + L.D);
+  float* G = reinterpret_cast<float*>(ws + L.G);
+  float* Delta = reinterpret_cast<float*>(ws + L.Delta);
+  float* sig = reinterpret_cast<float*>(ws + L.sig);
+  void* ews = ws + L.eora;
+  const size_t ebytes = e_layout(d_out, n, rank, 1).total;
+  HIP_TRY(launch_bid_residual(s, nullptr, codes, scales, zeros, g_idx, ng, d_out, n, Qh), "dequantise");
+  for (int cy = 0; cy < cycles; ++cy) {
+    // OLrC: the optimal rank-r B A for the current codes (the EoRA problem on W - W_hat)
+    if ((st = gptq_eora(stream, W, wdt, Qh, d_out, n, ldw, H, rank, 0, B, A, sig, ews, ebytes)) != GPTQ_OK)
+      return st;
+    // target T = W - B A
+    HIP_TRY(launch_gemm_f32(s, gemm(d_out, n, rank, B, rank, 0, A, n, 0, D, n)), "B A");
+    DevStatus* dst = reinterpret_cast<DevStatus*>(ws + L.eora + e_layout(d_out, n, rank, 1).status);
+    HIP_TRY(launch_status_init(s, dst), "status init");
+    HIP_TRY(launch_eora_delta(s, W, wdt == GPTQ_BF16, ldw, D, d_out, n, T, dst), "target");
+    // Bid-Up passes: G = (T - W_hat) H, then blocks of 128 columns with lazy trailing updates
+    for (int ps = 0; ps < passes; ++ps) {
+      HIP_TRY(launch_bid_residual(s, T, codes, scales, zeros, g_idx, ng, d_out, n, D), "residual");
+      HIP_TRY(launch_gemm_f32(s, gemm(d_out, n, n, D, n, 0, H, n, 0, G, n)), "gradient");
+      for (int64_t j0 = 0; j0 < n; j0 += 128) {
+        const int nb = (int)std::min<int64_t>(128, n - j0);
+        HIP_TRY(launch_bidup_block(s, G, n, H, codes, scales, g_idx, ng, d_out, j0, nb, bits, Delta),
+                "bid-up block");
+        const int64_t j1 = j0 + nb;
+        if (j1 < n) {
+          GemmArgs g = gemm(d_out, n - j1, nb, Delta, 128, 0, H + j0 * n + j1, n, 0, G + j1, n);
+          g.alpha = -1.f;
+          g.beta = 1.f;
+          HIP_TRY(launch_gemm_f32(s, g), "bid-up trailing update");
+        }
+      }
+    }
+    HIP_TRY(launch_bid_residual(s, nullptr, codes, scales, zeros, g_idx, ng, d_out, n, Qh), "dequantise");
+    int64_t col = -1;
+    if ((st = read_status(s, dst, nullptr, &col)) != GPTQ_OK) return st;
+  }
+  if (w_hat) HIP_TRY(hipMemcpyAsync(w_hat, Qh, sizeof(float) * d_out * n, hipMemcpyDeviceToDevice, s), "copy w_hat");
+  HIP_TRY(hipStreamSynchronize(s), "synchronize");
+  return GPTQ_OK;
+}
 }  // extern "C"

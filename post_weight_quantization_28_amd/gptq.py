@@ -78,6 +78,10 @@ def load():
         "gptq_eora_workspace_bytes": [c_i64, c_i64, ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(c_sz)],
         "gptq_eora": [c_vp, c_vp, ctypes.c_int, c_vp, c_i64, c_i64, c_i64, c_vp, ctypes.c_int32, ctypes.c_int32,
                       c_vp, c_vp, c_vp, c_vp, c_sz],
+        "gptq_refine_workspace_bytes": [c_i64, c_i64, ctypes.c_int32, ctypes.POINTER(c_sz)],
+        "gptq_refine_lowrank": [c_vp, c_vp, ctypes.c_int, c_i64, c_i64, c_i64, c_vp, ctypes.c_int32, ctypes.c_int32,
+                                c_vp, c_vp, c_vp, c_vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, c_vp, c_vp,
+                                c_vp, c_vp, c_sz],
         "gptq_profile_enable": [ctypes.c_int],
         "gptq_profile_collect": [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i64)],
     }
@@ -341,6 +345,36 @@ def eora(W, W_hat, H=None, rank=32, iters=0, workspace=None):
                          _dev(H, "H") if H is not None else ctypes.c_void_p(0), int(rank), int(iters),
                          _dev(B, "B"), _dev(A, "A"), _dev(sigma, "sigma"), wsp, need))
     return B, A, sigma
+
+
+# ---------------------------------------------------------------- OLrC / Bid-Up
+def refine_workspace_bytes(d_out, n, rank):
+    lib = load()
+    out = ctypes.c_size_t(0)
+    _check(lib.gptq_refine_workspace_bytes(int(d_out), int(n), int(rank), ctypes.byref(out)))
+    return out.value
+
+
+def refine_lowrank(W, H, codes, scales, zeros, g_idx, bits, group, rank=32, cycles=1, passes=1, workspace=None):
+    """OLrC / Bid-Up cycles on a quantized layer: returns (codes, B, A,
+    w_hat) with the codes refined on their fixed grid (a new tensor; the
+    input is not modified), W ~ w_hat + B A."""
+    lib = load()
+    for t, nm in ((W, "W"), (H, "H"), (codes, "codes"), (scales, "scales"), (zeros, "zeros"), (g_idx, "g_idx")):
+        _dev(t, nm)
+    d_out, n = W.shape
+    dev = W.device
+    c = codes.clone()
+    B = torch.empty((d_out, rank), dtype=torch.float32, device=dev)
+    A = torch.empty((rank, n), dtype=torch.float32, device=dev)
+    w_hat = torch.empty((d_out, n), dtype=torch.float32, device=dev)
+    need = refine_workspace_bytes(d_out, n, rank)
+    ws, wsp = _workspace(need, dev, workspace)
+    _check(lib.gptq_refine_lowrank(_stream(), _dev(W, "W"), _dtype_code(W), d_out, n, W.stride(0), _dev(H, "H"),
+                                   int(bits), int(group), _dev(g_idx, "g_idx"), _dev(scales, "scales"),
+                                   _dev(zeros, "zeros"), _dev(c, "codes"), int(rank), int(cycles), int(passes),
+                                   _dev(B, "B"), _dev(A, "A"), _dev(w_hat, "w_hat"), wsp, need))
+    return c, B, A, w_hat
 
 
 # ---------------------------------------------------------------- packing
