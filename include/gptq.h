@@ -301,6 +301,21 @@ gptq_status gptq_refine_lowrank(void *stream, const void *W, gptq_dtype wdt, int
                                 int32_t cycles, int32_t passes, float *B, float *A,
                                 float *w_hat, void *workspace, size_t workspace_bytes);
 
+/* ---- Round-to-nearest on the same grid ---------------------------------------
+ * codes (rows x cols uint8), scales / zeros (rows x cols/group fp32 / uint8)
+ * and, if x_hat != NULL, x_hat = s (q - z) (rows x cols fp32) for X (rows x
+ * cols fp32, row stride ldx): the quantizer's affine grid per group of
+ * `group` consecutive columns of a row, with no error feedback. For the
+ * low-rank factors of an adapter (B at 8 bits, A at 4 bits) and as the
+ * round-to-nearest baseline. bits 2..8; group divides cols; rows <= 65535.
+ * Asynchronous. ("Resumen Técnico: GPTQ-intrinsic LoRA", "Resultados
+ * Clave": quantizing the low-rank factors L and R to 4 and 8 bits is often
+ * lossless; "GPTQ", "Rendimiento y Precisión": round-to-nearest as the
+ * baseline.) */
+gptq_status gptq_quantize_rtn(void *stream, const float *X, int64_t rows, int64_t cols,
+                              int64_t ldx, int32_t bits, int32_t group, uint8_t *codes,
+                              float *scales, uint8_t *zeros, float *x_hat);
+
 /* ---- Diagnostics ------------------------------------------------------------ */
 const char *gptq_status_string(int status);
 const char *gptq_last_error(void); /* thread-local detail of the last failure */

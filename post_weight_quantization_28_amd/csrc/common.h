@@ -173,6 +173,9 @@ hipError_t launch_pack(hipStream_t s, const uint8_t* codes, int64_t ldc, const i
                        int64_t d_out, int64_t n_quant, int bits, uint32_t* qweight);
 hipError_t launch_unpack(hipStream_t s, const uint32_t* qweight, int64_t d_out, int64_t n_quant,
                          int bits, uint8_t* codes);
+// round-to-nearest on the quantizer's affine grid, groups along rows (2 <= bits <= 8)
+hipError_t launch_rtn(hipStream_t s, const float* X, int64_t ldx, int64_t rows, int64_t cols, int bits, int group,
+                      uint8_t* codes, float* scales, uint8_t* zeros, float* xh);
 hipError_t launch_finish(hipStream_t s, const float* Wf, const uint8_t* codes_p,
                          const int32_t* invperm, int64_t d_out, int64_t n, int64_t n_quant,
                          int group, float* w_hat, uint8_t* codes_out, int32_t* g_idx);

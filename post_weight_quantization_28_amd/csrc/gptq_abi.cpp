@@ -1014,4 +1014,18 @@ gptq_status gptq_refine_lowrank(void* stream, const void* W, gptq_dtype wdt, int
   HIP_TRY(hipStreamSynchronize(s), "synchronize");
   return GPTQ_OK;
 }
+
+// ---------------------------------------------------------------- round-to-nearest
+gptq_status gptq_quantize_rtn(void* stream, const float* X, int64_t rows, int64_t cols, int64_t ldx, int32_t bits,
+                              int32_t group, uint8_t* codes, float* scales, uint8_t* zeros, float* x_hat) {
+  if (bits < 2 || bits > 8) return fail(GPTQ_EINVAL, "bits must be in [2, 8]");
+  if (rows < 0 || cols < 0 || group < 1) return fail(GPTQ_EINVAL, "bad size");
+  if (cols % group != 0) return fail(GPTQ_EINVAL, "group must divide cols");
+  if (ldx < cols) return fail(GPTQ_EINVAL, "ldx < cols");
+  if (cols / group > 2147483647 || rows > 65535) return fail(GPTQ_EINVAL, "too many groups or rows for one launch");
+  if (rows * cols == 0) return GPTQ_OK;
+  if (!X || !codes || !scales || !zeros) return fail(GPTQ_EINVAL, "NULL pointer");
+  HIP_TRY(launch_rtn((hipStream_t)stream, X, ldx, rows, cols, bits, group, codes, scales, zeros, x_hat), "rtn");
+  return GPTQ_OK;
+}
 }  // extern "C"

@@ -123,3 +123,55 @@ hipError_t launch_finish(hipStream_t s, const float* Wf, const uint8_t* codes_p,
 }
 
 }  // namespace gq
+
+namespace gq {
+
+// Round-to-nearest of a matrix on the affine grid of the quantizer (range
+// widened to 0, (-1, 1) when degenerate, s = (xmax - xmin) / maxq,
+// z = rint(-xmin / s), q = clamp(rint(x / s) + z, 0, maxq), x_hat = s (q - z)),
+// groups of `group` consecutive columns of a row; one wave per (row, group).
+// "Resumen Técnico: GPTQ-intrinsic LoRA", "Resultados Clave": the low-rank
+// factors themselves quantized to 4 and 8 bits.
+__global__ void __launch_bounds__(64)
+k_rtn(const float* __restrict__ X, int64_t ldx, int64_t cols, int group, float maxq, uint8_t* __restrict__ codes,
+      float* __restrict__ scales, uint8_t* __restrict__ zeros, float* __restrict__ xh) {
+  const int64_t r = blockIdx.y, g = blockIdx.x, ng = cols / group;
+  const int lane = threadIdx.x;
+  const float* x = X + r * ldx + g * group;
+  float mn = INFINITY, mx = -INFINITY;
+  for (int c = lane; c < group; c += 64) {
+    mn = fminf(mn, x[c]);
+    mx = fmaxf(mx, x[c]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, o));
+    mx = fmaxf(mx, __shfl_xor(mx, o));
+  }
+  float xmin = fminf(mn, 0.f), xmax = fmaxf(mx, 0.f);
+  if (xmin == xmax) {
+    xmin = -1.f;
+    xmax = 1.f;
+  }
+  const float s = (xmax - xmin) / maxq;
+  const float z = rintf(-xmin / s);
+  if (lane == 0) {
+    scales[r * ng + g] = s;
+    zeros[r * ng + g] = (uint8_t)z;
+  }
+  for (int c = lane; c < group; c += 64) {
+    const float q = fminf(fmaxf(rintf(x[c] / s) + z, 0.f), maxq);
+    codes[r * cols + g * group + c] = (uint8_t)q;
+    if (xh) xh[r * cols + g * group + c] = s * (q - z);
+  }
+}
+
+hipError_t launch_rtn(hipStream_t s, const float* X, int64_t ldx, int64_t rows, int64_t cols, int bits, int group,
+                      uint8_t* codes, float* scales, uint8_t* zeros, float* xh) {
+  if (rows == 0 || cols == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_rtn, dim3((unsigned)(cols / group), (unsigned)rows), dim3(64), 0, s, X, ldx, cols, group,
+                     (float)((1 << bits) - 1), codes, scales, zeros, xh);
+  return hipGetLastError();
+}
+
+}  // namespace gq

@@ -82,6 +82,8 @@ def load():
         "gptq_refine_lowrank": [c_vp, c_vp, ctypes.c_int, c_i64, c_i64, c_i64, c_vp, ctypes.c_int32, ctypes.c_int32,
                                 c_vp, c_vp, c_vp, c_vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, c_vp, c_vp,
                                 c_vp, c_vp, c_sz],
+        "gptq_quantize_rtn": [c_vp, c_vp, c_i64, c_i64, c_i64, ctypes.c_int32, ctypes.c_int32, c_vp, c_vp, c_vp,
+                              c_vp],
         "gptq_profile_enable": [ctypes.c_int],
         "gptq_profile_collect": [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(c_i64)],
     }
@@ -375,6 +377,25 @@ def refine_lowrank(W, H, codes, scales, zeros, g_idx, bits, group, rank=32, cycl
                                    _dev(zeros, "zeros"), _dev(c, "codes"), int(rank), int(cycles), int(passes),
                                    _dev(B, "B"), _dev(A, "A"), _dev(w_hat, "w_hat"), wsp, need))
     return c, B, A, w_hat
+
+
+# ---------------------------------------------------------------- round-to-nearest
+def quantize_rtn(X, bits, group):
+    """(codes, scales, zeros, x_hat) of X (rows x cols fp32) on the affine
+    grid, groups of `group` columns, no feedback."""
+    lib = load()
+    _dev(X, "X")
+    if X.dtype != torch.float32:
+        raise TypeError("X must be float32")
+    rows, cols = X.shape
+    dev = X.device
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=dev)
+    scales = torch.empty((rows, cols // group), dtype=torch.float32, device=dev)
+    zeros = torch.empty((rows, cols // group), dtype=torch.uint8, device=dev)
+    xh = torch.empty((rows, cols), dtype=torch.float32, device=dev)
+    _check(lib.gptq_quantize_rtn(_stream(), _dev(X, "X"), rows, cols, X.stride(0), int(bits), int(group),
+                                 _dev(codes, "codes"), _dev(scales, "scales"), _dev(zeros, "zeros"), _dev(xh, "x_hat")))
+    return codes, scales, zeros, xh
 
 
 # ---------------------------------------------------------------- packing

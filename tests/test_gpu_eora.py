@@ -177,3 +177,56 @@ def test_attention_projection_full_size():
         f"loss left {left / total:.4f} of {total:.4e}")
     assert sig_err <= 1e-4
     assert (1 - 1e-5) * e_opt <= e_gpu <= e_opt * (1 + 1e-6) + 1e-12 * total
+
+
+# ---- quantized low-rank factors ----------------------------------------------
+@pytest.mark.parametrize("bits,group,shape", [(8, 64, (200, 64)), (4, 128, (64, 1024)), (2, 32, (33, 96)),
+                                              (3, 8, (17, 40))])
+def test_rtn_matches_oracle(bits, group, shape):
+    """gptq_quantize_rtn against the oracle's round-to-nearest: zero points
+    and codes identical except where the oracle's pre-rounding value is
+    within 1e-3 steps of a half-integer (no feedback: decisions are
+    independent), and x_hat = s (q - z) bit for bit with the GPU's grid."""
+    r = np.random.default_rng(bits * 100 + group)
+    X = (r.standard_t(4, shape) * 0.05).astype(np.float32)
+    X[0, :group] = 0.0                       # a degenerate group
+    codes, sc, zr, xh = G.quantize_rtn(cuda32(X), bits, group)
+    o = O.rtn(X.astype(np.float64), bits, group)
+    gi = np.arange(shape[1]) // group
+    s64, z64 = o["scales"], o["zeros"].astype(np.float64)
+    zpre = np.where(np.minimum(X.reshape(shape[0], -1, group).min(2), 0) ==
+                    np.maximum(X.reshape(shape[0], -1, group).max(2), 0), 1.0,
+                    -np.minimum(X.reshape(shape[0], -1, group).min(2), 0.0)) / s64
+    zg = zr.cpu().numpy()
+    zbad = (zg != o["zeros"]) & (O.tie_distance(zpre) >= 1e-3)
+    assert not zbad.any()
+    same_grid = (zg == o["zeros"])[:, gi]
+    pre = X.astype(np.float64) / s64[:, gi]
+    cg = codes.cpu().numpy()
+    cbad = same_grid & (cg != o["codes"]) & (O.tie_distance(pre) >= 1e-3)
+    assert not cbad.any()
+    say(f"rtn {bits}-bit g{group}: codes identical {np.mean(cg == o['codes']):.5f}")
+    scn, zn = sc.cpu().numpy(), zg.astype(np.float32)
+    assert np.array_equal(xh.cpu().numpy(), (scn[:, gi] * (cg.astype(np.float32) - zn[:, gi])).astype(np.float32))
+
+
+def test_adapter_with_quantized_factors():
+    """The EoRA adapter of a 2-bit GPTQ layer with B at 8 bits (one group per
+    row) and A at 4 bits (groups of 128): the page reports such quantized
+    factors as often lossless; here the adapter keeps most of its gain."""
+    wl = synth.make_workload("c2", d_out=512, n=1024, T=8192)
+    Wd = w_dev(wl)
+    H = G.accumulate_hessian(x_dev(wl))
+    q = G.quantize_layer(Wd, H, bits=2, group=128)
+    rank = 32
+    B, A, s = G.eora(Wd, q.w_hat, H, rank=rank)
+    _, _, _, Bq = G.quantize_rtn(B.contiguous(), 8, rank)
+    _, _, _, Aq = G.quantize_rtn(A.contiguous(), 4, 128)
+    Hn = H.cpu().numpy().astype(np.float64)
+    W_hat = q.w_hat.cpu().numpy().astype(np.float64)
+    l0 = E.layer_loss(wl.W, W_hat, Hn)
+    lf = E.layer_loss(wl.W, W_hat, Hn, B.cpu().numpy(), A.cpu().numpy())
+    lq = E.layer_loss(wl.W, W_hat, Hn, Bq.cpu().numpy(), Aq.cpu().numpy())
+    say(f"layer loss: no adapter {l0:.6e}, fp32 factors {lf:.6e}, 8/4-bit factors {lq:.6e} "
+        f"(gain kept {(l0 - lq) / (l0 - lf):.4f})")
+    assert lq < l0 and (l0 - lq) >= 0.9 * (l0 - lf)
