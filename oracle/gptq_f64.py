@@ -133,10 +133,36 @@ def upper_chol_of_inverse_by_reversal(Hd):
 # ---------------------------------------------------------------------------
 # The quantization grid ([BAL] section 1; R4-R6)
 # ---------------------------------------------------------------------------
-def group_grid(v, maxq, sym=False):
-    """Per-row (s, z, zpre) from the group's current values ``v`` (rows x g).
+def round_fp16(s):
+    """(s16, t, ulp): positive values rounded to IEEE binary16 (10 fraction
+    bits, round to nearest, ties to even), from the format's definition.
+    The binade of s is 2^e with e = floor(log2 s) (exact, through frexp),
+    held at -14 below the normal range, where the subnormals share the
+    spacing 2^-24; ulp = 2^(e - 10), t = s / ulp is the value the rounding
+    decides on and s16 = rint(t) ulp ("El balance de errores de la
+    inferencia de pocos bits", section 1: the precision of the scales is
+    part of the format). Reading: a value that rounds to 0 takes the
+    smallest subnormal, 2^-24, so that a group always has a positive
+    scale."""
+    s = np.asarray(s, np.float64)
+    _, ex = np.frexp(s)
+    e = np.maximum(ex - 1, -14).astype(np.float64)
+    ulp = np.exp2(e - 10.0)
+    t = s / ulp
+    s16 = np.rint(t) * ulp
+    return np.where(s16 == 0.0, 2.0 ** -24, s16), t, ulp
+
+
+def group_grid(v, maxq, sym=False, scale_fp16=False, alt_scale_rows=None):
+    """Per-row (s, z, zpre, smargin) from the group's current values ``v``
+    (rows x g).
 
     zpre = -xmin / s is the value rint() decides the zero point from.
+    scale_fp16: the scale is rounded to binary16 (round_fp16) before it is
+    used, and smargin is that rounding's tie distance in binary16 steps
+    (0.5 without the option: no decision); the rows in alt_scale_rows take
+    the other binary16 neighbour (the other branch of a scale tie). The
+    zero point and the codes use the rounded scale.
 
     sym: the symmetric alphabet {-A, ..., A} with A = (maxq - 1) / 2 =
     2^(b-1) - 1 levels on each side of zero ("Resumen Técnico:
@@ -155,15 +181,25 @@ def group_grid(v, maxq, sym=False):
         amax = np.maximum(-xmin, xmax)
         amax = np.where(amax == 0.0, 1.0, amax)
         s = amax / A
+    else:
+        same = xmin == xmax
+        xmin = np.where(same, -1.0, xmin)
+        xmax = np.where(same, 1.0, xmax)
+        s = (xmax - xmin) / maxq
+    smargin = np.full_like(s, 0.5)
+    if scale_fp16:
+        s16, t, ulp = round_fp16(s)
+        if alt_scale_rows:
+            rows = list(alt_scale_rows)
+            s16[rows] = np.maximum(other_neighbour(t[rows]), 1.0) * ulp[rows]
+        s = s16
+        smargin = tie_distance(t)
+    if sym:
         z = np.full_like(s, A)
-        return s, z, z.copy()
-    same = xmin == xmax
-    xmin = np.where(same, -1.0, xmin)
-    xmax = np.where(same, 1.0, xmax)
-    s = (xmax - xmin) / maxq
+        return s, z, z.copy(), smargin
     zpre = -xmin / s
     z = np.rint(zpre)
-    return s, z, zpre
+    return s, z, zpre, smargin
 
 
 def code_top(maxq, sym):
@@ -207,7 +243,7 @@ def _check_params(n, bits, group, block, n_quant):
 
 
 def _finish(W, Wp, perm, codes_p, scales, zeros, loss, n_quant, group,
-            margins, zmargins):
+            margins, zmargins, smargins):
     d_out, n = W.shape
     w_hat = np.empty_like(Wp)
     w_hat[:, perm] = Wp
@@ -217,14 +253,14 @@ def _finish(W, Wp, perm, codes_p, scales, zeros, loss, n_quant, group,
     g_idx[perm[:n_quant]] = np.arange(n_quant) // group
     return dict(codes=codes, scales=scales, zeros=zeros.astype(np.uint8),
                 g_idx=g_idx, w_hat=w_hat, row_loss=loss, perm=perm,
-                codes_proc=codes_p, margins=margins, zmargins=zmargins)
+                codes_proc=codes_p, margins=margins, zmargins=zmargins, smargins=smargins)
 
 
 # ---------------------------------------------------------------------------
 # O2: Cholesky of the inverse + lazy batches (the scalable form)
 # ---------------------------------------------------------------------------
 def gptq_o2(W, H, bits=4, group=128, damp=0.01, block=128, act_order=False,
-            n_quant=None, U=None, perm=None, alt=None, sym=False):
+            n_quant=None, U=None, perm=None, alt=None, sym=False, scale_fp16=False):
     """GPTQ sweep with the upper Cholesky factor U of H_d^{-1} and lazy
     batches of ``block`` columns ([GPTQ] "Enfoque Técnico"; [GIL]
     "Detalles de Implementación").
@@ -237,12 +273,13 @@ def gptq_o2(W, H, bits=4, group=128, damp=0.01, block=128, act_order=False,
 
     ``U``/``perm`` may be passed in to reuse a factorisation (the oracle
     still computes them with :func:`prepare` and LAPACK).
-    ``alt`` = (codes, zeros), two collections of (row, processing position)
-    and (row, group) pairs whose rounding takes the other neighbour of its
-    pre-rounding value instead of the nearest integer: the other branch of a
-    decision that sits at a tie, where either rounding is correct at the
-    precision of the inputs. Everything after such a decision follows from
-    it by the same rules.
+    ``alt`` = (codes, zeros[, scales]), collections of (row, processing
+    position) and (row, group) pairs whose rounding takes the other
+    neighbour of its pre-rounding value instead of the nearest one: the
+    other branch of a decision that sits at a tie, where either rounding is
+    correct at the precision of the inputs. Everything after such a
+    decision follows from it by the same rules.
+    ``scale_fp16``: scales rounded to binary16 before use (group_grid).
     Returns codes (original order), scales/zeros (group order), g_idx,
     w_hat, row_loss = sum_j e_j^2, and the tie distances of every decision.
     """
@@ -262,9 +299,10 @@ def gptq_o2(W, H, bits=4, group=128, damp=0.01, block=128, act_order=False,
     zeros = np.zeros((d_out, ng))
     margins = np.zeros((d_out, nq))
     zmargins = np.zeros((d_out, ng))
+    smargins = np.zeros((d_out, ng))
     loss = np.zeros(d_out)
-    alt_c, alt_z = {}, {}
-    for src, dst in zip(alt or ((), ()), (alt_c, alt_z)):
+    alt_c, alt_z, alt_s = {}, {}, {}
+    for src, dst in zip(alt or ((), (), ()), (alt_c, alt_z, alt_s)):
         for r, k in src:
             dst.setdefault(int(k), []).append(int(r))
     s = z = None
@@ -273,13 +311,15 @@ def gptq_o2(W, H, bits=4, group=128, damp=0.01, block=128, act_order=False,
         E = np.zeros((d_out, i1 - i0))
         for j in range(i0, i1):
             if j % group == 0:
-                s, z, zpre = group_grid(Wp[:, j:j + group], maxq, sym)
+                s, z, zpre, smg = group_grid(Wp[:, j:j + group], maxq, sym, scale_fp16,
+                                             alt_s.get(j // group))
                 rz = alt_z.get(j // group)
                 if rz:
                     z[rz] = np.clip(other_neighbour(zpre[rz]), 0.0, qtop)
                 scales[:, j // group] = s
                 zeros[:, j // group] = z
                 zmargins[:, j // group] = tie_distance(zpre)
+                smargins[:, j // group] = smg
             q, what, pre = quantize_column(Wp[:, j], s, z, qtop)
             rc = alt_c.get(j)
             if rc:
@@ -294,13 +334,14 @@ def gptq_o2(W, H, bits=4, group=128, damp=0.01, block=128, act_order=False,
             margins[:, j] = tie_distance(pre)
         Wp[:, i1:] -= E @ U[i0:i1, i1:]
     return _finish(W, Wp, perm, codes, scales, zeros, loss, nq, group,
-                   margins, zmargins)
+                   margins, zmargins, smargins)
 
 
 # ---------------------------------------------------------------------------
 # O1: the Optimal-Brain definition with explicit inverse downdates
 # ---------------------------------------------------------------------------
-def gptq_o1(W, H, bits=4, group=128, damp=0.01, act_order=False, n_quant=None, sym=False):
+def gptq_o1(W, H, bits=4, group=128, damp=0.01, act_order=False, n_quant=None, sym=False,
+            scale_fp16=False):
     """Column-by-column OBS form, eager updates ([GPTQ] "Enfoque Técnico").
 
     G is the inverse of H_d restricted to the columns not yet quantized.
@@ -325,14 +366,16 @@ def gptq_o1(W, H, bits=4, group=128, damp=0.01, act_order=False, n_quant=None, s
     zeros = np.zeros((d_out, ng))
     margins = np.zeros((d_out, nq))
     zmargins = np.zeros((d_out, ng))
+    smargins = np.zeros((d_out, ng))
     loss = np.zeros(d_out)
     s = z = None
     for j in range(nq):
         if j % group == 0:
-            s, z, zpre = group_grid(Wp[:, j:j + group], maxq, sym)
+            s, z, zpre, smg = group_grid(Wp[:, j:j + group], maxq, sym, scale_fp16)
             scales[:, j // group] = s
             zeros[:, j // group] = z
             zmargins[:, j // group] = tie_distance(zpre)
+            smargins[:, j // group] = smg
         q, what, pre = quantize_column(Wp[:, j], s, z, qtop)
         g00 = G[0, 0]
         delta = Wp[:, j] - what
@@ -343,13 +386,13 @@ def gptq_o1(W, H, bits=4, group=128, damp=0.01, act_order=False, n_quant=None, s
         margins[:, j] = tie_distance(pre)
         G = G[1:, 1:] - np.outer(G[1:, 0], G[0, 1:]) / g00
     return _finish(W, Wp, perm, codes, scales, zeros, loss, nq, group,
-                   margins, zmargins)
+                   margins, zmargins, smargins)
 
 
 # ---------------------------------------------------------------------------
 # Round-to-nearest and brute force
 # ---------------------------------------------------------------------------
-def rtn(W, bits=4, group=128, sym=False):
+def rtn(W, bits=4, group=128, sym=False, scale_fp16=False):
     """Round-to-nearest on the same grid rules (R4-R6), no feedback: the
     baseline GPTQ is compared with ([GPTQ] "Rendimiento y Precisión")."""
     W = np.asarray(W, np.float64)
@@ -363,7 +406,7 @@ def rtn(W, bits=4, group=128, sym=False):
     zeros = np.zeros((d_out, ng))
     for gi in range(ng):
         sl = slice(gi * group, (gi + 1) * group)
-        s, z, _ = group_grid(W[:, sl], maxq, sym)
+        s, z, _, _ = group_grid(W[:, sl], maxq, sym, scale_fp16)
         scales[:, gi] = s
         zeros[:, gi] = z
         for j in range(sl.start, sl.stop):

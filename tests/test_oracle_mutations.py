@@ -144,9 +144,17 @@ def pin_chol_reversal(O):
     assert np.abs(U.T @ U @ Hd - np.eye(24)).max() < 1e-10
 
 
+def pin_fp16(O):
+    s16, t, _ = O.round_fp16(np.array([1.0, 1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 3 * 2.0 ** -26, 0.1, 7e-5, 3e-6]))
+    ref = np.array([1.0, 1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 3 * 2.0 ** -26, 0.1, 7e-5, 3e-6]).astype(np.float16)
+    assert np.array_equal(s16, ref.astype(np.float64))
+    W = np.array([[-0.5, 1.0, 0.3, 0.0]])
+    assert O.rtn(W, 4, 4, scale_fp16=True)["codes"][0].tolist() == [0, 15, 8, 5]
+
+
 BATTERY = [pin_hessian, pin_grid, pin_o1_o2, pin_loss, pin_n2, pin_perm,
            pin_rtn_special, pin_block_inv, pin_tie_distance, pin_layer_error, pin_dead_column,
-           pin_chol_reversal]
+           pin_chol_reversal, pin_fp16]
 
 
 def _caught(O):
@@ -192,6 +200,10 @@ MUTATIONS = [
     ("dead-column value 2", "H[dead, dead] = 1.0", "H[dead, dead] = 2.0"),
     ("reversal route without the reversal", "A = np.array(np.asarray(Hd, np.float64)[::-1, ::-1], order=",
      "A = np.array(np.asarray(Hd, np.float64), order="),
+    ("binary16 with 11 fraction bits", "ulp = np.exp2(e - 10.0)", "ulp = np.exp2(e - 11.0)"),
+    ("binary16 without the subnormal floor", "e = np.maximum(ex - 1, -14).astype(np.float64)",
+     "e = (ex - 1).astype(np.float64)"),
+    ("binary16 rounding by truncation", "s16 = np.rint(t) * ulp", "s16 = np.floor(t) * ulp"),
     ("reversal route returns the lower factor", "return np.ascontiguousarray(Li[::-1, ::-1]).reshape(n, n)",
      "return np.ascontiguousarray(Li).reshape(n, n)"),
 ]

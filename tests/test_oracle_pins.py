@@ -649,3 +649,94 @@ def test_dead_column_in_act_order():
     want = sorted(range(len(d)), key=lambda i: (-d[i], i))
     _, perm = O.prepare(H, 0.01, act_order=True)
     assert list(perm) == want
+
+
+# ---------------------------------------------------------------- fp16 scales
+def test_round_fp16_is_binary16_rounding():
+    """The oracle's binary16 rounding (written from the format) equals
+    numpy's float16 conversion (a library routine) on values across the
+    normal and subnormal ranges, and the reading for values that round to
+    zero gives the smallest subnormal."""
+    r = np.random.default_rng(14)
+    s = np.concatenate([10.0 ** r.uniform(-7.5, 4.5, 20000), 2.0 ** np.arange(-24, 15, dtype=np.float64),
+                        (1.0 + (2 * np.arange(1, 200) + 1) * 2.0 ** -11)])
+    s16, t, ulp = O.round_fp16(s)
+    ref = s.astype(np.float16).astype(np.float64)
+    ok = ref > 0
+    assert np.array_equal(s16[ok], ref[ok])
+    assert np.all(s16[~ok] == 2.0 ** -24)
+    assert np.all(s16 > 0)
+
+
+def test_round_fp16_hand_values():
+    """1 is exact (t = 1024, margin 0.5); 1 + 2^-11 is an exact tie that goes
+    to the even neighbour 1 (margin 0); 1 + 3 * 2^-11 ties to 1 + 2^-9;
+    3 * 2^-26 lies in the subnormal range (ulp 2^-24, t = 0.75) and rounds
+    to 2^-24; 0.1 rounds to 1638 * 2^-14."""
+    s16, t, _ = O.round_fp16(np.array([1.0, 1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11, 3 * 2.0 ** -26, 0.1]))
+    assert s16.tolist() == [1.0, 1.0, 1 + 2.0 ** -9, 2.0 ** -24, 1638 * 2.0 ** -14]
+    assert np.allclose(O.tie_distance(t[:3]), [0.5, 0.0, 0.0], atol=1e-12)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_fp16_scales_diagonal_hessian_is_rtn(bits):
+    """With binary16 scales GPTQ on a diagonal H is round-to-nearest on the
+    same binary16 grid, and every stored scale is a binary16 value."""
+    r = np.random.default_rng(15 + bits)
+    W = r.standard_normal((9, 64)) * 0.02
+    o = O.gptq_o2(W, 2.0 * np.eye(64), bits, 16, 0.01, 16, scale_fp16=True)
+    rt = O.rtn(W, bits, 16, scale_fp16=True)
+    assert np.array_equal(o["codes"], rt["codes"])
+    assert np.array_equal(o["scales"], rt["scales"])
+    assert np.array_equal(o["scales"], o["scales"].astype(np.float16).astype(np.float64))
+    assert np.array_equal(o["w_hat"], rt["w_hat"])
+
+
+def test_fp16_scales_hand_worked_group():
+    """One 4-bit group (maxq 15) with range [-0.5, 1.0]: s = 0.1 exactly in
+    float64, binary16 0.0999755859375 (1638 * 2^-14); z = rint(0.5 / s16)
+    = rint(5.0012...) = 5; w = 0.3 -> rint(0.3 / s16) = 3 -> code 8,
+    w_hat = 3 s16."""
+    W = np.array([[-0.5, 1.0, 0.3, 0.0]])
+    rt = O.rtn(W, 4, 4, scale_fp16=True)
+    s16 = 1638 * 2.0 ** -14
+    assert rt["scales"][0, 0] == s16
+    assert rt["zeros"][0, 0] == 5
+    assert rt["codes"][0].tolist() == [0, 15, 8, 5]
+    assert rt["w_hat"][0, 2] == 3 * s16
+    plain = O.rtn(W, 4, 4)
+    assert plain["scales"][0, 0] == 0.1
+
+
+@pytest.mark.parametrize("act_order", [False, True])
+def test_fp16_scales_o1_equals_o2(act_order):
+    W, X = _tiny(41, 12, 96, 500, heavy=True)
+    H = O.hessian(X)
+    o1 = O.gptq_o1(W, H, 3, 32, 0.01, act_order=act_order, scale_fp16=True)
+    o2 = O.gptq_o2(W, H, 3, 32, 0.01, 16, act_order=act_order, scale_fp16=True)
+    ok = (o1["codes"] == o2["codes"]) | (o2["margins"][:, np.argsort(o2["perm"])] < 1e-8)
+    assert ok.all()
+    assert np.array_equal(o1["scales"], o2["scales"]) or np.all(o2["smargins"] < 1e-8)
+    assert np.allclose(o1["w_hat"], o2["w_hat"], atol=1e-10)
+    D = (W - o2["w_hat"])[:, o2["perm"]]
+    Hd, _ = O.prepare(H, 0.01, act_order)
+    assert np.allclose(o2["row_loss"], np.einsum("ri,ij,rj->r", D, Hd, D), rtol=1e-9)
+
+
+def test_fp16_scale_tie_branch():
+    """The other branch of a scale decision: that group's scale moves to the
+    other binary16 neighbour, earlier decisions are unchanged, and the run is
+    still a GPTQ run (loss identity)."""
+    W, X = _tiny(42, 6, 64, 400, heavy=True)
+    H = O.hessian(X)
+    Hd, perm = O.prepare(H, 0.01)
+    U = O.upper_chol_of_inverse(Hd)
+    a = O.gptq_o2(W, H, 3, 16, 0.01, 16, U=U, perm=perm, scale_fp16=True)
+    r, g = 2, 1
+    b = O.gptq_o2(W, H, 3, 16, 0.01, 16, U=U, perm=perm, scale_fp16=True, alt=((), (), [(r, g)]))
+    s_a, s_b = a["scales"][r, g], b["scales"][r, g]
+    assert s_a != s_b and abs(s_a - s_b) <= 2.0 ** -10 * s_a
+    assert np.array_equal(a["codes_proc"][r, :16 * g], b["codes_proc"][r, :16 * g])
+    assert np.array_equal(np.delete(a["codes_proc"], r, 0), np.delete(b["codes_proc"], r, 0))
+    D = (W - b["w_hat"])[:, perm]
+    assert np.allclose(b["row_loss"], np.einsum("ri,ij,rj->r", D, Hd, D), rtol=1e-9)
