@@ -68,7 +68,8 @@ typedef enum {
 typedef enum { GPTQ_BF16 = 0, GPTQ_F32 = 1 } gptq_dtype;
 
 typedef struct {
-  uint32_t struct_size; /* sizeof(gptq_params); at least offsetof(sym) */
+  uint32_t struct_size; /* sizeof(gptq_params); at least offsetof(sym); a
+                           field is read only when struct_size covers it */
   int32_t bits;         /* 2, 3 or 4 */
   int32_t group;        /* g >= 8; n_quant % g == 0; g % block == 0 or block % g == 0 */
   float damp;           /* lambda = damp * mean(diag H); >= 0, finite */
@@ -83,6 +84,18 @@ typedef struct {
                            covers it (older callers: 0). ("Resumen Técnico:
                            GPTQ-intrinsic LoRA": a finite integer alphabet of
                            size 2B + 1.) */
+  int32_t scale_fp16;   /* 0: scales in fp32; 1: each group's scale is rounded
+                           to binary16 (nearest, ties to even; 0 -> 2^-24)
+                           before the zero point, the codes and w_hat use it,
+                           so the fp32 scales output holds binary16 values
+                           that convert exactly. Read only when struct_size
+                           covers it (older callers: 0). ("El balance de
+                           errores de la inferencia de pocos bits", section
+                           1: the precision of the scales is part of the
+                           format.) */
+  int32_t reserved;     /* 0. (With it the block grew from 40 to 48 bytes, so a
+                           caller built before scale_fp16 existed, whose
+                           struct_size is 40, never has its padding read.) */
 } gptq_params;
 
 typedef struct {

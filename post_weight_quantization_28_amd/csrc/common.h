@@ -152,6 +152,7 @@ struct SweepArgs {
   int block;                    // B
   int group, bits;
   int sym;                      // 1: symmetric alphabet {-A..A}, z = A = 2^(bits-1) - 1
+  int scale16;                  // 1: group scales rounded to binary16 before use
   int64_t gbase;                // group index of column i0
   int gshift;                   // log2(group) when groups split a block, else 31
   float* scales; uint8_t* zeros; int64_t ngroups;

@@ -141,6 +141,12 @@ constexpr size_t kParamsMin = offsetof(gptq_params, sym);
 int params_sym(const gptq_params* p) {
   return p->struct_size >= offsetof(gptq_params, sym) + sizeof(int32_t) ? p->sym : 0;
 }
+// scale_fp16 arrived with `reserved`, which grew the block from 40 to 48
+// bytes: a 40-byte block predates it (its bytes 36..39 are padding).
+int params_scale16(const gptq_params* p) {
+  return p->struct_size >= offsetof(gptq_params, reserved) + sizeof(int32_t) ? p->scale_fp16 : 0;
+}
+static_assert(offsetof(gptq_params, reserved) + sizeof(int32_t) > 40, "the block must grow past 40 bytes");
 
 gptq_status check_params(int64_t d_out, int64_t n, const gptq_params* p) {
   if (!p) return fail(GPTQ_EINVAL, "params is NULL");
@@ -159,6 +165,8 @@ gptq_status check_params(int64_t d_out, int64_t n, const gptq_params* p) {
   if (p->act_order != 0 && p->act_order != 1) return fail(GPTQ_EINVAL, "act_order must be 0 or 1");
   const int sym = params_sym(p);
   if (sym != 0 && sym != 1) return fail(GPTQ_EINVAL, "sym must be 0 or 1");
+  const int s16 = params_scale16(p);
+  if (s16 != 0 && s16 != 1) return fail(GPTQ_EINVAL, "scale_fp16 must be 0 or 1");
   return GPTQ_OK;
 }
 
@@ -611,7 +619,7 @@ gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int
       float* Eb = E + (i0 - s0);
       SweepArgs a{};
       a.Wf = Wf; a.ldw = n; a.U = U; a.ldu = n; a.d_out = d_out; a.i0 = i0; a.ncols = nc;
-      a.block = B; a.group = p->group; a.bits = p->bits; a.sym = params_sym(p);
+      a.block = B; a.group = p->group; a.bits = p->bits; a.sym = params_sym(p); a.scale16 = params_scale16(p);
       a.gbase = i0 / p->group;
       a.gshift = 31;
       if (p->group < B)

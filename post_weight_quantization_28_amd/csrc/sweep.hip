@@ -146,15 +146,20 @@ __device__ __forceinline__ Grid group_start(const float (&w)[CPL], const SweepAr
     float amax = fmaxf(-xmin, xmax);
     if (amax == 0.f) amax = 1.f;
     g.s = amax / A;
-    g.z = A;
   } else {
     if (xmin == xmax) {
       xmin = -1.f;
       xmax = 1.f;
     }
     g.s = (xmax - xmin) / maxq;
-    g.z = rintf(-xmin / g.s);
   }
+  if (a.scale16) {
+    // binary16 scale precision: round to nearest even; a scale that rounds
+    // to 0 takes the smallest subnormal 2^-24
+    const float s16 = static_cast<float>(static_cast<_Float16>(g.s));
+    g.s = s16 > 0.f ? s16 : 5.9604644775390625e-8f;
+  }
+  g.z = a.sym ? 0.5f * (maxq - 1.f) : rintf(-xmin / g.s);
   g.inv_s = 1.f / g.s;
   if (row_ok && L == 0) {
     const int64_t gi = a.gbase + (LO >> a.gshift);

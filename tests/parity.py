@@ -51,23 +51,40 @@ def rel_fro(a, b):
     return float(np.linalg.norm(a - b) / np.linalg.norm(b))
 
 
-def first_mismatch_report(gpu_codes_orig, gpu_zeros, orc, group, tau=TAU):
+def _scale_mismatch(gpu_scales, orc):
+    """Groups whose scale differs, when the scale is itself a decision
+    (binary16 scales): the GPU's fp32 scale against the oracle's value."""
+    if gpu_scales is None:
+        return None
+    return np.asarray(gpu_scales, np.float64) != orc["scales"]
+
+
+def first_mismatch_report(gpu_codes_orig, gpu_zeros, orc, group, tau=TAU, gpu_scales=None):
     """Returns (identity_rate, rows_with_mismatch, bad_rows) where bad_rows
-    lists rows whose first differing decision is not an oracle tie."""
+    lists rows whose first differing decision is not an oracle tie. Within a
+    group the scale (when binary16 scales make it a rounding decision) is
+    decided first, then the zero point, then the codes."""
     perm = orc["perm"]
     nq = gpu_codes_orig.shape[1]
     g = np.asarray(gpu_codes_orig)[:, perm[:nq]]
     o = orc["codes_proc"]
     cm = g != o
     zm = np.asarray(gpu_zeros) != orc["zeros"]
+    sm = _scale_mismatch(gpu_scales, orc)
+    if sm is None:
+        sm = np.zeros_like(zm)
     rate = 1.0 - cm.mean()
     bad = []
-    rows = np.nonzero(cm.any(1) | zm.any(1))[0]
+    rows = np.nonzero(cm.any(1) | zm.any(1) | sm.any(1))[0]
     for r in rows:
         jc = int(np.argmax(cm[r])) if cm[r].any() else nq
         gz = int(np.argmax(zm[r])) if zm[r].any() else nq
         jz = gz * group if gz < zm.shape[1] else nq
-        if jz <= jc:
+        gs = int(np.argmax(sm[r])) if sm[r].any() else nq
+        js = gs * group if gs < sm.shape[1] else nq
+        if js <= jz and js <= jc:
+            ok = orc["smargins"][r, gs] < tau
+        elif jz <= jc:
             ok = orc["zmargins"][r, gz] < tau
         else:
             ok = orc["margins"][r, jc] < tau
@@ -76,7 +93,8 @@ def first_mismatch_report(gpu_codes_orig, gpu_zeros, orc, group, tau=TAU):
     return rate, len(rows), bad
 
 
-def tie_branch_report(gpu_codes_orig, gpu_zeros, W, H64, orc, params, nq, tau=TAU, max_ties=16, U=None):
+def tie_branch_report(gpu_codes_orig, gpu_zeros, W, H64, orc, params, nq, tau=TAU, max_ties=16, U=None,
+                      gpu_scales=None):
     """Follow the oracle's own branches at its ties.
 
     Where the first decision (processing order) in which a row differs is
@@ -97,15 +115,19 @@ def tie_branch_report(gpu_codes_orig, gpu_zeros, W, H64, orc, params, nq, tau=TA
     W = np.asarray(W)
     codes_o = orc["codes_proc"].copy()
     zeros_o = orc["zeros"].copy()
+    scales_o = orc["scales"].copy()
     margins = orc["margins"].copy()
     zmargins = orc["zmargins"].copy()
+    smargins = orc["smargins"].copy()
+    gs_ = None if gpu_scales is None else np.asarray(gpu_scales, np.float64)
     alts = {}
     ties = np.zeros(len(g), int)
     bad = set()
     for it in range(max_ties + 1):
         cm = g != codes_o
         zm = gz != zeros_o
-        pending = [int(r) for r in np.nonzero(cm.any(1) | zm.any(1))[0] if int(r) not in bad]
+        sm = np.zeros_like(zm) if gs_ is None or not p.get("scale_fp16", False) else gs_ != scales_o
+        pending = [int(r) for r in np.nonzero(cm.any(1) | zm.any(1) | sm.any(1))[0] if int(r) not in bad]
         if not pending:
             break
         if it == max_ties:
@@ -116,8 +138,15 @@ def tie_branch_report(gpu_codes_orig, gpu_zeros, W, H64, orc, params, nq, tau=TA
             jc = int(np.argmax(cm[r])) if cm[r].any() else nq
             zi = int(np.argmax(zm[r])) if zm[r].any() else zm.shape[1]
             jz = zi * p["group"] if zi < zm.shape[1] else nq
-            ac, az = alts.setdefault(r, ([], []))
-            if jz <= jc and zmargins[r, zi] < tau:
+            si = int(np.argmax(sm[r])) if sm[r].any() else sm.shape[1]
+            js = si * p["group"] if si < sm.shape[1] else nq
+            ac, az, as_ = alts.setdefault(r, ([], [], []))
+            if js <= jz and js <= jc and smargins[r, si] < tau:
+                as_.append(si)
+            elif js <= jz and js <= jc:
+                bad.add(r)
+                continue
+            elif jz <= jc and zmargins[r, zi] < tau:
                 az.append(zi)
             elif jz > jc and margins[r, jc] < tau:
                 ac.append(jc)
@@ -134,12 +163,16 @@ def tie_branch_report(gpu_codes_orig, gpu_zeros, W, H64, orc, params, nq, tau=TA
             del Hd
         alt_c = [(i, k) for i, r in enumerate(rerun) for k in alts[r][0]]
         alt_z = [(i, k) for i, r in enumerate(rerun) for k in alts[r][1]]
+        alt_s = [(i, k) for i, r in enumerate(rerun) for k in alts[r][2]]
         o = O.gptq_o2(W[rerun], None, p["bits"], p["group"], p["damp"], p["block"], p["act_order"], nq,
-                      U=U, perm=perm, alt=(alt_c, alt_z), sym=p.get("sym", False))
+                      U=U, perm=perm, alt=(alt_c, alt_z, alt_s), sym=p.get("sym", False),
+                      scale_fp16=p.get("scale_fp16", False))
         codes_o[rerun] = o["codes_proc"]
         zeros_o[rerun] = o["zeros"]
+        scales_o[rerun] = o["scales"]
         margins[rerun] = o["margins"]
         zmargins[rerun] = o["zmargins"]
+        smargins[rerun] = o["smargins"]
     rate = 1.0 - (g != codes_o).mean()
     return rate, ties, sorted(bad)
 
@@ -151,8 +184,9 @@ def check_quant(res, wl, H64, orc, params, nq, report=None, min_identity=0.999, 
     g_idx. U: the oracle's factor when the caller already has it."""
     codes = res.codes.cpu().numpy()
     zeros = res.zeros.cpu().numpy()
-    rate, nrows, bad = first_mismatch_report(codes, zeros, orc, params["group"])
-    brate, ties, bbad = tie_branch_report(codes, zeros, wl.W, H64, orc, params, nq, U=U)
+    scales = res.scales.cpu().numpy() if params.get("scale_fp16", False) else None
+    rate, nrows, bad = first_mismatch_report(codes, zeros, orc, params["group"], gpu_scales=scales)
+    brate, ties, bbad = tie_branch_report(codes, zeros, wl.W, H64, orc, params, nq, U=U, gpu_scales=scales)
     w_hat = res.w_hat.cpu().numpy().astype(np.float64)
     r_gpu = O.layer_error(wl.W, w_hat, H64)
     r_orc = O.layer_error(wl.W, orc["w_hat"], H64)

@@ -96,6 +96,23 @@ def test_params_versioning_and_sym_on_host():
     assert lib.gptq_workspace_bytes(64, 512, ctypes.byref(p), ctypes.byref(out)) == -1
 
 
+def test_params_versioning_of_scale_fp16():
+    """scale_fp16 came with a `reserved` field that grew the block from 40 to
+    48 bytes: a 40-byte block (built before the field existed, whose bytes
+    36..39 are padding) never has it read, whatever those bytes hold; with
+    a 48-byte block it must be 0 or 1."""
+    G, lib = _lib()
+    import ctypes
+    p = G.make_params(4, 128, 0.01, 128, False, None, 512, scale_fp16=True)
+    assert ctypes.sizeof(p) == 48 and p.struct_size == 48 and p.scale_fp16 == 1
+    out = ctypes.c_size_t(0)
+    assert lib.gptq_workspace_bytes(64, 512, ctypes.byref(p), ctypes.byref(out)) == 0
+    p.scale_fp16 = 7
+    assert lib.gptq_workspace_bytes(64, 512, ctypes.byref(p), ctypes.byref(out)) == -1
+    p.struct_size = 40                       # an older caller: bytes 36..39 are padding, not read
+    assert lib.gptq_workspace_bytes(64, 512, ctypes.byref(p), ctypes.byref(out)) == 0
+
+
 def test_dequant_matmul_validation_on_host():
     """Argument checks of the inference product run on the host, before
     anything is enqueued (NULL device pointers are never dereferenced)."""

@@ -71,7 +71,7 @@ def check_rows(wl, H64, res, rows, t0, U, perm, min_identity=0.999):
         sub, wsub = res, wl
     else:
         rt = torch.from_numpy(rows).cuda()
-        sub = types.SimpleNamespace(codes=res.codes[rt], zeros=res.zeros[rt], w_hat=res.w_hat[rt],
+        sub = types.SimpleNamespace(codes=res.codes[rt], zeros=res.zeros[rt], scales=res.scales[rt], w_hat=res.w_hat[rt],
                                     g_idx=res.g_idx)
         wsub = types.SimpleNamespace(W=wl.W[rows])
     rep = {}

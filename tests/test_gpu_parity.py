@@ -107,6 +107,14 @@ CASES = [
     ("c3", dict(d_out=256, n=1024, T=8192), dict(sym=True)),
     ("c3", dict(d_out=40, n=384, T=4096), dict(bits=2, group=64, block=128, sym=True)),
     ("c2", dict(d_out=64, n=1024, T=4096), dict(group=256, sym=True)),
+    # binary16 scales: 4-bit, 3-bit act-order, 2-bit g64, the symmetric
+    # alphabet, groups spanning two blocks, a kept fp32 tail
+    ("c2", dict(d_out=512, n=640, T=8192), dict(scale_fp16=True)),
+    ("c3", dict(d_out=256, n=1024, T=8192), dict(scale_fp16=True)),
+    ("c3", dict(d_out=128, n=384, T=4096), dict(bits=2, group=64, block=128, scale_fp16=True)),
+    ("c2", dict(d_out=128, n=640, T=8192), dict(sym=True, scale_fp16=True)),
+    ("c2", dict(d_out=64, n=1024, T=4096), dict(group=256, scale_fp16=True)),
+    ("c2", dict(d_out=72, n=300, T=4096), dict(n_quant=256, group=64, scale_fp16=True)),
 ]
 
 
@@ -117,15 +125,19 @@ def test_quantize_parity(name, kw, over):
     p.update(over)
     nq = p.pop("n_quant", wl.n_quant)
     sym = p.setdefault("sym", False)
+    s16 = p.setdefault("scale_fp16", False)
     say("quantize", name, kw, p, "n_quant", nq)
     H64 = O.hessian(wl.X)
     H32 = torch.from_numpy(H64.astype(np.float32)).cuda()
     res = G.quantize_layer(w_dev(wl), H32, bits=p["bits"], group=p["group"], damp=p["damp"],
                            block=p["block"], act_order=p["act_order"], n_quant=nq,
-                           want_codes=True, sym=sym)
+                           want_codes=True, sym=sym, scale_fp16=s16)
     torch.cuda.synchronize()
     orc = O.gptq_o2(wl.W, H64.astype(np.float32), p["bits"], p["group"], p["damp"], p["block"],
-                    p["act_order"], nq, sym=sym)
+                    p["act_order"], nq, sym=sym, scale_fp16=s16)
+    if s16:
+        sc = res.scales.cpu().numpy()
+        assert np.array_equal(sc, sc.astype(np.float16).astype(np.float32))   # binary16 values
     if sym:
         A = 2 ** (p["bits"] - 1) - 1
         assert res.codes.max().item() <= 2 * A and bool((res.zeros == A).all())

@@ -61,3 +61,33 @@ def test_zero_point_flip_away_from_a_tie_is_rejected():
     fz[r, g] += 1
     _, _, bad = parity.first_mismatch_report(orc["codes"], fz, orc, p["group"])
     assert bad == [int(r)]
+
+
+def test_binary16_scale_branch_is_accepted_and_a_flip_away_is_not():
+    """With binary16 scales the scale is a rounding decision too: a result
+    that took the other binary16 neighbour at the oracle's closest scale tie
+    is accepted (first mismatch rule and tie branches); one whose scale moved
+    where the oracle's decision is far from a tie is rejected."""
+    r = np.random.default_rng(8)
+    X = r.standard_t(4, (600, 128))
+    W = r.standard_normal((48, 128)) * 0.02
+    H = O.hessian(X)
+    p = dict(bits=3, group=32, damp=0.01, block=32, act_order=False, scale_fp16=True)
+    orc = O.gptq_o2(W, H, 3, 32, 0.01, 32, scale_fp16=True)
+    sm = orc["smargins"]
+    rr, gg = np.unravel_index(np.argmin(sm), sm.shape)
+    tau = 2.0 * sm[rr, gg] + 1e-12
+    br = O.gptq_o2(W, H, 3, 32, 0.01, 32, scale_fp16=True, alt=((), (), [(rr, gg)]))
+    assert br["scales"][rr, gg] != orc["scales"][rr, gg]
+    _, nrows, bad = parity.first_mismatch_report(br["codes"], br["zeros"], orc, 32, tau=tau,
+                                                 gpu_scales=br["scales"])
+    assert nrows == 1 and bad == []
+    brate, ties, bbad = parity.tie_branch_report(br["codes"], br["zeros"], W, H, orc, p, 128, tau=tau,
+                                                 gpu_scales=br["scales"])
+    assert brate == 1.0 and bbad == [] and ties.sum() >= 1
+    rf, gf = np.unravel_index(np.argmax(sm), sm.shape)
+    assert sm[rf, gf] > 0.3
+    fake = orc["scales"].copy()
+    fake[rf, gf] *= 1.0 + 2.0 ** -10
+    _, _, bad = parity.first_mismatch_report(orc["codes"], orc["zeros"], orc, 32, gpu_scales=fake)
+    assert bad == [int(rf)]
