@@ -168,6 +168,9 @@ struct SweepArgs {
   const DevStatus* st;
 };
 hipError_t launch_sweep(hipStream_t s, const SweepArgs& a);
+// the fused path's whole super-block [i0, i0 + ncols) in one launch (B = 128,
+// ncols a multiple of 128 up to 512, groups inside a block, E == Esb)
+hipError_t launch_sweep_super(hipStream_t s, const SweepArgs& a);
 
 // ---- pack.hip
 hipError_t launch_pack(hipStream_t s, const uint8_t* codes, int64_t ldc, const int32_t* invperm,

@@ -612,9 +612,29 @@ gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int
   // taken left-looking by the sweep kernel itself (each block first applies
   // the errors of the super-block's earlier blocks to its own columns).
   const bool fused = two && B == 128 && p->group <= B && nq % B == 0 && sw == 512;
+  // the fused path takes a whole super-block per launch when U's rows are
+  // 16-byte aligned (the tile loads are unpredicated float4)
+  const bool sbl = fused && n % 4 == 0 && ((uintptr_t)U & 15) == 0;
   for (int64_t s0 = 0; s0 < nq; s0 += sw) {
     const int64_t s1 = std::min<int64_t>(s0 + sw, nq);
-    for (int64_t i0 = s0; i0 < s1; i0 += B) {
+    if (sbl) {
+      SweepArgs a{};
+      a.Wf = Wf; a.ldw = n; a.U = U; a.ldu = n; a.d_out = d_out; a.i0 = s0; a.ncols = s1 - s0;
+      a.block = B; a.group = p->group; a.bits = p->bits; a.sym = params_sym(p); a.scale16 = params_scale16(p);
+      a.gbase = s0 / p->group;
+      a.gshift = 31;
+      if (p->group < B)
+        for (int sh = 0; sh < 31; ++sh)
+          if ((1 << sh) == p->group) a.gshift = sh;
+      a.scales = out->scales; a.zeros = out->zeros; a.ngroups = nq / p->group;
+      a.codes = codes; a.n_quant = nq; a.E = E; a.lde = sw; a.row_loss = loss; a.st = dst;
+      a.Esb = E; a.kb = 0;
+      a.Ehi = s1 < n ? Ehi : nullptr;
+      a.Elo = s1 < n ? Elo : nullptr;
+      Timed ph(GPTQ_PROF_SWEEP, s, 2);
+      HIP_TRY(launch_sweep_super(s, a), "sweep");
+    }
+    for (int64_t i0 = s0; i0 < s1 && !sbl; i0 += B) {
       const int64_t nc = std::min<int64_t>(B, s1 - i0);
       float* Eb = E + (i0 - s0);
       SweepArgs a{};

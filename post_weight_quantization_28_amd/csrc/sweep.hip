@@ -483,6 +483,132 @@ k_sweep(SweepArgs a) {
   }
 }
 
+// A whole super-block of the fused path in one launch (B = 128, whole
+// blocks, groups inside a block): each workgroup keeps its 16 rows for the
+// super-block's blocks b = 0 .. ncols / 128 - 1, with the same arithmetic,
+// in the same order, as one k_sweep<8> launch per block. Block b + 1's U
+// tile, diagonal and weights are requested before block b's chain starts,
+// so their latency hides behind it (they are not written in this launch:
+// the weights of later blocks change only through the near field below).
+// Block b + 1's near field reads the errors this workgroup stored for
+// blocks 0..b; the workgroup barrier after each block orders those stores
+// before the reads (all waves of a workgroup share one CU and its L1).
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+k_sweep_sb(SweepArgs a) {
+  constexpr int CPL = 8, B = 128;
+  constexpr int NV = B * B / 4 / 256;   // float4 of the U tile per thread
+  __shared__ float smem[B + B * B + 16 * kUpdP];
+  float* sInv = smem;
+  float* sU = smem + B;
+  float* upd = smem + B + B * B;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int L = lane & 15;
+  const int64_t row = (int64_t)blockIdx.x * 16 + wave * 4 + (lane >> 4);
+  const bool row_ok = row < a.d_out;
+  const float maxq = (float)((1 << a.bits) - 1);
+  const int64_t s0 = a.i0;
+  const int nblk = (int)(a.ncols / B);
+
+  float ut[NV][4];
+  float dg;
+  float wn[CPL];
+  // U tile, 1 / U_jj source and this row's weights of the block at i0 (the
+  // launcher guarantees 16-byte aligned tile rows)
+  auto fetch = [&](int64_t i0) {
+    const float* Ublk = a.U + i0 * a.ldu + i0;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int e4 = tid + 256 * v;
+      const int r = e4 / (B / 4), c0 = 4 * (e4 % (B / 4));
+      const float4 t = *reinterpret_cast<const float4*>(Ublk + (int64_t)r * a.ldu + c0);
+      ut[v][0] = t.x; ut[v][1] = t.y; ut[v][2] = t.z; ut[v][3] = t.w;
+    }
+    dg = tid < B ? Ublk[(int64_t)tid * a.ldu + tid] : 1.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) wn[c] = row_ok ? a.Wf[row * a.ldw + i0 + 16 * c + L] : 0.f;
+  };
+  fetch(s0);
+  float lossacc = (row_ok && L == 0) ? a.row_loss[row] : 0.f;
+  if (a.st->flags != 0) return;
+
+  SweepState<CPL> S;
+  S.nc = B;
+  S.gmask = (a.group < B) ? a.group - 1 : -1;
+  for (int b = 0; b < nblk; ++b) {
+    SweepArgs ab = a;
+    const int64_t i0 = s0 + (int64_t)b * B;
+    ab.i0 = i0;
+    ab.kb = (int64_t)b * B;
+    ab.gbase = a.gbase + (int64_t)b * (B / a.group);
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      S.w[c] = wn[c];
+      S.ev[c] = 0.f;
+      S.qv[c] = 0.f;
+    }
+    if (b == 1) near_update<4>(ab, sU, upd);
+    else if (b == 2) near_update<8>(ab, sU, upd);
+    else if (b == 3) near_update<12>(ab, sU, upd);   // each ends with a barrier: sU is free again
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int e4 = tid + 256 * v;
+      const int r = e4 / (B / 4), c0 = 4 * (e4 % (B / 4));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col = c0 + q;
+        sU[upos<CPL>(r, col / 16, col % 16)] = (col > r) ? ut[v][q] : 0.f;
+      }
+    }
+    if (tid < B) sInv[tid] = 1.f / dg;
+    __syncthreads();
+    if (b > 0) {
+      const float* ur = upd + (wave * 4 + (lane >> 4)) * kUpdP + L;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) S.w[c] -= ur[16 * c];
+    }
+    start_group<CPL, 0>(S, ab, L, row, row_ok, maxq);
+    if (b + 1 < nblk) fetch(i0 + B);
+
+    load_urow<CPL, 0, 0>(S, sU, sInv, L, 0);
+    load_urow<CPL, 1, 0>(S, sU, sInv, L, 1);
+    sweep_all<CPL>(S, ab, sU, sInv, L, row, row_ok, maxq, std::make_integer_sequence<int, B>{});
+
+    float loss = 0.f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) loss = fmaf(S.ev[c], S.ev[c], loss);
+    lossacc += row_sum16(loss);
+    if (row_ok) {
+      float* Eb = a.E + ab.kb;
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) {
+        const int col = 16 * c + L;
+        a.Wf[row * a.ldw + i0 + col] = S.gs[c] * (S.qv[c] - S.gz[c]);
+        a.codes[row * a.n_quant + i0 + col] = (uint8_t)S.qv[c];
+        Eb[row * a.lde + col] = S.ev[c];
+        if (a.Ehi) {
+          const uint16_t h = f32_to_bf16_rne(S.ev[c]);
+          a.Ehi[row * a.lde + ab.kb + col] = h;
+          a.Elo[row * a.lde + ab.kb + col] = f32_to_bf16_rne(S.ev[c] - bf16_to_f32(h));
+        }
+      }
+    }
+    // every wave is done with sU, and this block's errors are stored,
+    // before the next near field stages its operands over sU and reads them
+    if (b + 1 < nblk) __syncthreads();
+  }
+  if (row_ok && L == 0) a.row_loss[row] = lossacc;
+}
+
+hipError_t launch_sweep_super(hipStream_t s, const SweepArgs& a) {
+  if (a.d_out == 0 || a.ncols == 0) return hipSuccess;
+  if (a.block != 128 || a.ncols % 128 != 0 || a.ncols > 512 || a.group > 128 || 128 % a.group != 0 ||
+      a.i0 % 128 != 0 || a.ldu % 4 != 0 || ((uintptr_t)a.U & 15) != 0 || a.Esb != a.E)
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_sweep_sb, dim3((unsigned)ceil_div(a.d_out, 16)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_sweep(hipStream_t s, const SweepArgs& a) {
   if (a.d_out == 0 || a.ncols == 0) return hipSuccess;
   dim3 grid((unsigned)ceil_div(a.d_out, 16));
