@@ -88,6 +88,8 @@ struct GemmArgs {
 };
 hipError_t launch_gemm_f32(hipStream_t s, const GemmArgs& g);
 hipError_t launch_gemm_pair(hipStream_t s, const GemmArgs& a, const GemmArgs* b);
+// lower tiles of C = beta C + alpha A A^T (M == N, B == A, ta = 0, tb = 1)
+hipError_t launch_syrk_f32(hipStream_t s, const GemmArgs& g);
 // U = X with both indices reversed; if hi is non-null, also U's split-bf16
 // parts hi = bf16(U), lo = bf16(U - hi).
 hipError_t launch_rotate(hipStream_t s, const float* X, float* U, int64_t n, uint16_t* hi = nullptr,

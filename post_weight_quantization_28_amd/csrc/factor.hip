@@ -195,7 +195,10 @@ struct Operand {
   }
 };
 
-template <int BM, int BN, bool TA, bool TB>
+// LATE_C: the product is summed from zero and beta C added once at the end
+// (one rounding at C's magnitude per call instead of one per k), for
+// updates of a matrix whose entries are much larger than each product.
+template <int BM, int BN, bool TA, bool TB, bool LATE_C = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int tm, int tn, GemmSmem<BM, BN>& sm) {
   constexpr int WM = BM / 2, WN = BN / 2;          // per-wave block
   constexpr int FM = WM / 32, FN = WN / 32;        // MFMA tiles per wave
@@ -221,7 +224,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int tm, int tn, Gem
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float v = 0.f;
-        if (g.beta != 0.f) {
+        if (!LATE_C && g.beta != 0.f) {
           const int64_t i = m0 + WM * wm + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
           const int64_t j = n0 + WN * wn + 32 * b + lr;
           if (i < g.M && j < g.N) v = g.beta * g.C[i * g.ldc + j];
@@ -295,7 +298,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int tm, int tn, Gem
       for (int r = 0; r < 16; ++r) {
         const int64_t i = m0 + WM * wm + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         const int64_t j = n0 + WN * wn + 32 * b + lr;
-        if (i < g.M && j < g.N) g.C[i * g.ldc + j] = acc[a][b][r];
+        if (i < g.M && j < g.N) {
+          float v = acc[a][b][r];
+          if (LATE_C && g.beta != 0.f) v += g.beta * g.C[i * g.ldc + j];
+          g.C[i * g.ldc + j] = v;
+        }
       }
 }
 
@@ -375,6 +382,39 @@ hipError_t launch_gemm_pair(hipStream_t s, const GemmArgs& a, const GemmArgs* b)
 }
 
 hipError_t launch_gemm_f32(hipStream_t s, const GemmArgs& g) { return launch_gemm_pair(s, g, nullptr); }
+
+// C = beta C + alpha A A^T on the 128 x 128 tiles on or below the diagonal
+// only (A is N x K, k-contiguous rows; B = A): the symmetric rank-K update
+// of a wide factorisation's trailing matrix, summed from zero and added to
+// C once (as the K = 64 updates it replaces do per panel). The upper half of a diagonal
+// tile is written too (that part of the matrix is never read as L). Tiles
+// are numbered row by row over the lower triangle, so no workgroup is
+// spent on a tile above it, and dealt to the XCDs in contiguous runs
+// (workgroup b runs on XCD b % 8): the tiles resident on one XCD share
+// A's row block in its L2.
+__global__ void __launch_bounds__(256) k_syrk_f32(GemmArgs g, int ntile) {
+  __shared__ __align__(16) GemmSmem<128, 128> sm;
+  const int per = (ntile + 7) >> 3;
+  const int t = ((int)blockIdx.x & 7) * per + ((int)blockIdx.x >> 3);
+  if (t >= ntile) return;
+  // t = tm (tm + 1) / 2 + tn, 0 <= tn <= tm
+  int tm = (int)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
+  while ((tm + 1) * (tm + 2) / 2 <= t) ++tm;
+  while (tm * (tm + 1) / 2 > t) --tm;
+  const int tn = t - tm * (tm + 1) / 2;
+  gemm_tile<128, 128, false, true, true>(g, tm, tn, sm);
+}
+
+hipError_t launch_syrk_f32(hipStream_t s, const GemmArgs& g) {
+  if (g.M != g.N || g.A != g.B || g.lda != g.ldb || g.ta != 0 || g.tb != 1 || g.kmode != 0)
+    return hipErrorInvalidValue;
+  const int64_t nt = ceil_div(g.N, 128);
+  const int64_t ntile = nt * (nt + 1) / 2;
+  if (ntile == 0) return hipSuccess;
+  if (ntile > (1 << 28)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_syrk_f32, dim3((unsigned)(8 * ((ntile + 7) / 8))), dim3(256), 0, s, g, (int)ntile);
+  return hipGetLastError();
+}
 
 // ---------------------------------------------------------------- rotate
 // U[i][j] = X[n-1-i][n-1-j]: the flat array reversed; optionally with U's

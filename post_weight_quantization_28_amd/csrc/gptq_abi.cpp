@@ -190,34 +190,62 @@ gptq_status check_ws(void* ws, size_t have, size_t need) {
 }
 
 // ---------------------------------------------------------------- factorisation
+// Wide matrices are factorised in two levels. The 64-column panels of a
+// super-panel of kSuper columns update only the super-panel's own columns;
+// when its last panel is solved, one symmetric rank-kSuper product applies
+// all of them to the trailing matrix at once. The trailing matrix is then
+// read and written n / kSuper times instead of n / 64 times, and that
+// traffic is what bounds the K = 64 updates of a wide matrix. Narrower
+// matrices keep one level: their late panels are bound by the leaf chain,
+// and the per-super-panel product and leaf launch would only add to it.
+constexpr int64_t kSuper = 512;
+constexpr int64_t kTwoLevelMinN = 6144;
+
 // Right-looking Cholesky of the flipped matrix A with the inverse X = L^{-1}
-// carried along (see factor.hip): three launches per 64-column panel.
+// carried along (see factor.hip): two launches per 64-column panel.
 hipError_t factor_panels(hipStream_t s, float* A, float* X, int64_t n, const int32_t* perm,
                          DevStatus* st) {
   hipError_t e;
+  const int64_t S = n >= kTwoLevelMinN ? kSuper : n;
   // ---- phase 1: Cholesky, leaves write D = L11^{-1} into X's diagonal
   if ((e = launch_leaf(s, A, X, n, 0, std::min<int64_t>(kLeaf, n), perm, st)) != hipSuccess) return e;
-  for (int64_t k0 = 0; k0 < n; k0 += kLeaf) {
-    const int64_t m = std::min<int64_t>(kLeaf, n - k0);
-    const int64_t k1 = k0 + m, r = n - k1;
-    if (r == 0) break;
-    const float* D = X + k0 * n + k0;    // L11^{-1}, lower
-    float* L21 = A + k1 * n + k0;
-    // L21 = A21 D^T in place (m == 64 whenever rows remain below the panel)
-    if ((e = launch_panel_solve(s, L21, D, n, r)) != hipSuccess) return e;
-    // One launch: the next diagonal block (m2 rows) is updated and factored
-    // by its own workgroup while the rest runs
-    //   A[k1+m2:, k1:] -= L21[m2:] L21^T   (lower, i.e. j <= i + m2)
-    const int64_t m2 = std::min<int64_t>(kLeaf, r);
-    SlabArgs g3{};
-    g3.M = r - m2; g3.N = r; g3.K = m;
-    g3.A = L21 + m2 * n; g3.lda = n;
-    g3.B = L21; g3.ldb = n; g3.tb = 1;
-    g3.C = A + (k1 + m2) * n + k1; g3.ldc = n;
-    g3.alpha = -1.f; g3.beta = 1.f;
-    g3.lower_only = 1; g3.lower_off = m2;
-    LeafTask lt{L21, A, X, n, k1, (int)m2, (int)m, perm, st};
-    if ((e = launch_slab_leaf(s, g3, lt)) != hipSuccess) return e;
+  for (int64_t s0 = 0; s0 < n; s0 += S) {
+    const int64_t s1 = std::min<int64_t>(s0 + S, n);
+    for (int64_t k0 = s0; k0 < s1; k0 += kLeaf) {
+      const int64_t m = std::min<int64_t>(kLeaf, n - k0);
+      const int64_t k1 = k0 + m, r = n - k1;
+      if (r == 0) break;
+      const float* D = X + k0 * n + k0;    // L11^{-1}, lower
+      float* L21 = A + k1 * n + k0;
+      // L21 = A21 D^T in place (m == 64 whenever rows remain below the panel)
+      if ((e = launch_panel_solve(s, L21, D, n, r)) != hipSuccess) return e;
+      if (k1 == s1) break;                 // the super-panel's last panel: the product below updates
+      // One launch: the next diagonal block (m2 rows) is updated and factored
+      // by its own workgroup while the rest runs
+      //   A[k1+m2:, k1:s1] -= L21[m2:] L21[:s1-k1]^T   (lower, i.e. j <= i + m2)
+      const int64_t m2 = std::min<int64_t>(kLeaf, r);
+      SlabArgs g3{};
+      g3.M = r - m2; g3.N = s1 - k1; g3.K = m;
+      g3.A = L21 + m2 * n; g3.lda = n;
+      g3.B = L21; g3.ldb = n; g3.tb = 1;
+      g3.C = A + (k1 + m2) * n + k1; g3.ldc = n;
+      g3.alpha = -1.f; g3.beta = 1.f;
+      g3.lower_only = 1; g3.lower_off = m2;
+      LeafTask lt{L21, A, X, n, k1, (int)m2, (int)m, perm, st};
+      if ((e = launch_slab_leaf(s, g3, lt)) != hipSuccess) return e;
+    }
+    if (s1 < n) {
+      // A[s1:, s1:] -= L[s1:, s0:s1] L[s1:, s0:s1]^T on the lower tiles,
+      // then the next super-panel's first leaf
+      GemmArgs g{};
+      g.M = n - s1; g.N = n - s1; g.K = s1 - s0;
+      g.A = A + s1 * n + s0; g.lda = n; g.ta = 0;
+      g.B = A + s1 * n + s0; g.ldb = n; g.tb = 1;
+      g.C = A + s1 * n + s1; g.ldc = n;
+      g.alpha = -1.f; g.beta = 1.f; g.batch = 1;
+      if ((e = launch_syrk_f32(s, g)) != hipSuccess) return e;
+      if ((e = launch_leaf(s, A, X, n, s1, std::min<int64_t>(kLeaf, n - s1), perm, st)) != hipSuccess) return e;
+    }
   }
   // ---- phase 2: off-diagonal blocks of X = L^{-1}
   for (int64_t h = kLeaf; h < n; h *= 2) {
