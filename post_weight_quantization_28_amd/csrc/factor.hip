@@ -195,9 +195,12 @@ struct Operand {
   }
 };
 
-// LATE_C: the product is summed from zero and beta C added once at the end
-// (one rounding at C's magnitude per call instead of one per k), for
-// updates of a matrix whose entries are much larger than each product.
+// LATE_C: the product is summed in 32-deep slices, each slice from zero in
+// the MFMA accumulator and then added to a running fp32 total, and beta C
+// is added once at the end. Each rounding then happens at the magnitude of
+// a 32-term slice or of the total so far, never once per k at C's
+// magnitude, for long updates of a matrix whose entries are much larger
+// than its result (the trailing matrix of a Cholesky factorisation).
 template <int BM, int BN, bool TA, bool TB, bool LATE_C = false>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int tm, int tn, GemmSmem<BM, BN>& sm) {
   constexpr int WM = BM / 2, WN = BN / 2;          // per-wave block
@@ -231,6 +234,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int tm, int tn, Gem
         }
         acc[a][b][r] = v;
       }
+
+  f32x16_t tot[LATE_C ? FM : 1][LATE_C ? FN : 1];
+  if constexpr (LATE_C) {
+#pragma unroll
+    for (int a = 0; a < FM; ++a)
+#pragma unroll
+      for (int b = 0; b < FN; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) tot[a][b][r] = 0.f;
+  }
 
   float4 ra[OA::L], rb[OB::L];
   // interior chunks (the common case) take unpredicated 16-byte loads, so
@@ -286,6 +299,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int tm, int tn, Gem
           acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x2f32(fa[a].w, fb[b].w, acc[a][b], 0, 0, 0);
         }
     }
+    if constexpr (LATE_C) {
+#pragma unroll
+      for (int a = 0; a < FM; ++a)
+#pragma unroll
+        for (int b = 0; b < FN; ++b) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) tot[a][b][r] += acc[a][b][r];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+        }
+    }
     if (more) sstore(cur ^ 1);
     __syncthreads();
   }
@@ -299,7 +323,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int tm, int tn, Gem
         const int64_t i = m0 + WM * wm + 32 * a + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         const int64_t j = n0 + WN * wn + 32 * b + lr;
         if (i < g.M && j < g.N) {
-          float v = acc[a][b][r];
+          float v = LATE_C ? tot[a][b][r] : acc[a][b][r];
           if (LATE_C && g.beta != 0.f) v += g.beta * g.C[i * g.ldc + j];
           g.C[i * g.ldc + j] = v;
         }
@@ -385,8 +409,8 @@ hipError_t launch_gemm_f32(hipStream_t s, const GemmArgs& g) { return launch_gem
 
 // C = beta C + alpha A A^T on the 128 x 128 tiles on or below the diagonal
 // only (A is N x K, k-contiguous rows; B = A): the symmetric rank-K update
-// of a wide factorisation's trailing matrix, summed from zero and added to
-// C once (as the K = 64 updates it replaces do per panel). The upper half of a diagonal
+// of a wide factorisation's trailing matrix, summed in 32-deep slices and
+// added to C once (LATE_C). The upper half of a diagonal
 // tile is written too (that part of the matrix is never read as L). Tiles
 // are numbered row by row over the lower triangle, so no workgroup is
 // spent on a tile above it, and dealt to the XCDs in contiguous runs

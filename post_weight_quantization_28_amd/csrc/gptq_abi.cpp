@@ -198,7 +198,7 @@ gptq_status check_ws(void* ws, size_t have, size_t need) {
 // traffic is what bounds the K = 64 updates of a wide matrix. Narrower
 // matrices keep one level: their late panels are bound by the leaf chain,
 // and the per-super-panel product and leaf launch would only add to it.
-constexpr int64_t kSuper = 512;
+constexpr int64_t kSuper = 2048;
 constexpr int64_t kTwoLevelMinN = 6144;
 
 // Right-looking Cholesky of the flipped matrix A with the inverse X = L^{-1}
