@@ -330,8 +330,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, int tm, int tn, Gem
       }
 }
 
-template <int BM, int BN>
-__global__ void __launch_bounds__(256)
+// One operand layout (TA, TB) per instantiation: the four layouts in one
+// kernel would take the register count of the largest (288 at 128 x 128,
+// one workgroup per CU), each alone stays within 256 (two per CU).
+template <int BM, int BN, bool TA, bool TB>
+__global__ void __launch_bounds__(256, BM == 128 ? 2 : 1)
 k_gemm_f32(GemmPair gp) {
   __shared__ __align__(16) GemmSmem<BM, BN> sm;
   const int which = (int)blockIdx.x >= gp.nt0;
@@ -357,13 +360,7 @@ k_gemm_f32(GemmPair gp) {
   // triangular K ranges: dispatch the longest row tiles first
   if (g.kmode == 3) tm = per / gp.ntn[which] - 1 - tm;
   if (g.lower_only && tn * BN > tm * BM + BM - 1) return;
-  if (g.ta) {
-    if (g.tb) gemm_tile<BM, BN, true, true>(g, tm, tn, sm);
-    else gemm_tile<BM, BN, true, false>(g, tm, tn, sm);
-  } else {
-    if (g.tb) gemm_tile<BM, BN, false, true>(g, tm, tn, sm);
-    else gemm_tile<BM, BN, false, false>(g, tm, tn, sm);
-  }
+  gemm_tile<BM, BN, TA, TB>(g, tm, tn, sm);
 }
 
 template <int BM, int BN>
@@ -386,12 +383,20 @@ static hipError_t launch_pair(hipStream_t s, const GemmArgs& a, const GemmArgs* 
   }
   const int total = gp.nt0 + nt1;
   if (total == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_gemm_f32<BM, BN>), dim3(total), dim3(256), 0, s, gp);
+  const int ta = a.ta != 0, tb = a.tb != 0;
+  if (b && b->M > 0 && b->N > 0 && ((b->ta != 0) != ta || (b->tb != 0) != tb)) return hipErrorInvalidValue;
+  if (ta) {
+    if (tb) hipLaunchKernelGGL((k_gemm_f32<BM, BN, true, true>), dim3(total), dim3(256), 0, s, gp);
+    else hipLaunchKernelGGL((k_gemm_f32<BM, BN, true, false>), dim3(total), dim3(256), 0, s, gp);
+  } else {
+    if (tb) hipLaunchKernelGGL((k_gemm_f32<BM, BN, false, true>), dim3(total), dim3(256), 0, s, gp);
+    else hipLaunchKernelGGL((k_gemm_f32<BM, BN, false, false>), dim3(total), dim3(256), 0, s, gp);
+  }
   return hipGetLastError();
 }
 
-// One launch for one or two independent products; the tile shape follows
-// the larger one.
+// One launch for one or two independent products with the same operand
+// layout (ta, tb); the tile shape follows the larger one.
 hipError_t launch_gemm_pair(hipStream_t s, const GemmArgs& a, const GemmArgs* b) {
   // 128 x 128 tiles only when there are enough of them for four rounds of
   // the 256 CUs; otherwise 64 x 64 (four workgroups per CU), which also
