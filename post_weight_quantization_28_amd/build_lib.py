@@ -12,7 +12,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libgptq.so")
 BUILD = os.path.join(ROOT, "_build")
 SOURCES = ["hessian.hip", "prep.hip", "factor.hip", "sweep.hip", "slab.hip", "trail.hip", "pack.hip",
-           "dqmm.hip", "eora.hip", "bidup.hip", "gptq_abi.cpp"]
+           "dqmm.hip", "eora.hip", "syrk.hip", "bidup.hip", "gptq_abi.cpp"]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
          # packed fp32 VALU ops are kept out of the generated code

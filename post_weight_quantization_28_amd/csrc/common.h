@@ -90,6 +90,14 @@ hipError_t launch_gemm_f32(hipStream_t s, const GemmArgs& g);
 hipError_t launch_gemm_pair(hipStream_t s, const GemmArgs& a, const GemmArgs* b);
 // lower tiles of C = beta C + alpha A A^T (M == N, B == A, ta = 0, tb = 1)
 hipError_t launch_syrk_f32(hipStream_t s, const GemmArgs& g);
+
+// ---- syrk.hip
+// Lower tiles of C (N x N, ldc) -= A A^T for fp32 A (N x K, lda) on the bf16
+// matrix cores at fp32 accuracy (three bf16 pieces per value, six piece
+// products). `pieces` is scratch of 3 N K bf16 (16-byte aligned).
+bool syrk_x6_ok(int64_t N, int64_t K, int64_t lda, const float* A, int64_t ldc, const float* C);
+hipError_t launch_syrk_x6(hipStream_t s, const float* A, int64_t lda, float* C, int64_t ldc, int64_t N,
+                          int64_t K, uint16_t* pieces);
 // U = X with both indices reversed; if hi is non-null, also U's split-bf16
 // parts hi = bf16(U), lo = bf16(U - hi).
 hipError_t launch_rotate(hipStream_t s, const float* X, float* U, int64_t n, uint16_t* hi = nullptr,

@@ -107,8 +107,13 @@ int64_t super_width(const gptq_params* p) {
 // columns.
 bool use_two_level(int64_t n, const gptq_params* p) { return n % 8 == 0 && super_width(p) % 8 == 0; }
 
+// Super-panel width and the narrowest matrix factorised in two levels (see
+// factor_panels).
+constexpr int64_t kSuper = 2048;
+constexpr int64_t kTwoLevelMinN = 6144;
+
 struct QLayout {
-  size_t status, lam, diag, perm, invperm, A, X, Wf, E, Ehi, Elo, Uhi, Ulo, codes, loss, total;
+  size_t status, lam, diag, perm, invperm, A, X, Wf, E, Ehi, Elo, Uhi, Ulo, codes, loss, Sp, total;
 };
 
 QLayout q_layout(int64_t d_out, int64_t n, const gptq_params* p) {
@@ -131,6 +136,8 @@ QLayout q_layout(int64_t d_out, int64_t n, const gptq_params* p) {
   L.Ulo = c.take(two ? sizeof(uint16_t) * n * n : 0);
   L.codes = c.take((size_t)d_out * p->n_quant);
   L.loss = c.take(sizeof(float) * d_out);
+  // the bf16 pieces of a super-panel for the two-level factorisation's product
+  L.Sp = c.take(n >= kTwoLevelMinN ? 3 * sizeof(uint16_t) * n * kSuper : 0);
   L.total = c.off;
   return L;
 }
@@ -198,13 +205,11 @@ gptq_status check_ws(void* ws, size_t have, size_t need) {
 // traffic is what bounds the K = 64 updates of a wide matrix. Narrower
 // matrices keep one level: their late panels are bound by the leaf chain,
 // and the per-super-panel product and leaf launch would only add to it.
-constexpr int64_t kSuper = 2048;
-constexpr int64_t kTwoLevelMinN = 6144;
 
 // Right-looking Cholesky of the flipped matrix A with the inverse X = L^{-1}
 // carried along (see factor.hip): two launches per 64-column panel.
 hipError_t factor_panels(hipStream_t s, float* A, float* X, int64_t n, const int32_t* perm,
-                         DevStatus* st) {
+                         DevStatus* st, uint16_t* pieces) {
   hipError_t e;
   const int64_t S = n >= kTwoLevelMinN ? kSuper : n;
   // ---- phase 1: Cholesky, leaves write D = L11^{-1} into X's diagonal
@@ -243,7 +248,11 @@ hipError_t factor_panels(hipStream_t s, float* A, float* X, int64_t n, const int
       g.B = A + s1 * n + s0; g.ldb = n; g.tb = 1;
       g.C = A + s1 * n + s1; g.ldc = n;
       g.alpha = -1.f; g.beta = 1.f; g.batch = 1;
-      if ((e = launch_syrk_f32(s, g)) != hipSuccess) return e;
+      if (pieces && syrk_x6_ok(g.N, g.K, g.lda, g.A, g.ldc, g.C))
+        e = launch_syrk_x6(s, g.A, g.lda, g.C, g.ldc, g.N, g.K, pieces);
+      else
+        e = launch_syrk_f32(s, g);
+      if (e != hipSuccess) return e;
       if ((e = launch_leaf(s, A, X, n, s1, std::min<int64_t>(kLeaf, n - s1), perm, st)) != hipSuccess) return e;
     }
   }
@@ -304,7 +313,8 @@ gptq_status enqueue_factor(hipStream_t s, const float* H, int64_t n, const gptq_
     // the processing order is the identity without act-order
     HIP_TRY(launch_build_flipped(s, H, n, p->act_order ? perm : nullptr, diag, lam, A, st), "build");
   }
-  HIP_TRY(factor_panels(s, A, X, n, perm, st), "factor");
+  uint16_t* pieces = L.Sp != L.total && n >= kTwoLevelMinN ? reinterpret_cast<uint16_t*>(ws + L.Sp) : nullptr;
+  HIP_TRY(factor_panels(s, A, X, n, perm, st, pieces), "factor");
   HIP_TRY(launch_rotate(s, X, A, n, Uhi, Ulo), "rotate");
   return GPTQ_OK;
 }

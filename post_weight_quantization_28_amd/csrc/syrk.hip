@@ -1,0 +1,255 @@
+// Symmetric rank-K update of a wide factorisation's trailing matrix on the
+// bf16 matrix cores, at fp32 accuracy:
+//   C[i][j] -= sum_k P[i][k] P[j][k]      (tiles on or below the diagonal)
+// with P = the fp32 rows of the finished super-panel.
+//
+// "Resumen Técnico: GPTQ-intrinsic LoRA", "Detalles de Implementación": the
+// standard method factorises the regularised Hessian by Cholesky; this is
+// that factorisation's trailing update in its two-level form.
+//
+// Precision: each fp32 value is split exactly into three bf16 pieces,
+// p = p1 + p2 + p3 + r with p1 = bf16(p), p2 = bf16(p - p1), p3 =
+// bf16(p - p1 - p2), |r| <= 2^-24 |p| (each subtraction is exact). A
+// product of two pieces is exact in fp32. Of the nine piece products the
+// six with pieces (1,1), (1,2), (2,1), (2,2), (1,3), (3,1) are taken; the
+// dropped ones are below 2^-23 of the product, the size of an fp32
+// rounding, so the sum carries fp32-level error, with six bf16 MFMAs in
+// place of the fp32 one at 16 times its rate. The six products of a k slice
+// are added smallest first, and the MFMA accumulator is folded into an fp32
+// total after every 32 k (as in the fp32 update), so no rounding happens at
+// the magnitude of C's entries until the single final addition.
+//
+// Layout (MI355X): 128 x 128 tiles of C, one per workgroup of 4 waves (2 x
+// 2, each 64 x 64 = 2 x 2 accumulators of v_mfma_f32_32x32x16_bf16). K
+// streams through a 3-slot LDS ring of 16-deep stages (24 KiB: the three
+// pieces of the tile's 128 row-operand rows and of its 128 column-operand
+// rows, 32 bytes per row and piece) filled by buffer LDS-DMA, so two
+// workgroups share a CU. Both operands are rows of P (k contiguous), read
+// with ds_read_b128; the 16-byte chunk index of row r is XORed with
+// (r / 8) % 2 so 16 consecutive rows of one chunk column cover all banks.
+// The tiles are numbered row by row over the lower triangle and dealt to
+// the XCDs in contiguous runs.
+#include "common.h"
+#include "dma.h"
+
+namespace gq {
+
+typedef __bf16 s6_bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float s6_f32x16_t __attribute__((ext_vector_type(16)));
+
+constexpr int kS6T = 128;                    // tile edge
+constexpr int kS6K = 16;                     // k per stage
+constexpr int kS6Piece = kS6T * kS6K * 2;    // bytes of one piece of one operand per stage: 4 KiB
+constexpr int kS6Slot = 6 * kS6Piece;        // 24 KiB
+constexpr int kS6Slots = 3;
+constexpr int kS6Dma = 6;                    // DMA instructions per wave per stage
+
+// ---------------------------------------------------------------- split
+// dst_i[r][c] = piece i of src[r][c] (rows x cols, pitches lds / ldp).
+__global__ void k_split3(const float* __restrict__ src, int64_t rows, int64_t cols, int64_t lds,
+                         uint16_t* __restrict__ p1, uint16_t* __restrict__ p2, uint16_t* __restrict__ p3,
+                         int64_t ldp) {
+  const int64_t c4n = cols / 4;
+  const int64_t total = rows * c4n;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += stride) {
+    const int64_t r = q / c4n, c = 4 * (q - r * c4n);
+    const float4 v = *reinterpret_cast<const float4*>(src + r * lds + c);
+    const float x[4] = {v.x, v.y, v.z, v.w};
+    uint16_t h1[4], h2[4], h3[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      h1[e] = f32_to_bf16_rne(x[e]);
+      const float r1 = x[e] - bf16_to_f32(h1[e]);
+      h2[e] = f32_to_bf16_rne(r1);
+      h3[e] = f32_to_bf16_rne(r1 - bf16_to_f32(h2[e]));
+    }
+    const int64_t o = r * ldp + c;
+    *reinterpret_cast<uint2*>(p1 + o) = make_uint2(h1[0] | ((uint32_t)h1[1] << 16), h1[2] | ((uint32_t)h1[3] << 16));
+    *reinterpret_cast<uint2*>(p2 + o) = make_uint2(h2[0] | ((uint32_t)h2[1] << 16), h2[2] | ((uint32_t)h2[3] << 16));
+    *reinterpret_cast<uint2*>(p3 + o) = make_uint2(h3[0] | ((uint32_t)h3[1] << 16), h3[2] | ((uint32_t)h3[3] << 16));
+  }
+}
+
+// ---------------------------------------------------------------- SYRK
+__device__ __forceinline__ int s6_swz(int row) { return (row >> 3) & 1; }
+
+__device__ __forceinline__ void s6_wait_barrier(int stages) {
+  if (stages <= 0) asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  else asm volatile("s_waitcnt vmcnt(6)\n\ts_barrier" ::: "memory");
+}
+
+struct Syrk6Args {
+  int64_t N, K;                       // C is N x N (lower tiles), P is N x K
+  const uint16_t *P1, *P2, *P3;       // pieces, row pitch ldp
+  int64_t ldp;
+  float* C; int64_t ldc;
+};
+
+__device__ __forceinline__ s6_bf16x8_t s6_frag(uint32_t byte_off) {
+  return __builtin_bit_cast(s6_bf16x8_t, *reinterpret_cast<const __attribute__((address_space(3))) uint4*>(
+                                             (uintptr_t)byte_off));
+}
+
+__global__ void __launch_bounds__(256, 2) k_syrk_x6(Syrk6Args g, int ntile) {
+  __shared__ __align__(16) uint8_t sm[kS6Slots * kS6Slot];
+  const int per = (ntile + 7) >> 3;
+  const int t = ((int)blockIdx.x & 7) * per + ((int)blockIdx.x >> 3);
+  if (t >= ntile) return;
+  // t = tm (tm + 1) / 2 + tn, 0 <= tn <= tm
+  int tm = (int)((sqrt(8.0 * (double)t + 1.0) - 1.0) * 0.5);
+  while ((tm + 1) * (tm + 2) / 2 <= t) ++tm;
+  while (tm * (tm + 1) / 2 > t) --tm;
+  const int tn = t - tm * (tm + 1) / 2;
+  const int64_t m0 = (int64_t)tm * kS6T, n0 = (int64_t)tn * kS6T;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(sm));
+
+  // buffers over rows [m0, N) and [n0, N) of each piece: rows past N read as zeros
+  const int64_t bm = (g.N - m0) * g.ldp * 2, bn = (g.N - n0) * g.ldp * 2;
+  const v4i32_t r01 = make_rsrc(g.P1 + m0 * g.ldp, bm), r02 = make_rsrc(g.P2 + m0 * g.ldp, bm),
+                r03 = make_rsrc(g.P3 + m0 * g.ldp, bm);
+  const v4i32_t r11 = make_rsrc(g.P1 + n0 * g.ldp, bn), r12 = make_rsrc(g.P2 + n0 * g.ldp, bn),
+                r13 = make_rsrc(g.P3 + n0 * g.ldp, bn);
+  // DMA plan: instruction idx = 6 wave + q (0..23): operand op = idx / 12
+  // (0: the tile's rows, 1: its columns), piece (idx % 12) / 4, rows 32 p ..
+  // 32 p + 31 with p = idx % 4; lane l fills row 32 p + l / 2, LDS chunk l % 2,
+  // which holds global chunk (l % 2) ^ swz(row)
+  uint32_t voff[kS6Dma];
+#pragma unroll
+  for (int q = 0; q < kS6Dma; ++q) {
+    const int idx = kS6Dma * wave + q;
+    const int r = 32 * (idx & 3) + (lane >> 1);
+    const int c = (lane & 1) ^ s6_swz(r);
+    voff[q] = (uint32_t)((r * g.ldp + 8 * c) * 2);
+  }
+  auto issue = [&](int st, int slot) {
+    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)(st * kS6K * 2));
+#pragma unroll
+    for (int q = 0; q < kS6Dma; ++q) {
+      const int idx = kS6Dma * wave + q;
+      const int op = idx / 12, piece = (idx % 12) >> 2;   // wave-uniform
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + slot * kS6Slot + (op * 3 + piece) * kS6Piece +
+                                                          (idx & 3) * 1024);
+      const v4i32_t r = op == 0 ? (piece == 0 ? r01 : piece == 1 ? r02 : r03)
+                                : (piece == 0 ? r11 : piece == 1 ? r12 : r13);
+      dma16_rsrc(voff[q], r, soff, dst);
+    }
+  };
+
+  // fragment offsets (per lane, within a slot): row 64 w + 32 b + lane % 32,
+  // k chunk lane / 32
+  uint32_t offA[2], offB[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int ra = 64 * wm + 32 * b + (lane & 31), rb = 64 * wn + 32 * b + (lane & 31);
+    offA[b] = ra * 32 + (((lane >> 5) ^ s6_swz(ra)) * 16);
+    offB[b] = 3 * kS6Piece + rb * 32 + (((lane >> 5) ^ s6_swz(rb)) * 16);
+  }
+
+  s6_f32x16_t acc[2][2], tot[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        acc[a][b][r] = 0.f;
+        tot[a][b][r] = 0.f;
+      }
+  auto fold = [&]() {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          tot[a][b][r] -= acc[a][b][r];
+          acc[a][b][r] = 0.f;
+        }
+  };
+
+  const int nstage = (int)(g.K / kS6K);
+#pragma unroll
+  for (int ps = 0; ps < kS6Slots - 1; ++ps)
+    if (ps < nstage) issue(ps, ps);
+  for (int st = 0; st < nstage; ++st) {
+    s6_wait_barrier(min(kS6Slots - 2, nstage - 1 - st));
+    if (st + kS6Slots - 1 < nstage) issue(st + kS6Slots - 1, (st + kS6Slots - 1) % kS6Slots);
+    const uint32_t sbase = lds0 + (uint32_t)(st % kS6Slots) * kS6Slot;
+    s6_bf16x8_t fa[2][3], fb[2][3];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 3; ++i) {
+        fa[b][i] = s6_frag(sbase + i * kS6Piece + offA[b]);
+        fb[b][i] = s6_frag(sbase + i * kS6Piece + offB[b]);
+      }
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a][2], fb[b][0], acc[a][b], 0, 0, 0);
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a][0], fb[b][2], acc[a][b], 0, 0, 0);
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a][1], fb[b][1], acc[a][b], 0, 0, 0);
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a][1], fb[b][0], acc[a][b], 0, 0, 0);
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a][0], fb[b][1], acc[a][b], 0, 0, 0);
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a][0], fb[b][0], acc[a][b], 0, 0, 0);
+      }
+    if (st & 1) fold();
+  }
+  if (nstage & 1) fold();
+
+  // C += tot (tot holds minus the product); lane holds D[i][j], j = lane % 32,
+  // i = 8 (r / 4) + 4 (lane / 32) + r % 4. All 16 values of a block are
+  // loaded before its first store.
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t j = n0 + 64 * wn + 32 * b + (lane & 31);
+      const int64_t ib = m0 + 64 * wm + 32 * a + 4 * (lane >> 5);
+      float cv[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t i = min(ib + 8 * (r >> 2) + (r & 3), g.N - 1);
+        cv[r] = g.C[i * g.ldc + min(j, g.N - 1)];
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t i = ib + 8 * (r >> 2) + (r & 3);
+        if (i < g.N && j < g.N) g.C[i * g.ldc + j] = cv[r] + tot[a][b][r];
+      }
+    }
+}
+
+bool syrk_x6_ok(int64_t N, int64_t K, int64_t lda, const float* A, int64_t ldc, const float* C) {
+  return N > 0 && K > 0 && K % kS6K == 0 && lda % 4 == 0 && ((uintptr_t)A & 15) == 0 && ldc > 0 &&
+         C != nullptr && N * K * 2 < ((int64_t)1 << 31) && N * (N + 1) / 2 / (kS6T * kS6T) < ((int64_t)1 << 28);
+}
+
+hipError_t launch_syrk_x6(hipStream_t s, const float* A, int64_t lda, float* C, int64_t ldc, int64_t N,
+                          int64_t K, uint16_t* pieces) {
+  if (N <= 0) return hipSuccess;
+  if (!syrk_x6_ok(N, K, lda, A, ldc, C) || !pieces || ((uintptr_t)pieces & 15) != 0) return hipErrorInvalidValue;
+  uint16_t* p1 = pieces;
+  uint16_t* p2 = pieces + N * K;
+  uint16_t* p3 = pieces + 2 * N * K;
+  {
+    int64_t blocks = ceil_div(N * (K / 4), 256);
+    if (blocks > 16384) blocks = 16384;
+    hipLaunchKernelGGL(k_split3, dim3((unsigned)blocks), dim3(256), 0, s, A, N, K, lda, p1, p2, p3, K);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  Syrk6Args g{};
+  g.N = N; g.K = K; g.P1 = p1; g.P2 = p2; g.P3 = p3; g.ldp = K; g.C = C; g.ldc = ldc;
+  const int64_t nt = ceil_div(N, kS6T);
+  const int64_t ntile = nt * (nt + 1) / 2;
+  hipLaunchKernelGGL(k_syrk_x6, dim3((unsigned)(8 * ((ntile + 7) / 8))), dim3(256), 0, s, g, (int)ntile);
+  return hipGetLastError();
+}
+
+}  // namespace gq
