@@ -173,8 +173,10 @@ struct SweepArgs {
   // kb = 128, 256 or 384; 0 = none
   const float* Esb; int64_t kb;
   float* row_loss;
-  // if non-null, E's split-bf16 parts are written beside it (same pitch)
+  // if non-null, E's split-bf16 parts are written there (row pitch ldeh,
+  // the same column offsets as E)
   uint16_t *Ehi, *Elo;
+  int64_t ldeh;
   const DevStatus* st;
 };
 hipError_t launch_sweep(hipStream_t s, const SweepArgs& a);

@@ -107,6 +107,18 @@ int64_t super_width(const gptq_params* p) {
 // columns.
 bool use_two_level(int64_t n, const gptq_params* p) { return n % 8 == 0 && super_width(p) % 8 == 0; }
 
+// Far field in pairs of super-blocks: after the first of a pair only the
+// next super-block's columns are updated (a narrow product, the bridge);
+// after the second, one product with both super-blocks' errors (K = 2 sw)
+// updates everything to the right. The weights right of the pair are then
+// read and written once per pair instead of twice, which is what bounds the
+// far field of a large layer; on small ones the extra bridge launches cost
+// more than that saves.
+constexpr int64_t kPairMinWeights = (int64_t)1 << 27;   // d_out * n
+bool pair_far_field(int64_t d_out, int64_t n, const gptq_params* p) {
+  return use_two_level(n, p) && d_out * n >= kPairMinWeights;
+}
+
 // Super-panel width and the narrowest matrix factorised in two levels (see
 // factor_panels).
 constexpr int64_t kSuper = 2048;
@@ -121,6 +133,7 @@ QLayout q_layout(int64_t d_out, int64_t n, const gptq_params* p) {
   Carver c;
   const bool two = d_out > 0 && use_two_level(n, p);
   const int64_t ew = two ? super_width(p) : p->block;
+  const int64_t ewh = pair_far_field(d_out, n, p) ? 2 * ew : ew;   // columns of Ehi / Elo
   L.status = c.take(sizeof(DevStatus));
   L.lam = c.take(sizeof(double));
   L.diag = c.take(sizeof(float) * n);
@@ -130,8 +143,8 @@ QLayout q_layout(int64_t d_out, int64_t n, const gptq_params* p) {
   L.X = c.take(sizeof(float) * n * n);
   L.Wf = c.take(sizeof(float) * d_out * n);
   L.E = c.take(sizeof(float) * d_out * ew);
-  L.Ehi = c.take(two ? sizeof(uint16_t) * d_out * ew : 0);
-  L.Elo = c.take(two ? sizeof(uint16_t) * d_out * ew : 0);
+  L.Ehi = c.take(two ? sizeof(uint16_t) * d_out * ewh : 0);
+  L.Elo = c.take(two ? sizeof(uint16_t) * d_out * ewh : 0);
   L.Uhi = c.take(two ? sizeof(uint16_t) * n * n : 0);
   L.Ulo = c.take(two ? sizeof(uint16_t) * n * n : 0);
   L.codes = c.take((size_t)d_out * p->n_quant);
@@ -653,8 +666,15 @@ gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int
   // the fused path takes a whole super-block per launch when U's rows are
   // 16-byte aligned (the tile loads are unpredicated float4)
   const bool sbl = fused && n % 4 == 0 && ((uintptr_t)U & 15) == 0;
+  // far field in pairs of super-blocks (see pair_far_field): the second of a
+  // pair writes its bf16 error parts sw columns to the right of the first's
+  const bool pair = two && pair_far_field(d_out, n, p);
+  const int64_t ldeh = pair ? 2 * sw : sw;
+  bool owed = false;     // a first-of-pair super-block whose far field right of the next one is pending
+  int64_t ps0 = 0;       // its first column
   for (int64_t s0 = 0; s0 < nq; s0 += sw) {
     const int64_t s1 = std::min<int64_t>(s0 + sw, nq);
+    const int64_t eoff = pair && owed ? sw : 0;   // this super-block's columns in Ehi / Elo
     if (sbl) {
       SweepArgs a{};
       a.Wf = Wf; a.ldw = n; a.U = U; a.ldu = n; a.d_out = d_out; a.i0 = s0; a.ncols = s1 - s0;
@@ -667,8 +687,9 @@ gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int
       a.scales = out->scales; a.zeros = out->zeros; a.ngroups = nq / p->group;
       a.codes = codes; a.n_quant = nq; a.E = E; a.lde = sw; a.row_loss = loss; a.st = dst;
       a.Esb = E; a.kb = 0;
-      a.Ehi = s1 < n ? Ehi : nullptr;
-      a.Elo = s1 < n ? Elo : nullptr;
+      a.Ehi = s1 < n ? Ehi + eoff : nullptr;
+      a.Elo = s1 < n ? Elo + eoff : nullptr;
+      a.ldeh = ldeh;
       Timed ph(GPTQ_PROF_SWEEP, s, 2);
       HIP_TRY(launch_sweep_super(s, a), "sweep");
     }
@@ -686,8 +707,9 @@ gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int
       a.scales = out->scales; a.zeros = out->zeros; a.ngroups = nq / p->group;
       a.codes = codes; a.n_quant = nq; a.E = Eb; a.lde = sw; a.row_loss = loss; a.st = dst;
       a.Esb = E; a.kb = fused ? i0 - s0 : 0;
-      a.Ehi = two && s1 < n ? Ehi + (i0 - s0) : nullptr;
-      a.Elo = two && s1 < n ? Elo + (i0 - s0) : nullptr;
+      a.Ehi = two && s1 < n ? Ehi + eoff + (i0 - s0) : nullptr;
+      a.Elo = two && s1 < n ? Elo + eoff + (i0 - s0) : nullptr;
+      a.ldeh = ldeh;
       Timed ph(GPTQ_PROF_SWEEP, s, 2);
       HIP_TRY(launch_sweep(s, a), "sweep");
       const int64_t i1 = i0 + nc;
@@ -703,13 +725,20 @@ gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int
       }
     }
     if (two && s1 < n) {
+      // rows [k0, s1) of U and columns [s1, s1 + N) of W: the first of a
+      // pair updates only the next super-block (the bridge), the second
+      // applies both super-blocks' errors to everything to its right
+      const bool bridge = pair && !owed && s1 < nq;
+      const int64_t k0 = pair && owed ? ps0 : s0;
       TrailArgs t{};
-      t.M = d_out; t.N = n - s1; t.K = s1 - s0;
-      t.Ahi = Ehi; t.Alo = Elo; t.lda = sw;
-      t.Bhi = Uhi + s0 * n + s1; t.Blo = Ulo + s0 * n + s1; t.ldb = n;
+      t.M = d_out; t.N = bridge ? std::min<int64_t>(s1 + sw, nq) - s1 : n - s1; t.K = s1 - k0;
+      t.Ahi = Ehi; t.Alo = Elo; t.lda = ldeh;
+      t.Bhi = Uhi + k0 * n + s1; t.Blo = Ulo + k0 * n + s1; t.ldb = n;
       t.C = Wf + s1; t.ldc = n;
       Timed ph(GPTQ_PROF_FARFIELD, s, 2);
       HIP_TRY(launch_trail_x3(s, t), "far-field update");
+      owed = bridge;
+      if (bridge) ps0 = s0;
     }
   }
   Timed ph(GPTQ_PROF_PREP_FINISH, s, 2);

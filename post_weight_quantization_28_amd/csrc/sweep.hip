@@ -475,8 +475,8 @@ k_sweep(SweepArgs a) {
       a.E[row * a.lde + col] = S.ev[c];
       if (a.Ehi) {
         const uint16_t h = f32_to_bf16_rne(S.ev[c]);
-        a.Ehi[row * a.lde + col] = h;
-        a.Elo[row * a.lde + col] = f32_to_bf16_rne(S.ev[c] - bf16_to_f32(h));
+        a.Ehi[row * a.ldeh + col] = h;
+        a.Elo[row * a.ldeh + col] = f32_to_bf16_rne(S.ev[c] - bf16_to_f32(h));
       }
     }
     if (L == 0) a.row_loss[row] = loss0 + loss;
@@ -588,8 +588,8 @@ k_sweep_sb(SweepArgs a) {
         Eb[row * a.lde + col] = S.ev[c];
         if (a.Ehi) {
           const uint16_t h = f32_to_bf16_rne(S.ev[c]);
-          a.Ehi[row * a.lde + ab.kb + col] = h;
-          a.Elo[row * a.lde + ab.kb + col] = f32_to_bf16_rne(S.ev[c] - bf16_to_f32(h));
+          a.Ehi[row * a.ldeh + ab.kb + col] = h;
+          a.Elo[row * a.ldeh + ab.kb + col] = f32_to_bf16_rne(S.ev[c] - bf16_to_f32(h));
         }
       }
     }
