@@ -110,10 +110,35 @@ __global__ void k_gidx(const int32_t* __restrict__ invperm, int64_t nq, int grou
   if (k < nq) g_idx[k] = invperm[k] / group;
 }
 
+// The same with the row of Wf and of the codes staged in LDS (coalesced
+// reads, the permuted gather in LDS, coalesced writes).
+__global__ void __launch_bounds__(256)
+k_finish_lds(const float* __restrict__ Wf, const uint8_t* __restrict__ codes_p,
+             const int32_t* __restrict__ invperm, int64_t n, int64_t nq, float* __restrict__ w_hat,
+             uint8_t* __restrict__ codes_out) {
+  extern __shared__ __align__(16) float frow[];
+  uint8_t* crow = reinterpret_cast<uint8_t*>(frow + n);
+  const int64_t r = blockIdx.x;
+  if (w_hat)
+    for (int64_t k = threadIdx.x; k < n; k += 256) frow[k] = Wf[r * n + k];
+  if (codes_out)
+    for (int64_t k = threadIdx.x; k < nq; k += 256) crow[k] = codes_p[r * nq + k];
+  __syncthreads();
+  for (int64_t k = threadIdx.x; k < n; k += 256) {
+    const int64_t p = invperm[k];
+    if (w_hat) w_hat[r * n + k] = frow[p];
+    if (codes_out && k < nq) codes_out[r * nq + k] = crow[p];
+  }
+}
+
 hipError_t launch_finish(hipStream_t s, const float* Wf, const uint8_t* codes_p,
                          const int32_t* invperm, int64_t d_out, int64_t n, int64_t n_quant,
                          int group, float* w_hat, uint8_t* codes_out, int32_t* g_idx) {
-  if (d_out > 0 && (w_hat || codes_out))
+  const size_t lds = (size_t)n * sizeof(float) + (size_t)n_quant;
+  if (d_out > 0 && (w_hat || codes_out) && lds <= 65536)
+    hipLaunchKernelGGL(k_finish_lds, dim3((unsigned)d_out), dim3(256), lds, s, Wf, codes_p, invperm, n,
+                       n_quant, w_hat, codes_out);
+  else if (d_out > 0 && (w_hat || codes_out))
     hipLaunchKernelGGL(k_finish, dim3((unsigned)d_out), dim3(256), 0, s, Wf, codes_p, invperm, n,
                        n_quant, w_hat, codes_out);
   if (g_idx)

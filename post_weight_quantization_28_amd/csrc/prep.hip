@@ -12,6 +12,8 @@
 // later kernel work with lower-triangular storage.
 #include "common.h"
 
+#include <algorithm>
+
 namespace gq {
 
 __global__ void k_status_init(DevStatus* st) {
@@ -104,10 +106,58 @@ k_order(const float* __restrict__ diag, int64_t n, int64_t nq, int act_order,
   }
 }
 
+// The same ranks with the comparisons spread over a second grid dimension:
+// workgroup (x, y) counts, for its 256 entries i, the keys of the y-th chunk
+// of j that precede i, and adds the count to rank[i] (integer atomics: the
+// sums do not depend on the order). rank must start at zero.
+__global__ void __launch_bounds__(256)
+k_rank_part(const float* __restrict__ diag, int64_t nq, int64_t jchunk, int32_t* __restrict__ rank) {
+  __shared__ float keys[1024];
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const bool mine = i < nq;
+  const float ki = mine ? order_key(diag[i]) : 0.f;
+  const int64_t jlo = (int64_t)blockIdx.y * jchunk, jhi = min(nq, jlo + jchunk);
+  int cnt = 0;
+  for (int64_t base = jlo; base < jhi; base += 1024) {
+    __syncthreads();
+    for (int t = threadIdx.x; t < 1024; t += 256) keys[t] = (base + t < jhi) ? order_key(diag[base + t]) : 0.f;
+    __syncthreads();
+    if (mine) {
+      const int lim = (int)min((int64_t)1024, jhi - base);
+      for (int t = 0; t < lim; ++t) {
+        const float kj = keys[t];
+        const int64_t j = base + t;
+        cnt += (kj > ki) || (kj == ki && j < i);
+      }
+    }
+  }
+  if (mine && cnt) atomicAdd(&rank[i], cnt);
+}
+
+// invperm holds the ranks of the first nq entries; the rest keep their place
+__global__ void k_rank_write(int64_t n, int64_t nq, int32_t* __restrict__ perm, int32_t* __restrict__ invperm) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int32_t r = i < nq ? invperm[i] : (int32_t)i;
+  invperm[i] = r;
+  perm[r] = (int32_t)i;
+}
+
 hipError_t launch_order(hipStream_t s, const float* diag, int64_t n, int64_t n_quant,
                         int act_order, int32_t* perm, int32_t* invperm) {
-  hipLaunchKernelGGL(k_order, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s, diag, n,
-                     n_quant, act_order, perm, invperm);
+  if (!act_order || n_quant <= 1024) {
+    hipLaunchKernelGGL(k_order, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s, diag, n,
+                       n_quant, act_order, perm, invperm);
+    return hipGetLastError();
+  }
+  // about 1024 workgroups in all
+  const int64_t ib = ceil_div(n_quant, 256);
+  const int64_t nj = std::min<int64_t>(std::max<int64_t>(1, ceil_div(1024, ib)), ceil_div(n_quant, 256));
+  const int64_t jchunk = ceil_div(n_quant, nj);
+  hipError_t e = launch_fill_f32(s, reinterpret_cast<float*>(invperm), (size_t)n_quant, 0.f);   // int zero
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_rank_part, dim3((unsigned)ib, (unsigned)nj), dim3(256), 0, s, diag, n_quant, jchunk, invperm);
+  hipLaunchKernelGGL(k_rank_write, dim3((unsigned)ceil_div(n, 256)), dim3(256), 0, s, n, n_quant, perm, invperm);
   return hipGetLastError();
 }
 
@@ -155,10 +205,42 @@ k_build_flipped(const float* __restrict__ H, int64_t n, const int32_t* __restric
   }
 }
 
+// The permuted build with row p of H staged in LDS: the row is read once,
+// coalesced, and the permuted gather happens in LDS (read straight from
+// memory, each 4-byte element at a permuted column costs a whole sector).
+// Rows of up to 16384 floats (64 KiB of LDS).
+constexpr int64_t kRowLdsMax = 16384;
+
+__global__ void __launch_bounds__(256)
+k_build_flipped_lds(const float* __restrict__ H, int64_t n, const int32_t* __restrict__ perm,
+                    const float* __restrict__ diag, const double* __restrict__ lam,
+                    float* __restrict__ A, DevStatus* st) {
+  extern __shared__ __align__(16) float hrow[];
+  const int64_t a = blockIdx.x;
+  const int64_t p = perm[n - 1 - a];
+  const float lamf = (float)lam[0];
+  for (int64_t c = threadIdx.x; c < n; c += 256) hrow[c] = H[p * n + c];
+  __syncthreads();
+  for (int64_t b = threadIdx.x; b <= a; b += 256) {
+    const int64_t q = perm[n - 1 - b];
+    float v;
+    if (b == a) {
+      v = diag[p] + lamf;
+    } else {
+      v = hrow[q];
+      if (!isfinite(v)) raise_status(st, kNonFinite, min(p, q));
+    }
+    A[a * n + b] = v;
+  }
+}
+
 hipError_t launch_build_flipped(hipStream_t s, const float* H, int64_t n, const int32_t* perm,
                                 const float* diag, const double* lam, float* A, DevStatus* st) {
-  hipLaunchKernelGGL(k_build_flipped, dim3((unsigned)n), dim3(256), 0, s, H, n, perm, diag, lam,
-                     A, st);
+  if (perm && n <= kRowLdsMax)
+    hipLaunchKernelGGL(k_build_flipped_lds, dim3((unsigned)n), dim3(256), (size_t)n * sizeof(float), s, H, n,
+                       perm, diag, lam, A, st);
+  else
+    hipLaunchKernelGGL(k_build_flipped, dim3((unsigned)n), dim3(256), 0, s, H, n, perm, diag, lam, A, st);
   return hipGetLastError();
 }
 
@@ -213,10 +295,43 @@ k_w_prep(const void* __restrict__ Wv, int64_t n, int64_t ldw, const int32_t* __r
   }
 }
 
+// The permuted W preparation with the row staged in LDS as fp32 (coalesced
+// read, gather in LDS, coalesced write).
+template <bool kBF16>
+__global__ void __launch_bounds__(256)
+k_w_prep_lds(const void* __restrict__ Wv, int64_t n, int64_t ldw, const int32_t* __restrict__ perm,
+             float* __restrict__ Wf, DevStatus* st) {
+  extern __shared__ __align__(16) float wrow[];
+  const int64_t r = blockIdx.x;
+  for (int64_t c = threadIdx.x; c < n; c += 256) {
+    if (kBF16) {
+      const uint16_t u = reinterpret_cast<const uint16_t*>(Wv)[r * ldw + c];
+      wrow[c] = __uint_as_float((uint32_t)u << 16);
+    } else {
+      wrow[c] = reinterpret_cast<const float*>(Wv)[r * ldw + c];
+    }
+  }
+  __syncthreads();
+  for (int64_t q = threadIdx.x; q < n; q += 256) {
+    const int64_t c = perm[q];
+    const float v = wrow[c];
+    if (!isfinite(v)) raise_status(st, kNonFinite, c);
+    Wf[r * n + q] = v;
+  }
+}
+
 hipError_t launch_w_prep(hipStream_t s, const void* W, int wdt_bf16, int64_t d_out, int64_t n,
                          int64_t ldw, const int32_t* perm, float* Wf, DevStatus* st) {
   if (d_out == 0) return hipSuccess;
   dim3 grid((unsigned)d_out);
+  if (perm && n <= kRowLdsMax) {
+    const size_t lds = (size_t)n * sizeof(float);
+    if (wdt_bf16)
+      hipLaunchKernelGGL(k_w_prep_lds<true>, grid, dim3(256), lds, s, W, n, ldw, perm, Wf, st);
+    else
+      hipLaunchKernelGGL(k_w_prep_lds<false>, grid, dim3(256), lds, s, W, n, ldw, perm, Wf, st);
+    return hipGetLastError();
+  }
   if (wdt_bf16)
     hipLaunchKernelGGL(k_w_prep<true>, grid, dim3(256), 0, s, W, n, ldw, perm, Wf, st);
   else
