@@ -55,11 +55,46 @@ k_pack(const uint8_t* __restrict__ codes, int64_t ldc, const int32_t* __restrict
   }
 }
 
+// One workgroup per row with the row's codes staged in LDS (16-byte reads):
+// the permuted or 3-bit straddling gathers then read LDS, not scattered
+// bytes of memory. Rows of up to 64 KiB of codes.
+__global__ void __launch_bounds__(256)
+k_pack_lds(const uint8_t* __restrict__ codes, int64_t ldc, const int32_t* __restrict__ invperm, int64_t nq,
+           int bits, int64_t wpr, uint32_t* __restrict__ qw) {
+  extern __shared__ __align__(16) uint8_t crow[];
+  const int64_t r = blockIdx.x;
+  const uint8_t* row = codes + r * ldc;
+  const bool vec = ((ldc & 15) == 0) && (((uintptr_t)codes & 15) == 0);
+  const int64_t n16 = vec ? nq / 16 : 0;
+  for (int64_t v = threadIdx.x; v < n16; v += 256)
+    *reinterpret_cast<uint4*>(crow + 16 * v) = *reinterpret_cast<const uint4*>(row + 16 * v);
+  for (int64_t k = 16 * n16 + threadIdx.x; k < nq; k += 256) crow[k] = row[k];
+  __syncthreads();
+  const uint32_t mask = (1u << bits) - 1u;
+  for (int64_t w = threadIdx.x; w < wpr; w += 256) {
+    const int64_t bit0 = 32 * w;
+    const int64_t k0 = bit0 / bits;
+    const int64_t k1 = min(nq - 1, (bit0 + 31) / bits);
+    uint32_t word = 0;
+    for (int64_t k = k0; k <= k1; ++k) {
+      const uint32_t c = crow[invperm ? invperm[k] : k] & mask;
+      const int64_t o = k * bits - bit0;
+      word |= (o < 0) ? (c >> (-o)) : (c << o);
+    }
+    qw[r * wpr + w] = word;
+  }
+}
+
 hipError_t launch_pack(hipStream_t s, const uint8_t* codes, int64_t ldc, const int32_t* invperm,
                        int64_t d_out, int64_t n_quant, int bits, uint32_t* qweight) {
   const int64_t wpr = ceil_div(n_quant * bits, 32);
   const int64_t total = d_out * wpr;
   if (total == 0) return hipSuccess;
+  if ((invperm || bits == 3) && n_quant <= 65536) {
+    hipLaunchKernelGGL(k_pack_lds, dim3((unsigned)std::min<int64_t>(d_out, 1ll << 31)), dim3(256), (size_t)n_quant, s,
+                       codes, ldc, invperm, n_quant, bits, wpr, qweight);
+    return hipGetLastError();
+  }
   // rows run along the grid's y dimension (at most 65535, looped beyond)
   hipLaunchKernelGGL(k_pack, dim3((unsigned)ceil_div(wpr, 256), (unsigned)std::min<int64_t>(d_out, 65535)),
                      dim3(256), 0, s, codes, ldc,
