@@ -493,7 +493,12 @@ k_sweep(SweepArgs a) {
 // Block b + 1's near field reads the errors this workgroup stored for
 // blocks 0..b; the workgroup barrier after each block orders those stores
 // before the reads (all waves of a workgroup share one CU and its L1).
-__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// The prefetch needs a wave's whole register file (one workgroup per CU):
+// layers with more rows than one round of that (4096) take PF = false,
+// which requests each block's operands at its own start and fits two
+// workgroups per CU, so one's waits are covered by the other's work.
+template <bool PF>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(PF ? 1 : 2, PF ? 1 : 2)))
 k_sweep_sb(SweepArgs a) {
   constexpr int CPL = 8, B = 128;
   constexpr int NV = B * B / 4 / 256;   // float4 of the U tile per thread
@@ -528,7 +533,7 @@ k_sweep_sb(SweepArgs a) {
 #pragma unroll
     for (int c = 0; c < CPL; ++c) wn[c] = row_ok ? a.Wf[row * a.ldw + i0 + 16 * c + L] : 0.f;
   };
-  fetch(s0);
+  if (PF) fetch(s0);
   float lossacc = (row_ok && L == 0) ? a.row_loss[row] : 0.f;
   if (a.st->flags != 0) return;
 
@@ -541,15 +546,18 @@ k_sweep_sb(SweepArgs a) {
     ab.i0 = i0;
     ab.kb = (int64_t)b * B;
     ab.gbase = a.gbase + (int64_t)b * (B / a.group);
+    if (b == 1) near_update<4>(ab, sU, upd);
+    else if (b == 2) near_update<8>(ab, sU, upd);
+    else if (b == 3) near_update<12>(ab, sU, upd);   // each ends with a barrier: sU is free again
+    // without the prefetch, this block's operands are requested after its
+    // near field, so they are not live across that field's register ring
+    if (!PF) fetch(i0);
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       S.w[c] = wn[c];
       S.ev[c] = 0.f;
       S.qv[c] = 0.f;
     }
-    if (b == 1) near_update<4>(ab, sU, upd);
-    else if (b == 2) near_update<8>(ab, sU, upd);
-    else if (b == 3) near_update<12>(ab, sU, upd);   // each ends with a barrier: sU is free again
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       const int e4 = tid + 256 * v;
@@ -568,7 +576,7 @@ k_sweep_sb(SweepArgs a) {
       for (int c = 0; c < CPL; ++c) S.w[c] -= ur[16 * c];
     }
     start_group<CPL, 0>(S, ab, L, row, row_ok, maxq);
-    if (b + 1 < nblk) fetch(i0 + B);
+    if (PF && b + 1 < nblk) fetch(i0 + B);
 
     load_urow<CPL, 0, 0>(S, sU, sInv, L, 0);
     load_urow<CPL, 1, 0>(S, sU, sInv, L, 1);
@@ -605,7 +613,11 @@ hipError_t launch_sweep_super(hipStream_t s, const SweepArgs& a) {
   if (a.block != 128 || a.ncols % 128 != 0 || a.ncols > 512 || a.group > 128 || 128 % a.group != 0 ||
       a.i0 % 128 != 0 || a.ldu % 4 != 0 || ((uintptr_t)a.U & 15) != 0 || a.Esb != a.E)
     return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_sweep_sb, dim3((unsigned)ceil_div(a.d_out, 16)), dim3(256), 0, s, a);
+  const int64_t wgs = ceil_div(a.d_out, 16);
+  if (wgs <= 256)
+    hipLaunchKernelGGL(k_sweep_sb<true>, dim3((unsigned)wgs), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(k_sweep_sb<false>, dim3((unsigned)wgs), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
