@@ -67,39 +67,24 @@ __device__ inline void upper_tile(int t, int nt, int& bi, int& bj) {
   bj = row + t;
 }
 
-// Work item of block b: (split, tile). The dispatcher deals consecutive
-// block ids to the 8 XCDs in turn (b, b + 8, ... share one XCD and its L2).
-//  * chunk_major = 0 (a chunk's tiles fit in one round of the chip): block
-//    b takes item (b % 8) * per + b / 8 of the tile-fastest list, so each
-//    XCD walks one contiguous run of items, mostly one token chunk at a
-//    time, and its resident tiles stream the same X rows through its L2.
-//  * chunk_major = 1 (more tiles than that): every XCD works on the same
-//    token chunk at once, each on its own contiguous run of that chunk's
-//    tiles (r = ceil(tiles / 8) of them). With one chunk per XCD, eight
-//    chunks (144 MB each at n = 11008) would be live at once, more than the
-//    256 MB last-level cache holds, and X would be fetched from HBM again
-//    and again; the 11008-wide Gram kernel takes 7-8 % less time this way.
-// Returns false for padding blocks.
-__device__ inline bool hessian_item(int b, int ntile, int splits, int chunk_major, int& tile, int& split) {
-  if (chunk_major) {
-    const int r = (ntile + 7) >> 3;
-    const int q = b >> 3;
-    split = q / r;
-    tile = (b & 7) * r + (q - split * r);
-    return split < splits && tile < ntile;
-  }
-  const int total = ntile * splits;
-  const int per = (total + 7) >> 3;
-  const int w = (b & 7) * per + (b >> 3);
-  if (w >= total) return false;
+// Work item of block b: (split, tile), from the split-major item list (tile
+// fastest). The dispatcher deals consecutive block ids to the 8 XCDs in
+// turn, and an XCD holds one of these 128 KiB workgroups per CU, 32 at a
+// time. Blocks are read as rounds of 256: in round r, XCD x takes items
+// 256 r + 32 x ... 256 r + 32 x + 31. The 32 workgroups resident on an XCD
+// then work on consecutive tiles of one token chunk (their channel strips
+// meet in that XCD's L2), and the whole chip stays within about two
+// adjacent chunks at a time (144 MB of X at n = 4096), which the 256 MB
+// last-level cache holds while the XCDs re-read it.
+// Returns false for padding blocks (the grid is a whole number of rounds).
+__device__ inline bool hessian_item(int b, int ntile, int splits, int& tile, int& split) {
+  const int q = b >> 3;
+  const int w = (((q >> 5) << 3) + (b & 7)) * 32 + (q & 31);
+  if (w >= ntile * splits) return false;
   split = w / ntile;
   tile = w - split * ntile;
   return true;
 }
-
-// the work mapping of hessian_item: chunk-major once a chunk's tiles exceed
-// one round of the 256 CUs
-inline int hessian_chunk_major(int64_t ntile) { return ntile >= 256 ? 1 : 0; }
 
 // Load an 8(token) x 8(channel) bf16 block: rows X[t0+r][c0..c0+7].
 template <bool kAligned>
@@ -303,7 +288,7 @@ __device__ __forceinline__ void wait_stages_barrier(int stages) {
 template <int WAVES, int SLOTS>
 __global__ void __launch_bounds__(64 * WAVES)
 k_hessian_dma(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx,
-              float* __restrict__ part, int64_t chunk, int splits, int chunk_major) {
+              float* __restrict__ part, int64_t chunk, int splits) {
   static_assert(WAVES == 4 || WAVES == 8, "4 or 8 waves");
   static_assert(SLOTS >= 2 && SLOTS <= 5, "2..5 slots");
   constexpr int PER = 32 / WAVES;         // DMA instructions per wave per stage
@@ -312,7 +297,7 @@ k_hessian_dma(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx,
   __shared__ __align__(16) uint8_t dsm[SLOTS * kDSlotBytes];
   const int nt = (int)ceil_div(n, kHT);
   int tile, split, bi, bj;
-  if (!hessian_item(blockIdx.x, nt * (nt + 1) / 2, splits, chunk_major, tile, split)) return;
+  if (!hessian_item(blockIdx.x, nt * (nt + 1) / 2, splits, tile, split)) return;
   upper_tile(tile, nt, bi, bj);
   const int64_t kbeg = (int64_t)split * chunk;
   const int64_t kend = min(T, kbeg + chunk);
@@ -461,11 +446,9 @@ hipError_t launch_hessian_partials_bf16(hipStream_t s, const uint16_t* X, int64_
   const bool aligned = (n % 8 == 0) && (ldx % 8 == 0) && ((uintptr_t)X % 16 == 0);
   // 32-bit buffer offsets: a token chunk must span less than 2^31 bytes
   if (aligned && chunk * ldx * 2 < ((int64_t)1 << 31)) {
-    const int64_t ntile = (int64_t)nt * (nt + 1) / 2;
-    const int cm = hessian_chunk_major(ntile);
-    const int64_t grid = cm ? 8 * ((ntile + 7) / 8) * splits : 8 * ((items + 7) / 8);
+    const int64_t grid = 256 * (((int64_t)items + 255) / 256);   // whole rounds (hessian_item)
     hipLaunchKernelGGL((k_hessian_dma<kDWaves, kDSlotsUsed>), dim3((unsigned)grid), dim3(64 * kDWaves), 0,
-                       s, X, T, n, ldx, part, chunk, splits, cm);
+                       s, X, T, n, ldx, part, chunk, splits);
   } else {
     hipLaunchKernelGGL(k_hessian_bf16<false>, dim3(items), dim3(256), 0, s, X, T, n, ldx, part, chunk);
   }

@@ -31,7 +31,7 @@ def say(*a):
     ("c2", dict(d_out=8, n=640, T=8292)),             # bf16, ragged T, 2.5 tiles
     ("c3", dict(d_out=8, n=520, T=4100)),             # n % 8 == 0, ragged T
     ("c2", dict(d_out=8, n=300, T=1000)),             # n % 8 != 0: unaligned loads
-    ("c3", dict(d_out=8, n=5888, T=2050)),            # 276 tiles: chunk-major work mapping, padding blocks
+    ("c3", dict(d_out=8, n=5888, T=2050)),            # 276 tiles: a split spans more than one round of items, padding blocks
 ])
 def test_hessian_parity(name, kw):
     wl = synth.make_workload(name, group=4, **kw)
