@@ -235,9 +235,9 @@ k_hessian_bf16(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx
 // transposing LDS reads.
 //
 //  * buffer_load_dwordx4 ... lds moves 16-byte chunks (8 channels of one
-//    token) straight from HBM into LDS without passing through VGPRs, so
-//    four 32-token stages (128 KiB of LDS) are in flight at once: the load
-//    of stage s+3 is issued while stage s is multiplied. The buffer
+//    token) straight from HBM into LDS without passing through VGPRs, so a
+//    ring of four 32-token stages (128 KiB of LDS) keeps the fill two
+//    stages ahead of the one being multiplied. The buffer
 //    descriptor spans this workgroup's token chunk, so each lane's offset is
 //    fixed and one scalar offset advances a whole stage; chunks past the
 //    chunk's last token or the last channel are outside the descriptor's
@@ -250,8 +250,11 @@ k_hessian_bf16(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx
 //  * ds_read_b64_tr_b16 turns it into MFMA operands (4 consecutive tokens of
 //    one channel per read, two reads per 8-token K slice). A group's 16
 //    reads hit 4 rows x 32 bytes; the swizzle spreads them over all banks.
-//    Every read address is one of 8 per-lane bases (slot base added once
-//    per stage) plus a constant in the instruction's offset field.
+//    Every read address is one of 6 per-lane bases plus the slot base and a
+//    constant in the instruction's offset field.
+//  * The reads of a K slice are issued one half-stage ahead of its MFMAs,
+//    interleaved with the MFMAs of the slice before (across the stage
+//    barrier too), so the matrix cores do not wait for LDS after a barrier.
 //  * The DMA is issued from inline asm and completion tracked with vmcnt, in
 //    the same asm block as the barrier that publishes a stage (see dma.h).
 // ---------------------------------------------------------------------------
@@ -285,12 +288,24 @@ __device__ __forceinline__ void wait_stages_barrier(int stages) {
   else wait_vm_barrier<3 * PER>();
 }
 
+// Instruction scheduling groups for the compiler: one MFMA, then its share
+// of NR LDS reads, NM times (the reads spread evenly over the MFMAs).
+template <int NM, int NR, int I = 0>
+__device__ __forceinline__ void sched_interleave() {
+  if constexpr (I < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    constexpr int r = (I + 1) * NR / NM - I * NR / NM;
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);
+    sched_interleave<NM, NR, I + 1>();
+  }
+}
+
 template <int WAVES, int SLOTS>
 __global__ void __launch_bounds__(64 * WAVES)
 k_hessian_dma(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx,
               float* __restrict__ part, int64_t chunk, int splits) {
   static_assert(WAVES == 4 || WAVES == 8, "4 or 8 waves");
-  static_assert(SLOTS >= 2 && SLOTS <= 5, "2..5 slots");
+  static_assert(SLOTS >= 3 && SLOTS <= 5, "3..5 slots");
   constexpr int PER = 32 / WAVES;         // DMA instructions per wave per stage
   constexpr int WN = WAVES / 2;           // waves across the columns
   constexpr int NB = 4 / (WN / 2);        // 32-column blocks per wave: 4 or 2
@@ -388,38 +403,55 @@ k_hessian_dma(const uint16_t* __restrict__ X, int64_t T, int64_t n, int64_t ldx,
 #pragma unroll
   for (int ps = 0; ps < SLOTS - 1; ++ps)
     if (ps < nstage) issue(ps, ps);
+  // the A / B operands of one 16-token K slice of the stage in `slot`
+  auto read_slice = [&](int slot, int ks, bf16x8_t (&fa)[4], bf16x8_t (&fb)[NB]) {
+    const uint32_t sbase = lds0 + (uint32_t)slot * kDSlotBytes + (uint32_t)(16 * ks) * 512;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const v4i16_t lo = lds_tr16(off[4 + b] + sbase), hi = lds_tr16(off[4 + b] + sbase + 2048);
+      fb[b] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      const v4i16_t lo = lds_tr16(off[b] + sbase), hi = lds_tr16(off[b] + sbase + 2048);
+      fa[b] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  };
+  auto mfma_slice = [&](const bf16x8_t (&fa)[4], const bf16x8_t (&fb)[NB]) {
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < NB; ++nb)
+        acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mb], fb[nb], acc[mb][nb], 0, 0, 0);
+  };
+  // Software pipeline across the stage barrier. The barrier that opens
+  // stage st waits for the DMA of stages st and st + 1, so the first K slice
+  // of stage st + 1 can be read during stage st: each half-stage issues the
+  // MFMAs of one K slice interleaved with the reads of the next, and the
+  // MFMAs after a barrier start on operands already in registers. The refill
+  // issued after barrier st goes to the slot of stage st - 1, whose reads all
+  // completed before its MFMAs (so no wave still reads a slot being filled);
+  // the ring therefore runs SLOTS - 2 stages ahead. The last stage's read of
+  // the next slot touches no slot being filled and is unused.
+  bf16x8_t pa[4], pb[NB], qa[4], qb[NB];
+  // 4 NB MFMAs and 2 (4 + NB) reads per half-stage
+  auto interleave = [&]() { sched_interleave<4 * NB, 2 * (4 + NB)>(); };
   for (int st = 0; st < nstage; ++st) {
-    wait_stages_barrier<PER, SLOTS - 2>(min(SLOTS - 2, nstage - 1 - st));
+    const int pend = min(SLOTS - 3, nstage - 2 - st);
+    wait_stages_barrier<PER, SLOTS - 3>(pend < 0 ? 0 : pend);
     if (st + SLOTS - 1 < nstage) issue(st + SLOTS - 1, (st + SLOTS - 1) % SLOTS);
     if (idle) continue;
-    const uint32_t sbase = lds0 + (uint32_t)(st % SLOTS) * kDSlotBytes;
-    uint32_t bs[4 + NB];
-#pragma unroll
-    for (int b = 0; b < 4 + NB; ++b) bs[b] = off[b] + sbase;
-#pragma unroll
-    for (int ks = 0; ks < kDK / 16; ++ks) {
-      v4i16_t ra[2][4], rb[2][NB];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t row = (16 * ks + 4 * h) * 512;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) ra[h][b] = lds_tr16(bs[b] + row);
-#pragma unroll
-        for (int b = 0; b < NB; ++b) rb[h][b] = lds_tr16(bs[4 + b] + row);
-      }
-      bf16x8_t af[4], bfr[NB];
-#pragma unroll
-      for (int b = 0; b < 4; ++b)
-        af[b] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(ra[0][b], ra[1][b], 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-      for (int b = 0; b < NB; ++b)
-        bfr[b] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(rb[0][b], rb[1][b], 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mb], bfr[nb], acc[mb][nb], 0, 0, 0);
-    }
+    const int slot = st % SLOTS;
+    if (st == 0) read_slice(slot, 0, pa, pb);
+    __builtin_amdgcn_sched_barrier(0);
+    read_slice(slot, 1, qa, qb);
+    mfma_slice(pa, pb);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
+    read_slice(slot + 1 == SLOTS ? 0 : slot + 1, 0, pa, pb);
+    mfma_slice(qa, qb);
+    interleave();
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   if (idle) return;
