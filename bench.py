@@ -47,7 +47,7 @@ PEAK_HBM_GBS = 8000.0
 # null once hessian.hip changes.
 HESSIAN_TRAFFIC = {
     "bytes": 6567341205,
-    "source_sha256": "339095467c2e1eb940d7a352fd9c0db169fda8f3f680d70caf630746986cbc68",
+    "source_sha256": "1bb0fc52d0a4bfe86db77c89b69bbab173366867a7aa8cfedac7d90131647508",
     "profile": "profiles/k_hessian_dma_c2_hbm_traffic.md",
 }
 HESSIAN_SRC = os.path.join(ROOT, "post_weight_quantization_28_amd", "csrc", "hessian.hip")

@@ -7,15 +7,16 @@
 //
 // Design (MI355X):
 //  * Only output tiles on or above the diagonal are computed (symmetry).
-//  * 256x256 output tile per workgroup of 4 waves (2x2), each wave a 128x128
-//    block = 4x4 v_mfma_f32_32x32x16_bf16 accumulators (256 fp32 per lane,
-//    held in AGPRs).
+//  * 256x256 output tile per workgroup, accumulated by
+//    v_mfma_f32_32x32x16_bf16.
 //  * X is row-major (tokens x channels) while MFMA wants 8 consecutive
 //    tokens of one channel per lane. For 16-byte aligned X the tile streams
 //    through a 4-deep LDS ring filled by LDS-DMA in X's own layout and read
-//    with gfx950's transposing LDS reads (k_hessian_dma below). Other X
-//    (odd row stride) takes k_hessian_bf16: 16-byte register loads of
-//    8x8 blocks transposed with v_perm_b32 into a [channel][token] LDS layout.
+//    with gfx950's transposing LDS reads (k_hessian_dma below: 8 waves, each
+//    a 128x64 block of 4x2 accumulators, 128 fp32 per lane). Other X (odd
+//    row stride) takes k_hessian_bf16: 4 waves, each a 128x128 block (256
+//    fp32 per lane, held in AGPRs), fed by 16-byte register loads of 8x8
+//    blocks transposed with v_perm_b32 into a [channel][token] LDS layout.
 //  * The token range is split into chunks; each chunk writes an fp32 partial
 //    Gram matrix and a second kernel sums the partials in a fixed order,
 //    scales by 2, adds to H and mirrors it: deterministic, exactly
