@@ -94,8 +94,10 @@ hipError_t launch_syrk_f32(hipStream_t s, const GemmArgs& g);
 // ---- syrk.hip
 // Lower tiles of C (N x N, ldc) -= A A^T for fp32 A (N x K, lda) on the bf16
 // matrix cores at fp32 accuracy (three bf16 pieces per value, six piece
-// products). `pieces` is scratch of 3 N K bf16 (16-byte aligned).
+// products). `pieces` is scratch of syrk_x6_pieces(N, K) bf16 (16-byte
+// aligned): the pieces of N rows rounded up to a whole 128-row block.
 bool syrk_x6_ok(int64_t N, int64_t K, int64_t lda, const float* A, int64_t ldc, const float* C);
+int64_t syrk_x6_pieces(int64_t N, int64_t K);
 hipError_t launch_syrk_x6(hipStream_t s, const float* A, int64_t lda, float* C, int64_t ldc, int64_t N,
                           int64_t K, uint16_t* pieces);
 // U = X with both indices reversed; if hi is non-null, also U's split-bf16

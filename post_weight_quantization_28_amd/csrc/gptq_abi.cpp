@@ -150,7 +150,7 @@ QLayout q_layout(int64_t d_out, int64_t n, const gptq_params* p) {
   L.codes = c.take((size_t)d_out * p->n_quant);
   L.loss = c.take(sizeof(float) * d_out);
   // the bf16 pieces of a super-panel for the two-level factorisation's product
-  L.Sp = c.take(n >= kTwoLevelMinN ? 3 * sizeof(uint16_t) * n * kSuper : 0);
+  L.Sp = c.take(n >= kTwoLevelMinN ? sizeof(uint16_t) * syrk_x6_pieces(n, kSuper) : 0);
   L.total = c.off;
   return L;
 }

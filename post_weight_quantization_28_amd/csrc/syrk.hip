@@ -27,8 +27,13 @@
 // workgroups share a CU. Both operands are rows of P (k contiguous), read
 // with ds_read_b128; the 16-byte chunk index of row r is XORed with
 // (r / 8) % 2 so 16 consecutive rows of one chunk column cover all banks.
-// The tiles are numbered row by row over the lower triangle and dealt to
-// the XCDs in contiguous runs.
+// The pieces are stored tiled, in exactly the order a stage needs them:
+// for each 128-row block of P and each 16-deep k slice, piece by piece, a
+// 4 KiB block of 128 rows x 32 bytes. Every DMA instruction then reads 1
+// KiB of consecutive memory (row-major P would give 32 rows x 32 bytes,
+// a quarter of a cache line each: the fill took twice as long). The tiles
+// are numbered row by row over the lower triangle and dealt to the XCDs in
+// contiguous runs.
 #include "common.h"
 #include "dma.h"
 
@@ -45,16 +50,21 @@ constexpr int kS6Slots = 3;
 constexpr int kS6Dma = 6;                    // DMA instructions per wave per stage
 
 // ---------------------------------------------------------------- split
-// dst_i[r][c] = piece i of src[r][c] (rows x cols, pitches lds / ldp).
+// The three pieces of src (rows x cols fp32, pitch lds; cols % 16 == 0),
+// tiled: piece i of element (r, k) goes to
+//   dst + (((r / 128) * (cols / 16) + k / 16) * 3 + i) * 2048 + (r % 128) * 16 + k % 16
+// (bf16 elements). Rows rows .. 128 ceil(rows / 128) - 1 are written as zeros.
 __global__ void k_split3(const float* __restrict__ src, int64_t rows, int64_t cols, int64_t lds,
-                         uint16_t* __restrict__ p1, uint16_t* __restrict__ p2, uint16_t* __restrict__ p3,
-                         int64_t ldp) {
+                         uint16_t* __restrict__ dst) {
   const int64_t c4n = cols / 4;
-  const int64_t total = rows * c4n;
+  const int64_t prow = (rows + kS6T - 1) / kS6T * kS6T;
+  const int64_t total = prow * c4n;
+  const int64_t nst = cols / kS6K;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += stride) {
     const int64_t r = q / c4n, c = 4 * (q - r * c4n);
-    const float4 v = *reinterpret_cast<const float4*>(src + r * lds + c);
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (r < rows) v = *reinterpret_cast<const float4*>(src + r * lds + c);
     const float x[4] = {v.x, v.y, v.z, v.w};
     uint16_t h1[4], h2[4], h3[4];
 #pragma unroll
@@ -64,10 +74,11 @@ __global__ void k_split3(const float* __restrict__ src, int64_t rows, int64_t co
       h2[e] = f32_to_bf16_rne(r1);
       h3[e] = f32_to_bf16_rne(r1 - bf16_to_f32(h2[e]));
     }
-    const int64_t o = r * ldp + c;
-    *reinterpret_cast<uint2*>(p1 + o) = make_uint2(h1[0] | ((uint32_t)h1[1] << 16), h1[2] | ((uint32_t)h1[3] << 16));
-    *reinterpret_cast<uint2*>(p2 + o) = make_uint2(h2[0] | ((uint32_t)h2[1] << 16), h2[2] | ((uint32_t)h2[3] << 16));
-    *reinterpret_cast<uint2*>(p3 + o) = make_uint2(h3[0] | ((uint32_t)h3[1] << 16), h3[2] | ((uint32_t)h3[3] << 16));
+    const int64_t blk = ((r / kS6T) * nst + c / kS6K) * 3;
+    const int64_t o = (r % kS6T) * kS6K + c % kS6K;
+    *reinterpret_cast<uint2*>(dst + blk * 2048 + o) = make_uint2(h1[0] | ((uint32_t)h1[1] << 16), h1[2] | ((uint32_t)h1[3] << 16));
+    *reinterpret_cast<uint2*>(dst + (blk + 1) * 2048 + o) = make_uint2(h2[0] | ((uint32_t)h2[1] << 16), h2[2] | ((uint32_t)h2[3] << 16));
+    *reinterpret_cast<uint2*>(dst + (blk + 2) * 2048 + o) = make_uint2(h3[0] | ((uint32_t)h3[1] << 16), h3[2] | ((uint32_t)h3[3] << 16));
   }
 }
 
@@ -81,8 +92,7 @@ __device__ __forceinline__ void s6_wait_barrier(int stages) {
 
 struct Syrk6Args {
   int64_t N, K;                       // C is N x N (lower tiles), P is N x K
-  const uint16_t *P1, *P2, *P3;       // pieces, row pitch ldp
-  int64_t ldp;
+  const uint16_t* Pt;                 // the pieces, tiled as k_split3 writes them
   float* C; int64_t ldc;
 };
 
@@ -107,35 +117,36 @@ __global__ void __launch_bounds__(256, 2) k_syrk_x6(Syrk6Args g, int ntile) {
   const int wm = wave >> 1, wn = wave & 1;
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(sm));
 
-  // buffers over rows [m0, N) and [n0, N) of each piece: rows past N read as zeros
-  const int64_t bm = (g.N - m0) * g.ldp * 2, bn = (g.N - n0) * g.ldp * 2;
-  const v4i32_t r01 = make_rsrc(g.P1 + m0 * g.ldp, bm), r02 = make_rsrc(g.P2 + m0 * g.ldp, bm),
-                r03 = make_rsrc(g.P3 + m0 * g.ldp, bm);
-  const v4i32_t r11 = make_rsrc(g.P1 + n0 * g.ldp, bn), r12 = make_rsrc(g.P2 + n0 * g.ldp, bn),
-                r13 = make_rsrc(g.P3 + n0 * g.ldp, bn);
+  // one buffer per operand over its 128-row block of the tiled pieces
+  // (stage st, piece i at byte (3 st + i) * 4096; rows past N were written
+  // as zeros)
+  const int64_t nst = g.K / kS6K;
+  const int64_t blk_bytes = nst * 3 * kS6Piece;
+  const v4i32_t rA = make_rsrc(g.Pt + (int64_t)tm * (blk_bytes / 2), blk_bytes);
+  const v4i32_t rB = make_rsrc(g.Pt + (int64_t)tn * (blk_bytes / 2), blk_bytes);
   // DMA plan: instruction idx = 6 wave + q (0..23): operand op = idx / 12
   // (0: the tile's rows, 1: its columns), piece (idx % 12) / 4, rows 32 p ..
   // 32 p + 31 with p = idx % 4; lane l fills row 32 p + l / 2, LDS chunk l % 2,
-  // which holds global chunk (l % 2) ^ swz(row)
+  // which holds global chunk (l % 2) ^ swz(row): 1 KiB of consecutive memory
+  // per instruction
   uint32_t voff[kS6Dma];
 #pragma unroll
   for (int q = 0; q < kS6Dma; ++q) {
     const int idx = kS6Dma * wave + q;
+    const int piece = (idx % 12) >> 2;
     const int r = 32 * (idx & 3) + (lane >> 1);
     const int c = (lane & 1) ^ s6_swz(r);
-    voff[q] = (uint32_t)((r * g.ldp + 8 * c) * 2);
+    voff[q] = (uint32_t)(piece * kS6Piece + r * 32 + 16 * c);
   }
   auto issue = [&](int st, int slot) {
-    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)(st * kS6K * 2));
+    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)(st * 3 * kS6Piece));
 #pragma unroll
     for (int q = 0; q < kS6Dma; ++q) {
       const int idx = kS6Dma * wave + q;
       const int op = idx / 12, piece = (idx % 12) >> 2;   // wave-uniform
       const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + slot * kS6Slot + (op * 3 + piece) * kS6Piece +
                                                           (idx & 3) * 1024);
-      const v4i32_t r = op == 0 ? (piece == 0 ? r01 : piece == 1 ? r02 : r03)
-                                : (piece == 0 ? r11 : piece == 1 ? r12 : r13);
-      dma16_rsrc(voff[q], r, soff, dst);
+      dma16_rsrc(voff[q], op == 0 ? rA : rB, soff, dst);
     }
   };
 
@@ -227,25 +238,24 @@ __global__ void __launch_bounds__(256, 2) k_syrk_x6(Syrk6Args g, int ntile) {
 
 bool syrk_x6_ok(int64_t N, int64_t K, int64_t lda, const float* A, int64_t ldc, const float* C) {
   return N > 0 && K > 0 && K % kS6K == 0 && lda % 4 == 0 && ((uintptr_t)A & 15) == 0 && ldc > 0 &&
-         C != nullptr && N * K * 2 < ((int64_t)1 << 31) && N * (N + 1) / 2 / (kS6T * kS6T) < ((int64_t)1 << 28);
+         C != nullptr && kS6T * K * 6 < ((int64_t)1 << 31) && N * (N + 1) / 2 / (kS6T * kS6T) < ((int64_t)1 << 28);
 }
+
+int64_t syrk_x6_pieces(int64_t N, int64_t K) { return 3 * ((N + kS6T - 1) / kS6T * kS6T) * K; }
 
 hipError_t launch_syrk_x6(hipStream_t s, const float* A, int64_t lda, float* C, int64_t ldc, int64_t N,
                           int64_t K, uint16_t* pieces) {
   if (N <= 0) return hipSuccess;
   if (!syrk_x6_ok(N, K, lda, A, ldc, C) || !pieces || ((uintptr_t)pieces & 15) != 0) return hipErrorInvalidValue;
-  uint16_t* p1 = pieces;
-  uint16_t* p2 = pieces + N * K;
-  uint16_t* p3 = pieces + 2 * N * K;
   {
-    int64_t blocks = ceil_div(N * (K / 4), 256);
+    int64_t blocks = ceil_div(ceil_div(N, kS6T) * kS6T * (K / 4), 256);
     if (blocks > 16384) blocks = 16384;
-    hipLaunchKernelGGL(k_split3, dim3((unsigned)blocks), dim3(256), 0, s, A, N, K, lda, p1, p2, p3, K);
+    hipLaunchKernelGGL(k_split3, dim3((unsigned)blocks), dim3(256), 0, s, A, N, K, lda, pieces);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   Syrk6Args g{};
-  g.N = N; g.K = K; g.P1 = p1; g.P2 = p2; g.P3 = p3; g.ldp = K; g.C = C; g.ldc = ldc;
+  g.N = N; g.K = K; g.Pt = pieces; g.C = C; g.ldc = ldc;
   const int64_t nt = ceil_div(N, kS6T);
   const int64_t ntile = nt * (nt + 1) / 2;
   hipLaunchKernelGGL(k_syrk_x6, dim3((unsigned)(8 * ((ntile + 7) / 8))), dim3(256), 0, s, g, (int)ntile);
