@@ -56,13 +56,18 @@ constexpr int kS6Dma = 6;                    // DMA instructions per wave per st
 // (bf16 elements). Rows rows .. 128 ceil(rows / 128) - 1 are written as zeros.
 __global__ void k_split3(const float* __restrict__ src, int64_t rows, int64_t cols, int64_t lds,
                          uint16_t* __restrict__ dst) {
-  const int64_t c4n = cols / 4;
+  // thread q takes 4 consecutive k of one row, in the order of the tiled
+  // output (block (r / 128, k / 16), then row, then the 4-k group), so a
+  // wave writes 512 consecutive bytes of each piece and reads 64 bytes of
+  // each of its 16 rows
   const int64_t prow = (rows + kS6T - 1) / kS6T * kS6T;
-  const int64_t total = prow * c4n;
   const int64_t nst = cols / kS6K;
+  const int64_t total = prow * (cols / 4);
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += stride) {
-    const int64_t r = q / c4n, c = 4 * (q - r * c4n);
+    const int64_t b = q >> 9, w = q & 511;            // 512 groups of 4 per (block, stage)
+    const int64_t tr = b / nst, stg = b - tr * nst;
+    const int64_t r = tr * kS6T + (w >> 2), c = stg * kS6K + 4 * (w & 3);
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
     if (r < rows) v = *reinterpret_cast<const float4*>(src + r * lds + c);
     const float x[4] = {v.x, v.y, v.z, v.w};
