@@ -144,10 +144,25 @@ inline BandTiles band_tiles(int64_t M, int64_t N, int lower_only, int64_t lower_
 hipError_t launch_slab_leaf(hipStream_t s, const SlabArgs& g, const LeafTask& lt);
 
 // ---- trail.hip
+// E's split-bf16 parts (the far field's A operand) are stored tiled, in the
+// order the far field's LDS stages hold them: for each block of kEhRows rows
+// and each 16-column slice of the ld columns, a kEhRows x 16 block (8 KiB),
+// row-major. Element (row, col) of a tiled matrix with ld columns (ld a
+// multiple of 16) is at eh_index(row, col, ld); the last row block is
+// allocated whole.
+constexpr int64_t kEhRows = 256;
+__host__ __device__ inline int64_t eh_index(int64_t row, int64_t col, int64_t ld) {
+  return ((row / kEhRows) * (ld / 16) + col / 16) * (kEhRows * 16) + (row % kEhRows) * 16 + col % 16;
+}
+__host__ __device__ inline int64_t eh_elems(int64_t rows, int64_t ld) {
+  return (rows + kEhRows - 1) / kEhRows * kEhRows * ld;
+}
+
 // C[M x N] -= (Ahi + Alo)(Bhi + Blo) without the lo*lo term: split-bf16
-// products, fp32 accumulation. A is M x K (row-major, lda), B is K x N
-// (row-major, ldb), all bf16 bits. Requires lda, ldb, N and K multiples of 8
-// and 16-byte aligned A/B bases (hipErrorInvalidValue otherwise).
+// products, fp32 accumulation. A is M x K, tiled with lda columns (see
+// eh_index; columns from 0); B is K x N (row-major, ldb), all bf16 bits.
+// Requires lda a multiple of 16, ldb, N and K multiples of 8 and 16-byte
+// aligned A/B bases (hipErrorInvalidValue otherwise).
 struct TrailArgs {
   int64_t M, N, K;
   const uint16_t *Ahi, *Alo; int64_t lda;
@@ -175,10 +190,10 @@ struct SweepArgs {
   // kb = 128, 256 or 384; 0 = none
   const float* Esb; int64_t kb;
   float* row_loss;
-  // if non-null, E's split-bf16 parts are written there (row pitch ldeh,
-  // the same column offsets as E)
+  // if non-null, E's split-bf16 parts are written there, tiled with ldeh
+  // columns (eh_index), this launch's column 0 at column ehcol
   uint16_t *Ehi, *Elo;
-  int64_t ldeh;
+  int64_t ldeh, ehcol;
   const DevStatus* st;
 };
 hipError_t launch_sweep(hipStream_t s, const SweepArgs& a);

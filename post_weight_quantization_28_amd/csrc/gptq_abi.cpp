@@ -143,8 +143,8 @@ QLayout q_layout(int64_t d_out, int64_t n, const gptq_params* p) {
   L.X = c.take(sizeof(float) * n * n);
   L.Wf = c.take(sizeof(float) * d_out * n);
   L.E = c.take(sizeof(float) * d_out * ew);
-  L.Ehi = c.take(two ? sizeof(uint16_t) * d_out * ewh : 0);
-  L.Elo = c.take(two ? sizeof(uint16_t) * d_out * ewh : 0);
+  L.Ehi = c.take(two ? sizeof(uint16_t) * eh_elems(d_out, ewh) : 0);
+  L.Elo = c.take(two ? sizeof(uint16_t) * eh_elems(d_out, ewh) : 0);
   L.Uhi = c.take(two ? sizeof(uint16_t) * n * n : 0);
   L.Ulo = c.take(two ? sizeof(uint16_t) * n * n : 0);
   L.codes = c.take((size_t)d_out * p->n_quant);
@@ -687,9 +687,10 @@ gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int
       a.scales = out->scales; a.zeros = out->zeros; a.ngroups = nq / p->group;
       a.codes = codes; a.n_quant = nq; a.E = E; a.lde = sw; a.row_loss = loss; a.st = dst;
       a.Esb = E; a.kb = 0;
-      a.Ehi = s1 < n ? Ehi + eoff : nullptr;
-      a.Elo = s1 < n ? Elo + eoff : nullptr;
+      a.Ehi = s1 < n ? Ehi : nullptr;
+      a.Elo = s1 < n ? Elo : nullptr;
       a.ldeh = ldeh;
+      a.ehcol = eoff;
       Timed ph(GPTQ_PROF_SWEEP, s, 2);
       HIP_TRY(launch_sweep_super(s, a), "sweep");
     }
@@ -707,9 +708,10 @@ gptq_status gptq_quantize_layer(void* stream, const void* W, gptq_dtype wdt, int
       a.scales = out->scales; a.zeros = out->zeros; a.ngroups = nq / p->group;
       a.codes = codes; a.n_quant = nq; a.E = Eb; a.lde = sw; a.row_loss = loss; a.st = dst;
       a.Esb = E; a.kb = fused ? i0 - s0 : 0;
-      a.Ehi = two && s1 < n ? Ehi + eoff + (i0 - s0) : nullptr;
-      a.Elo = two && s1 < n ? Elo + eoff + (i0 - s0) : nullptr;
+      a.Ehi = two && s1 < n ? Ehi : nullptr;
+      a.Elo = two && s1 < n ? Elo : nullptr;
       a.ldeh = ldeh;
+      a.ehcol = eoff + (i0 - s0);
       Timed ph(GPTQ_PROF_SWEEP, s, 2);
       HIP_TRY(launch_sweep(s, a), "sweep");
       const int64_t i1 = i0 + nc;

@@ -475,8 +475,9 @@ k_sweep(SweepArgs a) {
       a.E[row * a.lde + col] = S.ev[c];
       if (a.Ehi) {
         const uint16_t h = f32_to_bf16_rne(S.ev[c]);
-        a.Ehi[row * a.ldeh + col] = h;
-        a.Elo[row * a.ldeh + col] = f32_to_bf16_rne(S.ev[c] - bf16_to_f32(h));
+        const int64_t o = eh_index(row, a.ehcol + col, a.ldeh);
+        a.Ehi[o] = h;
+        a.Elo[o] = f32_to_bf16_rne(S.ev[c] - bf16_to_f32(h));
       }
     }
     if (L == 0) a.row_loss[row] = loss0 + loss;
@@ -596,8 +597,9 @@ k_sweep_sb(SweepArgs a) {
         Eb[row * a.lde + col] = S.ev[c];
         if (a.Ehi) {
           const uint16_t h = f32_to_bf16_rne(S.ev[c]);
-          a.Ehi[row * a.ldeh + ab.kb + col] = h;
-          a.Elo[row * a.ldeh + ab.kb + col] = f32_to_bf16_rne(S.ev[c] - bf16_to_f32(h));
+          const int64_t o = eh_index(row, a.ehcol + ab.kb + col, a.ldeh);
+          a.Ehi[o] = h;
+          a.Elo[o] = f32_to_bf16_rne(S.ev[c] - bf16_to_f32(h));
         }
       }
     }

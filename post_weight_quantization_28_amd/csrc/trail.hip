@@ -17,13 +17,17 @@
 // of 16-deep stages (24 KiB each) filled by buffer LDS-DMA, so a workgroup
 // needs 72 KiB and two independent workgroups share a CU: one's barrier and
 // DMA waits are covered by the other's MFMAs. A_hi, A_lo are stored
-// [row][k] (32-byte rows, 16-byte chunk index XOR-swizzled with (row / 8) %
-// 2) and read with ds_read_b128; B_hi, B_lo as [k][column] (256-byte rows,
-// swizzled like the Hessian tile) and read with transposing
-// ds_read_b64_tr_b16. The buffer descriptors end at the last row of A and at
-// row K of B, so rows past M and k past K read as zeros; B chunks past N get
-// an offset outside the buffer. Each wave issues 6 of the 24 DMA
-// instructions of a stage.
+// [row][k] in LDS (32-byte rows, 16-byte chunk index XOR-swizzled with (row
+// / 8) % 2) and read with ds_read_b128; B_hi, B_lo as [k][column] (256-byte
+// rows, swizzled like the Hessian tile) and read with transposing
+// ds_read_b64_tr_b16. In memory A is tiled (eh_index: 256 rows x 16 k per
+// 8 KiB block), so a stage of A is one consecutive 8 KiB block and every
+// DMA instruction reads 1 KiB of consecutive memory (row-major A gave 32
+// rows x 32 bytes per instruction, a quarter of a cache line each). The
+// last row block's rows past M hold anything; an output row depends only
+// on its own A row, and rows past M are not stored. B's descriptor ends at
+// row K, so k past K reads as zeros; B chunks past N get an offset outside
+// the buffer. Each wave issues 6 of the 24 DMA instructions of a stage.
 #include "common.h"
 #include "dma.h"
 
@@ -70,15 +74,18 @@ k_trail_x3(TrailArgs g) {
   const int wm = wave >> 1, wn = wave & 1;
   const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(sm));
 
-  // buffers: A rows [m0, M), B rows [0, K) from column n0 on
-  const v4i32_t rAh = make_rsrc(g.Ahi + m0 * g.lda, (g.M - m0) * g.lda * 2);
-  const v4i32_t rAl = make_rsrc(g.Alo + m0 * g.lda, (g.M - m0) * g.lda * 2);
+  // buffers: A's 256-row block of this tile (all lda / 16 slices), B rows
+  // [0, K) from column n0 on
+  const int64_t ablk = g.lda / 16 * (kTM * kTK);   // elements of one row block
+  const v4i32_t rAh = make_rsrc(g.Ahi + tm * ablk, ablk * 2);
+  const v4i32_t rAl = make_rsrc(g.Alo + tm * ablk, ablk * 2);
   const int64_t bbytes = ((g.K - 1) * g.ldb + (g.N - n0)) * 2;
   const v4i32_t rBh = make_rsrc(g.Bhi + n0, bbytes);
   const v4i32_t rBl = make_rsrc(g.Blo + n0, bbytes);
 
   // DMA plan: instruction idx = 6 w + q, q = 0..5:
   //   0..7 A_hi, 8..15 A_lo: rows 32p .. 32p+31, 2 chunks of 8 k each
+  //     (1 KiB of consecutive memory in the stage's 8 KiB block)
   //   16..19 B_hi, 20..23 B_lo: k rows 4p .. 4p+3, 16 chunks of 8 columns
   uint32_t voff[kTDma];
 #pragma unroll
@@ -88,7 +95,7 @@ k_trail_x3(TrailArgs g) {
       const int p = idx & 7;
       const int r = 32 * p + (lane >> 1);
       const int c = (lane & 1) ^ swz_a(r);
-      voff[q] = (uint32_t)((r * g.lda + 8 * c) * 2);
+      voff[q] = (uint32_t)(r * 32 + 16 * c);
     } else {
       const int p = idx & 3;
       const int kr = 4 * p + (lane >> 4);
@@ -97,7 +104,7 @@ k_trail_x3(TrailArgs g) {
     }
   }
   auto issue = [&](int st, int slot) {
-    const uint32_t sa = __builtin_amdgcn_readfirstlane((uint32_t)(st * kTK * 2));
+    const uint32_t sa = __builtin_amdgcn_readfirstlane((uint32_t)(st * kTA));
     const uint32_t sb = __builtin_amdgcn_readfirstlane((uint32_t)(st * kTK * g.ldb * 2));
 #pragma unroll
     for (int q = 0; q < kTDma; ++q) {
@@ -237,11 +244,11 @@ hipError_t launch_trail_x3(hipStream_t s, const TrailArgs& g) {
   if (g.M <= 0 || g.N <= 0 || g.K <= 0) return hipSuccess;
   // 16-byte DMA chunks: rows of A and B, and the column origin of B, must be
   // 8-element aligned, and N a multiple of 8 (a chunk never straddles N)
-  if ((g.lda % 8) || (g.ldb % 8) || (g.N % 8) || (g.K % 8) || ((uintptr_t)g.Ahi % 16) ||
+  if ((g.lda % 16) || g.K > g.lda || (g.ldb % 8) || (g.N % 8) || (g.K % 8) || ((uintptr_t)g.Ahi % 16) ||
       ((uintptr_t)g.Alo % 16) || ((uintptr_t)g.Bhi % 16) || ((uintptr_t)g.Blo % 16))
     return hipErrorInvalidValue;
   // 32-bit buffer offsets
-  if (g.M * g.lda * 2 >= ((int64_t)1 << 31) || g.K * g.ldb * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  if (g.lda * kTM * 2 >= ((int64_t)1 << 31) || g.K * g.ldb * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const int64_t tiles = ceil_div(g.M, kTM) * ceil_div(g.N, kTN);
   hipLaunchKernelGGL(k_trail_x3, dim3((unsigned)(8 * ceil_div(tiles, 8))), dim3(256), 0, s, g);
   return hipGetLastError();
