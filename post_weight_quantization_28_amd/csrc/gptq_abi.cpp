@@ -125,8 +125,10 @@ constexpr int64_t kSuper = 2048;
 constexpr int64_t kTwoLevelMinN = 6144;
 
 struct QLayout {
-  size_t status, lam, diag, perm, invperm, A, X, Wf, E, Ehi, Elo, Uhi, Ulo, codes, loss, Sp, total;
+  size_t status, lam, diag, perm, invperm, A, X, Wf, E, Ehi, Elo, Uhi, Ulo, codes, loss, Sp, Ip, total;
 };
+
+int64_t inv_x6_pieces(int64_t n);
 
 QLayout q_layout(int64_t d_out, int64_t n, const gptq_params* p) {
   QLayout L{};
@@ -151,6 +153,8 @@ QLayout q_layout(int64_t d_out, int64_t n, const gptq_params* p) {
   L.loss = c.take(sizeof(float) * d_out);
   // the bf16 pieces of a super-panel for the two-level factorisation's product
   L.Sp = c.take(n >= kTwoLevelMinN ? sizeof(uint16_t) * syrk_x6_pieces(n, kSuper) : 0);
+  // the bf16 pieces of the inverse's largest six-product block product
+  L.Ip = c.take(sizeof(uint16_t) * inv_x6_pieces(n));
   L.total = c.off;
   return L;
 }
@@ -221,8 +225,43 @@ gptq_status check_ws(void* ws, size_t have, size_t need) {
 
 // Right-looking Cholesky of the flipped matrix A with the inverse X = L^{-1}
 // carried along (see factor.hip): two launches per 64-column panel.
+// Phase 2's block products go to the six-product bf16 kernels (fp32
+// accuracy, see syrk.hip) for the pairs of blocks of h >= kInvX6MinH rows
+// whose first product has at least 1024 tiles of 128 x 128, i.e. two rounds
+// of two workgroups per CU. Smaller ones stay on the fp32 MFMA GEMM: with
+// one 128 x 128 workgroup per CU and K ranges up to 2048 a lone tile's
+// stage chain is slower than the fp32 kernel's four 64 x 64 tiles per CU
+// (measured: factorisation of a 4096-wide matrix 1.76 ms with the fp32
+// products, 1.84 with its 2048-row level on the six-product kernels;
+// 11008 wide 11.18 -> 10.20 ms and 28672 wide 128.0 -> 108.0 ms with the
+// levels of 1024 or more tiles moved to them).
+constexpr int64_t kInvX6MinH = 1024;
+constexpr int64_t kInvX6MinTiles = 1024;
+bool inv_x6(int64_t h, int64_t hj, int64_t batch) {
+  return h >= kInvX6MinH && ceil_div(h, 128) * ceil_div(hj, 128) * batch >= kInvX6MinTiles;
+}
+
+// Scratch for the pieces of the largest such product (bf16 elements).
+int64_t inv_x6_pieces(int64_t n) {
+  int64_t need = 0;
+  for (int64_t h = kLeaf; h < n; h *= 2) {
+    const int64_t full = n / (2 * h);
+    const int64_t bp_last = full * 2 * h + h;
+    const int64_t hj_last = bp_last < n ? n - bp_last : 0;
+    auto take = [&](int64_t hj, int64_t batch) {
+      if (batch <= 0 || hj <= 0 || !inv_x6(h, hj, batch)) return;
+      need = std::max(need, batch * (x6_op_elems(h, h) + x6_op_elems(hj, h)));
+      need = std::max(need, batch * (x6_op_elems(hj, hj) + x6_op_elems(h, hj)));
+    };
+    take(h, full);
+    take(hj_last, 1);
+  }
+  return need;
+}
+
 hipError_t factor_panels(hipStream_t s, float* A, float* X, int64_t n, const int32_t* perm,
-                         DevStatus* st, uint16_t* pieces) {
+                         DevStatus* st, uint16_t* pieces,
+                         uint16_t* ipieces) {
   hipError_t e;
   const int64_t S = n >= kTwoLevelMinN ? kSuper : n;
   // ---- phase 1: Cholesky, leaves write D = L11^{-1} into X's diagonal
@@ -297,6 +336,31 @@ hipError_t factor_panels(hipStream_t s, float* A, float* X, int64_t n, const int
     GemmArgs f1{}, f2{}, p1{}, p2{};
     if (full > 0) gemms(0, h, (int)full, f1, f2);
     if (hj_last > 0) gemms(full * 2 * h, hj_last, 1, p1, p2);
+    const bool x6f = ipieces && full > 0 && inv_x6(h, h, full);
+    const bool x6p = ipieces && hj_last > 0 && inv_x6(h, hj_last, 1);
+    if (x6f || x6p) {
+      // the same two products per pair, each operand split into its pieces
+      // first: g1's A is X_ii read down its columns (X_ii^T), its B the rows
+      // of L_ji; g2's A the rows of X_jj, its B the rows of T^T
+      auto x6 = [&](const GemmArgs& g1, const GemmArgs& g2) -> hipError_t {
+        const int bt = std::max(g1.batch, 1);
+        hipError_t r;
+        if ((r = launch_gemm_x6(s, g1.M, g1.N, g1.K, bt, X6Operand{g1.A, g1.lda, g1.sA, 1},
+                                X6Operand{g1.B, g1.ldb, g1.sB, 0}, g1.C, g1.ldc, g1.sC, g1.alpha, g1.kmode,
+                                ipieces)) != hipSuccess)
+          return r;
+        return launch_gemm_x6(s, g2.M, g2.N, g2.K, bt, X6Operand{g2.A, g2.lda, g2.sA, 0},
+                              X6Operand{g2.B, g2.ldb, g2.sB, 0}, g2.C, g2.ldc, g2.sC, g2.alpha, g2.kmode, ipieces);
+      };
+      auto f32 = [&](const GemmArgs& g1, const GemmArgs& g2) -> hipError_t {
+        hipError_t r;
+        if ((r = launch_gemm_pair(s, g1, nullptr)) != hipSuccess) return r;
+        return launch_gemm_pair(s, g2, nullptr);
+      };
+      if (full > 0 && (e = x6f ? x6(f1, f2) : f32(f1, f2)) != hipSuccess) return e;
+      if (hj_last > 0 && (e = x6p ? x6(p1, p2) : f32(p1, p2)) != hipSuccess) return e;
+      continue;
+    }
     const GemmArgs* first1 = full > 0 ? &f1 : &p1;
     const GemmArgs* second1 = (full > 0 && hj_last > 0) ? &p1 : nullptr;
     const GemmArgs* first2 = full > 0 ? &f2 : &p2;
@@ -327,7 +391,8 @@ gptq_status enqueue_factor(hipStream_t s, const float* H, int64_t n, const gptq_
     HIP_TRY(launch_build_flipped(s, H, n, p->act_order ? perm : nullptr, diag, lam, A, st), "build");
   }
   uint16_t* pieces = L.Sp != L.total && n >= kTwoLevelMinN ? reinterpret_cast<uint16_t*>(ws + L.Sp) : nullptr;
-  HIP_TRY(factor_panels(s, A, X, n, perm, st, pieces), "factor");
+  uint16_t* ipieces = L.Ip != L.total ? reinterpret_cast<uint16_t*>(ws + L.Ip) : nullptr;
+  HIP_TRY(factor_panels(s, A, X, n, perm, st, pieces, ipieces), "factor");
   HIP_TRY(launch_rotate(s, X, A, n, Uhi, Ulo), "rotate");
   return GPTQ_OK;
 }

@@ -267,4 +267,231 @@ hipError_t launch_syrk_x6(hipStream_t s, const float* A, int64_t lda, float* C, 
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- general products
+// The triangular inverse's block products (X_ji = -X_jj (L_ji X_ii)) in the
+// same six-product form. Each operand is split once per launch into the
+// tiled piece layout above (128-row blocks, 16-deep k slices, rows past the
+// operand and k past K written as zeros), for a batch of instances; the
+// product kernel then runs the SYRK's stage loop over the k range its tile
+// needs, with each tile's own row block of each operand.
+
+__host__ __device__ int64_t x6_op_elems(int64_t rows, int64_t K) { return 3 * ceil_div(rows, kS6T) * kS6T * ceil_div(K, kS6K) * kS6K; }
+
+struct Split6Args {
+  const float* src; int64_t ld, stride;
+  int64_t R, K;
+  int trans, vec, batch;
+  uint16_t* dst;
+};
+
+// Thread q takes 4 consecutive k of one row of one instance. Untransposed
+// sources are walked as k_split3 walks them (4 threads per row, 16-byte
+// loads when rows are 16-byte aligned); transposed ones with the row index
+// fastest, so that each of a thread's four loads is one consecutive run of
+// the source across the wave.
+__global__ void __launch_bounds__(256) k_split3_op(Split6Args a) {
+  const int64_t nst = ceil_div(a.K, kS6K);
+  const int64_t per = ceil_div(a.R, kS6T) * nst * 512;
+  const int64_t total = per * a.batch;
+  const int64_t out_per = x6_op_elems(a.R, a.K);
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += stride) {
+    const int64_t b = q / per, rem = q - b * per;
+    const int64_t blk = rem >> 9;
+    const int w = (int)(rem & 511);
+    const int64_t tr = blk / nst, stg = blk - tr * nst;
+    const int rr = a.trans ? (w & 127) : (w >> 2);
+    const int kg = a.trans ? (w >> 7) : (w & 3);
+    const int64_t r = tr * kS6T + rr, k = stg * kS6K + 4 * kg;
+    const float* src = a.src + b * a.stride;
+    float x[4];
+    if (!a.trans && a.vec && r < a.R && k + 3 < a.K) {
+      const float4 v = *reinterpret_cast<const float4*>(src + r * a.ld + k);
+      x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t kk = k + e;
+        x[e] = (r < a.R && kk < a.K) ? (a.trans ? src[kk * a.ld + r] : src[r * a.ld + kk]) : 0.f;
+      }
+    }
+    uint16_t h1[4], h2[4], h3[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      h1[e] = f32_to_bf16_rne(x[e]);
+      const float r1 = x[e] - bf16_to_f32(h1[e]);
+      h2[e] = f32_to_bf16_rne(r1);
+      h3[e] = f32_to_bf16_rne(r1 - bf16_to_f32(h2[e]));
+    }
+    uint16_t* d = a.dst + b * out_per + blk * 3 * 2048 + rr * kS6K + 4 * kg;
+    *reinterpret_cast<uint2*>(d) = make_uint2(h1[0] | ((uint32_t)h1[1] << 16), h1[2] | ((uint32_t)h1[3] << 16));
+    *reinterpret_cast<uint2*>(d + 2048) = make_uint2(h2[0] | ((uint32_t)h2[1] << 16), h2[2] | ((uint32_t)h2[3] << 16));
+    *reinterpret_cast<uint2*>(d + 4096) = make_uint2(h3[0] | ((uint32_t)h3[1] << 16), h3[2] | ((uint32_t)h3[3] << 16));
+  }
+}
+
+struct Gemm6Args {
+  int64_t M, N, K;
+  const uint16_t* Ap; const uint16_t* Bp;   // pieces: M rows of A, N rows of B, per instance
+  float* C; int64_t ldc, sC;
+  float alpha;
+  int kmode, batch, ntm, ntn;
+};
+
+// One 128 x 128 tile of one instance per workgroup (the SYRK's layout and
+// stage loop). Tiles are numbered row tile by row tile across the batch,
+// the longest k ranges first.
+__global__ void __launch_bounds__(256, 2) k_gemm_x6(Gemm6Args g) {
+  __shared__ __align__(16) uint8_t sm[kS6Slots * kS6Slot];
+  const int per_row = g.batch * g.ntn;
+  const int t = (int)blockIdx.x;
+  const int tmi = t / per_row, rem = t - tmi * per_row;
+  const int inst = rem / g.ntn, tn = rem - inst * g.ntn;
+  const int tm = g.kmode == 3 ? g.ntm - 1 - tmi : tmi;
+  const int64_t m0 = (int64_t)tm * kS6T, n0 = (int64_t)tn * kS6T;
+  const int64_t nst = ceil_div(g.K, kS6K);
+  int s_lo = 0, s_hi = (int)nst;
+  if (g.kmode == 4) s_lo = (int)(m0 / kS6K);
+  else if (g.kmode == 3) s_hi = (int)ceil_div(min(g.K, m0 + kS6T), kS6K);
+  const int ns = max(s_hi - s_lo, 0);
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(sm));
+
+  const int64_t blk_elems = nst * 3 * (kS6Piece / 2);   // one 128-row block's pieces
+  const uint16_t* pa = g.Ap + (int64_t)inst * ceil_div(g.M, kS6T) * blk_elems + tm * blk_elems;
+  const uint16_t* pb = g.Bp + (int64_t)inst * ceil_div(g.N, kS6T) * blk_elems + tn * blk_elems;
+  const v4i32_t rA = make_rsrc(pa, blk_elems * 2);
+  const v4i32_t rB = make_rsrc(pb, blk_elems * 2);
+  uint32_t voff[kS6Dma];
+#pragma unroll
+  for (int q = 0; q < kS6Dma; ++q) {
+    const int idx = kS6Dma * wave + q;
+    const int piece = (idx % 12) >> 2;
+    const int r = 32 * (idx & 3) + (lane >> 1);
+    const int c = (lane & 1) ^ s6_swz(r);
+    voff[q] = (uint32_t)(piece * kS6Piece + r * 32 + 16 * c);
+  }
+  auto issue = [&](int st, int slot) {
+    const uint32_t soff = __builtin_amdgcn_readfirstlane((uint32_t)(st * 3 * kS6Piece));
+#pragma unroll
+    for (int q = 0; q < kS6Dma; ++q) {
+      const int idx = kS6Dma * wave + q;
+      const int op = idx / 12, piece = (idx % 12) >> 2;
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds0 + slot * kS6Slot + (op * 3 + piece) * kS6Piece +
+                                                          (idx & 3) * 1024);
+      dma16_rsrc(voff[q], op == 0 ? rA : rB, soff, dst);
+    }
+  };
+  uint32_t offA[2], offB[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int ra = 64 * wm + 32 * b + (lane & 31), rb = 64 * wn + 32 * b + (lane & 31);
+    offA[b] = ra * 32 + (((lane >> 5) ^ s6_swz(ra)) * 16);
+    offB[b] = 3 * kS6Piece + rb * 32 + (((lane >> 5) ^ s6_swz(rb)) * 16);
+  }
+
+  s6_f32x16_t acc[2][2], tot[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        acc[a][b][r] = 0.f;
+        tot[a][b][r] = 0.f;
+      }
+  auto fold = [&]() {
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          tot[a][b][r] += acc[a][b][r];
+          acc[a][b][r] = 0.f;
+        }
+  };
+
+#pragma unroll
+  for (int ps = 0; ps < kS6Slots - 1; ++ps)
+    if (ps < ns) issue(s_lo + ps, ps);
+  for (int i = 0; i < ns; ++i) {
+    s6_wait_barrier(min(kS6Slots - 2, ns - 1 - i));
+    if (i + kS6Slots - 1 < ns) issue(s_lo + i + kS6Slots - 1, (i + kS6Slots - 1) % kS6Slots);
+    const uint32_t sbase = lds0 + (uint32_t)(i % kS6Slots) * kS6Slot;
+    s6_bf16x8_t fa[2][3], fb[2][3];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        fa[b][p] = s6_frag(sbase + p * kS6Piece + offA[b]);
+        fb[b][p] = s6_frag(sbase + p * kS6Piece + offB[b]);
+      }
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a][2], fb[b][0], acc[a][b], 0, 0, 0);
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a][0], fb[b][2], acc[a][b], 0, 0, 0);
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a][1], fb[b][1], acc[a][b], 0, 0, 0);
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a][1], fb[b][0], acc[a][b], 0, 0, 0);
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a][0], fb[b][1], acc[a][b], 0, 0, 0);
+        acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[a][0], fb[b][0], acc[a][b], 0, 0, 0);
+      }
+    if (i & 1) fold();
+  }
+  if (ns & 1) fold();
+
+  float* C = g.C + (int64_t)inst * g.sC;
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int64_t j = n0 + 64 * wn + 32 * b + (lane & 31);
+      const int64_t ib = m0 + 64 * wm + 32 * a + 4 * (lane >> 5);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t i = ib + 8 * (r >> 2) + (r & 3);
+        if (i < g.M && j < g.N) C[i * g.ldc + j] = g.alpha * tot[a][b][r];
+      }
+    }
+}
+
+static hipError_t split_op(hipStream_t s, const X6Operand& o, int64_t R, int64_t K, int batch, uint16_t* dst) {
+  Split6Args a{};
+  a.src = o.src; a.ld = o.ld; a.stride = o.stride;
+  a.R = R; a.K = K; a.trans = o.trans; a.batch = batch; a.dst = dst;
+  a.vec = !o.trans && o.ld % 4 == 0 && o.stride % 4 == 0 && ((uintptr_t)o.src & 15) == 0;
+  int64_t blocks = ceil_div(ceil_div(R, kS6T) * ceil_div(K, kS6K) * 512 * batch, 256);
+  if (blocks > 16384) blocks = 16384;
+  hipLaunchKernelGGL(k_split3_op, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_x6(hipStream_t s, int64_t M, int64_t N, int64_t K, int batch, const X6Operand& a,
+                          const X6Operand& b, float* C, int64_t ldc, int64_t sC, float alpha, int kmode,
+                          uint16_t* pieces) {
+  if (M <= 0 || N <= 0 || batch <= 0) return hipSuccess;
+  if (K <= 0 || !pieces || ((uintptr_t)pieces & 15) != 0 || !(kmode == 0 || kmode == 3 || kmode == 4))
+    return hipErrorInvalidValue;
+  const int64_t ntm = ceil_div(M, kS6T), ntn = ceil_div(N, kS6T);
+  const int64_t tiles = ntm * ntn * batch;
+  // buffer sizes and stage offsets are 32-bit
+  if (tiles >= ((int64_t)1 << 31) || ceil_div(K, kS6K) * 3 * kS6Piece >= ((int64_t)1 << 31))
+    return hipErrorInvalidValue;
+  uint16_t* pa = pieces;
+  uint16_t* pb = pieces + x6_op_elems(M, K) * batch;
+  hipError_t e;
+  if ((e = split_op(s, a, M, K, batch, pa)) != hipSuccess) return e;
+  if ((e = split_op(s, b, N, K, batch, pb)) != hipSuccess) return e;
+  Gemm6Args g{};
+  g.M = M; g.N = N; g.K = K; g.Ap = pa; g.Bp = pb;
+  g.C = C; g.ldc = ldc; g.sC = sC; g.alpha = alpha;
+  g.kmode = kmode; g.batch = batch; g.ntm = (int)ntm; g.ntn = (int)ntn;
+  hipLaunchKernelGGL(k_gemm_x6, dim3((unsigned)tiles), dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
 }  // namespace gq

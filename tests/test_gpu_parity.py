@@ -64,13 +64,17 @@ def test_hessian_streaming_accumulates():
 # ---------------------------------------------------------------- factorisation
 # n = 202: rows not a multiple of 4 floats, so the trailing updates and the
 # flipped-matrix build take their general (unvectorised) kernels
-# n >= 6144: the two-level factorisation (256-column super-panels, the last
+# n >= 6144: the two-level factorisation (2048-column super-panels, the last
 # one partial; n = 6150 also has a last panel of 6 columns and rows that are
 # not a multiple of 4 floats)
+# n = 10246: the inverse's block products with 1024 or more output tiles run
+# on the six-product bf16 kernels: the pair of 4096-row blocks, and the
+# partial pair of 8192 and 2054 rows (k not a multiple of 16, rows not a
+# multiple of 128); the last panel has 6 columns
 @pytest.mark.parametrize("n,act_order", [(64, False), (200, False), (202, False), (320, True), (1000, False),
-                                         (6208, False), (6150, True)])
+                                         (4096, False), (6208, False), (6150, True), (10246, True)])
 def test_factor_matches_lapack(n, act_order):
-    wl = synth.make_workload("c2", d_out=4, n=n, T=4 * n, group=4)
+    wl = synth.make_workload("c2", d_out=4, n=n, T=4 * n if n <= 6208 else n + 512, group=4)
     H64 = O.hessian(wl.X)
     H32 = H64.astype(np.float32)
     U, perm = G.factor_hinv(torch.from_numpy(H32).cuda(), damp=0.01, act_order=act_order)
