@@ -223,8 +223,6 @@ gptq_status check_ws(void* ws, size_t have, size_t need) {
 // matrices keep one level: their late panels are bound by the leaf chain,
 // and the per-super-panel product and leaf launch would only add to it.
 
-// Right-looking Cholesky of the flipped matrix A with the inverse X = L^{-1}
-// carried along (see factor.hip): two launches per 64-column panel.
 // Phase 2's block products go to the six-product bf16 kernels (fp32
 // accuracy, see syrk.hip) for the pairs of blocks of h >= kInvX6MinH rows
 // whose first product has at least 1024 tiles of 128 x 128, i.e. two rounds
@@ -259,6 +257,8 @@ int64_t inv_x6_pieces(int64_t n) {
   return need;
 }
 
+// Right-looking Cholesky of the flipped matrix A with the inverse X = L^{-1}
+// carried along (see factor.hip): two launches per 64-column panel.
 hipError_t factor_panels(hipStream_t s, float* A, float* X, int64_t n, const int32_t* perm,
                          DevStatus* st, uint16_t* pieces,
                          uint16_t* ipieces) {
