@@ -141,8 +141,11 @@ gptq_status gptq_accumulate_hessian(void *stream, const void *X, gptq_dtype xdt,
  * Workspace: gptq_workspace_bytes(d_out, n, p) bytes, 256-byte aligned,
  * owned by the caller, not read before it is written (its contents on entry
  * do not matter). It holds the factorisation (two n x n fp32 matrices and
- * U's split-bf16 parts), the fp32 working weights, one super-block of
- * errors and the processing-order codes.
+ * U's split-bf16 parts; for n >= 6144 also the bf16 pieces of one
+ * 2048-column super-panel, and for the inverse's block products of 1024 or
+ * more output tiles the pieces of the largest one's operands: 2.8 GB at
+ * n = 28672), the fp32 working weights, one super-block of errors and the
+ * processing-order codes.
  * ("GPTQ" (wikiprompt.org), "Enfoque Técnico": the columns are quantized in
  * turn and the columns not yet quantized get the closed-form Optimal Brain
  * Quantization correction, with groups of weights sharing a scale;
