@@ -38,6 +38,7 @@ if ROOT not in sys.path:
 METRIC = "GPTQ layer time & quantized weights/s (4096², 4-bit g128); Hessian TFLOP/s"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0
+PEAK_FP32_TFLOPS = 157.3      # MI355X dense fp32 MFMA
 
 # HBM bytes moved by one k_hessian_dma launch on this workload, from two
 # rocprofv3 counter runs of `bench.py --steps 1 --warmup 0 --no-cpu-baseline
@@ -261,6 +262,30 @@ CONFIG_TEXT = {
           "65536x5184 bf16 Student-t(4); 2-bit asymmetric, group 128, block 128, damp 0.01, 5120 columns "
           "quantized, 64 kept in fp32",
 }
+
+
+def inverse_x6_work(n):
+    """(flops, products) of the triangular inverse's block products that run
+    on the six-product bf16 kernel: for every level h of the recursive
+    doubling with h >= 1024 whose first product has at least 1024 output
+    tiles of 128 x 128, each pair (h rows, partner hj rows) costs
+    hj h (h + 1) flop (T^T = X_ii^T L_ji^T, X_ii triangular) plus
+    h hj (hj + 1) flop (X_ji = -X_jj T, X_jj triangular)."""
+    flops, products = 0.0, 0
+    h = 64
+    while h < n:
+        full = n // (2 * h)
+        bp_last = full * 2 * h + h
+        hj_last = n - bp_last if bp_last < n else 0
+        for hj, batch in ((h, full), (hj_last, 1)):
+            if batch <= 0 or hj <= 0 or h < 1024:
+                continue
+            if -(-h // 128) * -(-hj // 128) * batch < 1024:
+                continue
+            flops += batch * (hj * h * (h + 1) + h * hj * (hj + 1))
+            products += 2
+        h *= 2
+    return flops, products
 
 
 def far_field_flops(d_out, n, nq, group, block=128):
@@ -636,12 +661,29 @@ def main():
                             "traffic": hessian_traffic() if cfg == "c2" else None,
                             "work": "T*n*(n+1) flop per launch (upper triangle of 2 X^T X)"}
     else:
-        # H given: the far-field update is the largest part of the layer
-        line["roofline"] = {"bound": "mfma", "kernel": "k_trail_x3", "achieved": ff_tf,
-                            "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                            "frac": ff_tf / PEAK_BF16_TFLOPS if ff_tf else None, "traffic": None,
-                            "work": "sum over super-blocks of 2 d_out K N flop per call (fp32-accurate "
-                                    "product taken as three bf16 products; frac counts one)"}
+        inv_flops, inv_products = inverse_x6_work(n)
+        inv_ms, inv_n = ph["inverse_x6"]
+        if inv_products > 0 and inv_n == inv_products and inv_ms > 0:
+            # H given: the largest kernel is the six-product block product of
+            # the factorisation's triangular inverse (fp32-accurate result
+            # from six bf16 MFMA products per value)
+            inv_tf = inv_flops / (inv_ms / 1e3) / 1e12
+            line["roofline"] = {"bound": "mfma", "kernel": "k_gemm_x6", "achieved": inv_tf,
+                                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": inv_tf / PEAK_BF16_TFLOPS,
+                                "traffic": None,
+                                "frac_six_products": 6 * inv_tf / PEAK_BF16_TFLOPS,
+                                "frac_of_fp32_peak": inv_tf / PEAK_FP32_TFLOPS,
+                                "work": f"{inv_flops:.4e} flop of fp32-accurate triangular block products per "
+                                        f"call over {inv_products} launches, each value taken as six bf16 "
+                                        "piece products; frac counts one product against the bf16 peak, "
+                                        "frac_six_products all six, frac_of_fp32_peak compares the "
+                                        "fp32-accurate rate with the fp32 MFMA peak"}
+        else:
+            line["roofline"] = {"bound": "mfma", "kernel": "k_trail_x3", "achieved": ff_tf,
+                                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                                "frac": ff_tf / PEAK_BF16_TFLOPS if ff_tf else None, "traffic": None,
+                                "work": "sum over super-blocks of 2 d_out K N flop per call (fp32-accurate "
+                                        "product taken as three bf16 products; frac counts one)"}
     if not args.no_peaks:
         line["measured_peaks"] = measured_peaks(dev)
     if not args.no_cpu_baseline:

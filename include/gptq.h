@@ -344,8 +344,12 @@ const char *gptq_last_error(void); /* thread-local detail of the last failure */
  * enable >= 2 also records the phases of quantize_layer: the factorisation
  * (preparation of H included), the W preparation and the final un-permute /
  * pack, every sweep launch (with its near-field update), every far-field
- * update; that adds a few microseconds per launch and is meant for one
- * untimed breakdown pass. enable == 0 stops. gptq_profile_collect
+ * update, and every block product of the factorisation's inverse that runs
+ * on the six-product bf16 kernel (the product alone, not its operand
+ * splits; those products are also inside the factorisation's interval);
+ * that adds a few microseconds per launch and is meant for one untimed
+ * breakdown pass. The arrays given to gptq_profile_collect hold
+ * GPTQ_PROF_NCLASSES entries. enable == 0 stops. gptq_profile_collect
  * synchronises the recorded events and returns, for class c in
  * [0, GPTQ_PROF_NCLASSES), the summed milliseconds and the number of timed
  * intervals, then clears. */
@@ -357,7 +361,8 @@ enum {
   GPTQ_PROF_PREP_FINISH = 4,
   GPTQ_PROF_SWEEP = 5,
   GPTQ_PROF_FARFIELD = 6,
-  GPTQ_PROF_NCLASSES = 7
+  GPTQ_PROF_INVERSE_X6 = 7,
+  GPTQ_PROF_NCLASSES = 8
 };
 gptq_status gptq_profile_enable(int enable);
 gptq_status gptq_profile_collect(double *ms, int64_t *count);

@@ -105,16 +105,18 @@ hipError_t launch_syrk_x6(hipStream_t s, const float* A, int64_t lda, float* C, 
 // (kmode 0: all k; 3: k < m0 + 128; 4: k >= m0, m0 the first row of a
 // 128-row tile: the zero triangles of a triangular operand are skipped).
 // An operand is given as fp32 rows of K values (or, when trans, as K rows of
-// M values read down their columns); x6_split writes its pieces into
-// scratch of x6_op_elems(rows, K) bf16 per instance.
+// M values read down their columns). x6_split writes both operands' pieces
+// into scratch of (x6_op_elems(M, K) + x6_op_elems(N, K)) * batch bf16 at
+// `pieces`; x6_product then reads them there.
 struct X6Operand {
   const float* src; int64_t ld, stride;   // instance b at src + b * stride
   int trans;                              // element (r, k) at src[k * ld + r]
 };
 __host__ __device__ int64_t x6_op_elems(int64_t rows, int64_t K);
-hipError_t launch_gemm_x6(hipStream_t s, int64_t M, int64_t N, int64_t K, int batch, const X6Operand& a,
-                          const X6Operand& b, float* C, int64_t ldc, int64_t sC, float alpha, int kmode,
-                          uint16_t* pieces);
+hipError_t x6_split(hipStream_t s, int64_t M, int64_t N, int64_t K, int batch, const X6Operand& a,
+                    const X6Operand& b, uint16_t* pieces);
+hipError_t x6_product(hipStream_t s, int64_t M, int64_t N, int64_t K, int batch, float* C, int64_t ldc,
+                      int64_t sC, float alpha, int kmode, const uint16_t* pieces);
 // U = X with both indices reversed; if hi is non-null, also U's split-bf16
 // parts hi = bf16(U), lo = bf16(U - hi).
 hipError_t launch_rotate(hipStream_t s, const float* X, float* U, int64_t n, uint16_t* hi = nullptr,

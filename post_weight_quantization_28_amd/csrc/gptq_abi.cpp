@@ -345,12 +345,20 @@ hipError_t factor_panels(hipStream_t s, float* A, float* X, int64_t n, const int
       auto x6 = [&](const GemmArgs& g1, const GemmArgs& g2) -> hipError_t {
         const int bt = std::max(g1.batch, 1);
         hipError_t r;
-        if ((r = launch_gemm_x6(s, g1.M, g1.N, g1.K, bt, X6Operand{g1.A, g1.lda, g1.sA, 1},
-                                X6Operand{g1.B, g1.ldb, g1.sB, 0}, g1.C, g1.ldc, g1.sC, g1.alpha, g1.kmode,
-                                ipieces)) != hipSuccess)
+        if ((r = x6_split(s, g1.M, g1.N, g1.K, bt, X6Operand{g1.A, g1.lda, g1.sA, 1},
+                          X6Operand{g1.B, g1.ldb, g1.sB, 0}, ipieces)) != hipSuccess)
           return r;
-        return launch_gemm_x6(s, g2.M, g2.N, g2.K, bt, X6Operand{g2.A, g2.lda, g2.sA, 0},
-                              X6Operand{g2.B, g2.ldb, g2.sB, 0}, g2.C, g2.ldc, g2.sC, g2.alpha, g2.kmode, ipieces);
+        {
+          Timed t(GPTQ_PROF_INVERSE_X6, s, 2);
+          if ((r = x6_product(s, g1.M, g1.N, g1.K, bt, g1.C, g1.ldc, g1.sC, g1.alpha, g1.kmode, ipieces)) !=
+              hipSuccess)
+            return r;
+        }
+        if ((r = x6_split(s, g2.M, g2.N, g2.K, bt, X6Operand{g2.A, g2.lda, g2.sA, 0},
+                          X6Operand{g2.B, g2.ldb, g2.sB, 0}, ipieces)) != hipSuccess)
+          return r;
+        Timed t(GPTQ_PROF_INVERSE_X6, s, 2);
+        return x6_product(s, g2.M, g2.N, g2.K, bt, g2.C, g2.ldc, g2.sC, g2.alpha, g2.kmode, ipieces);
       };
       auto f32 = [&](const GemmArgs& g1, const GemmArgs& g2) -> hipError_t {
         hipError_t r;

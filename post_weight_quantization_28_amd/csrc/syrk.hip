@@ -470,27 +470,32 @@ static hipError_t split_op(hipStream_t s, const X6Operand& o, int64_t R, int64_t
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_x6(hipStream_t s, int64_t M, int64_t N, int64_t K, int batch, const X6Operand& a,
-                          const X6Operand& b, float* C, int64_t ldc, int64_t sC, float alpha, int kmode,
-                          uint16_t* pieces) {
+static bool x6_args_ok(int64_t M, int64_t N, int64_t K, int batch, const uint16_t* pieces, int kmode) {
+  if (K <= 0 || !pieces || ((uintptr_t)pieces & 15) != 0 || !(kmode == 0 || kmode == 3 || kmode == 4)) return false;
+  // tile count and buffer sizes / stage offsets are 32-bit
+  return ceil_div(M, kS6T) * ceil_div(N, kS6T) * batch < ((int64_t)1 << 31) &&
+         ceil_div(K, kS6K) * 3 * kS6Piece < ((int64_t)1 << 31);
+}
+
+hipError_t x6_split(hipStream_t s, int64_t M, int64_t N, int64_t K, int batch, const X6Operand& a,
+                    const X6Operand& b, uint16_t* pieces) {
   if (M <= 0 || N <= 0 || batch <= 0) return hipSuccess;
-  if (K <= 0 || !pieces || ((uintptr_t)pieces & 15) != 0 || !(kmode == 0 || kmode == 3 || kmode == 4))
-    return hipErrorInvalidValue;
-  const int64_t ntm = ceil_div(M, kS6T), ntn = ceil_div(N, kS6T);
-  const int64_t tiles = ntm * ntn * batch;
-  // buffer sizes and stage offsets are 32-bit
-  if (tiles >= ((int64_t)1 << 31) || ceil_div(K, kS6K) * 3 * kS6Piece >= ((int64_t)1 << 31))
-    return hipErrorInvalidValue;
-  uint16_t* pa = pieces;
-  uint16_t* pb = pieces + x6_op_elems(M, K) * batch;
+  if (!x6_args_ok(M, N, K, batch, pieces, 0)) return hipErrorInvalidValue;
   hipError_t e;
-  if ((e = split_op(s, a, M, K, batch, pa)) != hipSuccess) return e;
-  if ((e = split_op(s, b, N, K, batch, pb)) != hipSuccess) return e;
+  if ((e = split_op(s, a, M, K, batch, pieces)) != hipSuccess) return e;
+  return split_op(s, b, N, K, batch, pieces + x6_op_elems(M, K) * batch);
+}
+
+hipError_t x6_product(hipStream_t s, int64_t M, int64_t N, int64_t K, int batch, float* C, int64_t ldc,
+                      int64_t sC, float alpha, int kmode, const uint16_t* pieces) {
+  if (M <= 0 || N <= 0 || batch <= 0) return hipSuccess;
+  if (!x6_args_ok(M, N, K, batch, pieces, kmode)) return hipErrorInvalidValue;
+  const int64_t ntm = ceil_div(M, kS6T), ntn = ceil_div(N, kS6T);
   Gemm6Args g{};
-  g.M = M; g.N = N; g.K = K; g.Ap = pa; g.Bp = pb;
+  g.M = M; g.N = N; g.K = K; g.Ap = pieces; g.Bp = pieces + x6_op_elems(M, K) * batch;
   g.C = C; g.ldc = ldc; g.sC = sC; g.alpha = alpha;
   g.kmode = kmode; g.batch = batch; g.ntm = (int)ntm; g.ntn = (int)ntn;
-  hipLaunchKernelGGL(k_gemm_x6, dim3((unsigned)tiles), dim3(256), 0, s, g);
+  hipLaunchKernelGGL(k_gemm_x6, dim3((unsigned)(ntm * ntn * batch)), dim3(256), 0, s, g);
   return hipGetLastError();
 }
 

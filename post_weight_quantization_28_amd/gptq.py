@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(_HERE, "libgptq.so")
 
 OK, EINVAL, ENOTPD, ENONFINITE, EHIP, EWORKSPACE = 0, -1, -2, -3, -4, -5
 BF16, F32 = 0, 1
-PROF_CLASSES = ["hessian_syrk", "hessian_reduce", "quantize", "factor", "prep_finish", "sweep", "far_field"]
+PROF_CLASSES = ["hessian_syrk", "hessian_reduce", "quantize", "factor", "prep_finish", "sweep", "far_field",
+                "inverse_x6"]
 
 
 class GPTQError(RuntimeError):
