@@ -399,7 +399,7 @@ gptq_status enqueue_factor(hipStream_t s, const float* H, int64_t n, const gptq_
     HIP_TRY(launch_build_flipped(s, H, n, p->act_order ? perm : nullptr, diag, lam, A, st), "build");
   }
   uint16_t* pieces = L.Sp != L.total && n >= kTwoLevelMinN ? reinterpret_cast<uint16_t*>(ws + L.Sp) : nullptr;
-  uint16_t* ipieces = L.Ip != L.total ? reinterpret_cast<uint16_t*>(ws + L.Ip) : nullptr;
+  uint16_t* ipieces = inv_x6_pieces(n) > 0 ? reinterpret_cast<uint16_t*>(ws + L.Ip) : nullptr;
   HIP_TRY(factor_panels(s, A, X, n, perm, st, pieces, ipieces), "factor");
   HIP_TRY(launch_rotate(s, X, A, n, Uhi, Ulo), "rotate");
   return GPTQ_OK;
