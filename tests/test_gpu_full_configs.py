@@ -196,7 +196,8 @@ C4_ORACLE_ROWS = 1024
 # (margins at most 2.8e-7 steps), identity 0.9974; with the oracle sweeping
 # on the GPU's own U: 8 rows. 0.999 needs a working precision beyond fp32.
 # (Those figures are for the one-level factorisation; with the two-level one
-# of wide matrices all 1024 rows give 0.9963 against 0.9968.)
+# of wide matrices all 1024 rows give 0.9969, 0.9963 with the inverse's
+# block products all in fp32, against 0.9968.)
 C4_MIN_IDENTITY = 0.995
 
 
