@@ -88,6 +88,30 @@ def test_factor_matches_lapack(n, act_order):
     assert err < 5e-6
 
 
+def test_inverse_six_product_launches_are_timed():
+    """The phase pass times every six-product block product of the inverse,
+    and the benchmark's roofline for H-given layers divides its count of
+    flops by exactly those intervals: at n = 10246 the pair of 4096-row
+    blocks and the partial pair of 8192 and 2054 rows, two products each."""
+    import bench
+    n = 10246
+    g = torch.Generator(device="cuda").manual_seed(7)
+    X = torch.randn(n + 256, n, device="cuda", generator=g)
+    H = (X.T @ X) / (n + 256)
+    del X
+    G.profile_enable(True, phases=True)
+    try:
+        G.factor_hinv(H, damp=0.01)
+        prof = G.profile_collect()
+    finally:
+        G.profile_enable(False)
+    flops, products = bench.inverse_x6_work(n)
+    assert products == 4 and flops > 0
+    ms, count = prof["inverse_x6"]
+    say("inverse six-product products", count, "in", ms, "ms")
+    assert count == products and ms > 0
+
+
 # ---------------------------------------------------------------- quantize_layer
 CASES = [
     # name, workload kwargs, param overrides
