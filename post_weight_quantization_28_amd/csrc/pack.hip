@@ -150,10 +150,29 @@ __global__ void k_gidx(const int32_t* __restrict__ invperm, int64_t nq, int grou
 __global__ void __launch_bounds__(256)
 k_finish_lds(const float* __restrict__ Wf, const uint8_t* __restrict__ codes_p,
              const int32_t* __restrict__ invperm, int64_t n, int64_t nq, float* __restrict__ w_hat,
-             uint8_t* __restrict__ codes_out) {
+             uint8_t* __restrict__ codes_out, int vec) {
   extern __shared__ __align__(16) float frow[];
   uint8_t* crow = reinterpret_cast<uint8_t*>(frow + n);
   const int64_t r = blockIdx.x;
+  if (vec) {
+    // n % 4 == 0, nq % 16 == 0 and 16-byte aligned rows: 16-byte loads, four
+    // gathered values per store
+    if (w_hat)
+      for (int64_t k = threadIdx.x; k < n / 4; k += 256)
+        reinterpret_cast<float4*>(frow)[k] = reinterpret_cast<const float4*>(Wf + r * n)[k];
+    if (codes_out)
+      for (int64_t k = threadIdx.x; k < nq / 16; k += 256)
+        reinterpret_cast<uint4*>(crow)[k] = reinterpret_cast<const uint4*>(codes_p + r * nq)[k];
+    __syncthreads();
+    for (int64_t k0 = 4 * (int64_t)threadIdx.x; k0 < n; k0 += 1024) {
+      const int4 pv = *reinterpret_cast<const int4*>(invperm + k0);
+      if (w_hat)
+        *reinterpret_cast<float4*>(w_hat + r * n + k0) = make_float4(frow[pv.x], frow[pv.y], frow[pv.z], frow[pv.w]);
+      if (codes_out && k0 < nq)
+        *reinterpret_cast<uchar4*>(codes_out + r * nq + k0) = make_uchar4(crow[pv.x], crow[pv.y], crow[pv.z], crow[pv.w]);
+    }
+    return;
+  }
   if (w_hat)
     for (int64_t k = threadIdx.x; k < n; k += 256) frow[k] = Wf[r * n + k];
   if (codes_out)
@@ -170,9 +189,11 @@ hipError_t launch_finish(hipStream_t s, const float* Wf, const uint8_t* codes_p,
                          const int32_t* invperm, int64_t d_out, int64_t n, int64_t n_quant,
                          int group, float* w_hat, uint8_t* codes_out, int32_t* g_idx) {
   const size_t lds = (size_t)n * sizeof(float) + (size_t)n_quant;
+  const int vec = n % 4 == 0 && n_quant % 16 == 0 && ((uintptr_t)Wf & 15) == 0 && ((uintptr_t)codes_p & 15) == 0 &&
+                  ((uintptr_t)invperm & 15) == 0 && ((uintptr_t)w_hat & 15) == 0 && ((uintptr_t)codes_out & 3) == 0;
   if (d_out > 0 && (w_hat || codes_out) && lds <= 65536)
     hipLaunchKernelGGL(k_finish_lds, dim3((unsigned)d_out), dim3(256), lds, s, Wf, codes_p, invperm, n,
-                       n_quant, w_hat, codes_out);
+                       n_quant, w_hat, codes_out, vec);
   else if (d_out > 0 && (w_hat || codes_out))
     hipLaunchKernelGGL(k_finish, dim3((unsigned)d_out), dim3(256), 0, s, Wf, codes_p, invperm, n,
                        n_quant, w_hat, codes_out);

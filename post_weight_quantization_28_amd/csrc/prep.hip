@@ -214,13 +214,52 @@ constexpr int64_t kRowLdsMax = 16384;
 __global__ void __launch_bounds__(256)
 k_build_flipped_lds(const float* __restrict__ H, int64_t n, const int32_t* __restrict__ perm,
                     const float* __restrict__ diag, const double* __restrict__ lam,
-                    float* __restrict__ A, DevStatus* st) {
+                    float* __restrict__ A, DevStatus* st, int vec) {
   extern __shared__ __align__(16) float hrow[];
   const int64_t a = blockIdx.x;
   const int64_t p = perm[n - 1 - a];
   const float lamf = (float)lam[0];
-  for (int64_t c = threadIdx.x; c < n; c += 256) hrow[c] = H[p * n + c];
+  if (vec) {
+    // n % 4 == 0 and 16-byte aligned rows: 16-byte loads and stores
+    const float4* src = reinterpret_cast<const float4*>(H + p * n);
+    for (int64_t c = threadIdx.x; c < n / 4; c += 256) reinterpret_cast<float4*>(hrow)[c] = src[c];
+  } else {
+    for (int64_t c = threadIdx.x; c < n; c += 256) hrow[c] = H[p * n + c];
+  }
   __syncthreads();
+  if (vec) {
+    // four consecutive b per thread; the group that holds the diagonal (and
+    // the columns past it, which are not stored) goes element by element
+    for (int64_t b0 = 4 * (int64_t)threadIdx.x; b0 <= a; b0 += 1024) {
+      // perm[n-4-b0 .. n-1-b0] holds q for b0+3, b0+2, b0+1, b0
+      const int4 qv = *reinterpret_cast<const int4*>(perm + (n - 4 - b0));
+      const int64_t q[4] = {qv.w, qv.z, qv.y, qv.x};
+      if (b0 + 3 < a) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          v[e] = hrow[q[e]];
+          if (!isfinite(v[e])) raise_status(st, kNonFinite, min(p, q[e]));
+        }
+        *reinterpret_cast<float4*>(A + a * n + b0) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t b = b0 + e;
+          if (b > a) break;
+          float v;
+          if (b == a) {
+            v = diag[p] + lamf;
+          } else {
+            v = hrow[q[e]];
+            if (!isfinite(v)) raise_status(st, kNonFinite, min(p, q[e]));
+          }
+          A[a * n + b] = v;
+        }
+      }
+    }
+    return;
+  }
   for (int64_t b = threadIdx.x; b <= a; b += 256) {
     const int64_t q = perm[n - 1 - b];
     float v;
@@ -236,9 +275,11 @@ k_build_flipped_lds(const float* __restrict__ H, int64_t n, const int32_t* __res
 
 hipError_t launch_build_flipped(hipStream_t s, const float* H, int64_t n, const int32_t* perm,
                                 const float* diag, const double* lam, float* A, DevStatus* st) {
-  if (perm && n <= kRowLdsMax)
+  if (perm && n <= kRowLdsMax) {
+    const int vec = n % 4 == 0 && ((uintptr_t)H & 15) == 0 && ((uintptr_t)A & 15) == 0 && ((uintptr_t)perm & 15) == 0;
     hipLaunchKernelGGL(k_build_flipped_lds, dim3((unsigned)n), dim3(256), (size_t)n * sizeof(float), s, H, n,
-                       perm, diag, lam, A, st);
+                       perm, diag, lam, A, st, vec);
+  }
   else
     hipLaunchKernelGGL(k_build_flipped, dim3((unsigned)n), dim3(256), 0, s, H, n, perm, diag, lam, A, st);
   return hipGetLastError();
@@ -300,9 +341,41 @@ k_w_prep(const void* __restrict__ Wv, int64_t n, int64_t ldw, const int32_t* __r
 template <bool kBF16>
 __global__ void __launch_bounds__(256)
 k_w_prep_lds(const void* __restrict__ Wv, int64_t n, int64_t ldw, const int32_t* __restrict__ perm,
-             float* __restrict__ Wf, DevStatus* st) {
+             float* __restrict__ Wf, DevStatus* st, int vec) {
   extern __shared__ __align__(16) float wrow[];
   const int64_t r = blockIdx.x;
+  if (vec) {
+    // n % 8 == 0, ldw % 8 == 0 and 16-byte aligned rows: 16-byte loads of
+    // the row, four gathered values per 16-byte store
+    if (kBF16) {
+      const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(Wv) + r * ldw);
+      for (int64_t c = threadIdx.x; c < n / 8; c += 256) {
+        const uint4 u = src[c];
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+        float4* d = reinterpret_cast<float4*>(wrow + 8 * c);
+        d[0] = make_float4(__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xFFFF0000u),
+                           __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xFFFF0000u));
+        d[1] = make_float4(__uint_as_float(w[2] << 16), __uint_as_float(w[2] & 0xFFFF0000u),
+                           __uint_as_float(w[3] << 16), __uint_as_float(w[3] & 0xFFFF0000u));
+      }
+    } else {
+      const float4* src = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(Wv) + r * ldw);
+      for (int64_t c = threadIdx.x; c < n / 4; c += 256) reinterpret_cast<float4*>(wrow)[c] = src[c];
+    }
+    __syncthreads();
+    for (int64_t q0 = 4 * (int64_t)threadIdx.x; q0 < n; q0 += 1024) {
+      const int4 cv = *reinterpret_cast<const int4*>(perm + q0);
+      const int64_t c[4] = {cv.x, cv.y, cv.z, cv.w};
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e] = wrow[c[e]];
+        if (!isfinite(v[e])) raise_status(st, kNonFinite, c[e]);
+      }
+      *reinterpret_cast<float4*>(Wf + r * n + q0) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+    return;
+  }
   for (int64_t c = threadIdx.x; c < n; c += 256) {
     if (kBF16) {
       const uint16_t u = reinterpret_cast<const uint16_t*>(Wv)[r * ldw + c];
@@ -326,10 +399,12 @@ hipError_t launch_w_prep(hipStream_t s, const void* W, int wdt_bf16, int64_t d_o
   dim3 grid((unsigned)d_out);
   if (perm && n <= kRowLdsMax) {
     const size_t lds = (size_t)n * sizeof(float);
+    const int vec = n % 8 == 0 && ldw % 8 == 0 && ((uintptr_t)W & 15) == 0 && ((uintptr_t)Wf & 15) == 0 &&
+                    ((uintptr_t)perm & 15) == 0;
     if (wdt_bf16)
-      hipLaunchKernelGGL(k_w_prep_lds<true>, grid, dim3(256), lds, s, W, n, ldw, perm, Wf, st);
+      hipLaunchKernelGGL(k_w_prep_lds<true>, grid, dim3(256), lds, s, W, n, ldw, perm, Wf, st, vec);
     else
-      hipLaunchKernelGGL(k_w_prep_lds<false>, grid, dim3(256), lds, s, W, n, ldw, perm, Wf, st);
+      hipLaunchKernelGGL(k_w_prep_lds<false>, grid, dim3(256), lds, s, W, n, ldw, perm, Wf, st, vec);
     return hipGetLastError();
   }
   if (wdt_bf16)
