@@ -280,53 +280,59 @@ __host__ __device__ int64_t x6_op_elems(int64_t rows, int64_t K) { return 3 * ce
 struct Split6Args {
   const float* src; int64_t ld, stride;
   int64_t R, K;
-  int trans, vec, batch;
+  int trans, batch;
   uint16_t* dst;
 };
 
-// Thread q takes 4 consecutive k of one row of one instance. Untransposed
-// sources are walked as k_split3 walks them (4 threads per row, 16-byte
-// loads when rows are 16-byte aligned); transposed ones with the row index
-// fastest, so that each of a thread's four loads is one consecutive run of
-// the source across the wave.
+// A workgroup takes one (instance, 128-row block, 16-deep k slice) item at
+// a time, 512 groups of 4 consecutive k, two per thread (the index
+// arithmetic is done once per item, in 32 bits). Untransposed sources are
+// walked as k_split3 walks them (4 threads per row, 16-byte loads when rows
+// are 16-byte aligned); transposed ones with the row index fastest, so that
+// each of a thread's four loads is one consecutive run of the source across
+// the wave.
+template <bool TRANS, bool VEC>
 __global__ void __launch_bounds__(256) k_split3_op(Split6Args a) {
-  const int64_t nst = ceil_div(a.K, kS6K);
-  const int64_t per = ceil_div(a.R, kS6T) * nst * 512;
-  const int64_t total = per * a.batch;
+  const int nst = (int)ceil_div(a.K, kS6K);
+  const int nrb = (int)ceil_div(a.R, kS6T);
+  const int per = nrb * nst;                       // items per instance
+  const int items = per * a.batch;
   const int64_t out_per = x6_op_elems(a.R, a.K);
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < total; q += stride) {
-    const int64_t b = q / per, rem = q - b * per;
-    const int64_t blk = rem >> 9;
-    const int w = (int)(rem & 511);
-    const int64_t tr = blk / nst, stg = blk - tr * nst;
-    const int rr = a.trans ? (w & 127) : (w >> 2);
-    const int kg = a.trans ? (w >> 7) : (w & 3);
-    const int64_t r = tr * kS6T + rr, k = stg * kS6K + 4 * kg;
-    const float* src = a.src + b * a.stride;
-    float x[4];
-    if (!a.trans && a.vec && r < a.R && k + 3 < a.K) {
-      const float4 v = *reinterpret_cast<const float4*>(src + r * a.ld + k);
-      x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
-    } else {
+  for (int it = blockIdx.x; it < items; it += gridDim.x) {
+    const int b = it / per, blk = it - b * per;
+    const int tr = blk / nst, stg = blk - tr * nst;
+    const float* src = a.src + (int64_t)b * a.stride;
+    uint16_t* dblk = a.dst + (int64_t)b * out_per + (int64_t)blk * 3 * 2048;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      const int w = (int)threadIdx.x + 256 * half;
+      const int rr = TRANS ? (w & 127) : (w >> 2);
+      const int kg = TRANS ? (w >> 7) : (w & 3);
+      const int64_t r = (int64_t)tr * kS6T + rr, k = (int64_t)stg * kS6K + 4 * kg;
+      float x[4];
+      if (VEC && r < a.R && k + 3 < a.K) {
+        const float4 v = *reinterpret_cast<const float4*>(src + r * a.ld + k);
+        x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t kk = k + e;
+          x[e] = (r < a.R && kk < a.K) ? (TRANS ? src[kk * a.ld + r] : src[r * a.ld + kk]) : 0.f;
+        }
+      }
+      uint16_t h1[4], h2[4], h3[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int64_t kk = k + e;
-        x[e] = (r < a.R && kk < a.K) ? (a.trans ? src[kk * a.ld + r] : src[r * a.ld + kk]) : 0.f;
+        h1[e] = f32_to_bf16_rne(x[e]);
+        const float r1 = x[e] - bf16_to_f32(h1[e]);
+        h2[e] = f32_to_bf16_rne(r1);
+        h3[e] = f32_to_bf16_rne(r1 - bf16_to_f32(h2[e]));
       }
+      uint16_t* d = dblk + rr * kS6K + 4 * kg;
+      *reinterpret_cast<uint2*>(d) = make_uint2(h1[0] | ((uint32_t)h1[1] << 16), h1[2] | ((uint32_t)h1[3] << 16));
+      *reinterpret_cast<uint2*>(d + 2048) = make_uint2(h2[0] | ((uint32_t)h2[1] << 16), h2[2] | ((uint32_t)h2[3] << 16));
+      *reinterpret_cast<uint2*>(d + 4096) = make_uint2(h3[0] | ((uint32_t)h3[1] << 16), h3[2] | ((uint32_t)h3[3] << 16));
     }
-    uint16_t h1[4], h2[4], h3[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      h1[e] = f32_to_bf16_rne(x[e]);
-      const float r1 = x[e] - bf16_to_f32(h1[e]);
-      h2[e] = f32_to_bf16_rne(r1);
-      h3[e] = f32_to_bf16_rne(r1 - bf16_to_f32(h2[e]));
-    }
-    uint16_t* d = a.dst + b * out_per + blk * 3 * 2048 + rr * kS6K + 4 * kg;
-    *reinterpret_cast<uint2*>(d) = make_uint2(h1[0] | ((uint32_t)h1[1] << 16), h1[2] | ((uint32_t)h1[3] << 16));
-    *reinterpret_cast<uint2*>(d + 2048) = make_uint2(h2[0] | ((uint32_t)h2[1] << 16), h2[2] | ((uint32_t)h2[3] << 16));
-    *reinterpret_cast<uint2*>(d + 4096) = make_uint2(h3[0] | ((uint32_t)h3[1] << 16), h3[2] | ((uint32_t)h3[3] << 16));
   }
 }
 
@@ -463,10 +469,13 @@ static hipError_t split_op(hipStream_t s, const X6Operand& o, int64_t R, int64_t
   Split6Args a{};
   a.src = o.src; a.ld = o.ld; a.stride = o.stride;
   a.R = R; a.K = K; a.trans = o.trans; a.batch = batch; a.dst = dst;
-  a.vec = !o.trans && o.ld % 4 == 0 && o.stride % 4 == 0 && ((uintptr_t)o.src & 15) == 0;
-  int64_t blocks = ceil_div(ceil_div(R, kS6T) * ceil_div(K, kS6K) * 512 * batch, 256);
-  if (blocks > 16384) blocks = 16384;
-  hipLaunchKernelGGL(k_split3_op, dim3((unsigned)blocks), dim3(256), 0, s, a);
+  const bool vec = !o.trans && o.ld % 4 == 0 && o.stride % 4 == 0 && ((uintptr_t)o.src & 15) == 0;
+  const int64_t items = ceil_div(R, kS6T) * ceil_div(K, kS6K) * batch;   // one per workgroup iteration
+  if (items >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+  const unsigned blocks = (unsigned)std::min<int64_t>(items, 16384);
+  if (o.trans) hipLaunchKernelGGL((k_split3_op<true, false>), dim3(blocks), dim3(256), 0, s, a);
+  else if (vec) hipLaunchKernelGGL((k_split3_op<false, true>), dim3(blocks), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_split3_op<false, false>), dim3(blocks), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
