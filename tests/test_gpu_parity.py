@@ -71,8 +71,11 @@ def test_hessian_streaming_accumulates():
 # on the six-product bf16 kernels: the pair of 4096-row blocks, and the
 # partial pair of 8192 and 2054 rows (k not a multiple of 16, rows not a
 # multiple of 128); the last panel has 6 columns
+# n = 12388: one level mixes the two kinds (the pair of 4096-row blocks on
+# the six-product kernels, the partial pair of 4096 and 100 rows on fp32)
 @pytest.mark.parametrize("n,act_order", [(64, False), (200, False), (202, False), (320, True), (1000, False),
-                                         (4096, False), (6208, False), (6150, True), (10246, True)])
+                                         (4096, False), (6208, False), (6150, True), (10246, True),
+                                         (12388, False)])
 def test_factor_matches_lapack(n, act_order):
     wl = synth.make_workload("c2", d_out=4, n=n, T=4 * n if n <= 6208 else n + 512, group=4)
     H64 = O.hessian(wl.X)
